@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-KV decode path on one MI355X.
+
+One step = one decode step of the streaming hot path on one layer cache: append one
+float16 K/V token per sequence (flushing the residual window into the 2/4-bit store
+when it is full), then decode attention of the new query over all cached tokens.
+Steps rotate over ``copies`` independent layer caches (like the layers of a model)
+whose total size exceeds the 256 MB last-level cache, so that each step reads its
+cache from HBM.  Inputs are resident in HBM before timing starts.
+
+Printed (one JSON line): value = algorithmic bytes of the timed steps / wall time
+(GB/s), tokens/s, the decode kernel's roofline against the HBM peak, measured with
+HIP events on the launch stream, the CPU oracle's throughput on a bounded sample,
+and the output quality against unquantized fp32 attention (reported, not gated).
+
+Algorithmic bytes of a decode launch, per (sequence, KV head): packed codes
+T_q*d*b/8 for K and for V, float16 scale+zero 4*d per Key group and 4*(d/G_v) per
+token, the float16 residual 2*2*r*d, plus q (2*d per query head) and out (4*d per
+query head).  An append adds the new rows (2*2*d read, 2*2*d written) and, when it
+flushes, the window read (2*2*R*d) and its codes and scales written.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "quantized-KV decode attention: effective HBM GB/s & % of peak; tokens/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20
+
+
+def decode_bytes(w, T):
+    """Algorithmic bytes of one decode launch at T cached tokens (see module doc)."""
+    R = w.residual
+    r = 0 if T == 0 else (T - 1) % R + 1
+    Tq = T - r
+    d = w.head_dim
+    per_pair = (2 * Tq * d * w.bits // 8            # K and V codes
+                + (Tq // w.group_k) * d * 4         # K scale + zero
+                + Tq * (d // w.group_v) * 4         # V scale + zero
+                + 2 * r * d * 2)                    # float16 residual K and V
+    pairs = w.batch * w.kv_heads
+    return pairs * per_pair + w.batch * w.q_heads * d * (2 + 4)
+
+
+def append_bytes(w, T_before):
+    R = w.residual
+    d = w.head_dim
+    pairs = w.batch * w.kv_heads
+    rows = pairs * 2 * d * 2 * 2                    # k_new, v_new read; residual row written
+    r = 0 if T_before == 0 else (T_before - 1) % R + 1
+    if r == R:                                      # flush the window
+        codes = 2 * R * d * w.bits // 8
+        meta = (R // w.group_k) * d * 4 + R * (d // w.group_v) * 4
+        rows += pairs * (2 * R * d * 2 + codes + meta)
+    return rows
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama8b_32k")
+    p.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0: auto)")
+    p.add_argument("--n-split", type=int, default=0, help="token splits (0: library default)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
+    return p.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 2 ** 30 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)        # one elementwise kernel: reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": 2 ** 30, "bytes_written": 2 ** 30,
+                      "launches": 5}), flush=True)
+
+
+def cpu_baseline(w, host_pairs, budget_s):
+    """Time the CPU oracle's decode step (append + attend) on a bounded sample.
+
+    A few (sequence, KV head) pairs of the workload are prefilled (untimed); then
+    consecutive decode steps (append the next token, attend over the cache) run
+    round-robin over those pairs until ``budget_s`` seconds of oracle time are used.
+    """
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    one = w.replace(batch=1, kv_heads=1, q_heads=w.gqa)
+    caches = []
+    for (Kh, Vh, k_rows, v_rows, qh, T) in host_pairs:
+        m = math.lcm(16, w.group_k, w.residual)
+        cap = (T + len(k_rows) + 1 + m - 1) // m * m
+        oc = O.LayerCache(1, 1, w.head_dim, w.bits, w.group_k, w.group_v, w.residual, cap)
+        oc.prefill(Kh, Vh)
+        caches.append((oc, k_rows, v_rows, qh))
+    done_bytes, t_used, steps, T_last = 0, 0.0, 0, 0
+    j = 0
+    while t_used < budget_s:
+        oc, k_rows, v_rows, qh = caches[steps % len(caches)]
+        j = steps // len(caches)
+        if j >= len(k_rows):
+            break
+        T = oc.T
+        t0 = time.perf_counter()
+        oc.append(k_rows[j][None, None], v_rows[j][None, None])
+        oc.attend(qh, w.sm_scale)
+        t_used += time.perf_counter() - t0
+        done_bytes += decode_bytes(one, T + 1) + append_bytes(one, T)
+        steps += 1
+        T_last = T + 1
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{steps} oracle decode steps (append + attend, {w.gqa} query heads, "
+                       f"~{T_last} tokens) round-robin over {len(caches)} (sequence, KV head) "
+                       f"pairs of the workload, {t_used:.1f} s of oracle time; "
+                       f"os.cpu_count()={os.cpu_count()}, BLAS threads={threads}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
+              f"multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from bit_quantization_amd import kivi as k
+
+    torch.cuda.set_device(0)
+    w = W.get(args.workload)
+    if w.layers != 1:
+        # multi-layer workload: every layer is one cache of the rotation
+        w1 = w.replace(layers=1)
+    else:
+        w1 = w
+    total_steps = args.steps + args.warmup
+    per_copy_bytes = decode_bytes(w1, w1.tokens)
+    copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy_bytes))
+    if w.layers > 1:
+        copies = args.copies or min(w.layers, max(copies, 2))
+    steps_per_copy = math.ceil(total_steps / copies) + 1
+    extra_rows = max(steps_per_copy, 1024)          # rows appended on the GPU / by the oracle
+    Tmax = w1.replace(stream_steps=steps_per_copy).max_tokens()
+    dims = k.Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, w1.bits, w1.group_k,
+                  w1.group_v, w1.residual, Tmax)
+    print(f"[bench] workload {w.name}: {copies} layer caches x {per_copy_bytes / 1e6:.1f} MB "
+          f"decode reads, {args.warmup}+{args.steps} steps", file=sys.stderr, flush=True)
+
+    caches, Ts, news = [], [], []
+    keep = None
+    host_pairs = []
+    rng = np.random.default_rng(0)
+    sample_pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, w1.batch, 64),
+                                                      rng.integers(0, w1.kv_heads, 64))]
+    for c in range(copies):
+        K, V = W.make_kv(w1, c, device="cuda", total_tokens=w1.tokens + extra_rows)
+        cache = k.Cache(dims)
+        k.kivi_quantize_k(dims, cache, 0, K, w1.tokens, K.shape[2])
+        k.kivi_quantize_v(dims, cache, 0, V, w1.tokens, V.shape[2])
+        caches.append(cache)
+        Ts.append(w1.tokens)
+        # new rows per step, [steps, B, H, d] so that each step's rows are contiguous
+        news.append((K[:, :, w1.tokens:w1.tokens + steps_per_copy].permute(2, 0, 1, 3).contiguous(),
+                     V[:, :, w1.tokens:w1.tokens + steps_per_copy].permute(2, 0, 1, 3).contiguous()))
+        if c == 0:
+            keep = (K, V)
+            if not args.no_cpu_baseline:
+                q0 = W.make_q(w1, 0, 0, device="cuda").cpu().numpy()
+                g = w1.gqa
+                for (b, h) in sample_pairs[:6]:
+                    host_pairs.append((K[b:b + 1, h:h + 1, :w1.tokens].cpu().numpy(),
+                                       V[b:b + 1, h:h + 1, :w1.tokens].cpu().numpy(),
+                                       K[b, h, w1.tokens:].cpu().numpy(),
+                                       V[b, h, w1.tokens:].cpu().numpy(),
+                                       q0[b:b + 1, h * g:(h + 1) * g], w1.tokens))
+        else:
+            del K, V
+    qs = [W.make_q(w1, 0, s, device="cuda") for s in range(8)]
+    out = torch.empty((w1.batch, w1.q_heads, w1.head_dim), dtype=torch.float32, device="cuda")
+    ws = k.new_workspace(dims, Tmax, args.n_split)
+    n_split = args.n_split or k.kivi_decode_splits(dims, w1.tokens)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, record=None):
+        c = i % copies
+        T_before = Ts[c]
+        j = T_before - w1.tokens
+        kn, vn = news[c]
+        k.kivi_append_flush(dims, caches[c], 0, T_before, kn[j], vn[j])
+        T = T_before + 1
+        if record is not None:
+            record[0].record(stream)
+        k.kivi_decode_attn(dims, caches[c], 0, T, qs[i % len(qs)], w1.sm_scale, out, ws,
+                           n_split=args.n_split)
+        if record is not None:
+            record[1].record(stream)
+        Ts[c] = T
+        return decode_bytes(w1, T), append_bytes(w1, T_before)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    dec_bytes = 0
+    app_bytes = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        db, ab = step(args.warmup + i, events[i])
+        dec_bytes += db
+        app_bytes += ab
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    dec_ms = [a.elapsed_time(b) for a, b in events]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    dec_med_s = sorted(dec_ms)[len(dec_ms) // 2] / 1e3
+    dec_per_launch = dec_bytes / args.steps
+
+    # Quality versus unquantized fp32 attention on copy 0 (reported, not gated).
+    K, V = keep
+    Tq = Ts[0]
+    qq = qs[0]
+    k.kivi_decode_attn(dims, caches[0], 0, Tq, qq, w1.sm_scale, out, ws, n_split=args.n_split)
+    g = w1.gqa
+    Kf = K[:, :, :Tq].float()
+    Vf = V[:, :, :Tq].float()
+    qf = qq.float().view(w1.batch, w1.kv_heads, g, w1.head_dim)
+    logits = torch.matmul(qf, Kf.transpose(-1, -2).contiguous()) * float(np.float32(w1.sm_scale))
+    ref = torch.matmul(torch.softmax(logits, dim=-1), Vf).view_as(out)
+    o = out.double()
+    rd = ref.double()
+    quality = {"vs": "unquantized fp32 attention on the same float16 K/V",
+               "rel_l2": float((o - rd).norm() / rd.norm()),
+               "cosine": float(torch.nn.functional.cosine_similarity(o.flatten(), rd.flatten(),
+                                                                     dim=0)),
+               "max_abs": float((o - rd).abs().max())}
+    del K, V, Kf, Vf, keep
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w1, host_pairs, args.cpu_seconds)
+
+    total_bytes = dec_bytes + app_bytes
+    value = total_bytes / wall / 1e9
+    achieved = dec_per_launch / dec_avg_s / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/Q with x50 Key outlier channels and x100 Value "
+                "outlier tokens; no dataset or weights)",
+        "config": {"workload": w.name, "batch": w1.batch, "kv_heads": w1.kv_heads,
+                   "q_heads": w1.q_heads, "head_dim": w1.head_dim, "tokens": w1.tokens,
+                   "bits": w1.bits, "group_k": w1.group_k, "group_v": w1.group_v,
+                   "residual": w1.residual, "layer_caches": copies, "n_split": n_split,
+                   "step": "append(+flush) + decode attention"},
+        "tokens_per_s": round(w1.batch * args.steps / wall, 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "kivi_decode_attn (split-K + merge)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": int(dec_per_launch),
+                     "avg_launch_us": round(dec_avg_s * 1e6, 3),
+                     "median_launch_us": round(dec_med_s * 1e6, 3),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "quality": quality,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

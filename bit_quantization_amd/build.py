@@ -1,0 +1,60 @@
+"""Build the HIP library ``libkivi.so`` in-tree for gfx950 with hipcc.
+
+Every source under ``csrc/`` is compiled into one shared library next to this file.
+Run as ``python -m bit_quantization_amd.build``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+LIB = os.path.join(HERE, "libkivi.so")
+
+SOURCES = ["kivi_api.cpp", "quantize.hip", "decode.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # keep packed float32 instructions out of generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE float32 division/sqrt (the quantizer's arithmetic is bit-exact by contract)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Wall",
+    "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found; the HIP toolchain is required to build libkivi.so")
+    return exe
+
+
+def build_library(verbose: bool = True) -> str:
+    srcs = []
+    for name in SOURCES:
+        src = os.path.join(CSRC, name)
+        # hipcc compiles .cpp sources as host C++; the API file launches through
+        # launchers defined in the .hip sources, so it needs only the HIP headers.
+        srcs += ["-x", "hip", src] if name.endswith(".hip") else ["-x", "hip", src]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    if verbose:
+        print("[build]", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build_library()
+    sys.exit(0)

@@ -1,0 +1,298 @@
+// C ABI entry points: argument validation, per-layer views, launches.
+// Nothing is enqueued unless every check passes; no C++ exception crosses the ABI.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+#include "../../include/kivi.h"
+#include "kivi_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kivi_status fail(kivi_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kivi_status ok() {
+  g_err[0] = '\0';
+  return KIVI_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_one_of(int v, std::initializer_list<int> set) {
+  for (int x : set)
+    if (v == x) return true;
+  return false;
+}
+
+kivi_status check_dims(const kivi_dims* d) {
+  if (!d) return fail(KIVI_ERR_ARG, "dims is NULL");
+  if (d->layers < 1 || d->batch < 1 || d->kv_heads < 1 || d->q_heads < 1)
+    return fail(KIVI_ERR_ARG, "layers, batch, kv_heads and q_heads must be >= 1");
+  if ((int64_t)d->batch * d->kv_heads > 65535)
+    return fail(KIVI_ERR_UNSUPPORTED, "batch * kv_heads = %lld exceeds 65535",
+                (long long)d->batch * d->kv_heads);
+  if (d->q_heads % d->kv_heads != 0)
+    return fail(KIVI_ERR_ARG, "q_heads (%d) is not a multiple of kv_heads (%d)", d->q_heads,
+                d->kv_heads);
+  if (!is_one_of(d->q_heads / d->kv_heads, {1, 2, 4, 8}))
+    return fail(KIVI_ERR_UNSUPPORTED, "q_heads / kv_heads = %d; supported: 1, 2, 4, 8",
+                d->q_heads / d->kv_heads);
+  if (d->bits != 2 && d->bits != 4)
+    return fail(KIVI_ERR_UNSUPPORTED, "bits = %d; supported: 2, 4", d->bits);
+  if (d->head_dim != kivi::kHeadDim)
+    return fail(KIVI_ERR_UNSUPPORTED, "head_dim = %d; supported: %d", d->head_dim,
+                kivi::kHeadDim);
+  if (!is_one_of(d->group_k, {16, 32, 64}))
+    return fail(KIVI_ERR_UNSUPPORTED, "group_k = %d; supported: 16, 32, 64", d->group_k);
+  if (d->group_v < 1 || d->head_dim % d->group_v != 0)
+    return fail(KIVI_ERR_ARG, "group_v = %d does not divide head_dim = %d", d->group_v,
+                d->head_dim);
+  if (!is_one_of(d->group_v, {16, 32, 64, 128}))
+    return fail(KIVI_ERR_UNSUPPORTED, "group_v = %d; supported: 16, 32, 64, 128", d->group_v);
+  if (d->residual < 1 || d->residual % d->group_k != 0 || d->residual % kivi::kVRun != 0)
+    return fail(KIVI_ERR_ARG, "residual = %d must be a positive multiple of group_k (%d) and 16",
+                d->residual, d->group_k);
+  if (d->reserved != 0) return fail(KIVI_ERR_ARG, "dims.reserved must be 0");
+  if (d->max_tokens < 1 || d->max_tokens % d->group_k != 0 || d->max_tokens % kivi::kVRun != 0)
+    return fail(KIVI_ERR_ARG, "max_tokens = %lld must be a positive multiple of group_k and 16",
+                (long long)d->max_tokens);
+  return KIVI_OK;
+}
+
+void buffer_sizes(const kivi_dims* d, size_t out[KIVI_NUM_BUFFERS]) {
+  const size_t unit = (size_t)d->layers * d->batch * d->kv_heads;
+  const size_t T = (size_t)d->max_tokens;
+  const size_t codes = unit * T * d->head_dim * d->bits / 8;
+  const size_t kmeta = unit * (T / d->group_k) * d->head_dim * 2;
+  const size_t vmeta = unit * T * (d->head_dim / d->group_v) * 2;
+  const size_t resid = unit * d->residual * d->head_dim * 2;
+  out[0] = codes;
+  out[1] = kmeta;
+  out[2] = kmeta;
+  out[3] = codes;
+  out[4] = vmeta;
+  out[5] = vmeta;
+  out[6] = resid;
+  out[7] = resid;
+}
+
+kivi_status check_cache(const kivi_cache* c) {
+  if (!c) return fail(KIVI_ERR_ARG, "cache is NULL");
+  const void* p[8] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes,
+                      c->v_scale, c->v_zero,  c->k_resid, c->v_resid};
+  static const char* names[8] = {"k_codes", "k_scale", "k_zero", "v_codes",
+                                 "v_scale", "v_zero",  "k_resid", "v_resid"};
+  for (int i = 0; i < 8; ++i) {
+    if (!p[i]) return fail(KIVI_ERR_ARG, "cache.%s is NULL", names[i]);
+    if (!aligned16(p[i])) return fail(KIVI_ERR_ALIGN, "cache.%s is not 16-byte aligned", names[i]);
+  }
+  return KIVI_OK;
+}
+
+kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer) {
+  size_t sz[KIVI_NUM_BUFFERS];
+  buffer_sizes(d, sz);
+  kivi::LayerView L;
+  const size_t Ld = (size_t)d->layers;
+  L.k_codes = static_cast<uint8_t*>(c->k_codes) + layer * (sz[0] / Ld);
+  L.k_scale = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->k_scale) + layer * (sz[1] / Ld));
+  L.k_zero = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->k_zero) + layer * (sz[2] / Ld));
+  L.v_codes = static_cast<uint8_t*>(c->v_codes) + layer * (sz[3] / Ld);
+  L.v_scale = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->v_scale) + layer * (sz[4] / Ld));
+  L.v_zero = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->v_zero) + layer * (sz[5] / Ld));
+  L.k_resid = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->k_resid) + layer * (sz[6] / Ld));
+  L.v_resid = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->v_resid) + layer * (sz[7] / Ld));
+  L.B = d->batch;
+  L.H = d->kv_heads;
+  L.d = d->head_dim;
+  L.bits = d->bits;
+  L.G = d->group_k;
+  L.Gv = d->group_v;
+  L.R = d->residual;
+  L.Tmax = d->max_tokens;
+  return L;
+}
+
+kivi_status check_common(const kivi_dims* d, const kivi_cache* c, int32_t layer) {
+  kivi_status st = check_dims(d);
+  if (st != KIVI_OK) return st;
+  st = check_cache(c);
+  if (st != KIVI_OK) return st;
+  if (layer < 0 || layer >= d->layers)
+    return fail(KIVI_ERR_ARG, "layer = %d outside [0, %d)", layer, d->layers);
+  return KIVI_OK;
+}
+
+kivi_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KIVI_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                            const void* x, int64_t T, int64_t ld, void* stream, bool keys) {
+  kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  if (T < 0) return fail(KIVI_ERR_ARG, "T = %lld is negative", (long long)T);
+  if (T > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T = %lld exceeds max_tokens = %lld", (long long)T,
+                (long long)dims->max_tokens);
+  if (ld < T) return fail(KIVI_ERR_ARG, "ld_tokens = %lld < T = %lld", (long long)ld, (long long)T);
+  if (T == 0) return ok();
+  if (!x) return fail(KIVI_ERR_ARG, "%s input is NULL", keys ? "key" : "value");
+  if (!aligned16(x)) return fail(KIVI_ERR_ALIGN, "%s input is not 16-byte aligned", keys ? "key" : "value");
+  const kivi::LayerView L = layer_view(dims, cache, layer);
+  hipError_t e = keys ? kivi::launch_quantize_k(L, static_cast<const __half*>(x), ld, T,
+                                                static_cast<hipStream_t>(stream))
+                      : kivi::launch_quantize_v(L, static_cast<const __half*>(x), ld, T,
+                                                static_cast<hipStream_t>(stream));
+  return device_status(e, keys ? "kivi_quantize_k launch" : "kivi_quantize_v launch");
+}
+
+kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                          int64_t T, const void* q, float sm_scale, float* out, void* ws,
+                          size_t ws_bytes, int32_t n_split, void* stream) {
+  kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  if (dims->group_v != dims->head_dim)
+    return fail(KIVI_ERR_UNSUPPORTED, "decode requires group_v == head_dim (got %d)",
+                dims->group_v);
+  if (dims->group_k % 32 != 0)
+    return fail(KIVI_ERR_UNSUPPORTED, "decode requires group_k in {32, 64} (got %d)",
+                dims->group_k);
+  if (T < 1) return fail(KIVI_ERR_ARG, "T = %lld must be >= 1", (long long)T);
+  if (T > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T = %lld exceeds max_tokens = %lld", (long long)T,
+                (long long)dims->max_tokens);
+  if (n_split < 0) return fail(KIVI_ERR_ARG, "n_split = %d is negative", n_split);
+  if (!q || !out) return fail(KIVI_ERR_ARG, "q or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(KIVI_ERR_ALIGN, "q or out is not 16-byte aligned");
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(KIVI_ERR_ARG, "sm_scale is not finite");
+  const kivi::LayerView L = layer_view(dims, cache, layer);
+  const kivi::DecodePlan plan = kivi::plan_decode(L, dims->q_heads, T, n_split);
+  if (!ws) return fail(KIVI_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(ws)) return fail(KIVI_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < plan.ws_total)
+    return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, plan.ws_total);
+  hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
+                                     out, ws, plan, static_cast<hipStream_t>(stream));
+  return device_status(e, "kivi_decode_attn launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_cache_sizes(const kivi_dims* dims, size_t bytes[KIVI_NUM_BUFFERS]) {
+  kivi_status st = check_dims(dims);
+  if (st != KIVI_OK) return st;
+  if (!bytes) return fail(KIVI_ERR_ARG, "bytes is NULL");
+  buffer_sizes(dims, bytes);
+  return ok();
+}
+
+kivi_status kivi_quantize_k(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                            const void* k, int64_t T, int64_t ld_tokens, void* stream) {
+  return quantize_common(dims, cache, layer, k, T, ld_tokens, stream, true);
+}
+
+kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                            const void* v, int64_t T, int64_t ld_tokens, void* stream) {
+  return quantize_common(dims, cache, layer, v, T, ld_tokens, stream, false);
+}
+
+kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                              int64_t T_before, const void* k_new, const void* v_new,
+                              void* stream) {
+  kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  if (T_before < 0) return fail(KIVI_ERR_ARG, "T_before = %lld is negative", (long long)T_before);
+  if (T_before + 1 > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T_before + 1 = %lld exceeds max_tokens = %lld",
+                (long long)(T_before + 1), (long long)dims->max_tokens);
+  if (!k_new || !v_new) return fail(KIVI_ERR_ARG, "k_new or v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(KIVI_ERR_ALIGN, "k_new or v_new is not 16-byte aligned");
+  const kivi::LayerView L = layer_view(dims, cache, layer);
+  hipError_t e = kivi::launch_append_flush(L, T_before, static_cast<const __half*>(k_new),
+                                           static_cast<const __half*>(v_new),
+                                           static_cast<hipStream_t>(stream));
+  return device_status(e, "kivi_append_flush launch");
+}
+
+kivi_status kivi_decode_workspace_bytes_split(const kivi_dims* dims, int64_t T, int32_t n_split,
+                                              size_t* bytes) {
+  kivi_status st = check_dims(dims);
+  if (st != KIVI_OK) return st;
+  if (!bytes) return fail(KIVI_ERR_ARG, "bytes is NULL");
+  if (T < 1 || T > dims->max_tokens)
+    return fail(T < 1 ? KIVI_ERR_ARG : KIVI_ERR_CAPACITY, "T = %lld outside [1, max_tokens]",
+                (long long)T);
+  if (n_split < 0) return fail(KIVI_ERR_ARG, "n_split = %d is negative", n_split);
+  kivi::LayerView L{};
+  L.B = dims->batch;
+  L.H = dims->kv_heads;
+  L.d = dims->head_dim;
+  L.bits = dims->bits;
+  L.G = dims->group_k;
+  L.Gv = dims->group_v;
+  L.R = dims->residual;
+  L.Tmax = dims->max_tokens;
+  *bytes = kivi::plan_decode(L, dims->q_heads, T, n_split).ws_total;
+  return ok();
+}
+
+kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t* bytes) {
+  return kivi_decode_workspace_bytes_split(dims, T, 0, bytes);
+}
+
+kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_split) {
+  kivi_status st = check_dims(dims);
+  if (st != KIVI_OK) return st;
+  if (!n_split) return fail(KIVI_ERR_ARG, "n_split is NULL");
+  if (T < 1 || T > dims->max_tokens)
+    return fail(T < 1 ? KIVI_ERR_ARG : KIVI_ERR_CAPACITY, "T = %lld outside [1, max_tokens]",
+                (long long)T);
+  kivi::LayerView L{};
+  L.B = dims->batch;
+  L.H = dims->kv_heads;
+  L.d = dims->head_dim;
+  L.bits = dims->bits;
+  L.G = dims->group_k;
+  L.Gv = dims->group_v;
+  L.R = dims->residual;
+  L.Tmax = dims->max_tokens;
+  *n_split = kivi::plan_decode(L, dims->q_heads, T, 0).n_split;
+  return ok();
+}
+
+kivi_status kivi_decode_attn(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                             int64_t T, const void* q, float sm_scale, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(dims, cache, layer, T, q, sm_scale, out, workspace, workspace_bytes, 0,
+                       stream);
+}
+
+kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cache,
+                                   int32_t layer, int64_t T, const void* q, float sm_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   int32_t n_split, void* stream) {
+  return decode_common(dims, cache, layer, T, q, sm_scale, out, workspace, workspace_bytes,
+                       n_split, stream);
+}
+
+const char* kivi_last_error(void) { return g_err; }
+
+int32_t kivi_abi_version(void) { return 1; }
+
+}  // extern "C"

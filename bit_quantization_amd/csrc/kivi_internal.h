@@ -1,0 +1,64 @@
+// Internal declarations shared by the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kivi {
+
+constexpr int kHeadDim = 128;   // head_dim this build's kernels are written for
+constexpr int kVRun = 16;       // tokens per packed Value run
+
+// Device pointers of one layer, already offset to that layer, plus the dims.
+struct LayerView {
+  uint8_t* k_codes;   // [B][H][Tmax][d*b/8]
+  __half* k_scale;    // [B][H][Tmax/G][d]
+  __half* k_zero;
+  uint8_t* v_codes;   // [B][H][Tmax/16][d][16*b/8]
+  __half* v_scale;    // [B][H][Tmax][d/Gv]
+  __half* v_zero;
+  __half* k_resid;    // [B][H][R][d]
+  __half* v_resid;
+  int B, H, d, bits, G, Gv, R;
+  int64_t Tmax;
+
+  // Per-(b, h) element strides of each buffer.
+  __host__ __device__ int64_t kc_pair() const { return Tmax * (d * bits / 8); }
+  __host__ __device__ int64_t ks_pair() const { return (Tmax / G) * d; }
+  __host__ __device__ int64_t vc_pair() const { return Tmax * (d * bits / 8); }
+  __host__ __device__ int64_t vs_pair() const { return Tmax * (d / Gv); }
+  __host__ __device__ int64_t rs_pair() const { return (int64_t)R * d; }
+};
+
+inline int64_t residual_len(int64_t T, int R) { return T == 0 ? 0 : (T - 1) % R + 1; }
+inline int64_t quantized_len(int64_t T, int R) { return T - residual_len(T, R); }
+
+// ---- launchers (return hipGetLastError() of the launch) -------------------------
+
+// Prefill: quantize tokens [0, Tq) of src ([B][H][ld][d]) and copy [Tq, T) to the
+// residual rows [0, T - Tq).
+hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
+                             hipStream_t s);
+hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
+                             hipStream_t s);
+
+// Append one row; flush the full window first when r(T_before) == R.
+hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __half* k_new,
+                               const __half* v_new, hipStream_t s);
+
+// Decode attention: split-K partials + fixed-order merge.
+struct DecodePlan {
+  int n_split;          // token splits per (b, kv head)
+  int64_t n_groups;     // quantized Key groups per (b, kv head)
+  int r;                // residual tokens
+  size_t ws_partials;   // bytes of partial results
+  size_t ws_counters;   // bytes of arrival counters (zero between calls)
+  size_t ws_total;
+};
+DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_req);
+hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __half* q,
+                         float sm_scale, float* out, void* ws, const DecodePlan& plan,
+                         hipStream_t s);
+
+}  // namespace kivi

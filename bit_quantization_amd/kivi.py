@@ -1,0 +1,230 @@
+"""Python binding of ``libkivi.so`` (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks that tensors live on the GPU with the expected
+dtype and contiguity, passes their device pointers and the current HIP stream, and
+turns a non-OK status into an exception carrying ``kivi_last_error()``.  PyTorch
+provides device memory and streams only.
+
+If the library is missing, importing this module raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkivi.so")
+
+STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_ERR_CAPACITY",
+          4: "KIVI_ERR_ALIGN", 5: "KIVI_ERR_WORKSPACE", 6: "KIVI_ERR_DEVICE"}
+
+EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
+           "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
+           "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
+           "kivi_abi_version")
+
+
+class KiviError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class kivi_dims(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group_k", ctypes.c_int32), ("group_v", ctypes.c_int32),
+                ("residual", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64)]
+
+
+BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
+
+
+class kivi_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with `python -m bit_quantization_amd.build` "
+                          f"(the HIP path has no fallback)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    D, C = ctypes.POINTER(kivi_dims), ctypes.POINTER(kivi_cache)
+    sig = {
+        "kivi_cache_sizes": (I32, [D, ctypes.POINTER(SZ)]),
+        "kivi_quantize_k": (I32, [D, C, I32, P, I64, I64, P]),
+        "kivi_quantize_v": (I32, [D, C, I32, P, I64, I64, P]),
+        "kivi_append_flush": (I32, [D, C, I32, I64, P, P, P]),
+        "kivi_decode_workspace_bytes": (I32, [D, I64, ctypes.POINTER(SZ)]),
+        "kivi_decode_workspace_bytes_split": (I32, [D, I64, I32, ctypes.POINTER(SZ)]),
+        "kivi_decode_splits": (I32, [D, I64, ctypes.POINTER(I32)]),
+        "kivi_decode_attn": (I32, [D, C, I32, I64, P, F32, P, P, SZ, P]),
+        "kivi_decode_attn_split": (I32, [D, C, I32, I64, P, F32, P, P, SZ, I32, P]),
+        "kivi_last_error": (ctypes.c_char_p, []),
+        "kivi_abi_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+
+
+def _check(status: int):
+    if status != 0:
+        raise KiviError(status, _lib.kivi_last_error().decode())
+
+
+def _ptr(t, dtype, name, numel=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library works on device memory)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Dims:
+    layers: int
+    batch: int
+    kv_heads: int
+    q_heads: int
+    head_dim: int
+    bits: int
+    group_k: int
+    group_v: int
+    residual: int
+    max_tokens: int
+
+    def c(self) -> kivi_dims:
+        return kivi_dims(self.layers, self.batch, self.kv_heads, self.q_heads, self.head_dim,
+                         self.bits, self.group_k, self.group_v, self.residual, 0,
+                         self.max_tokens)
+
+
+def kivi_cache_sizes(dims: Dims):
+    out = (ctypes.c_size_t * 8)()
+    _check(_lib.kivi_cache_sizes(ctypes.byref(dims.c()), out))
+    return list(out)
+
+
+class Cache:
+    """The eight caller-owned device buffers of a cache, allocated with torch."""
+
+    def __init__(self, dims: Dims, device="cuda"):
+        self.dims = dims
+        sizes = kivi_cache_sizes(dims)
+        self.buffers = {}
+        for name, nbytes in zip(BUFFERS, sizes):
+            self.buffers[name] = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+    def c(self) -> kivi_cache:
+        return kivi_cache(*[self.buffers[n].data_ptr() for n in BUFFERS])
+
+    # typed views (for reading results back)
+    def view(self, name: str):
+        d = self.dims
+        L, B, H, T, D = d.layers, d.batch, d.kv_heads, d.max_tokens, d.head_dim
+        buf = self.buffers[name]
+        if name == "k_codes":
+            return buf.view(L, B, H, T, D * d.bits // 8)
+        if name in ("k_scale", "k_zero"):
+            return buf.view(torch.float16).view(L, B, H, T // d.group_k, D)
+        if name == "v_codes":
+            return buf.view(L, B, H, T // 16, D, 16 * d.bits // 8)
+        if name in ("v_scale", "v_zero"):
+            return buf.view(torch.float16).view(L, B, H, T, D // d.group_v)
+        if name in ("k_resid", "v_resid"):
+            return buf.view(torch.float16).view(L, B, H, d.residual, D)
+        raise KeyError(name)
+
+
+def kivi_quantize_k(dims: Dims, cache: Cache, layer: int, k: torch.Tensor, T: int,
+                    ld_tokens: int | None = None, stream=None):
+    ld = T if ld_tokens is None else ld_tokens
+    need = dims.batch * dims.kv_heads * ld * dims.head_dim if T else None
+    _check(_lib.kivi_quantize_k(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                _ptr(k, torch.float16, "k", need), T, ld, _stream(stream)))
+
+
+def kivi_quantize_v(dims: Dims, cache: Cache, layer: int, v: torch.Tensor, T: int,
+                    ld_tokens: int | None = None, stream=None):
+    ld = T if ld_tokens is None else ld_tokens
+    need = dims.batch * dims.kv_heads * ld * dims.head_dim if T else None
+    _check(_lib.kivi_quantize_v(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                _ptr(v, torch.float16, "v", need), T, ld, _stream(stream)))
+
+
+def kivi_append_flush(dims: Dims, cache: Cache, layer: int, T_before: int, k_new, v_new,
+                      stream=None):
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    _check(_lib.kivi_append_flush(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                  T_before, _ptr(k_new, torch.float16, "k_new", need),
+                                  _ptr(v_new, torch.float16, "v_new", need), _stream(stream)))
+
+
+def kivi_decode_workspace_bytes(dims: Dims, T: int, n_split: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.kivi_decode_workspace_bytes_split(ctypes.byref(dims.c()), T, n_split,
+                                                  ctypes.byref(n)))
+    return n.value
+
+
+def kivi_decode_splits(dims: Dims, T: int) -> int:
+    n = ctypes.c_int32()
+    _check(_lib.kivi_decode_splits(ctypes.byref(dims.c()), T, ctypes.byref(n)))
+    return n.value
+
+
+def new_workspace(dims: Dims, T: int, n_split: int = 0, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (the contract asks for zeros before first use)."""
+    return torch.zeros(kivi_decode_workspace_bytes(dims, T, n_split), dtype=torch.uint8,
+                       device=device)
+
+
+def kivi_decode_attn(dims: Dims, cache: Cache, layer: int, T: int, q: torch.Tensor,
+                     sm_scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                     n_split: int = 0, stream=None):
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    qp = _ptr(q, torch.float16, "q", nq)
+    op = _ptr(out, torch.float32, "out", nq)
+    wp = _ptr(workspace, torch.uint8, "workspace")
+    wb = workspace.numel()
+    if n_split:
+        st = _lib.kivi_decode_attn_split(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                         T, qp, ctypes.c_float(sm_scale), op, wp, wb, n_split,
+                                         _stream(stream))
+    else:
+        st = _lib.kivi_decode_attn(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, T,
+                                   qp, ctypes.c_float(sm_scale), op, wp, wb, _stream(stream))
+    _check(st)
+
+
+def kivi_abi_version() -> int:
+    return int(_lib.kivi_abi_version())

@@ -1,0 +1,198 @@
+/*
+ * kivi.h — C ABI of the MI355X (gfx950) KIVI-style quantized KV cache.
+ *
+ * Keys are quantized per channel over groups of G consecutive tokens and Values per
+ * token over groups of G_v consecutive channels, each group to 2 or 4 bits with an
+ * asymmetric min/max float16 scale and zero.  The most recent tokens stay in a
+ * float16 residual window that is flushed into the quantized store when it is full.
+ * Decode attention reads the packed cache directly.
+ *
+ * Sources (page titles; sections):
+ *   "KV Cache Quantization (KIVI & FP4): How 2-Bit Key-Value Compression Scales LLM
+ *    Contexts to 1 Million Tokens" — §3 (per-channel Keys, per-token Values, FP16
+ *    residual window), §4 (four 2-bit codes per byte, dequantization fused into the
+ *    attention kernel), §6 (prefill stays high precision, then a streaming pass
+ *    stores low-bit codes).
+ *   "09 — KV Cache Quantization" — "KIVI — the reference paper" (fp16 scale and zero
+ *    per channel, int2/int4 storage, residual buffer), "Per-channel vs per-token in
+ *    the actual attention kernel" (dequantize inside the attention tile loop, never
+ *    into a full fp16 buffer).
+ *   "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache" — "The streaming
+ *    complication" (complete groups quantized once and frozen).
+ *   "4.4 KV Cache quantization" — §1 (M_KV = 2 L B T H_KV d b and its arguments),
+ *    §3.1 (the two grouping directions, min/max asymmetric mapping inside a group),
+ *    §3.2 (residual cache joins attention and is moved into the history in a batch).
+ *   "KV Cache INT4 Quantization for 1M+ Token Context Windows" — §2 (unsigned codes
+ *    in [0, 2^b - 1], scale from the group range, two 4-bit codes per byte).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All cache buffers, inputs and outputs are DEVICE pointers owned by the caller.
+ *    The library never allocates or frees device memory and keeps no state between
+ *    calls except a thread-local error message.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *    returns without synchronizing.  Buffers must stay valid until the stream has
+ *    passed the enqueued work.  Calls are reentrant; calls that write the same cache
+ *    layer must be ordered by the caller (same stream or events).
+ *  - Arguments are validated before anything is enqueued.  On any status other than
+ *    KIVI_OK nothing was enqueued (except KIVI_ERR_DEVICE, returned when the HIP
+ *    runtime rejected a launch) and kivi_last_error() describes the problem.
+ *  - Device pointers must be 16-byte aligned.  Inputs must be finite.
+ *  - Index arithmetic is 64-bit; a layer may hold more than 4 GiB.
+ *
+ * Cache layout (every buffer has a leading [layers] dimension; all row-major):
+ *    k_codes  uint8   [L][B][H_kv][T_max][d*b/8]       per token, channels packed
+ *    k_scale  float16 [L][B][H_kv][T_max/G][d]         per (Key group, channel)
+ *    k_zero   float16 [L][B][H_kv][T_max/G][d]
+ *    v_codes  uint8   [L][B][H_kv][T_max/16][d][2*b]   per channel, runs of 16 tokens
+ *    v_scale  float16 [L][B][H_kv][T_max][d/G_v]       per (token, Value group)
+ *    v_zero   float16 [L][B][H_kv][T_max][d/G_v]
+ *    k_resid  float16 [L][B][H_kv][R][d]               residual window rows
+ *    v_resid  float16 [L][B][H_kv][R][d]
+ *  Codes are packed LSB-first: code j of a packed run sits at bits
+ *  [b*(j mod (8/b)), b*(j mod (8/b)) + b) of byte j / (8/b).
+ *
+ * Quantizer (per group of float16 values x_i; float32 arithmetic, IEEE division,
+ * round-half-to-even):  x_i += 0 (so -0 becomes +0);  mn = min x_i;  mx = max x_i;
+ *  scale = float16_rne((mx - mn) / (2^b - 1));  zero = float16(mn) (exact);
+ *  s = float(scale);  code_i = s == 0 ? 0 : clamp(rint((x_i - mn) / s), 0, 2^b - 1).
+ *  Dequantized value: code * scale + zero.
+ *
+ * Residual window: after T tokens it holds r(T) = T == 0 ? 0 : ((T - 1) mod R) + 1
+ * tokens and the quantized history holds T_q(T) = T - r(T) tokens.  Appending when
+ * r == R first quantizes the R window rows into the history at token T - R, then
+ * stores the new token in row 0.  Prefill of T tokens gives the same bytes as T
+ * appends.  All sequences of a batch share T.
+ *
+ * Grouped-query attention: query head j reads KV head j / (H_q / H_kv).
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kivi_status {
+  KIVI_OK = 0,
+  KIVI_ERR_ARG = 1,          /* a bad argument (null pointer, bad layer, bad sizes) */
+  KIVI_ERR_UNSUPPORTED = 2,  /* a valid configuration this build has no kernel for */
+  KIVI_ERR_CAPACITY = 3,     /* the token count does not fit max_tokens */
+  KIVI_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned */
+  KIVI_ERR_WORKSPACE = 5,    /* the decode workspace is null or too small */
+  KIVI_ERR_DEVICE = 6        /* the HIP runtime rejected a launch */
+} kivi_status;
+
+/* Problem statement of one cache ("4.4 KV Cache quantization" §1 and §3: layers,
+ * batch, KV heads, head_dim, bits, group size, residual length). */
+typedef struct kivi_dims {
+  int32_t layers;      /* L >= 1 */
+  int32_t batch;       /* B >= 1 */
+  int32_t kv_heads;    /* H_kv >= 1 */
+  int32_t q_heads;     /* H_q, a multiple of H_kv with H_q / H_kv in {1, 2, 4, 8} */
+  int32_t head_dim;    /* d; this build supports 128 */
+  int32_t bits;        /* b in {2, 4} */
+  int32_t group_k;     /* G: tokens per Key group, in {16, 32, 64} */
+  int32_t group_v;     /* G_v: channels per Value group, divides d, in {16, 32, 64, 128} */
+  int32_t residual;    /* R: residual window, a multiple of G and of 16 */
+  int32_t reserved;    /* must be 0 */
+  int64_t max_tokens;  /* T_max: token capacity per sequence, a multiple of G and 16 */
+} kivi_dims;
+
+/* The eight device buffers of a cache; layout above. */
+typedef struct kivi_cache {
+  void* k_codes;
+  void* k_scale;
+  void* k_zero;
+  void* v_codes;
+  void* v_scale;
+  void* v_zero;
+  void* k_resid;
+  void* v_resid;
+} kivi_cache;
+
+#define KIVI_NUM_BUFFERS 8
+
+/* Byte size of each of the eight buffers, in kivi_cache field order, for all
+ * layers.  Host-only; enqueues nothing. */
+kivi_status kivi_cache_sizes(const kivi_dims* dims, size_t bytes[KIVI_NUM_BUFFERS]);
+
+/* Prefill quantization of the Keys of one layer ("4.4 KV Cache quantization" §3.1:
+ * fix a channel, group consecutive tokens; "KV Cache Quantization (KIVI & FP4)" §6:
+ * quantize the prompt's cache after prefill).
+ *   k      float16 [B][H_kv][ld_tokens][d] device; tokens [0, T) are read.
+ *   T      prompt length, 0 <= T <= T_max.
+ *   ld     token stride of `k` (>= T).
+ * Quantizes tokens [0, T_q(T)) into k_codes/k_scale/k_zero of `layer` and copies
+ * tokens [T_q(T), T) into rows [0, r(T)) of k_resid. */
+kivi_status kivi_quantize_k(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                            const void* k, int64_t T, int64_t ld_tokens, void* stream);
+
+/* Prefill quantization of the Values of one layer ("4.4 KV Cache quantization" §3.1:
+ * fix a token, group along channels).  Same arguments as kivi_quantize_k, writing
+ * v_codes/v_scale/v_zero and v_resid. */
+kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                            const void* v, int64_t T, int64_t ld_tokens, void* stream);
+
+/* Append one decode token per sequence to one layer ("KIVI: A Tuning-Free ...", "The
+ * streaming complication"; "4.4 KV Cache quantization" §3.2).
+ *   T_before   tokens cached before this call (0 <= T_before, T_before + 1 <= T_max).
+ *   k_new, v_new  float16 [B][H_kv][d] device.
+ * If r(T_before) == R the window is first quantized into the history at token
+ * T_before - R (same arithmetic as the prefill calls); the new row then goes to row
+ * r(T_before) mod R.  The cache then holds T_before + 1 tokens. */
+kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                              int64_t T_before, const void* k_new, const void* v_new,
+                              void* stream);
+
+/* Workspace bytes kivi_decode_attn needs for T cached tokens (host-only). */
+kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t* bytes);
+
+/* Decode attention over the quantized cache of one layer, dequantizing inside the
+ * kernel ("09 — KV Cache Quantization", "Per-channel vs per-token in the actual
+ * attention kernel"; "KV Cache Quantization (KIVI & FP4)" §2 and §4):
+ *   out[b][j][:] = softmax_t(sm_scale * q[b][j] . k_t) v_t over the T cached tokens of
+ *   sequence b and KV head j / (H_q / H_kv); k_t, v_t are dequantized codes for the
+ *   T_q(T) history tokens and the float16 window rows for the last r(T).
+ *   q          float16 [B][H_q][d] device.
+ *   out        float32 [B][H_q][d] device.
+ *   T          1 <= T <= T_max.
+ *   workspace  device scratch of at least kivi_decode_workspace_bytes(dims, T) bytes,
+ *              private to the library.  Zero-fill it once before its first use; it
+ *              can then be reused by later calls without clearing.  Calls that may
+ *              run concurrently must use distinct workspaces.
+ * The result is deterministic: partial results of the token splits are combined in
+ * a fixed order and no floating-point atomics are used.
+ * Value groups: this build's decode kernels require G_v == d (UNSUPPORTED otherwise). */
+kivi_status kivi_decode_attn(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                             int64_t T, const void* q, float sm_scale, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* As kivi_decode_attn with an explicit number of token splits per (sequence, KV
+ * head) (0 = the library's choice).  Splits beyond the number of Key groups are
+ * clamped.  Workspace size: kivi_decode_workspace_bytes_split. */
+kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cache,
+                                   int32_t layer, int64_t T, const void* q, float sm_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   int32_t n_split, void* stream);
+kivi_status kivi_decode_workspace_bytes_split(const kivi_dims* dims, int64_t T,
+                                              int32_t n_split, size_t* bytes);
+
+/* Number of token splits kivi_decode_attn uses for T tokens (host-only). */
+kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_split);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none).
+ * Valid until the next kivi_* call on the same thread. */
+const char* kivi_last_error(void);
+
+/* ABI version of this library (bumped on any incompatible change). */
+int32_t kivi_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H */

@@ -1,0 +1,165 @@
+"""The C ABI without a GPU: the library loads, exports what include/kivi.h declares,
+sizes buffers as documented, and rejects every bad argument before launching.
+
+No test here ever reaches a launch: each call fails validation first, so fake
+(aligned, never dereferenced) pointers are safe.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+kv = pytest.importorskip("bit_quantization_amd.kivi")
+
+HEADER = os.path.join(ROOT, "include", "kivi.h")
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:kivi_status|const char\*|int32_t)\s+(kivi_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
+            "kivi_decode_attn"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", kv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kivi_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(kv.EXPORTS) == set(names)
+
+
+def test_abi_version():
+    assert kv.kivi_abi_version() == 1
+
+
+def good_dims(**kw):
+    d = dict(layers=2, batch=3, kv_heads=2, q_heads=8, head_dim=128, bits=2, group_k=32,
+             group_v=128, residual=64, max_tokens=512)
+    d.update(kw)
+    return kv.Dims(**d)
+
+
+def fake_cache(**overrides):
+    ptrs = {n: FAKE + 0x1000000 * i for i, n in enumerate(kv.BUFFERS)}
+    ptrs.update(overrides)
+    return kv.kivi_cache(*[ptrs[n] for n in kv.BUFFERS])
+
+
+def call(fn, *args):
+    st = getattr(kv._lib, fn)(*args)
+    return st, kv._lib.kivi_last_error().decode()
+
+
+def test_cache_sizes_follow_the_documented_layout():
+    d = good_dims(bits=4, group_v=64)
+    sizes = kv.kivi_cache_sizes(d)
+    unit = d.layers * d.batch * d.kv_heads
+    codes = unit * d.max_tokens * d.head_dim * d.bits // 8
+    assert sizes == [codes, unit * (d.max_tokens // 32) * 128 * 2, unit * (d.max_tokens // 32) * 128 * 2,
+                     codes, unit * d.max_tokens * 2 * 2, unit * d.max_tokens * 2 * 2,
+                     unit * 64 * 128 * 2, unit * 64 * 128 * 2]
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("bits", 3, 2), ("bits", 8, 2), ("head_dim", 64, 2), ("group_k", 48, 2),
+    ("group_v", 48, 1), ("group_v", 8, 2), ("residual", 40, 1), ("residual", 0, 1),
+    ("q_heads", 7, 1), ("q_heads", 32, 2), ("max_tokens", 100, 1), ("layers", 0, 1),
+    ("batch", 0, 1), ("kv_heads", 0, 1),
+])
+def test_bad_dims_are_rejected(field, value, status):
+    d = good_dims(**{field: value})
+    sizes = (ctypes.c_size_t * 8)()
+    st, msg = call("kivi_cache_sizes", ctypes.byref(d.c()), sizes)
+    assert st == status and msg
+    st, msg = call("kivi_quantize_k", ctypes.byref(d.c()), ctypes.byref(fake_cache()), 0, FAKE,
+                   16, 16, None)
+    assert st == status and msg
+
+
+def test_reserved_field_must_be_zero():
+    c = good_dims().c()
+    c.reserved = 1
+    st, _ = call("kivi_quantize_v", ctypes.byref(c), ctypes.byref(fake_cache()), 0, FAKE, 16, 16,
+                 None)
+    assert st == 1
+
+
+def test_null_and_misaligned_pointers():
+    d = good_dims().c()
+    st, msg = call("kivi_quantize_k", ctypes.byref(d), ctypes.byref(fake_cache(k_scale=0)), 0,
+                   FAKE, 16, 16, None)
+    assert st == 1 and "k_scale" in msg
+    st, msg = call("kivi_quantize_k", ctypes.byref(d), ctypes.byref(fake_cache(v_resid=FAKE + 8)),
+                   0, FAKE, 16, 16, None)
+    assert st == 4 and "v_resid" in msg
+    st, _ = call("kivi_quantize_k", ctypes.byref(d), ctypes.byref(fake_cache()), 0, None, 16, 16,
+                 None)
+    assert st == 1
+    st, _ = call("kivi_quantize_k", ctypes.byref(d), ctypes.byref(fake_cache()), 0, FAKE + 2, 16,
+                 16, None)
+    assert st == 4
+    st, _ = call("kivi_append_flush", ctypes.byref(d), ctypes.byref(fake_cache()), 0, 5, FAKE,
+                 FAKE + 4, None)
+    assert st == 4
+    st, _ = call("kivi_cache_sizes", None, (ctypes.c_size_t * 8)())
+    assert st == 1
+    st, _ = call("kivi_quantize_k", ctypes.byref(d), None, 0, FAKE, 16, 16, None)
+    assert st == 1
+
+
+def test_layer_token_and_capacity_checks():
+    d = good_dims().c()
+    c = ctypes.byref(fake_cache())
+    assert call("kivi_quantize_k", ctypes.byref(d), c, 2, FAKE, 16, 16, None)[0] == 1
+    assert call("kivi_quantize_k", ctypes.byref(d), c, -1, FAKE, 16, 16, None)[0] == 1
+    assert call("kivi_quantize_k", ctypes.byref(d), c, 0, FAKE, 513, 513, None)[0] == 3
+    assert call("kivi_quantize_k", ctypes.byref(d), c, 0, FAKE, 16, 8, None)[0] == 1
+    assert call("kivi_quantize_k", ctypes.byref(d), c, 0, FAKE, -1, 0, None)[0] == 1
+    assert call("kivi_append_flush", ctypes.byref(d), c, 0, 512, FAKE, FAKE, None)[0] == 3
+    assert call("kivi_append_flush", ctypes.byref(d), c, 0, -1, FAKE, FAKE, None)[0] == 1
+    # T == 0 quantizes nothing and succeeds without touching the GPU
+    assert call("kivi_quantize_k", ctypes.byref(d), c, 0, None, 0, 0, None)[0] == 0
+
+
+def test_decode_argument_checks():
+    d = good_dims()
+    dc = d.c()
+    c = ctypes.byref(fake_cache())
+    need = kv.kivi_decode_workspace_bytes(d, 300)
+    assert need > 0
+    args = lambda T, q, out, ws, wsb: (ctypes.byref(dc), c, 0, T, q, ctypes.c_float(0.1), out,
+                                       ws, wsb, None)
+    assert call("kivi_decode_attn", *args(0, FAKE, FAKE, FAKE, need))[0] == 1
+    assert call("kivi_decode_attn", *args(513, FAKE, FAKE, FAKE, need))[0] == 3
+    assert call("kivi_decode_attn", *args(300, None, FAKE, FAKE, need))[0] == 1
+    assert call("kivi_decode_attn", *args(300, FAKE, FAKE + 4, FAKE, need))[0] == 4
+    assert call("kivi_decode_attn", *args(300, FAKE, FAKE, None, need))[0] == 5
+    assert call("kivi_decode_attn", *args(300, FAKE, FAKE, FAKE, need - 1))[0] == 5
+    bad = ctypes.byref(dc), c, 0, 300, FAKE, ctypes.c_float(float("nan")), FAKE, FAKE, need, None
+    assert call("kivi_decode_attn", *bad)[0] == 1
+    # decode kernels need G_v == d and G in {32, 64}
+    d2 = good_dims(group_v=64).c()
+    assert call("kivi_decode_attn", ctypes.byref(d2), c, 0, 300, FAKE, ctypes.c_float(0.1), FAKE,
+                FAKE, need, None)[0] == 2
+    d3 = good_dims(group_k=16).c()
+    assert call("kivi_decode_attn", ctypes.byref(d3), c, 0, 300, FAKE, ctypes.c_float(0.1), FAKE,
+                FAKE, need, None)[0] == 2
+
+
+def test_split_plan_is_clamped_and_workspace_grows_with_splits():
+    d = good_dims()
+    assert 1 <= kv.kivi_decode_splits(d, 300) <= (300 - 44) // 32 + 1
+    assert kv.kivi_decode_splits(d, 10) == 1          # no quantized group yet
+    a = kv.kivi_decode_workspace_bytes(d, 448, 1)
+    b = kv.kivi_decode_workspace_bytes(d, 448, 4)
+    assert b > a
+    assert kv.kivi_decode_workspace_bytes(d, 448, 1000) == kv.kivi_decode_workspace_bytes(d, 448, 12)

@@ -55,6 +55,7 @@ class Workload:
     residual: int            # R: fp16 residual window
     k_outlier_channels: int = 4
     k_outlier_scale: float = 50.0
+    v_outlier_scale: float = 100.0
     v_outlier_frac: float = 0.01    # fraction of tokens with outlier Values
     v_outlier_count: Optional[int] = None  # fixed count instead of a fraction
     v_outlier_include_token0: bool = True
