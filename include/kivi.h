@@ -171,9 +171,11 @@ kivi_status kivi_decode_attn(const kivi_dims* dims, const kivi_cache* cache, int
                              int64_t T, const void* q, float sm_scale, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* As kivi_decode_attn with an explicit number of token splits per (sequence, KV
- * head) (0 = the library's choice).  Splits beyond the number of Key groups are
- * clamped.  Workspace size: kivi_decode_workspace_bytes_split. */
+/* As kivi_decode_attn with an explicit number of workgroups over the quantized
+ * history of each (sequence, KV head) (0 = the library's choice).  The history is
+ * cut into 64-token blocks and the count is clamped to the number of blocks; the
+ * float16 window always gets one workgroup of its own.  Workspace size:
+ * kivi_decode_workspace_bytes_split. */
 kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cache,
                                    int32_t layer, int64_t T, const void* q, float sm_scale,
                                    float* out, void* workspace, size_t workspace_bytes,
@@ -181,7 +183,8 @@ kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cach
 kivi_status kivi_decode_workspace_bytes_split(const kivi_dims* dims, int64_t T,
                                               int32_t n_split, size_t* bytes);
 
-/* Number of token splits kivi_decode_attn uses for T tokens (host-only). */
+/* Number of workgroups over the quantized history kivi_decode_attn uses for T
+ * tokens (0 when nothing is quantized yet; host-only). */
 kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_split);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none).

@@ -157,8 +157,10 @@ def test_decode_argument_checks():
 
 def test_split_plan_is_clamped_and_workspace_grows_with_splits():
     d = good_dims()
-    assert 1 <= kv.kivi_decode_splits(d, 300) <= (300 - 44) // 32 + 1
-    assert kv.kivi_decode_splits(d, 10) == 1          # no quantized group yet
+    # splits cover the quantized history in 64-token blocks; the fp16 window has its
+    # own workgroup
+    assert 1 <= kv.kivi_decode_splits(d, 300) <= (300 - 44 + 63) // 64
+    assert kv.kivi_decode_splits(d, 10) == 0          # nothing quantized yet
     a = kv.kivi_decode_workspace_bytes(d, 448, 1)
     b = kv.kivi_decode_workspace_bytes(d, 448, 4)
     assert b > a
