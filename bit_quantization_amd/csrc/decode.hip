@@ -63,8 +63,8 @@ struct DecodeArgs {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                            0xF, true));
 }
 // Reductions over the 16 lanes of a DPP row (rotations stay inside the row).
 __device__ __forceinline__ float row_max16(float x) {
@@ -86,11 +86,22 @@ __device__ __forceinline__ float wave_max(float x) {
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
   return x;
 }
+// LDS hand-off between lanes of one wave: LDS operations of a wave execute in order,
+// so only the compiler must be kept from moving LDS accesses across this point; the
+// wait covers LDS (lgkm) only and leaves prefetched global loads in flight.
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
+// Partials are exchanged between workgroups with system-scope relaxed stores/loads,
+// which write through / bypass the per-XCD L2, so no L2 write-back fence is needed.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+// Wait until this thread's global stores have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ float h2f(unsigned short h) {
   return __half2float(__ushort_as_half(h));
 }
@@ -150,61 +161,363 @@ __device__ __forceinline__ i32x4 unpack16(uint32_t w0, uint32_t w1) {
   return u;
 }
 
-// Per-wave LDS of the quantized path.
+// Per-wave LDS of the quantized path.  The query-limb operand of one (group, M-tile,
+// K-step) is 16 rows of 4 lane-group blocks of 16 bytes; rows are padded to 80 bytes
+// and K-steps to 1344 bytes so that the 16-bit limb writes of the group preparation hit
+// at most two lanes per bank and the 16-byte operand reads of 8 lanes are conflict-free.
+constexpr int QA_ROW = 80;                 // bytes per operand row (64 used)
+constexpr int QA_KS = 16 * QA_ROW + 64;    // bytes per K-step block
 template <int NMT>
 struct WaveLds {
-  uint8_t qa[2][NMT][2][16][4][16];   // [group in block][M-tile][K-step][row][lane grp][pos]
+  uint8_t qa[2][NMT][2][QA_KS];       // [group in block][M-tile][K-step][row*QA_ROW + jg*16 + pos]
   uint8_t pa[NMT][16][4][16];         // [M-tile][row][run][pos]
 };
 
 // ---- the quantized token range of one wave ----------------------------------------
+
+// Global-memory inputs of one 64-token block for one lane (loaded a block ahead).
+template <int BITS>
+struct BlockRegs {
+  static constexpr int KW = BITS == 2 ? 2 : 4;    // Key-code words per token per lane
+  static constexpr int VW = BITS == 2 ? 8 : 16;   // Value-code words per lane
+  uint32_t k[4][KW];        // N-tile nt: token tb + 16nt + lo, channels 32j .. 32j+31
+  uint32_t v[VW];           // run j of the block, channels 8lo .. 8lo+7
+  i32x4 ks[2], kz[2];       // Key scale/zero of the block's groups, channels 8lo .. 8lo+7
+  unsigned short sv[4], zv[4];   // token tb + 16nt + lo: Value scale and zero
+};
+
+// Buffer descriptors of one (sequence, KV head) pair's slabs, and the lane offsets
+// that stay fixed from block to block (the block base goes in the scalar offset).
+struct PairBufs {
+  __amdgpu_buffer_rsrc_t kc, ksc, kze, vc, vsc, vze;
+  int off_k, off_v, off_ks, off_sv;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes < 0x7FFFFFFF ? (int)bytes : 0x7FFFFFFF;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// FULL: all 64 tokens of the block are in the history (compile-time: no branches).
+template <int BITS, int G, bool FULL>
+__device__ __forceinline__ void load_block(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
+                                           int n_valid, int j) {
+  constexpr int KB = D * BITS / 8;
+  constexpr int RB = kVRun * BITS / 8;
+  const int n_tiles = FULL ? 4 : n_valid / 16;
+  const int sk = (int)(tb * KB);
+  const int ssv = (int)(tb * 2);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    if (FULL || nt < n_tiles) {
+      if constexpr (BITS == 2) {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
+        R.k[nt][0] = (uint32_t)u[0];
+        R.k[nt][1] = (uint32_t)u[1];
+      } else {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) R.k[nt][w] = (uint32_t)u[w];
+      }
+      R.sv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vsc, pb.off_sv + 32 * nt, ssv, 0);
+      R.zv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vze, pb.off_sv + 32 * nt, ssv, 0);
+    } else {
+#pragma unroll
+      for (int w = 0; w < BlockRegs<BITS>::KW; ++w) R.k[nt][w] = 0u;
+      R.sv[nt] = 0;
+      R.zv[nt] = 0;
+    }
+  }
+  constexpr int NG = BLK / G;                       // groups in a full block
+  const int n_groups = FULL ? NG : (n_valid + G - 1) / G;
+  const int sg = (int)((tb / G) * D * 2);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    if (FULL || gi < n_groups) {
+      R.ks[gi] = __builtin_amdgcn_raw_buffer_load_b128(pb.ksc, pb.off_ks + gi * D * 2, sg, 0);
+      R.kz[gi] = __builtin_amdgcn_raw_buffer_load_b128(pb.kze, pb.off_ks + gi * D * 2, sg, 0);
+    } else {
+      R.ks[gi] = i32x4{0, 0, 0, 0};
+      R.kz[gi] = i32x4{0, 0, 0, 0};
+    }
+  }
+  const int sv_off = (int)((tb / kVRun) * D * RB);
+  if (FULL || j < n_tiles) {
+#pragma unroll
+    for (int q4 = 0; q4 < BlockRegs<BITS>::VW / 4; ++q4) {
+      const auto u = __builtin_amdgcn_raw_buffer_load_b128(pb.vc, pb.off_v + 16 * q4, sv_off, 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) R.v[4 * q4 + w] = (uint32_t)u[w];
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < BlockRegs<BITS>::VW; ++w) R.v[w] = 0u;
+  }
+}
+
+// Online-softmax and accumulator state of one wave (head 4mt + j on this lane's row).
+template <int NMT>
+struct WaveState {
+  float m_run[NMT], l_run[NMT], pz_run[NMT];
+  float acc_f[NMT][8];            // channels 8lo + n, in units of 2^Ev
+  i32x4 acc_i[NMT][8];
+};
+
+// One 64-token block: group preparation, Q.K^T, online softmax, P.V.
+template <int BITS, int GQA, int G, bool FULL>
+__device__ __forceinline__ void process_block(const BlockRegs<BITS>& R, int n_valid,
+                                              const float (&qv)[(GQA + 3) / 4][8],
+                                              float k_unscale, int Ev,
+                                              WaveLds<(GQA + 3) / 4>& lds,
+                                              WaveState<(GQA + 3) / 4>& st, int lo, int j) {
+  constexpr int NMT = (GQA + 3) / 4;
+  constexpr int NG = BLK / G;
+  const int n_groups_blk = FULL ? NG : (n_valid + G - 1) / G;
+  const int n_tiles = FULL ? 4 : n_valid / 16;
+
+  // (1) group preparation: query limbs into LDS, and sum_c q_c z_c per head.
+  // Lane (lo, j) owns channels 8lo .. 8lo+7 of head 4mt + j; its limbs are transposed
+  // in registers (v_perm) so that each write carries one limb of 2 (2-bit) or 4 (4-bit)
+  // channels that are adjacent in the operand.
+  float qz[NG][NMT];
+  const int jg = lo >> 2, ksl = (lo >> 1) & 1;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) qz[gi][mt] = 0.f;
+    if (FULL || gi < n_groups_blk) {
+      const uint32_t sw[4] = {(uint32_t)R.ks[gi][0], (uint32_t)R.ks[gi][1], (uint32_t)R.ks[gi][2],
+                              (uint32_t)R.ks[gi][3]};
+      const uint32_t zw[4] = {(uint32_t)R.kz[gi][0], (uint32_t)R.kz[gi][1], (uint32_t)R.kz[gi][2],
+                              (uint32_t)R.kz[gi][3]};
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        uint32_t x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sc = h2f((unsigned short)(sw[i >> 1] >> (16 * (i & 1))));
+          const float ze = h2f((unsigned short)(zw[i >> 1] >> (16 * (i & 1))));
+          x[i] = to_limbs(qv[mt][i] * sc);
+          qz[gi][mt] = fmaf(qv[mt][i], ze, qz[gi][mt]);
+        }
+        uint8_t* blkp = &lds.qa[gi][mt][ksl][(4 * j) * QA_ROW + jg * 16];
+        if constexpr (BITS == 2) {
+          // channel 8lo + i sits at position 4(i%4) + 2(lo%2) + i/4 of its row block
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const uint32_t w01 = __builtin_amdgcn_perm(x[s4 + 4], x[s4], 0x05010400u);
+            const uint32_t w23 = __builtin_amdgcn_perm(x[s4 + 4], x[s4], 0x07030602u);
+            uint8_t* d = blkp + 4 * s4 + 2 * (lo & 1);
+            *reinterpret_cast<uint16_t*>(d) = (uint16_t)w01;
+            *reinterpret_cast<uint16_t*>(d + QA_ROW) = (uint16_t)(w01 >> 16);
+            *reinterpret_cast<uint16_t*>(d + 2 * QA_ROW) = (uint16_t)w23;
+            *reinterpret_cast<uint16_t*>(d + 3 * QA_ROW) = (uint16_t)(w23 >> 16);
+          }
+        } else {
+          // channel 8lo + i sits at position 4(2(lo%2) + i%2) + i/2 of its row block
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const uint32_t a = x[s2], b = x[s2 + 2], c = x[s2 + 4], e = x[s2 + 6];
+            const uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+            const uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+            const uint32_t t2 = __builtin_amdgcn_perm(e, c, 0x05010400u);   // c0 e0 c1 e1
+            const uint32_t t3 = __builtin_amdgcn_perm(e, c, 0x07030602u);   // c2 e2 c3 e3
+            uint8_t* d = blkp + 4 * (2 * (lo & 1) + s2);
+            *reinterpret_cast<uint32_t*>(d) = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(d + QA_ROW) = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+            *reinterpret_cast<uint32_t*>(d + 2 * QA_ROW) = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(d + 3 * QA_ROW) = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+          }
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) qz[gi][mt] = row_sum16(qz[gi][mt]) * k_unscale;
+    }
+  }
+  wave_lds_sync();
+
+  // (2) Q.K^T on the matrix cores: C[mt][nt] rows (head, limb), columns tokens.
+  i32x4 cqk[NMT][4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) cqk[mt][nt] = i32x4{0, 0, 0, 0};
+    if (FULL || nt < n_tiles) {
+      const int gi = nt * 16 / G;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const i32x4 bop = BITS == 2 ? unpack16<BITS>(R.k[nt][ks], 0u)
+                                    : unpack16<BITS>(R.k[nt][2 * ks % BlockRegs<BITS>::KW],
+                                                     R.k[nt][(2 * ks + 1) % BlockRegs<BITS>::KW]);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const i32x4 aop = *reinterpret_cast<const i32x4*>(&lds.qa[gi][mt][ks][lo * QA_ROW + j * 16]);
+          cqk[mt][nt] = mfma_i8(aop, bop, cqk[mt][nt]);
+        }
+      }
+    }
+  }
+
+  // (3) logits, online softmax, probability limbs into LDS.
+  float sv[4], zv[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    sv[nt] = h2f(R.sv[nt]);
+    zv[nt] = h2f(R.zv[nt]);
+  }
+  const float k_hi = 65536.f * k_unscale;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    float z[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int gi = nt * 16 / G;
+      const i32x4 c = cqk[mt][nt];
+      const float lo16 = (float)(c[0] + c[1] * 256);      // |c_i| < 2^18: exact int
+      const float hi16 = (float)(c[2] + c[3] * 256);
+      z[nt] = fmaf(hi16, k_hi, fmaf(lo16, k_unscale, qz[gi][mt]));
+      if (!FULL && nt >= n_tiles) z[nt] = -INFINITY;
+      bm = fmaxf(bm, z[nt]);
+    }
+    bm = row_max16(bm);
+    const float m_new = fmaxf(st.m_run[mt], bm);
+    // The running max rose on some row: fold the integer accumulators of those rows
+    // into float and rescale (a wave-uniform branch; alpha = 1 on the other rows).
+    if (__builtin_amdgcn_read_exec() & __ballot(m_new > st.m_run[mt])) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run[mt] - m_new);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const i32x4 ci = st.acc_i[mt][n];
+        const float v = st.acc_f[mt][n] + (float)ci[0] + 256.f * (float)ci[1] +
+                        65536.f * (float)ci[2] + 16777216.f * (float)ci[3];
+        st.acc_f[mt][n] = v * alpha;
+        st.acc_i[mt][n] = i32x4{0, 0, 0, 0};
+      }
+      st.l_run[mt] *= alpha;
+      st.pz_run[mt] *= alpha;
+      st.m_run[mt] = m_new;
+    }
+    const float m_shift = st.m_run[mt] - (float)Ev;     // p' = p * 2^Ev
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float p = __builtin_amdgcn_exp2f(z[nt] - m_shift);
+      if (!FULL && nt >= n_tiles) p = 0.f;
+      st.l_run[mt] += p;
+      st.pz_run[mt] = fmaf(p, zv[nt], st.pz_run[mt]);
+      const uint32_t lw = to_limbs(p * sv[nt]);
+      uint8_t* dst = &lds.pa[mt][4 * j][nt][run_token_to_pos<BITS>(lo)];
+      dst[0] = (uint8_t)lw;
+      dst[64] = (uint8_t)(lw >> 8);
+      dst[128] = (uint8_t)(lw >> 16);
+      dst[192] = (uint8_t)(lw >> 24);
+    }
+  }
+  wave_lds_sync();
+
+  // (4) P.V on the matrix cores: rows (head, limb), K = 64 tokens, columns channels
+  // 8lo + n (n = 0..7) of the lane's Value run j.
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const i32x4 aop = *reinterpret_cast<const i32x4*>(&lds.pa[mt][lo][j][0]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const i32x4 bop = BITS == 2 ? unpack16<BITS>(R.v[n], 0u)
+                                  : unpack16<BITS>(R.v[2 * n], R.v[2 * n + 1]);
+      st.acc_i[mt][n] = mfma_i8(aop, bop, st.acc_i[mt][n]);
+    }
+  }
+}
+
 // Writes comb[GQA][PSTRIDE] (acc with the Value-zero term folded in, m, l).
-template <int BITS, int GQA>
+template <int BITS, int GQA, int G>
 __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, int64_t blk1,
                                WaveLds<(GQA + 3) / 4>& lds, float* comb) {
   constexpr int NMT = (GQA + 3) / 4;              // M-tiles of 4 heads x 4 limbs
-  constexpr int KB = D * BITS / 8;                // Key code bytes per token
-  constexpr int RB = kVRun * BITS / 8;            // Value code bytes per (run, channel)
   const LayerView& L = a.L;
-  const int G = L.G;
   const int lane = threadIdx.x & 63;
   const int lo = lane & 15, j = lane >> 4;
   const int64_t b = pair / L.H, h = pair % L.H;
 
+  constexpr int KB = D * BITS / 8;
+  constexpr int VRB = kVRun * BITS / 8;             // Value code bytes per (run, channel)
   const uint8_t* kc = L.k_codes + pair * L.kc_pair();
   const __half* ksc = L.k_scale + pair * L.ks_pair();
   const __half* kze = L.k_zero + pair * L.ks_pair();
   const uint8_t* vc = L.v_codes + pair * L.vc_pair();
   const unsigned short* vsc = reinterpret_cast<const unsigned short*>(L.v_scale + pair * L.vs_pair());
   const unsigned short* vze = reinterpret_cast<const unsigned short*>(L.v_zero + pair * L.vs_pair());
+  PairBufs pb;
+  pb.kc = make_rsrc(kc, L.kc_pair());
+  pb.ksc = make_rsrc(ksc, L.ks_pair() * 2);
+  pb.kze = make_rsrc(kze, L.ks_pair() * 2);
+  pb.vc = make_rsrc(vc, L.vc_pair());
+  pb.vsc = make_rsrc(vsc, L.vs_pair() * 2);
+  pb.vze = make_rsrc(vze, L.vs_pair() * 2);
+  pb.off_k = lo * KB + j * (KB / 4);
+  pb.off_v = j * D * VRB + 8 * lo * VRB;
+  pb.off_ks = 16 * lo;
+  pb.off_sv = 2 * lo;
   const int Hq = L.H * GQA;
   const __half* qp = a.q + (b * Hq + h * GQA) * D;
 
   const int64_t t_lo = blk0 * BLK;
   const int64_t t_hi = blk1 * BLK < a.Tq ? blk1 * BLK : a.Tq;
+  // Blocks [blk0, nfull) hold 64 tokens; a last half block (32 tokens) may follow.
+  const int64_t nfull = (t_hi - t_lo) / BLK + blk0;
+  const bool tail = nfull < blk1;
+
+  // The first block's loads go out before the pre-pass so that both latencies overlap.
+  BlockRegs<BITS> RA, RB;
+  if (nfull > blk0) load_block<BITS, G, true>(RA, pb, blk0 * BLK, BLK, j);
 
   // -- pre-pass: largest |q| (scaled), largest Key scale and Value scale in range --
+  // Lane (lo, j) holds the query values it prepares later: head 4mt + j, channels
+  // 8lo .. 8lo+7, i.e. the 16 bytes at offset 16*lane of M-tile mt's 4 heads.
+  float qraw[NMT][8];
   float qmax = 0.f;
-  for (int i = lane; i < GQA * D; i += 64) qmax = fmaxf(qmax, fabsf(__half2float(qp[i])));
-  qmax = wave_max(qmax) * fabsf(a.qscale);
-  float skmax = 0.f, svmax = 0.f;
-  if (t_hi > t_lo) {
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int hd = 4 * mt + j;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (hd < GQA) u = *reinterpret_cast<const uint4*>(qp + (int64_t)hd * D + 8 * lo);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qraw[mt][i] = h2f((unsigned short)(w[i >> 1] >> (16 * (i & 1))));
+      qmax = fmaxf(qmax, fabsf(qraw[mt][i]));
+    }
+  }
+  uint32_t mk = 0, mv = 0;
+  {
     const int64_t g_lo = t_lo / G, g_hi = (t_hi + G - 1) / G;
     const uint4* ks4 = reinterpret_cast<const uint4*>(ksc + g_lo * D);
-    const int64_t n4 = (g_hi - g_lo) * D / 8;
-    uint32_t mk = 0;
-    for (int64_t i = lane; i < n4; i += 64) {
-      const uint4 u = ks4[i];
+    const int64_t n4 = (g_hi - g_lo) * (D / 8);
+    const uint4* vs4 = reinterpret_cast<const uint4*>(vsc + t_lo);
+    const int64_t v4 = (t_hi - t_lo) / 8;
+    auto fold = [](uint32_t m, const uint4& u) {
+      // non-negative float16 values order like their bit patterns
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) mk = max(mk, max(w[k] & 0xFFFFu, w[k] >> 16));
+      for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0xFFFFu, w[k] >> 16));
+      return m;
+    };
+    int64_t i = lane;
+    for (; i + 192 < n4; i += 256) {
+      const uint4 u0 = ks4[i], u1 = ks4[i + 64], u2 = ks4[i + 128], u3 = ks4[i + 192];
+      mk = fold(fold(fold(fold(mk, u0), u1), u2), u3);
     }
-    uint32_t mv = 0;
-    for (int64_t t = t_lo + lane; t < t_hi; t += 64) mv = max(mv, (uint32_t)vsc[t]);
-    // non-negative float16 values order like their bit patterns
-    skmax = wave_max(h2f((unsigned short)mk));
-    svmax = wave_max(h2f((unsigned short)mv));
+    for (; i < n4; i += 64) mk = fold(mk, ks4[i]);
+    i = lane;
+    for (; i + 64 < v4; i += 128) {
+      const uint4 u0 = vs4[i], u1 = vs4[i + 64];
+      mv = fold(fold(mv, u0), u1);
+    }
+    for (; i < v4; i += 64) mv = fold(mv, vs4[i]);
   }
+  qmax = wave_max(qmax) * fabsf(a.qscale);
+  const float skmax = wave_max(h2f((unsigned short)mk));
+  const float svmax = wave_max(h2f((unsigned short)mv));
   const int Ek = fixed_exponent(qmax * skmax);
   const int Ev = fixed_exponent(svmax);
   const float k_unscale = __builtin_amdgcn_ldexpf(1.f, -Ek);
@@ -214,204 +527,57 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
   // 8lo .. 8lo+7, scaled by sm_scale*log2(e)*2^Ek.
   float qv[NMT][8];
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
-    const int hd = 4 * mt + j;
+  for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      qv[mt][i] = hd < GQA ? __builtin_amdgcn_ldexpf(__half2float(qp[hd * D + 8 * lo + i]) * a.qscale, Ek)
-                           : 0.f;
-  }
+    for (int i = 0; i < 8; ++i) qv[mt][i] = __builtin_amdgcn_ldexpf(qraw[mt][i] * a.qscale, Ek);
 
-  // Online-softmax state per M-tile: head 4mt + j for this lane's row.
-  float m_run[NMT], l_run[NMT], pz_run[NMT];
-  float acc_f[NMT][8];            // channels 8lo + n, in units of 2^Ev
-  i32x4 acc_i[NMT][8];
+  WaveState<NMT> st;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
-    m_run[mt] = -INFINITY;
-    l_run[mt] = 0.f;
-    pz_run[mt] = 0.f;
+    st.m_run[mt] = -INFINITY;
+    st.l_run[mt] = 0.f;
+    st.pz_run[mt] = 0.f;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      acc_f[mt][n] = 0.f;
-      acc_i[mt][n] = i32x4{0, 0, 0, 0};
+      st.acc_f[mt][n] = 0.f;
+      st.acc_i[mt][n] = i32x4{0, 0, 0, 0};
     }
   }
 
-  for (int64_t blk = blk0; blk < blk1; ++blk) {
-    const int64_t tb = blk * BLK;
-    const int n_valid = (int)((a.Tq - tb) < BLK ? (a.Tq - tb) : BLK);    // 64 or 32
-    const int n_groups_blk = (n_valid + G - 1) / G;                      // groups touched
-    const int n_tiles = n_valid / 16;
-
-    // (1) group preparation: query limbs into LDS, and sum_c q_c z_c per head.
-    float qz[2][NMT];
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) qz[gi][mt] = 0.f;
-      if (gi < n_groups_blk) {
-        const int64_t grp = tb / G + gi;
-        const uint4 su = *reinterpret_cast<const uint4*>(ksc + grp * D + 8 * lo);
-        const uint4 zu = *reinterpret_cast<const uint4*>(kze + grp * D + 8 * lo);
-        const uint32_t sw[4] = {su.x, su.y, su.z, su.w};
-        const uint32_t zw[4] = {zu.x, zu.y, zu.z, zu.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float s = h2f((unsigned short)(sw[i >> 1] >> (16 * (i & 1))));
-          const float z = h2f((unsigned short)(zw[i >> 1] >> (16 * (i & 1))));
-          const int c = 8 * lo + i;
-          int ks, jg, p;
-          channel_to_pos<BITS>(c, ks, jg, p);
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
-            const uint32_t lw = to_limbs(qv[mt][i] * s);
-            uint8_t* dst = &lds.qa[gi][mt][ks][4 * j][jg][p];
-            dst[0] = (uint8_t)lw;
-            dst[64] = (uint8_t)(lw >> 8);
-            dst[128] = (uint8_t)(lw >> 16);
-            dst[192] = (uint8_t)(lw >> 24);
-            qz[gi][mt] += qv[mt][i] * z;
-          }
-        }
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) qz[gi][mt] = row_sum16(qz[gi][mt]) * k_unscale;
-      }
-      if (G == 64) break;     // one group spans the whole block
-    }
-    wave_lds_sync();
-
-    // (2) Q.K^T on the matrix cores: C[mt][nt] rows (head, limb), columns tokens.
-    i32x4 cqk[NMT][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) cqk[mt][nt] = i32x4{0, 0, 0, 0};
-      if (nt < n_tiles) {
-        const int gi = (G == 64) ? 0 : (nt >> 1);
-        const uint8_t* row = kc + (tb + 16 * nt + lo) * KB;
-        uint32_t w[4];
-        if constexpr (BITS == 2) {
-          const uint2 u = *reinterpret_cast<const uint2*>(row + 8 * j);
-          w[0] = u.x; w[1] = 0; w[2] = u.y; w[3] = 0;
-        } else {
-          const uint4 u = *reinterpret_cast<const uint4*>(row + 16 * j);
-          w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const i32x4 bop = unpack16<BITS>(w[2 * ks], w[2 * ks + 1]);
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
-            const i32x4 aop = *reinterpret_cast<const i32x4*>(&lds.qa[gi][mt][ks][lo][j][0]);
-            cqk[mt][nt] = mfma_i8(aop, bop, cqk[mt][nt]);
-          }
-        }
-      }
-    }
-
-    // (3) logits, online softmax, probability limbs into LDS.
-    float sv[4], zv[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t t = tb + 16 * nt + lo;
-      sv[nt] = nt < n_tiles ? h2f(vsc[t]) : 0.f;
-      zv[nt] = nt < n_tiles ? h2f(vze[t]) : 0.f;
-    }
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      float z[4];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int gi = (G == 64) ? 0 : (nt >> 1);
-        const i32x4 c = cqk[mt][nt];
-        const float lo16 = (float)(c[0] + c[1] * 256);      // |c_i| < 2^18: exact int
-        const float hi16 = (float)(c[2] + c[3] * 256);
-        z[nt] = nt < n_tiles ? fmaf(hi16, 65536.f * k_unscale, fmaf(lo16, k_unscale, qz[gi][mt]))
-                             : -INFINITY;
-        bm = fmaxf(bm, z[nt]);
-      }
-      bm = row_max16(bm);
-      const float m_new = fmaxf(m_run[mt], bm);
-      if (m_new > m_run[mt]) {               // the running max rose: rescale what we have
-        const float alpha = __builtin_amdgcn_exp2f(m_run[mt] - m_new);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const i32x4 ci = acc_i[mt][n];
-          float v = acc_f[mt][n] + (float)ci[0] + 256.f * (float)ci[1] + 65536.f * (float)ci[2] +
-                    16777216.f * (float)ci[3];
-          acc_f[mt][n] = v * alpha;
-          acc_i[mt][n] = i32x4{0, 0, 0, 0};
-        }
-        l_run[mt] *= alpha;
-        pz_run[mt] *= alpha;
-        m_run[mt] = m_new;
-      }
-      const float m_shift = m_run[mt] - (float)Ev;     // p' = p * 2^Ev
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float p = nt < n_tiles ? __builtin_amdgcn_exp2f(z[nt] - m_shift) : 0.f;
-        l_run[mt] += p;
-        pz_run[mt] = fmaf(p, zv[nt], pz_run[mt]);
-        const uint32_t lw = nt < n_tiles ? to_limbs(p * sv[nt]) : 0u;
-        uint8_t* dst = &lds.pa[mt][4 * j][nt][run_token_to_pos<BITS>(lo)];
-        dst[0] = (uint8_t)lw;
-        dst[64] = (uint8_t)(lw >> 8);
-        dst[128] = (uint8_t)(lw >> 16);
-        dst[192] = (uint8_t)(lw >> 24);
-      }
-    }
-    wave_lds_sync();
-
-    // (4) P.V on the matrix cores: rows (head, limb), K = 64 tokens, columns channels
-    // 8lo + n (n = 0..7) of the lane's Value run j.
-    {
-      const uint8_t* vrow = vc + (tb / kVRun + j) * (int64_t)(D * RB) + (8 * lo) * RB;
-      uint32_t vw[8][2];
-      const bool run_ok = j < n_tiles;
-      if constexpr (BITS == 2) {
-        const uint4 u0 = run_ok ? *reinterpret_cast<const uint4*>(vrow) : make_uint4(0, 0, 0, 0);
-        const uint4 u1 = run_ok ? *reinterpret_cast<const uint4*>(vrow + 16) : make_uint4(0, 0, 0, 0);
-        const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int n = 0; n < 8; ++n) { vw[n][0] = w[n]; vw[n][1] = 0; }
-      } else {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint4 u = run_ok ? *reinterpret_cast<const uint4*>(vrow + 16 * q4) : make_uint4(0, 0, 0, 0);
-          vw[2 * q4][0] = u.x; vw[2 * q4][1] = u.y;
-          vw[2 * q4 + 1][0] = u.z; vw[2 * q4 + 1][1] = u.w;
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const i32x4 aop = *reinterpret_cast<const i32x4*>(&lds.pa[mt][lo][j][0]);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const i32x4 bop = unpack16<BITS>(vw[n][0], vw[n][1]);
-          acc_i[mt][n] = mfma_i8(aop, bop, acc_i[mt][n]);
-        }
-      }
-    }
+  // Full blocks, two register buffers: block k+1's loads are in flight while block k
+  // computes.  Prefetches are unconditional (clamped to the last full block, whose
+  // duplicate load is simply not used) so that no branch surrounds a load.
+  const int64_t last_full = nfull - 1;
+  for (int64_t blk = blk0; blk < nfull; blk += 2) {
+    const int64_t b1 = blk + 1 < last_full ? blk + 1 : last_full;
+    load_block<BITS, G, true>(RB, pb, b1 * BLK, BLK, j);
+    process_block<BITS, GQA, G, true>(RA, BLK, qv, k_unscale, Ev, lds, st, lo, j);
+    const int64_t b2 = blk + 2 < last_full ? blk + 2 : last_full;
+    load_block<BITS, G, true>(RA, pb, b2 * BLK, BLK, j);
+    if (blk + 1 < nfull) process_block<BITS, GQA, G, true>(RB, BLK, qv, k_unscale, Ev, lds, st, lo, j);
+  }
+  if (tail) {
+    const int nv = (int)(t_hi - nfull * BLK);
+    load_block<BITS, G, false>(RA, pb, nfull * BLK, nv, j);
+    process_block<BITS, GQA, G, false>(RA, nv, qv, k_unscale, Ev, lds, st, lo, j);
   }
 
   // Finish: fold the integer accumulators and the Value-zero term, undo 2^Ev.
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int hd = 4 * mt + j;
-    const float lsum = row_sum16(l_run[mt]);
-    const float pz = row_sum16(pz_run[mt]);
+    const float lsum = row_sum16(st.l_run[mt]);
+    const float pz = row_sum16(st.pz_run[mt]);
     if (hd < GQA) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const i32x4 ci = acc_i[mt][n];
-        const float v = acc_f[mt][n] + (float)ci[0] + 256.f * (float)ci[1] + 65536.f * (float)ci[2] +
-                        16777216.f * (float)ci[3];
+        const i32x4 ci = st.acc_i[mt][n];
+        const float v = st.acc_f[mt][n] + (float)ci[0] + 256.f * (float)ci[1] +
+                        65536.f * (float)ci[2] + 16777216.f * (float)ci[3];
         comb[hd * PSTRIDE + 8 * lo + n] = (v + pz) * v_unscale;
       }
       if (lo == 0) {
-        comb[hd * PSTRIDE + D] = m_run[mt];
+        comb[hd * PSTRIDE + D] = st.m_run[mt];
         comb[hd * PSTRIDE + D + 1] = lsum * v_unscale;
       }
     }
@@ -477,16 +643,23 @@ __device__ void residual_wave(const DecodeArgs& a, int64_t pair, int t0, int t1,
       if (t_l == 0) palpha[hd] = alpha;
     }
     wave_lds_sync();
-    // every lane needs every head's running max for the final write
+    // All 32 rows' Value pairs of this lane are loaded before use (rows past the
+    // chunk re-read its last row; their probabilities are 0).
+    __half2 vv[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int row = t < n_valid ? t : n_valid - 1;
+      vv[t] = *reinterpret_cast<const __half2*>(vr + (int64_t)(c0 + row) * D + 2 * lane);
+    }
 #pragma unroll
     for (int hd = 0; hd < GQA; ++hd) {
       const float al = palpha[hd];
       float s0 = acc[hd][0] * al, s1 = acc[hd][1] * al;
-      for (int t = 0; t < n_valid; ++t) {
-        const __half2 v = *reinterpret_cast<const __half2*>(vr + (int64_t)(c0 + t) * D + 2 * lane);
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
         const float p = pw[hd * 32 + t];
-        s0 = fmaf(p, __low2float(v), s0);
-        s1 = fmaf(p, __high2float(v), s1);
+        s0 = fmaf(p, __low2float(vv[t]), s0);
+        s1 = fmaf(p, __high2float(vv[t]), s1);
       }
       acc[hd][0] = s0;
       acc[hd][1] = s1;
@@ -530,10 +703,10 @@ __device__ __forceinline__ void combine(int n, Src src, float* dst, int64_t dst_
       }
     }
     if (with_ml) {
-      dst[hd * dst_hstride + c] = o;
+      store_coherent(&dst[hd * dst_hstride + c], o);
       if (c == 0) {
-        dst[hd * dst_hstride + D] = mstar;
-        dst[hd * dst_hstride + D + 1] = l;
+        store_coherent(&dst[hd * dst_hstride + D], mstar);
+        store_coherent(&dst[hd * dst_hstride + D + 1], l);
       }
     } else {
       dst[hd * dst_hstride + c] = o / l;
@@ -541,8 +714,76 @@ __device__ __forceinline__ void combine(int n, Src src, float* dst, int64_t dst_
   }
 }
 
+// Workgroups per CU the register budget allows: the double-buffered block inputs plus
+// the integer accumulators of 8 query heads (or of 4-bit codes) need more than half of
+// the register file.
+// Final merge by the last workgroup of a pair: the n_parts partials are spread over
+// the 4 waves (part i goes to wave i mod 4) and each lane keeps a running
+// (m, l, acc) per head for channels 2*lane, 2*lane+1.  Loads of U parts are issued
+// before any of them is used, so the partials written by other CUs are fetched in a
+// few round trips.  The 4 per-wave records are then combined in `scratch` (LDS).
+template <int GQA>
+__device__ void merge_pair(const float* __restrict__ base, int n_parts, float* __restrict__ out,
+                           float (*scratch)[GQA * PSTRIDE]) {
+  constexpr int U = 32 / GQA;                    // parts in flight per lane
+  const int lane = threadIdx.x & 63, pg = threadIdx.x >> 6;
+  float m[GQA], l[GQA], o0[GQA], o1[GQA];
+#pragma unroll
+  for (int hd = 0; hd < GQA; ++hd) {
+    m[hd] = -INFINITY;
+    l[hd] = 0.f;
+    o0[hd] = o1[hd] = 0.f;
+  }
+  for (int i0 = pg; i0 < n_parts; i0 += WAVES * U) {
+    float2 ml[U][GQA], ov[U][GQA];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + WAVES * u;
+#pragma unroll
+      for (int hd = 0; hd < GQA; ++hd) {
+        const float* rec = base + ((int64_t)i * GQA + hd) * PSTRIDE;
+        ml[u][hd] = i < n_parts ? make_float2(load_coherent(rec + D), load_coherent(rec + D + 1))
+                                : make_float2(0.f, 0.f);
+        ov[u][hd] = i < n_parts ? make_float2(load_coherent(rec + 2 * lane),
+                                              load_coherent(rec + 2 * lane + 1))
+                                : make_float2(0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int hd = 0; hd < GQA; ++hd) {
+        if (ml[u][hd].y > 0.f) {                 // skip empty partials (l == 0)
+          const float mn = fmaxf(m[hd], ml[u][hd].x);
+          const float wa = __builtin_amdgcn_exp2f(m[hd] - mn);
+          const float wb = __builtin_amdgcn_exp2f(ml[u][hd].x - mn);
+          l[hd] = l[hd] * wa + ml[u][hd].y * wb;
+          o0[hd] = o0[hd] * wa + ov[u][hd].x * wb;
+          o1[hd] = o1[hd] * wa + ov[u][hd].y * wb;
+          m[hd] = mn;
+        }
+      }
+    }
+  }
+  float* rec = scratch[pg];
+#pragma unroll
+  for (int hd = 0; hd < GQA; ++hd) {
+    rec[hd * PSTRIDE + 2 * lane] = o0[hd];
+    rec[hd * PSTRIDE + 2 * lane + 1] = o1[hd];
+    if (lane == 0) {
+      rec[hd * PSTRIDE + D] = m[hd];
+      rec[hd * PSTRIDE + D + 1] = l[hd];
+    }
+  }
+  __syncthreads();
+  combine<GQA>(WAVES, [&](int i) { return (const float*)scratch[i]; }, out, D, false);
+}
+
 template <int BITS, int GQA>
-__global__ __launch_bounds__(NT, 2) void decode_kernel(DecodeArgs a) {
+constexpr int wgs_per_cu() { return (BITS == 2 && GQA <= 4) ? 2 : 1; }
+
+template <int BITS, int GQA, int G>
+__global__ __launch_bounds__(NT, (wgs_per_cu<BITS, GQA>())) void decode_kernel(DecodeArgs a) {
   constexpr int NMT = (GQA + 3) / 4;
   struct ResidLds {
     float qf[GQA * D];
@@ -559,7 +800,7 @@ __global__ __launch_bounds__(NT, 2) void decode_kernel(DecodeArgs a) {
   const int64_t P = (int64_t)a.L.B * a.L.H;
   const int64_t pair = blockIdx.x % P;
   const int s = (int)(blockIdx.x / P);            // 0: residual rows, s >= 1: split s - 1
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_parts = a.n_split + 1;
 
   if (s == 0) {
@@ -586,7 +827,7 @@ __global__ __launch_bounds__(NT, 2) void decode_kernel(DecodeArgs a) {
     for (int i = threadIdx.x & 63; i < GQA * PSTRIDE; i += 64) cw[i] = 0.f;
     for (int hd = 0; hd < GQA; ++hd) cw[hd * PSTRIDE + D] = -INFINITY;
     wave_lds_sync();
-    if (blk1 > blk0) quantized_wave<BITS, GQA>(a, pair, blk0, blk1, lds.wave[wave], cw);
+    if (blk1 > blk0) quantized_wave<BITS, GQA, G>(a, pair, blk0, blk1, lds.wave[wave], cw);
   }
   __syncthreads();
 
@@ -594,29 +835,36 @@ __global__ __launch_bounds__(NT, 2) void decode_kernel(DecodeArgs a) {
   float* mine = a.part + ((pair * n_parts + s) * GQA) * PSTRIDE;
   combine<GQA>(WAVES, [&](int i) { return (const float*)comb[i]; }, mine, PSTRIDE, true);
 
-  // Last workgroup of the pair merges all partials and resets the counter.
-  __threadfence();
+  // Last workgroup of the pair merges all partials and resets the counter.  Every
+  // thread's partial stores complete before the arrival is counted; the merging
+  // workgroup reads the partials with coherent loads after it has seen all arrivals.
+  wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.counters[pair], 1u);
+    const unsigned prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == (unsigned)(n_parts - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
   const float* base = a.part + (pair * n_parts * GQA) * PSTRIDE;
   const int64_t b = pair / a.L.H, h = pair % a.L.H;
   float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
-  combine<GQA>(n_parts, [&](int i) { return base + (int64_t)i * GQA * PSTRIDE; }, o, D, false);
-  if (threadIdx.x == 0) a.counters[pair] = 0u;
+  merge_pair<GQA>(base, n_parts, o, comb);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename F>
-bool dispatch_decode(int bits, int gqa, F&& f) {
-#define KIVI_CASE(B, Q) \
-  if (bits == B && gqa == Q) return f(std::integral_constant<int, B>{}, std::integral_constant<int, Q>{});
-  KIVI_CASE(2, 1) KIVI_CASE(2, 2) KIVI_CASE(2, 4) KIVI_CASE(2, 8)
-  KIVI_CASE(4, 1) KIVI_CASE(4, 2) KIVI_CASE(4, 4) KIVI_CASE(4, 8)
+bool dispatch_decode(int bits, int gqa, int G, F&& f) {
+#define KIVI_CASE(B, Q, GG)                                                              \
+  if (bits == B && gqa == Q && G == GG)                                                 \
+    return f(std::integral_constant<int, B>{}, std::integral_constant<int, Q>{},         \
+             std::integral_constant<int, GG>{});
+  KIVI_CASE(2, 1, 32) KIVI_CASE(2, 2, 32) KIVI_CASE(2, 4, 32) KIVI_CASE(2, 8, 32)
+  KIVI_CASE(4, 1, 32) KIVI_CASE(4, 2, 32) KIVI_CASE(4, 4, 32) KIVI_CASE(4, 8, 32)
+  KIVI_CASE(2, 1, 64) KIVI_CASE(2, 2, 64) KIVI_CASE(2, 4, 64) KIVI_CASE(2, 8, 64)
+  KIVI_CASE(4, 1, 64) KIVI_CASE(4, 2, 64) KIVI_CASE(4, 4, 64) KIVI_CASE(4, 8, 64)
 #undef KIVI_CASE
   return false;
 }
@@ -633,9 +881,10 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   const int64_t pairs = (int64_t)L.B * L.H;
   int64_t ns = n_split_req;
   if (ns <= 0) {
-    // about two 4-wave workgroups per CU on 256 CUs, at least 4 blocks per wave
-    const int64_t target_wgs = 512;
-    ns = (target_wgs + pairs - 1) / pairs;
+    // one round of resident workgroups on 256 CUs, at least 4 blocks per wave
+    const int per_cu = (L.bits == 2 && gqa <= 4) ? 2 : 1;     // wgs_per_cu<>() on the host
+    const int64_t target_wgs = 256 * per_cu;                    // incl. one residual wg/pair
+    ns = target_wgs > 2 * pairs ? (target_wgs - pairs) / pairs : 1;
     const int64_t cap = (nblk + 4 * WAVES - 1) / (4 * WAVES);
     if (ns > cap) ns = cap;
   }
@@ -668,9 +917,9 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.qscale = sm_scale * 1.4426950408889634f;
   const int64_t P = (int64_t)L.B * L.H;
   const dim3 grid((unsigned)(P * (plan.n_split + 1)));
-  bool ok = dispatch_decode(L.bits, gqa, [&](auto b, auto g) {
-    hipLaunchKernelGGL((decode_kernel<decltype(b)::value, decltype(g)::value>), grid, dim3(NT), 0,
-                       s, a);
+  bool ok = dispatch_decode(L.bits, gqa, L.G, [&](auto b, auto g, auto gg) {
+    hipLaunchKernelGGL((decode_kernel<decltype(b)::value, decltype(g)::value, decltype(gg)::value>),
+                       grid, dim3(NT), 0, s, a);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
