@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall",
     "-Wno-unused-function",
+    # a kernel that misses the occupancy its launch bounds ask for is a build error:
+    # the split planner sizes the grid from that occupancy
+    "-Werror=pass-failed",
 ]
 
 

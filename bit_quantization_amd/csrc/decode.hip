@@ -100,6 +100,12 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+typedef __attribute__((address_space(1))) unsigned long long global_u64;
+__device__ __forceinline__ float2 load_coherent2(const float* p) {
+  const unsigned long long u = __hip_atomic_load((global_u64*)(p), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_SYSTEM);
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
 // Wait until this thread's global stores have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ float h2f(unsigned short h) {
@@ -198,51 +204,59 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// FULL: all 64 tokens of the block are in the history (compile-time: no branches).
-template <int BITS, int G, bool FULL>
-__device__ __forceinline__ void load_block(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
-                                           int n_valid, int j) {
+// The loads of one block come in four sets, each refilled for the next block right
+// after its last use in the current one.  FULL: all 64 tokens of the block are in the
+// history (compile-time: no branches); otherwise n_valid (a multiple of 16) are.
+template <int BITS, bool FULL>
+__device__ __forceinline__ void load_kcodes(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
+                                            int n_valid, int nt) {
   constexpr int KB = D * BITS / 8;
-  constexpr int RB = kVRun * BITS / 8;
-  const int n_tiles = FULL ? 4 : n_valid / 16;
   const int sk = (int)(tb * KB);
+  if (FULL || nt < n_valid / 16) {
+    if constexpr (BITS == 2) {
+      const auto u = __builtin_amdgcn_raw_buffer_load_b64(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
+      R.k[nt][0] = (uint32_t)u[0];
+      R.k[nt][1] = (uint32_t)u[1];
+    } else {
+      const auto u = __builtin_amdgcn_raw_buffer_load_b128(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) R.k[nt][w] = (uint32_t)u[w];
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < BlockRegs<BITS>::KW; ++w) R.k[nt][w] = 0u;
+  }
+}
+template <int BITS, bool FULL>
+__device__ __forceinline__ void load_vscale(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
+                                            int n_valid, int nt) {
   const int ssv = (int)(tb * 2);
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    if (FULL || nt < n_tiles) {
-      if constexpr (BITS == 2) {
-        const auto u = __builtin_amdgcn_raw_buffer_load_b64(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
-        R.k[nt][0] = (uint32_t)u[0];
-        R.k[nt][1] = (uint32_t)u[1];
-      } else {
-        const auto u = __builtin_amdgcn_raw_buffer_load_b128(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) R.k[nt][w] = (uint32_t)u[w];
-      }
-      R.sv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vsc, pb.off_sv + 32 * nt, ssv, 0);
-      R.zv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vze, pb.off_sv + 32 * nt, ssv, 0);
-    } else {
-#pragma unroll
-      for (int w = 0; w < BlockRegs<BITS>::KW; ++w) R.k[nt][w] = 0u;
-      R.sv[nt] = 0;
-      R.zv[nt] = 0;
-    }
+  if (FULL || nt < n_valid / 16) {
+    R.sv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vsc, pb.off_sv + 32 * nt, ssv, 0);
+    R.zv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vze, pb.off_sv + 32 * nt, ssv, 0);
+  } else {
+    R.sv[nt] = 0;
+    R.zv[nt] = 0;
   }
-  constexpr int NG = BLK / G;                       // groups in a full block
-  const int n_groups = FULL ? NG : (n_valid + G - 1) / G;
+}
+template <int BITS, int G, bool FULL>
+__device__ __forceinline__ void load_kscale(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
+                                            int n_valid, int gi) {
   const int sg = (int)((tb / G) * D * 2);
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    if (FULL || gi < n_groups) {
-      R.ks[gi] = __builtin_amdgcn_raw_buffer_load_b128(pb.ksc, pb.off_ks + gi * D * 2, sg, 0);
-      R.kz[gi] = __builtin_amdgcn_raw_buffer_load_b128(pb.kze, pb.off_ks + gi * D * 2, sg, 0);
-    } else {
-      R.ks[gi] = i32x4{0, 0, 0, 0};
-      R.kz[gi] = i32x4{0, 0, 0, 0};
-    }
+  if (FULL || gi < (n_valid + G - 1) / G) {
+    R.ks[gi] = __builtin_amdgcn_raw_buffer_load_b128(pb.ksc, pb.off_ks + gi * D * 2, sg, 0);
+    R.kz[gi] = __builtin_amdgcn_raw_buffer_load_b128(pb.kze, pb.off_ks + gi * D * 2, sg, 0);
+  } else {
+    R.ks[gi] = i32x4{0, 0, 0, 0};
+    R.kz[gi] = i32x4{0, 0, 0, 0};
   }
-  const int sv_off = (int)((tb / kVRun) * D * RB);
-  if (FULL || j < n_tiles) {
+}
+template <int BITS, bool FULL>
+__device__ __forceinline__ void load_vcodes(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
+                                            int n_valid, int j) {
+  constexpr int VRB = kVRun * BITS / 8;
+  const int sv_off = (int)((tb / kVRun) * D * VRB);
+  if (FULL || j < n_valid / 16) {
 #pragma unroll
     for (int q4 = 0; q4 < BlockRegs<BITS>::VW / 4; ++q4) {
       const auto u = __builtin_amdgcn_raw_buffer_load_b128(pb.vc, pb.off_v + 16 * q4, sv_off, 0);
@@ -254,6 +268,21 @@ __device__ __forceinline__ void load_block(BlockRegs<BITS>& R, const PairBufs& p
     for (int w = 0; w < BlockRegs<BITS>::VW; ++w) R.v[w] = 0u;
   }
 }
+template <int BITS, int G, bool FULL>
+__device__ __forceinline__ void load_block(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
+                                           int n_valid, int j) {
+#pragma unroll
+  for (int gi = 0; gi < BLK / G; ++gi) load_kscale<BITS, G, FULL>(R, pb, tb, n_valid, gi);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    load_kcodes<BITS, FULL>(R, pb, tb, n_valid, nt);
+    load_vscale<BITS, FULL>(R, pb, tb, n_valid, nt);
+  }
+  load_vcodes<BITS, FULL>(R, pb, tb, n_valid, j);
+}
+// Keeps the scheduler from moving a refill above the last use of the registers it
+// overwrites.
+__device__ __forceinline__ void refill_point() { __builtin_amdgcn_sched_barrier(0); }
 
 // Online-softmax and accumulator state of one wave (head 4mt + j on this lane's row).
 template <int NMT>
@@ -264,12 +293,15 @@ struct WaveState {
 };
 
 // One 64-token block: group preparation, Q.K^T, online softmax, P.V.
-template <int BITS, int GQA, int G, bool FULL>
-__device__ __forceinline__ void process_block(const BlockRegs<BITS>& R, int n_valid,
+// REFILL: each register set is reloaded with the full block at token tb_next right
+// after its last use here.
+template <int BITS, int GQA, int G, bool FULL, bool REFILL>
+__device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
                                               const float (&qv)[(GQA + 3) / 4][8],
                                               float k_unscale, int Ev,
                                               WaveLds<(GQA + 3) / 4>& lds,
-                                              WaveState<(GQA + 3) / 4>& st, int lo, int j) {
+                                              WaveState<(GQA + 3) / 4>& st, int lo, int j,
+                                              const PairBufs& pb, int64_t tb_next) {
   constexpr int NMT = (GQA + 3) / 4;
   constexpr int NG = BLK / G;
   const int n_groups_blk = FULL ? NG : (n_valid + G - 1) / G;
@@ -333,6 +365,10 @@ __device__ __forceinline__ void process_block(const BlockRegs<BITS>& R, int n_va
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) qz[gi][mt] = row_sum16(qz[gi][mt]) * k_unscale;
     }
+    if constexpr (REFILL) {
+      refill_point();
+      load_kscale<BITS, G, true>(R, pb, tb_next, BLK, gi);
+    }
   }
   wave_lds_sync();
 
@@ -356,6 +392,10 @@ __device__ __forceinline__ void process_block(const BlockRegs<BITS>& R, int n_va
         }
       }
     }
+    if constexpr (REFILL) {
+      refill_point();
+      load_kcodes<BITS, true>(R, pb, tb_next, BLK, nt);
+    }
   }
 
   // (3) logits, online softmax, probability limbs into LDS.
@@ -364,6 +404,11 @@ __device__ __forceinline__ void process_block(const BlockRegs<BITS>& R, int n_va
   for (int nt = 0; nt < 4; ++nt) {
     sv[nt] = h2f(R.sv[nt]);
     zv[nt] = h2f(R.zv[nt]);
+  }
+  if constexpr (REFILL) {
+    refill_point();
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) load_vscale<BITS, true>(R, pb, tb_next, BLK, nt);
   }
   const float k_hi = 65536.f * k_unscale;
 #pragma unroll
@@ -427,6 +472,10 @@ __device__ __forceinline__ void process_block(const BlockRegs<BITS>& R, int n_va
       st.acc_i[mt][n] = mfma_i8(aop, bop, st.acc_i[mt][n]);
     }
   }
+  if constexpr (REFILL) {
+    refill_point();
+    load_vcodes<BITS, true>(R, pb, tb_next, BLK, j);
+  }
 }
 
 // Writes comb[GQA][PSTRIDE] (acc with the Value-zero term folded in, m, l).
@@ -468,8 +517,8 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
   const bool tail = nfull < blk1;
 
   // The first block's loads go out before the pre-pass so that both latencies overlap.
-  BlockRegs<BITS> RA, RB;
-  if (nfull > blk0) load_block<BITS, G, true>(RA, pb, blk0 * BLK, BLK, j);
+  BlockRegs<BITS> R;
+  if (nfull > blk0) load_block<BITS, G, true>(R, pb, blk0 * BLK, BLK, j);
 
   // -- pre-pass: largest |q| (scaled), largest Key scale and Value scale in range --
   // Lane (lo, j) holds the query values it prepares later: head 4mt + j, channels
@@ -502,18 +551,27 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
       for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0xFFFFu, w[k] >> 16));
       return m;
     };
-    int64_t i = lane;
-    for (; i + 192 < n4; i += 256) {
-      const uint4 u0 = ks4[i], u1 = ks4[i + 64], u2 = ks4[i + 128], u3 = ks4[i + 192];
-      mk = fold(fold(fold(fold(mk, u0), u1), u2), u3);
+    // Every load of a round is issued before any is folded: one round covers 16 blocks.
+    constexpr int UK = 8, UV = 2;
+    const int64_t rounds_k = (n4 + 64 * UK - 1) / (64 * UK), rounds_v = (v4 + 64 * UV - 1) / (64 * UV);
+    const int64_t rounds = rounds_k > rounds_v ? rounds_k : rounds_v;
+    for (int64_t r = 0; r < rounds; ++r) {
+      uint4 uk[UK], uv[UV];
+#pragma unroll
+      for (int u = 0; u < UK; ++u) {
+        const int64_t i = r * 64 * UK + 64 * u + lane;
+        uk[u] = i < n4 ? ks4[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        const int64_t i = r * 64 * UV + 64 * u + lane;
+        uv[u] = i < v4 ? vs4[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UK; ++u) mk = fold(mk, uk[u]);
+#pragma unroll
+      for (int u = 0; u < UV; ++u) mv = fold(mv, uv[u]);
     }
-    for (; i < n4; i += 64) mk = fold(mk, ks4[i]);
-    i = lane;
-    for (; i + 64 < v4; i += 128) {
-      const uint4 u0 = vs4[i], u1 = vs4[i + 64];
-      mv = fold(fold(mv, u0), u1);
-    }
-    for (; i < v4; i += 64) mv = fold(mv, vs4[i]);
   }
   qmax = wave_max(qmax) * fabsf(a.qscale);
   const float skmax = wave_max(h2f((unsigned short)mk));
@@ -544,22 +602,19 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
     }
   }
 
-  // Full blocks, two register buffers: block k+1's loads are in flight while block k
-  // computes.  Prefetches are unconditional (clamped to the last full block, whose
-  // duplicate load is simply not used) so that no branch surrounds a load.
+  // Full blocks: every register set is refilled with the next block right after its
+  // last use, so each set's loads have a whole block of work to hide behind.  The
+  // refills are unconditional (clamped to the last full block, whose repeated load hits
+  // the cache and is not used) so that no branch surrounds a load.
   const int64_t last_full = nfull - 1;
-  for (int64_t blk = blk0; blk < nfull; blk += 2) {
-    const int64_t b1 = blk + 1 < last_full ? blk + 1 : last_full;
-    load_block<BITS, G, true>(RB, pb, b1 * BLK, BLK, j);
-    process_block<BITS, GQA, G, true>(RA, BLK, qv, k_unscale, Ev, lds, st, lo, j);
-    const int64_t b2 = blk + 2 < last_full ? blk + 2 : last_full;
-    load_block<BITS, G, true>(RA, pb, b2 * BLK, BLK, j);
-    if (blk + 1 < nfull) process_block<BITS, GQA, G, true>(RB, BLK, qv, k_unscale, Ev, lds, st, lo, j);
+  for (int64_t blk = blk0; blk < nfull; ++blk) {
+    const int64_t nb = blk + 1 < last_full ? blk + 1 : last_full;
+    process_block<BITS, GQA, G, true, true>(R, BLK, qv, k_unscale, Ev, lds, st, lo, j, pb, nb * BLK);
   }
   if (tail) {
     const int nv = (int)(t_hi - nfull * BLK);
-    load_block<BITS, G, false>(RA, pb, nfull * BLK, nv, j);
-    process_block<BITS, GQA, G, false>(RA, nv, qv, k_unscale, Ev, lds, st, lo, j);
+    load_block<BITS, G, false>(R, pb, nfull * BLK, nv, j);
+    process_block<BITS, GQA, G, false, false>(R, nv, qv, k_unscale, Ev, lds, st, lo, j, pb, 0);
   }
 
   // Finish: fold the integer accumulators and the Value-zero term, undo 2^Ev.
@@ -714,76 +769,94 @@ __device__ __forceinline__ void combine(int n, Src src, float* dst, int64_t dst_
   }
 }
 
-// Workgroups per CU the register budget allows: the double-buffered block inputs plus
-// the integer accumulators of 8 query heads (or of 4-bit codes) need more than half of
-// the register file.
-// Final merge by the last workgroup of a pair: the n_parts partials are spread over
-// the 4 waves (part i goes to wave i mod 4) and each lane keeps a running
-// (m, l, acc) per head for channels 2*lane, 2*lane+1.  Loads of U parts are issued
-// before any of them is used, so the partials written by other CUs are fetched in a
-// few round trips.  The 4 per-wave records are then combined in `scratch` (LDS).
+// Final merge by the last workgroup of a pair, 32 partials per round.  Each (partial,
+// head) pair's (m, l) is loaded once, by one thread, into LDS ([head][partial]); thread
+// (head hd, channels c, c+1) loads the accumulators of every partial of the round, and
+// both kinds of loads are in flight together.  The fold has no branches: indices past
+// the last partial are clamped and weighted 0, and empty partials (l == 0) weigh 0.
+// Partials are folded in a fixed order with an online rescale.
 template <int GQA>
-__device__ void merge_pair(const float* __restrict__ base, int n_parts, float* __restrict__ out,
-                           float (*scratch)[GQA * PSTRIDE]) {
-  constexpr int U = 32 / GQA;                    // parts in flight per lane
-  const int lane = threadIdx.x & 63, pg = threadIdx.x >> 6;
-  float m[GQA], l[GQA], o0[GQA], o1[GQA];
+__device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n_parts,
+                                           float* __restrict__ out, float2* ml_lds) {
+  constexpr int MERGE_CH = 32;
+  constexpr int ITEMS = GQA * (D / 2);
+  constexpr int IPT = (ITEMS + NT - 1) / NT;       // (head, channel pair) items per thread
+  static_assert(MERGE_CH * GQA <= NT, "one (m, l) load per thread and round");
+  float m[IPT], l[IPT], o0[IPT], o1[IPT];
 #pragma unroll
-  for (int hd = 0; hd < GQA; ++hd) {
-    m[hd] = -INFINITY;
-    l[hd] = 0.f;
-    o0[hd] = o1[hd] = 0.f;
+  for (int it = 0; it < IPT; ++it) {
+    m[it] = -INFINITY;
+    l[it] = o0[it] = o1[it] = 0.f;
   }
-  for (int i0 = pg; i0 < n_parts; i0 += WAVES * U) {
-    float2 ml[U][GQA], ov[U][GQA];
+  for (int i0 = 0; i0 < n_parts; i0 += MERGE_CH) {
+    const int nc = n_parts - i0 < MERGE_CH ? n_parts - i0 : MERGE_CH;
+    float2 ov[IPT][MERGE_CH];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + WAVES * u;
+    for (int it = 0; it < IPT; ++it) {
+      const int idx = threadIdx.x + it * NT;
+      const int hd = min(idx / (D / 2), GQA - 1), c = 2 * (idx % (D / 2));
 #pragma unroll
-      for (int hd = 0; hd < GQA; ++hd) {
-        const float* rec = base + ((int64_t)i * GQA + hd) * PSTRIDE;
-        ml[u][hd] = i < n_parts ? make_float2(load_coherent(rec + D), load_coherent(rec + D + 1))
-                                : make_float2(0.f, 0.f);
-        ov[u][hd] = i < n_parts ? make_float2(load_coherent(rec + 2 * lane),
-                                              load_coherent(rec + 2 * lane + 1))
-                                : make_float2(0.f, 0.f);
+      for (int u = 0; u < MERGE_CH; ++u) {
+        const int i = min(i0 + u, n_parts - 1);
+        ov[it][u] = load_coherent2(base + ((int64_t)i * GQA + hd) * PSTRIDE + c);
       }
     }
+    if (threadIdx.x < MERGE_CH * GQA) {
+      const int u = threadIdx.x / GQA, hd = threadIdx.x % GQA;
+      const int i = min(i0 + u, n_parts - 1);
+      const float2 ml = load_coherent2(base + ((int64_t)i * GQA + hd) * PSTRIDE + D);
+      ml_lds[hd * MERGE_CH + u] = u < nc ? ml : make_float2(-INFINITY, 0.f);
+    }
+    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int it = 0; it < IPT; ++it) {
+      const int idx = threadIdx.x + it * NT;
+      const int hd = min(idx / (D / 2), GQA - 1);
+      float2 ml[MERGE_CH];
 #pragma unroll
-      for (int hd = 0; hd < GQA; ++hd) {
-        if (ml[u][hd].y > 0.f) {                 // skip empty partials (l == 0)
-          const float mn = fmaxf(m[hd], ml[u][hd].x);
-          const float wa = __builtin_amdgcn_exp2f(m[hd] - mn);
-          const float wb = __builtin_amdgcn_exp2f(ml[u][hd].x - mn);
-          l[hd] = l[hd] * wa + ml[u][hd].y * wb;
-          o0[hd] = o0[hd] * wa + ov[u][hd].x * wb;
-          o1[hd] = o1[hd] * wa + ov[u][hd].y * wb;
-          m[hd] = mn;
-        }
+      for (int u = 0; u < MERGE_CH; u += 2) {
+        const float4 q = *reinterpret_cast<const float4*>(&ml_lds[hd * MERGE_CH + u]);
+        ml[u] = make_float2(q.x, q.y);
+        ml[u + 1] = make_float2(q.z, q.w);
       }
-    }
-  }
-  float* rec = scratch[pg];
+      float mc = m[it];
 #pragma unroll
-  for (int hd = 0; hd < GQA; ++hd) {
-    rec[hd * PSTRIDE + 2 * lane] = o0[hd];
-    rec[hd * PSTRIDE + 2 * lane + 1] = o1[hd];
-    if (lane == 0) {
-      rec[hd * PSTRIDE + D] = m[hd];
-      rec[hd * PSTRIDE + D + 1] = l[hd];
+      for (int u = 0; u < MERGE_CH; ++u) mc = fmaxf(mc, ml[u].y > 0.f ? ml[u].x : -INFINITY);
+      const float mref = mc > -INFINITY ? mc : 0.f;
+      const float wa = __builtin_amdgcn_exp2f(m[it] - mref);
+      float lt = l[it] * wa, a0 = o0[it] * wa, a1 = o1[it] * wa;
+#pragma unroll
+      for (int u = 0; u < MERGE_CH; ++u) {
+        const float w = ml[u].y > 0.f ? __builtin_amdgcn_exp2f(ml[u].x - mref) : 0.f;
+        lt = fmaf(ml[u].y, w, lt);
+        a0 = fmaf(ov[it][u].x, w, a0);
+        a1 = fmaf(ov[it][u].y, w, a1);
+      }
+      l[it] = lt;
+      o0[it] = a0;
+      o1[it] = a1;
+      m[it] = mc;
     }
+    __syncthreads();                                 // ml_lds is rewritten next round
   }
-  __syncthreads();
-  combine<GQA>(WAVES, [&](int i) { return (const float*)scratch[i]; }, out, D, false);
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int idx = threadIdx.x + it * NT;
+    if (idx >= ITEMS) continue;
+    const int hd = idx / (D / 2), c = 2 * (idx % (D / 2));
+    const float inv = 1.f / l[it];
+    *reinterpret_cast<float2*>(out + (int64_t)hd * D + c) = make_float2(o0[it] * inv, o1[it] * inv);
+  }
 }
 
-template <int BITS, int GQA>
-constexpr int wgs_per_cu() { return (BITS == 2 && GQA <= 4) ? 2 : 1; }
+// Workgroups per CU that the register budget of each variant allows (the build turns
+// a missed occupancy target into an error, so this table stays true).
+constexpr int wgs_per_cu(int bits, int gqa, int G) {
+  return gqa > 4 ? 1 : (bits == 2 || G == 64) ? 3 : 2;
+}
 
 template <int BITS, int GQA, int G>
-__global__ __launch_bounds__(NT, (wgs_per_cu<BITS, GQA>())) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NT, wgs_per_cu(BITS, GQA, G)) void decode_kernel(DecodeArgs a) {
   constexpr int NMT = (GQA + 3) / 4;
   struct ResidLds {
     float qf[GQA * D];
@@ -850,7 +923,7 @@ __global__ __launch_bounds__(NT, (wgs_per_cu<BITS, GQA>())) void decode_kernel(D
   const float* base = a.part + (pair * n_parts * GQA) * PSTRIDE;
   const int64_t b = pair / a.L.H, h = pair % a.L.H;
   float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
-  merge_pair<GQA>(base, n_parts, o, comb);
+  merge_pair<GQA>(base, n_parts, o, reinterpret_cast<float2*>(&comb[0][0]));
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -882,7 +955,7 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   int64_t ns = n_split_req;
   if (ns <= 0) {
     // one round of resident workgroups on 256 CUs, at least 4 blocks per wave
-    const int per_cu = (L.bits == 2 && gqa <= 4) ? 2 : 1;     // wgs_per_cu<>() on the host
+    const int per_cu = wgs_per_cu(L.bits, gqa, L.G);
     const int64_t target_wgs = 256 * per_cu;                    // incl. one residual wg/pair
     ns = target_wgs > 2 * pairs ? (target_wgs - pairs) / pairs : 1;
     const int64_t cap = (nblk + 4 * WAVES - 1) / (4 * WAVES);
