@@ -17,18 +17,22 @@
 // integers (one shift and mask per four codes), and the real side is written in
 // 32-bit fixed point as four balanced int8 limbs, one MFMA row per limb:
 //   x = round_toward_zero(v * 2^E),  x = l0 + 2^8 l1 + 2^16 l2 + 2^24 l3,  l_i in [-128, 127]
-// E is chosen per wave from the largest |q| s (resp. s_t) of the wave's token range
-// so that |x| <= 2^30.  Integer products are exact; the limb sums are recombined in
-// float32.
+// E is chosen per (sequence, KV head) from its largest |q| s (resp. s_t), which the
+// quantizer keeps in scale_max, so that |x| <= 2^30.  Integer products are exact; the
+// limb sums are recombined in float32.
 //
-// Work split.  Each (sequence, KV head) pair's quantized tokens are cut into 64-token
-// blocks; the 4 waves of each of n_split workgroups take contiguous runs of blocks,
-// each wave with its own online softmax (running max m, sum l).
-// One extra workgroup per pair attends over the float16 residual rows.  The 4 waves
-// of a workgroup combine in LDS; the workgroups of a pair write partials, and the
-// last one to arrive (an integer arrival counter, reset by that workgroup) merges
-// them in split order:  m* = max m_s,  l* = sum l_s 2^(m_s - m*),  o = sum acc_s
-// 2^(m_s - m*) / l*.  No floating-point atomics; the result is deterministic.
+// Work split.  One workgroup per CU holds all the waves that fit there.  Each
+// (sequence, KV head) pair's quantized tokens are cut into 64-token blocks, and
+// n_split workgroups take contiguous shares of them; the first also takes the float16
+// window rows in 32-row chunks.  Inside a workgroup the waves take chunks and blocks
+// from an LDS counter, each wave with its own online softmax (running max m, sum l),
+// so waves that run ahead take more blocks.  The waves combine in LDS in wave order;
+// the workgroups of a pair write partials, and the last one to arrive (an integer
+// arrival counter, reset by that workgroup) merges them in split order:
+//   m* = max m_s,  l* = sum l_s 2^(m_s - m*),  o = sum acc_s 2^(m_s - m*) / l*.
+// No floating-point atomics.  Which wave takes which block varies from run to run,
+// and float sums in a different order round differently, so repeated runs agree to
+// float32 rounding rather than bit for bit.
 //
 // Logits are kept in base 2 (the query is pre-multiplied by sm_scale * log2(e)).
 #include <type_traits>
@@ -39,8 +43,6 @@ namespace kivi {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int WAVES = 4;
-constexpr int NT = 64 * WAVES;
 constexpr int BLK = 64;              // tokens per block step of a wave
 constexpr int PSTRIDE = D + 2;       // partial per head: acc[D], m, l
 
@@ -55,9 +57,17 @@ struct DecodeArgs {
   int64_t Tq;           // quantized tokens
   int64_t nblk;         // 64-token blocks per pair (the last may hold 32 tokens)
   int r;                // residual tokens
-  int n_split;          // quantized workgroups per pair
+  int nw;               // workgroups per pair
   float qscale;         // sm_scale * log2(e)
 };
+
+// Waves per SIMD that the register budget of each variant allows; a workgroup holds
+// 4 SIMDs' worth.  The build turns a kernel that misses this occupancy into an error
+// (launch bounds of one workgroup per CU with a register limit derived from it).
+constexpr int waves_per_simd(int bits, int gqa, int G) {
+  return gqa > 4 ? 1 : gqa > 2 ? 2 : (bits == 2 || G == 64) ? 3 : 2;
+}
+constexpr int kCUs = 256;            // compute units of one MI355X
 
 // ---- small device helpers ---------------------------------------------------------
 
@@ -81,10 +91,24 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp<0x121>(x);
   return x;
 }
+// Lane ^ 16 inside each 32-lane half (ds_swizzle bit-mask mode: and 0x1F, xor 0x10),
+// then reductions over 32 lanes and over the wave without lane-index registers.
+__device__ __forceinline__ float swizzle_xor16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+__device__ __forceinline__ float half_max32(float x) {
+  x = row_max16(x);
+  return fmaxf(x, swizzle_xor16(x));
+}
+__device__ __forceinline__ float half_sum32(float x) {
+  x = row_sum16(x);
+  return x + swizzle_xor16(x);
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
+  x = half_max32(x);
+  const int b = __builtin_bit_cast(int, x);
+  return fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+               __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)));
 }
 // LDS hand-off between lanes of one wave: LDS operations of a wave execute in order,
 // so only the compiler must be kept from moving LDS accesses across this point; the
@@ -111,10 +135,14 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 __device__ __forceinline__ float h2f(unsigned short h) {
   return __half2float(__ushort_as_half(h));
 }
-// 32-bit fixed point -> four balanced int8 limbs packed in one word (byte i = limb i).
-__device__ __forceinline__ uint32_t to_limbs(float v) {
-  const int x = (int)v;                          // round toward zero, |x| <= 2^30
-  return ((uint32_t)x + 0x00808080u) ^ 0x00808080u;
+// 32-bit fixed point -> four balanced int8 limbs packed in one word (byte i = limb i,
+// sum of limb_i * 256^i = x).  The caller passes vb = v + LIMB_BIAS computed in float
+// (one fused multiply-add with the product that forms v); for |v| < 2^30 the float
+// addition rounds by at most 64, far below the resolution of the operands, and then
+// x = trunc(vb) - 0x808080 has the limbs trunc(vb) ^ 0x808080.
+constexpr float LIMB_BIAS = 8421504.f;           // 0x808080
+__device__ __forceinline__ uint32_t limbs_biased(float vb) {
+  return (uint32_t)(int)vb ^ 0x00808080u;
 }
 // exponent E with |v| * 2^E < 2^30 for every |v| <= vmax (0 if vmax == 0)
 __device__ __forceinline__ int fixed_exponent(float vmax) {
@@ -127,37 +155,25 @@ __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Code operand layouts (byte position p of a lane's 16-byte operand <-> element).
-// Keys, one token, K-step ks, lane group j: the 16 channels 32j + 16ks + [0, 16).
-//   2-bit: p = 4s + b  <-> channel 32j + 16ks + 4b + s
-//   4-bit: p = 4(2dd + s) + b <-> channel 32j + 16ks + 8dd + 2b + s
-// Values, one channel, one 16-token run: same formulas with "token of the run".
+// Code operands.  With the word-interleaved packing, shifting a packed word right by
+// BITS*s and masking one field per byte yields codes 4s .. 4s+3 of the word in byte
+// order, so a lane's 16-byte operand holds its codes in natural order (Keys: channels
+// 32j + 16ks + [0, 16) of one token; Values: the 16 tokens of run j of one channel).
+// 2-bit words skip the shift where a mask alone isolates the field: byte p of the
+// operand then carries code * 2^code_shift(p), and the other operand of the product
+// carries the matching 2^-code_shift(p).
 template <int BITS>
-__device__ __forceinline__ void channel_to_pos(int c, int& ks, int& j, int& p) {
-  j = c >> 5;
-  ks = (c >> 4) & 1;
-  if constexpr (BITS == 2) {
-    const int b = (c & 15) >> 2, s = c & 3;
-    p = 4 * s + b;
-  } else {
-    const int dd = (c >> 3) & 1, b = (c & 7) >> 1, s = c & 1;
-    p = 4 * (2 * dd + s) + b;
-  }
+__host__ __device__ constexpr int code_shift(int p) {
+  return BITS == 2 ? 2 * (((p & 15) >> 2) < 2 ? ((p & 15) >> 2) : 2) : 0;
 }
-template <int BITS>
-__device__ __forceinline__ int run_token_to_pos(int u) {
-  if constexpr (BITS == 2) return 4 * (u & 3) + (u >> 2);
-  else return 8 * (u >> 3) + 4 * (u & 1) + ((u & 7) >> 1);
-}
-// Unpack 16 codes of one K-step (2-bit: one word; 4-bit: two words) into int8 bytes.
 template <int BITS>
 __device__ __forceinline__ i32x4 unpack16(uint32_t w0, uint32_t w1) {
   i32x4 u;
   if constexpr (BITS == 2) {
-    u[0] = (int)(w0 & 0x03030303u);
-    u[1] = (int)((w0 >> 2) & 0x03030303u);
-    u[2] = (int)((w0 >> 4) & 0x03030303u);
-    u[3] = (int)((w0 >> 6) & 0x03030303u);
+    u[0] = (int)(w0 & 0x03030303u);            // codes 0..3    (x1)
+    u[1] = (int)(w0 & 0x0C0C0C0Cu);            // codes 4..7    (x4)
+    u[2] = (int)(w0 & 0x30303030u);            // codes 8..11   (x16)
+    u[3] = (int)((w0 >> 2) & 0x30303030u);     // codes 12..15  (x16)
   } else {
     u[0] = (int)(w0 & 0x0F0F0F0Fu);
     u[1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
@@ -169,27 +185,33 @@ __device__ __forceinline__ i32x4 unpack16(uint32_t w0, uint32_t w1) {
 
 // Per-wave LDS of the quantized path.  The query-limb operand of one (group, M-tile,
 // K-step) is 16 rows of 4 lane-group blocks of 16 bytes; rows are padded to 80 bytes
-// and K-steps to 1344 bytes so that the 16-bit limb writes of the group preparation hit
-// at most two lanes per bank and the 16-byte operand reads of 8 lanes are conflict-free.
+// so that the 16-byte operand reads of 8 lanes are conflict-free.  The probability
+// operand is 16 rows of 4 Value runs of 16 bytes.
 constexpr int QA_ROW = 80;                 // bytes per operand row (64 used)
 constexpr int QA_KS = 16 * QA_ROW + 64;    // bytes per K-step block
 template <int NMT>
 struct WaveLds {
-  uint8_t qa[2][NMT][2][QA_KS];       // [group in block][M-tile][K-step][row*QA_ROW + jg*16 + pos]
-  uint8_t pa[NMT][16][4][16];         // [M-tile][row][run][pos]
+  alignas(16) uint8_t qa[2][NMT][2][QA_KS];   // [group in block][M-tile][K-step][row*QA_ROW + jg*16 + pos]
+  alignas(16) uint8_t pa[NMT][16][4][16];     // [M-tile][row][run][token in run]
 };
 
 // ---- the quantized token range of one wave ----------------------------------------
 
-// Global-memory inputs of one 64-token block for one lane (loaded a block ahead).
+// Column lo of Q.K^T N-tile nt is token 2lo + (nt & 1) + 32 (nt >> 1) of the block:
+// tiles 0-1 cover tokens 0..31 and tiles 2-3 tokens 32..63, so each tile lies in one
+// Key group, and a lane's four tokens are two adjacent pairs of the Value runs lo/8
+// and 2 + lo/8.
+__device__ __forceinline__ int tile_token(int lo, int nt) { return 2 * lo + (nt & 1) + 32 * (nt >> 1); }
+
+// Global-memory inputs of one 64-token block for one lane.
 template <int BITS>
 struct BlockRegs {
   static constexpr int KW = BITS == 2 ? 2 : 4;    // Key-code words per token per lane
   static constexpr int VW = BITS == 2 ? 8 : 16;   // Value-code words per lane
-  uint32_t k[4][KW];        // N-tile nt: token tb + 16nt + lo, channels 32j .. 32j+31
+  uint32_t k[4][KW];        // N-tile nt: token tile_token(lo, nt), channels 32j .. 32j+31
   uint32_t v[VW];           // run j of the block, channels 8lo .. 8lo+7
   i32x4 ks[2], kz[2];       // Key scale/zero of the block's groups, channels 8lo .. 8lo+7
-  unsigned short sv[4], zv[4];   // token tb + 16nt + lo: Value scale and zero
+  uint32_t sv[2], zv[2];    // Value scale/zero of tokens 32k + 2lo, 32k + 2lo + 1
 };
 
 // Buffer descriptors of one (sequence, KV head) pair's slabs, and the lane offsets
@@ -206,19 +228,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 // The loads of one block come in four sets, each refilled for the next block right
 // after its last use in the current one.  FULL: all 64 tokens of the block are in the
-// history (compile-time: no branches); otherwise n_valid (a multiple of 16) are.
+// history (compile-time: no branches); otherwise the first n_valid = 32 are.
 template <int BITS, bool FULL>
 __device__ __forceinline__ void load_kcodes(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
                                             int n_valid, int nt) {
   constexpr int KB = D * BITS / 8;
   const int sk = (int)(tb * KB);
-  if (FULL || nt < n_valid / 16) {
+  const int off = pb.off_k + ((nt & 1) + 32 * (nt >> 1)) * KB;
+  if (FULL || 32 * (nt >> 1) < n_valid) {
     if constexpr (BITS == 2) {
-      const auto u = __builtin_amdgcn_raw_buffer_load_b64(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
+      const auto u = __builtin_amdgcn_raw_buffer_load_b64(pb.kc, off, sk, 0);
       R.k[nt][0] = (uint32_t)u[0];
       R.k[nt][1] = (uint32_t)u[1];
     } else {
-      const auto u = __builtin_amdgcn_raw_buffer_load_b128(pb.kc, pb.off_k + 16 * KB * nt, sk, 0);
+      const auto u = __builtin_amdgcn_raw_buffer_load_b128(pb.kc, off, sk, 0);
 #pragma unroll
       for (int w = 0; w < 4; ++w) R.k[nt][w] = (uint32_t)u[w];
     }
@@ -229,14 +252,14 @@ __device__ __forceinline__ void load_kcodes(BlockRegs<BITS>& R, const PairBufs& 
 }
 template <int BITS, bool FULL>
 __device__ __forceinline__ void load_vscale(BlockRegs<BITS>& R, const PairBufs& pb, int64_t tb,
-                                            int n_valid, int nt) {
+                                            int n_valid, int k) {
   const int ssv = (int)(tb * 2);
-  if (FULL || nt < n_valid / 16) {
-    R.sv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vsc, pb.off_sv + 32 * nt, ssv, 0);
-    R.zv[nt] = __builtin_amdgcn_raw_buffer_load_b16(pb.vze, pb.off_sv + 32 * nt, ssv, 0);
+  if (FULL || 32 * k < n_valid) {
+    R.sv[k] = __builtin_amdgcn_raw_buffer_load_b32(pb.vsc, pb.off_sv + 64 * k, ssv, 0);
+    R.zv[k] = __builtin_amdgcn_raw_buffer_load_b32(pb.vze, pb.off_sv + 64 * k, ssv, 0);
   } else {
-    R.sv[nt] = 0;
-    R.zv[nt] = 0;
+    R.sv[k] = 0u;
+    R.zv[k] = 0u;
   }
 }
 template <int BITS, int G, bool FULL>
@@ -274,10 +297,9 @@ __device__ __forceinline__ void load_block(BlockRegs<BITS>& R, const PairBufs& p
 #pragma unroll
   for (int gi = 0; gi < BLK / G; ++gi) load_kscale<BITS, G, FULL>(R, pb, tb, n_valid, gi);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    load_kcodes<BITS, FULL>(R, pb, tb, n_valid, nt);
-    load_vscale<BITS, FULL>(R, pb, tb, n_valid, nt);
-  }
+  for (int nt = 0; nt < 4; ++nt) load_kcodes<BITS, FULL>(R, pb, tb, n_valid, nt);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) load_vscale<BITS, FULL>(R, pb, tb, n_valid, k);
   load_vcodes<BITS, FULL>(R, pb, tb, n_valid, j);
 }
 // Keeps the scheduler from moving a refill above the last use of the registers it
@@ -292,25 +314,45 @@ struct WaveState {
   i32x4 acc_i[NMT][8];
 };
 
+// Fold the integer accumulators into the float ones (scale factor alpha).
+template <int NMT>
+__device__ __forceinline__ void fold_acc(WaveState<NMT>& st, int mt, float alpha) {
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const i32x4 ci = st.acc_i[mt][n];
+    const float v = st.acc_f[mt][n] + (float)ci[0] + 256.f * (float)ci[1] +
+                    65536.f * (float)ci[2] + 16777216.f * (float)ci[3];
+    st.acc_f[mt][n] = v * alpha;
+    st.acc_i[mt][n] = i32x4{0, 0, 0, 0};
+  }
+}
+
+// Per-lane constants of the quantized path.
+struct LaneConsts {
+  float k_unscale;     // 2^-Ek
+  float zk[2];         // 2^(code_shift - Ek) of the lane's channels 8lo+0..3 and 8lo+4..7
+  int Ev;              // probability limbs carry p * 2^(Ev - vshift)
+  int vshift;          // code_shift of the lane's token positions 2(lo%8), 2(lo%8)+1
+};
+
 // One 64-token block: group preparation, Q.K^T, online softmax, P.V.
 // REFILL: each register set is reloaded with the full block at token tb_next right
 // after its last use here.
 template <int BITS, int GQA, int G, bool FULL, bool REFILL>
 __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
-                                              const float (&qv)[(GQA + 3) / 4][8],
-                                              float k_unscale, int Ev,
+                                              const float (&qk)[(GQA + 3) / 4][8],
+                                              const LaneConsts& lc,
                                               WaveLds<(GQA + 3) / 4>& lds,
                                               WaveState<(GQA + 3) / 4>& st, int lo, int j,
                                               const PairBufs& pb, int64_t tb_next) {
   constexpr int NMT = (GQA + 3) / 4;
   constexpr int NG = BLK / G;
   const int n_groups_blk = FULL ? NG : (n_valid + G - 1) / G;
-  const int n_tiles = FULL ? 4 : n_valid / 16;
 
   // (1) group preparation: query limbs into LDS, and sum_c q_c z_c per head.
-  // Lane (lo, j) owns channels 8lo .. 8lo+7 of head 4mt + j; its limbs are transposed
-  // in registers (v_perm) so that each write carries one limb of 2 (2-bit) or 4 (4-bit)
-  // channels that are adjacent in the operand.
+  // Lane (lo, j) owns channels 8lo .. 8lo+7 of head 4mt + j: operand row 4j + limb,
+  // K-step (lo/2)%2, bytes 16(lo/4) + 8(lo%2) .. +7.  The four limbs of its 8 values
+  // are transposed in registers (v_perm) and written as one 8-byte store per limb.
   float qz[NG][NMT];
   const int jg = lo >> 2, ksl = (lo >> 1) & 1;
 #pragma unroll
@@ -325,45 +367,35 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         uint32_t x[8];
+        float za = 0.f, zb = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float sc = h2f((unsigned short)(sw[i >> 1] >> (16 * (i & 1))));
           const float ze = h2f((unsigned short)(zw[i >> 1] >> (16 * (i & 1))));
-          x[i] = to_limbs(qv[mt][i] * sc);
-          qz[gi][mt] = fmaf(qv[mt][i], ze, qz[gi][mt]);
+          x[i] = limbs_biased(fmaf(qk[mt][i], sc, LIMB_BIAS));
+          if (i < 4) za = fmaf(qk[mt][i], ze, za);
+          else zb = fmaf(qk[mt][i], ze, zb);
         }
-        uint8_t* blkp = &lds.qa[gi][mt][ksl][(4 * j) * QA_ROW + jg * 16];
-        if constexpr (BITS == 2) {
-          // channel 8lo + i sits at position 4(i%4) + 2(lo%2) + i/4 of its row block
+        qz[gi][mt] = fmaf(za, lc.zk[0], zb * lc.zk[1]);
+        uint32_t t[2][4];                         // t[h][L]: limb L of values 4h .. 4h+3
 #pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4) {
-            const uint32_t w01 = __builtin_amdgcn_perm(x[s4 + 4], x[s4], 0x05010400u);
-            const uint32_t w23 = __builtin_amdgcn_perm(x[s4 + 4], x[s4], 0x07030602u);
-            uint8_t* d = blkp + 4 * s4 + 2 * (lo & 1);
-            *reinterpret_cast<uint16_t*>(d) = (uint16_t)w01;
-            *reinterpret_cast<uint16_t*>(d + QA_ROW) = (uint16_t)(w01 >> 16);
-            *reinterpret_cast<uint16_t*>(d + 2 * QA_ROW) = (uint16_t)w23;
-            *reinterpret_cast<uint16_t*>(d + 3 * QA_ROW) = (uint16_t)(w23 >> 16);
-          }
-        } else {
-          // channel 8lo + i sits at position 4(2(lo%2) + i%2) + i/2 of its row block
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const uint32_t a = x[s2], b = x[s2 + 2], c = x[s2 + 4], e = x[s2 + 6];
-            const uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
-            const uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
-            const uint32_t t2 = __builtin_amdgcn_perm(e, c, 0x05010400u);   // c0 e0 c1 e1
-            const uint32_t t3 = __builtin_amdgcn_perm(e, c, 0x07030602u);   // c2 e2 c3 e3
-            uint8_t* d = blkp + 4 * (2 * (lo & 1) + s2);
-            *reinterpret_cast<uint32_t*>(d) = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-            *reinterpret_cast<uint32_t*>(d + QA_ROW) = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-            *reinterpret_cast<uint32_t*>(d + 2 * QA_ROW) = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-            *reinterpret_cast<uint32_t*>(d + 3 * QA_ROW) = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-          }
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t a01 = __builtin_amdgcn_perm(x[4 * hh + 1], x[4 * hh], 0x05010400u);
+          const uint32_t b01 = __builtin_amdgcn_perm(x[4 * hh + 1], x[4 * hh], 0x07030602u);
+          const uint32_t a23 = __builtin_amdgcn_perm(x[4 * hh + 3], x[4 * hh + 2], 0x05010400u);
+          const uint32_t b23 = __builtin_amdgcn_perm(x[4 * hh + 3], x[4 * hh + 2], 0x07030602u);
+          t[hh][0] = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+          t[hh][1] = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+          t[hh][2] = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+          t[hh][3] = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
         }
+        uint8_t* rowp = &lds.qa[gi][mt][ksl][(4 * j) * QA_ROW + jg * 16 + 8 * (lo & 1)];
+#pragma unroll
+        for (int L = 0; L < 4; ++L)
+          *reinterpret_cast<uint2*>(rowp + L * QA_ROW) = make_uint2(t[0][L], t[1][L]);
       }
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) qz[gi][mt] = row_sum16(qz[gi][mt]) * k_unscale;
+      for (int mt = 0; mt < NMT; ++mt) qz[gi][mt] = row_sum16(qz[gi][mt]);
     }
     if constexpr (REFILL) {
       refill_point();
@@ -372,24 +404,30 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
   }
   wave_lds_sync();
 
-  // (2) Q.K^T on the matrix cores: C[mt][nt] rows (head, limb), columns tokens.
+  // (2) Q.K^T on the matrix cores: C[mt][nt] rows (head, limb), columns tokens.  The
+  // query operands of a group are read once, at the group's first tile.
   i32x4 cqk[NMT][4];
+  i32x4 aop[NMT][2];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) cqk[mt][nt] = i32x4{0, 0, 0, 0};
-    if (FULL || nt < n_tiles) {
+    if (FULL || 32 * (nt >> 1) < n_valid) {
       const int gi = nt * 16 / G;
+      if ((nt * 16) % G == 0) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            aop[mt][ks] = *reinterpret_cast<const i32x4*>(&lds.qa[gi][mt][ks][lo * QA_ROW + j * 16]);
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const i32x4 bop = BITS == 2 ? unpack16<BITS>(R.k[nt][ks], 0u)
                                     : unpack16<BITS>(R.k[nt][2 * ks % BlockRegs<BITS>::KW],
                                                      R.k[nt][(2 * ks + 1) % BlockRegs<BITS>::KW]);
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          const i32x4 aop = *reinterpret_cast<const i32x4*>(&lds.qa[gi][mt][ks][lo * QA_ROW + j * 16]);
-          cqk[mt][nt] = mfma_i8(aop, bop, cqk[mt][nt]);
-        }
+        for (int mt = 0; mt < NMT; ++mt) cqk[mt][nt] = mfma_i8(aop[mt][ks], bop, cqk[mt][nt]);
       }
     }
     if constexpr (REFILL) {
@@ -402,15 +440,15 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
   float sv[4], zv[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    sv[nt] = h2f(R.sv[nt]);
-    zv[nt] = h2f(R.zv[nt]);
+    sv[nt] = h2f((unsigned short)(R.sv[nt >> 1] >> (16 * (nt & 1))));
+    zv[nt] = h2f((unsigned short)(R.zv[nt >> 1] >> (16 * (nt & 1))));
   }
   if constexpr (REFILL) {
     refill_point();
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) load_vscale<BITS, true>(R, pb, tb_next, BLK, nt);
+    for (int k = 0; k < 2; ++k) load_vscale<BITS, true>(R, pb, tb_next, BLK, k);
   }
-  const float k_hi = 65536.f * k_unscale;
+  const float k_hi = 65536.f * lc.k_unscale;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     float z[4];
@@ -419,10 +457,12 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
     for (int nt = 0; nt < 4; ++nt) {
       const int gi = nt * 16 / G;
       const i32x4 c = cqk[mt][nt];
-      const float lo16 = (float)(c[0] + c[1] * 256);      // |c_i| < 2^18: exact int
+      // |c_i| < 2^20, so c0 + 256 c1 fits in int32; rounding it to float stays far
+      // below the resolution of the fixed-point operands
+      const float lo16 = (float)(c[0] + c[1] * 256);
       const float hi16 = (float)(c[2] + c[3] * 256);
-      z[nt] = fmaf(hi16, k_hi, fmaf(lo16, k_unscale, qz[gi][mt]));
-      if (!FULL && nt >= n_tiles) z[nt] = -INFINITY;
+      z[nt] = fmaf(hi16, k_hi, fmaf(lo16, lc.k_unscale, qz[gi][mt]));
+      if (!FULL && 32 * (nt >> 1) >= n_valid) z[nt] = -INFINITY;
       bm = fmaxf(bm, z[nt]);
     }
     bm = row_max16(bm);
@@ -431,31 +471,34 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
     // into float and rescale (a wave-uniform branch; alpha = 1 on the other rows).
     if (__builtin_amdgcn_read_exec() & __ballot(m_new > st.m_run[mt])) {
       const float alpha = __builtin_amdgcn_exp2f(st.m_run[mt] - m_new);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const i32x4 ci = st.acc_i[mt][n];
-        const float v = st.acc_f[mt][n] + (float)ci[0] + 256.f * (float)ci[1] +
-                        65536.f * (float)ci[2] + 16777216.f * (float)ci[3];
-        st.acc_f[mt][n] = v * alpha;
-        st.acc_i[mt][n] = i32x4{0, 0, 0, 0};
-      }
+      fold_acc(st, mt, alpha);
       st.l_run[mt] *= alpha;
       st.pz_run[mt] *= alpha;
       st.m_run[mt] = m_new;
     }
-    const float m_shift = st.m_run[mt] - (float)Ev;     // p' = p * 2^Ev
+    // p' = p * 2^(Ev - vshift): the Value operand bytes of this lane's token positions
+    // carry 2^vshift.
+    const float m_shift = st.m_run[mt] - (float)(lc.Ev - lc.vshift);
+    uint32_t lw[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float p = __builtin_amdgcn_exp2f(z[nt] - m_shift);
-      if (!FULL && nt >= n_tiles) p = 0.f;
+      if (!FULL && 32 * (nt >> 1) >= n_valid) p = 0.f;
       st.l_run[mt] += p;
       st.pz_run[mt] = fmaf(p, zv[nt], st.pz_run[mt]);
-      const uint32_t lw = to_limbs(p * sv[nt]);
-      uint8_t* dst = &lds.pa[mt][4 * j][nt][run_token_to_pos<BITS>(lo)];
-      dst[0] = (uint8_t)lw;
-      dst[64] = (uint8_t)(lw >> 8);
-      dst[128] = (uint8_t)(lw >> 16);
-      dst[192] = (uint8_t)(lw >> 24);
+      lw[nt] = limbs_biased(fmaf(p, sv[nt], LIMB_BIAS));
+    }
+    // tokens 2lo, 2lo+1 sit at positions 2(lo%8), 2(lo%8)+1 of run lo/8; tokens
+    // 32+2lo, 33+2lo at the same positions of run 2 + lo/8; row 4j + limb.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t l01 = __builtin_amdgcn_perm(lw[2 * hh + 1], lw[2 * hh], 0x05010400u);
+      const uint32_t l23 = __builtin_amdgcn_perm(lw[2 * hh + 1], lw[2 * hh], 0x07030602u);
+      uint8_t* dst = &lds.pa[mt][4 * j][2 * hh + (lo >> 3)][2 * (lo & 7)];
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)l01;
+      *reinterpret_cast<uint16_t*>(dst + 64) = (uint16_t)(l01 >> 16);
+      *reinterpret_cast<uint16_t*>(dst + 128) = (uint16_t)l23;
+      *reinterpret_cast<uint16_t*>(dst + 192) = (uint16_t)(l23 >> 16);
     }
   }
   wave_lds_sync();
@@ -478,10 +521,27 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
   }
 }
 
-// Writes comb[GQA][PSTRIDE] (acc with the Value-zero term folded in, m, l).
+// ---- work queue of one workgroup ---------------------------------------------------
+
+// Items of a workgroup's queue: the first n_res are 32-row chunks of the float16
+// window (first workgroup of a pair only), the rest its share of 64-token blocks.
+// Waves take items in order from an LDS counter; lane 0 does the LDS atomic.
+__device__ __forceinline__ int grab_item(int* counter) {
+  int v = 0;
+  if ((threadIdx.x & 63) == 0) v = atomicAdd(counter, 1);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// ---- the quantized blocks of one wave -----------------------------------------------
+
+// Processes the block items handed out by the queue, starting with `item` (>= n_res),
+// and writes comb[GQA][PSTRIDE] (acc with the Value-zero term folded in, m, l).  The
+// fixed-point exponents come from the pair's largest Key/Value scale, so they hold for
+// any block of the pair.
 template <int BITS, int GQA, int G>
-__device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, int64_t blk1,
-                               WaveLds<(GQA + 3) / 4>& lds, float* comb) {
+__device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pair, int item, int n_res,
+                                int n_items, int64_t b_lo, int64_t b_hi, int* counter,
+                                WaveLds<(GQA + 3) / 4>& lds, float* comb) {
   constexpr int NMT = (GQA + 3) / 4;              // M-tiles of 4 heads x 4 limbs
   const LayerView& L = a.L;
   const int lane = threadIdx.x & 63;
@@ -490,39 +550,35 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
 
   constexpr int KB = D * BITS / 8;
   constexpr int VRB = kVRun * BITS / 8;             // Value code bytes per (run, channel)
-  const uint8_t* kc = L.k_codes + pair * L.kc_pair();
-  const __half* ksc = L.k_scale + pair * L.ks_pair();
-  const __half* kze = L.k_zero + pair * L.ks_pair();
-  const uint8_t* vc = L.v_codes + pair * L.vc_pair();
-  const unsigned short* vsc = reinterpret_cast<const unsigned short*>(L.v_scale + pair * L.vs_pair());
-  const unsigned short* vze = reinterpret_cast<const unsigned short*>(L.v_zero + pair * L.vs_pair());
   PairBufs pb;
-  pb.kc = make_rsrc(kc, L.kc_pair());
-  pb.ksc = make_rsrc(ksc, L.ks_pair() * 2);
-  pb.kze = make_rsrc(kze, L.ks_pair() * 2);
-  pb.vc = make_rsrc(vc, L.vc_pair());
-  pb.vsc = make_rsrc(vsc, L.vs_pair() * 2);
-  pb.vze = make_rsrc(vze, L.vs_pair() * 2);
-  pb.off_k = lo * KB + j * (KB / 4);
+  pb.kc = make_rsrc(L.k_codes + pair * L.kc_pair(), L.kc_pair());
+  pb.ksc = make_rsrc(L.k_scale + pair * L.ks_pair(), L.ks_pair() * 2);
+  pb.kze = make_rsrc(L.k_zero + pair * L.ks_pair(), L.ks_pair() * 2);
+  pb.vc = make_rsrc(L.v_codes + pair * L.vc_pair(), L.vc_pair());
+  pb.vsc = make_rsrc(L.v_scale + pair * L.vs_pair(), L.vs_pair() * 2);
+  pb.vze = make_rsrc(L.v_zero + pair * L.vs_pair(), L.vs_pair() * 2);
+  pb.off_k = 2 * lo * KB + j * (KB / 4);
   pb.off_v = j * D * VRB + 8 * lo * VRB;
   pb.off_ks = 16 * lo;
-  pb.off_sv = 2 * lo;
-  const int Hq = L.H * GQA;
-  const __half* qp = a.q + (b * Hq + h * GQA) * D;
+  pb.off_sv = 4 * lo;
+  const __half* qp = a.q + (b * L.H * GQA + h * GQA) * D;
 
-  const int64_t t_lo = blk0 * BLK;
-  const int64_t t_hi = blk1 * BLK < a.Tq ? blk1 * BLK : a.Tq;
-  // Blocks [blk0, nfull) hold 64 tokens; a last half block (32 tokens) may follow.
-  const int64_t nfull = (t_hi - t_lo) / BLK + blk0;
-  const bool tail = nfull < blk1;
+  // The last block of the history holds 32 tokens when T_q is not a multiple of 64.
+  // In the share that contains it, it is the first block item, so the wave that takes
+  // it handles it before any full block and the loop below sees full blocks only.
+  const bool has_partial = (a.Tq % BLK) != 0 && b_hi == a.nblk && b_hi > b_lo;
+  auto block_of = [&](int it) -> int64_t {
+    if (!has_partial) return b_lo + (it - n_res);
+    return it == n_res ? a.nblk - 1 : b_lo + (it - n_res - 1);
+  };
+  const int partial_item = has_partial ? n_res : -1;
 
-  // The first block's loads go out before the pre-pass so that both latencies overlap.
+  // The first block's loads go out before the exponent set-up so that both overlap.
   BlockRegs<BITS> R;
-  if (nfull > blk0) load_block<BITS, G, true>(R, pb, blk0 * BLK, BLK, j);
+  if (item < n_items && item != partial_item)
+    load_block<BITS, G, true>(R, pb, block_of(item) * BLK, BLK, j);
 
-  // -- pre-pass: largest |q| (scaled), largest Key scale and Value scale in range --
-  // Lane (lo, j) holds the query values it prepares later: head 4mt + j, channels
-  // 8lo .. 8lo+7, i.e. the 16 bytes at offset 16*lane of M-tile mt's 4 heads.
+  // Query values of this lane: head 4mt + j, channels 8lo .. 8lo+7.
   float qraw[NMT][8];
   float qmax = 0.f;
 #pragma unroll
@@ -537,57 +593,25 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
       qmax = fmaxf(qmax, fabsf(qraw[mt][i]));
     }
   }
-  uint32_t mk = 0, mv = 0;
-  {
-    const int64_t g_lo = t_lo / G, g_hi = (t_hi + G - 1) / G;
-    const uint4* ks4 = reinterpret_cast<const uint4*>(ksc + g_lo * D);
-    const int64_t n4 = (g_hi - g_lo) * (D / 8);
-    const uint4* vs4 = reinterpret_cast<const uint4*>(vsc + t_lo);
-    const int64_t v4 = (t_hi - t_lo) / 8;
-    auto fold = [](uint32_t m, const uint4& u) {
-      // non-negative float16 values order like their bit patterns
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0xFFFFu, w[k] >> 16));
-      return m;
-    };
-    // Every load of a round is issued before any is folded: one round covers 16 blocks.
-    constexpr int UK = 8, UV = 2;
-    const int64_t rounds_k = (n4 + 64 * UK - 1) / (64 * UK), rounds_v = (v4 + 64 * UV - 1) / (64 * UV);
-    const int64_t rounds = rounds_k > rounds_v ? rounds_k : rounds_v;
-    for (int64_t r = 0; r < rounds; ++r) {
-      uint4 uk[UK], uv[UV];
-#pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        const int64_t i = r * 64 * UK + 64 * u + lane;
-        uk[u] = i < n4 ? ks4[i] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        const int64_t i = r * 64 * UV + 64 * u + lane;
-        uv[u] = i < v4 ? vs4[i] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < UK; ++u) mk = fold(mk, uk[u]);
-#pragma unroll
-      for (int u = 0; u < UV; ++u) mv = fold(mv, uv[u]);
-    }
-  }
   qmax = wave_max(qmax) * fabsf(a.qscale);
-  const float skmax = wave_max(h2f((unsigned short)mk));
-  const float svmax = wave_max(h2f((unsigned short)mv));
-  const int Ek = fixed_exponent(qmax * skmax);
-  const int Ev = fixed_exponent(svmax);
-  const float k_unscale = __builtin_amdgcn_ldexpf(1.f, -Ek);
-  const float v_unscale = __builtin_amdgcn_ldexpf(1.f, -Ev);
-
-  // Query values of this lane for the group preparation: heads 4mt + j, channels
-  // 8lo .. 8lo+7, scaled by sm_scale*log2(e)*2^Ek.
-  float qv[NMT][8];
+  const float kmax = L.scale_max[2 * pair], vmax = L.scale_max[2 * pair + 1];
+  const int Ek = fixed_exponent(qmax * kmax);
+  LaneConsts lc;
+  lc.Ev = fixed_exponent(vmax);
+  lc.k_unscale = __builtin_amdgcn_ldexpf(1.f, -Ek);
+  const float v_unscale = __builtin_amdgcn_ldexpf(1.f, -lc.Ev);
+  // this lane's channels 8lo + i sit at operand positions 8(lo%2) + i
+  const int ksh0 = code_shift<BITS>(8 * (lo & 1)), ksh1 = code_shift<BITS>(8 * (lo & 1) + 4);
+  lc.zk[0] = __builtin_amdgcn_ldexpf(1.f, ksh0 - Ek);
+  lc.zk[1] = __builtin_amdgcn_ldexpf(1.f, ksh1 - Ek);
+  lc.vshift = code_shift<BITS>(2 * (lo & 7));
+  // scaled by sm_scale*log2(e)*2^(Ek - code_shift)
+  float qk[NMT][8];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qv[mt][i] = __builtin_amdgcn_ldexpf(qraw[mt][i] * a.qscale, Ek);
+    for (int i = 0; i < 8; ++i)
+      qk[mt][i] = __builtin_amdgcn_ldexpf(qraw[mt][i] * a.qscale, Ek - (i < 4 ? ksh0 : ksh1));
 
   WaveState<NMT> st;
 #pragma unroll
@@ -602,27 +626,43 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
     }
   }
 
-  // Full blocks: every register set is refilled with the next block right after its
-  // last use, so each set's loads have a whole block of work to hide behind.  The
-  // refills are unconditional (clamped to the last full block, whose repeated load hits
-  // the cache and is not used) so that no branch surrounds a load.
-  const int64_t last_full = nfull - 1;
-  for (int64_t blk = blk0; blk < nfull; ++blk) {
-    const int64_t nb = blk + 1 < last_full ? blk + 1 : last_full;
-    process_block<BITS, GQA, G, true, true>(R, BLK, qv, k_unscale, Ev, lds, st, lo, j, pb, nb * BLK);
+  // Every register set is refilled with the wave's next block right after its last
+  // use, so each set's loads have a whole block of work to hide behind; the item after
+  // that is taken from the queue one block ahead.  Refills target the current block
+  // again when there is no next full block (a cache hit whose data is not used).
+  // Every 1024 blocks the integer accumulators are folded into float, which bounds
+  // them by 1024 * 64 * 128 * 48 < 2^31.
+  if (item == partial_item) {
+    const int64_t blk = a.nblk - 1;
+    const int nv = (int)(a.Tq - blk * BLK);
+    load_block<BITS, G, false>(R, pb, blk * BLK, nv, j);
+    process_block<BITS, GQA, G, false, false>(R, nv, qk, lc, lds, st, lo, j, pb, 0);
+    item = grab_item(counter);
+    if (item < n_items) load_block<BITS, G, true>(R, pb, block_of(item) * BLK, BLK, j);
   }
-  if (tail) {
-    const int nv = (int)(t_hi - nfull * BLK);
-    load_block<BITS, G, false>(R, pb, nfull * BLK, nv, j);
-    process_block<BITS, GQA, G, false, false>(R, nv, qv, k_unscale, Ev, lds, st, lo, j, pb, 0);
+  int nxt = item < n_items ? grab_item(counter) : n_items;
+  int done = 0;
+  while (item < n_items) {
+    const int after = nxt < n_items ? grab_item(counter) : n_items;
+    const int64_t blk = block_of(item);
+    const int64_t nb = nxt < n_items ? block_of(nxt) : blk;
+    process_block<BITS, GQA, G, true, true>(R, BLK, qk, lc, lds, st, lo, j, pb, nb * BLK);
+    if ((++done & 1023) == 0) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) fold_acc(st, mt, 1.f);
+    }
+    item = nxt;
+    nxt = after;
   }
 
-  // Finish: fold the integer accumulators and the Value-zero term, undo 2^Ev.
+  // Finish: fold the integer accumulators and the Value-zero term, undo 2^Ev (and the
+  // lane's 2^-vshift on l and the zero term).
+  const float vsh = __builtin_amdgcn_ldexpf(1.f, lc.vshift);
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int hd = 4 * mt + j;
-    const float lsum = row_sum16(st.l_run[mt]);
-    const float pz = row_sum16(st.pz_run[mt]);
+    const float lsum = row_sum16(st.l_run[mt] * vsh);
+    const float pz = row_sum16(st.pz_run[mt] * vsh);
     if (hd < GQA) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
@@ -639,112 +679,149 @@ __device__ void quantized_wave(const DecodeArgs& a, int64_t pair, int64_t blk0, 
   }
 }
 
-// ---- float16 residual rows [t0, t1) of one wave (VALU) ------------------------------
+// ---- float16 window rows ------------------------------------------------------------
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Online-softmax state of one wave over window rows.  Q.K^T runs on the float16
+// matrix cores (v_mfma_f32_16x16x32_f16: query heads as rows, window rows as
+// columns), so lane group j = lane / 16 holds heads 4j .. 4j+3: m[i] and l[i] are those
+// heads' running max and sum, equal over the 16 lanes of the group.  P.V runs on the
+// VALU with every lane holding channels 2*lane, 2*lane+1 of acc for every head.
 template <int GQA>
-__device__ void residual_wave(const DecodeArgs& a, int64_t pair, int t0, int t1, const float* qf,
-                              float* pw, float* comb) {
+struct ResidState {
+  float m[4], l[4];
+  float acc[GQA][2];
+};
+
+// Query operand of the window product: lane (lo, j) holds head lo (zero past GQA),
+// channels 32ks + 8j .. +7 for K-step ks.
+template <int GQA>
+__device__ __forceinline__ void load_q_f16(const __half* qp, f16x8 (&aq)[4]) {
+  const int lane = threadIdx.x & 63, lo = lane & 15, j = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    f16x8 v = {};
+    if (lo < GQA) v = *reinterpret_cast<const f16x8*>(qp + (int64_t)lo * D + 32 * ks + 8 * j);
+    aq[ks] = v;
+  }
+}
+
+// Window rows [c0, c0 + n_valid), n_valid <= 32.  Every Key and Value load of the
+// chunk goes out before any is used (rows past the chunk re-read its last row; their
+// probabilities are 0).  Float16 products are exact in float32 (subnormal operands
+// aside), accumulated in float32.
+template <int GQA>
+__device__ __forceinline__ void residual_rows(const DecodeArgs& a, int64_t pair, int c0,
+                                              int n_valid, const f16x8 (&aq)[4], float* pw,
+                                              ResidState<GQA>& rs) {
   const LayerView& L = a.L;
-  const int lane = threadIdx.x & 63;
-  const int t_l = lane & 31, half = lane >> 5;
+  const int lane = threadIdx.x & 63, lo = lane & 15, j = lane >> 4;
   const __half* kr = L.k_resid + pair * L.rs_pair();
   const __half* vr = L.v_resid + pair * L.rs_pair();
-  constexpr int NH = (GQA + 1) / 2;              // heads per lane in the logit phase
-  float m_run[GQA], l_run[GQA];
-  float acc[GQA][2];                             // channels 2*lane, 2*lane+1
+  float* palpha = pw + GQA * 32;
+  // Key operands: column lo of tile nt is row 16nt + lo; lane group j holds channels
+  // 32ks + 8j .. +7 of K-step ks.
+  f16x8 bk[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int rr = 16 * nt + lo < n_valid ? 16 * nt + lo : n_valid - 1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      bk[nt][ks] = *reinterpret_cast<const f16x8*>(kr + (int64_t)(c0 + rr) * D + 32 * ks + 8 * j);
+  }
+  // Value pairs, channels 2*lane, 2*lane+1 of the 32 rows (one descriptor: shared lane
+  // offset, wave-uniform row offset in the scalar offset)
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(vr, L.rs_pair() * 2);
+  __half2 vv[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int rr = t < n_valid ? t : n_valid - 1;
+    vv[t] = __builtin_bit_cast(__half2, __builtin_amdgcn_raw_buffer_load_b32(vres, 4 * lane,
+                                                                            (c0 + rr) * D * 2, 0));
+  }
+  f32x4 d[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    d[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      d[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[ks], bk[nt][ks], d[nt], 0, 0, 0);
+  }
+  // logits of head 4j + i, rows lo and 16 + lo, in base 2
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hd = 4 * j + i;
+    const float z0 = lo < n_valid ? d[0][i] * a.qscale : -INFINITY;
+    const float z1 = 16 + lo < n_valid ? d[1][i] * a.qscale : -INFINITY;
+    const float m_new = fmaxf(rs.m[i], row_max16(fmaxf(z0, z1)));
+    const float alpha = __builtin_amdgcn_exp2f(rs.m[i] - m_new);
+    const float p0 = __builtin_amdgcn_exp2f(z0 - m_new), p1 = __builtin_amdgcn_exp2f(z1 - m_new);
+    rs.l[i] = rs.l[i] * alpha + row_sum16(p0 + p1);
+    rs.m[i] = m_new;
+    if (hd < GQA) {
+      pw[hd * 32 + lo] = p0;
+      pw[hd * 32 + 16 + lo] = p1;
+      if (lo == 0) palpha[hd] = alpha;
+    }
+  }
+  wave_lds_sync();
 #pragma unroll
   for (int hd = 0; hd < GQA; ++hd) {
-    m_run[hd] = -INFINITY;
-    l_run[hd] = 0.f;
-    acc[hd][0] = acc[hd][1] = 0.f;
+    const float al = palpha[hd];
+    rs.acc[hd][0] *= al;
+    rs.acc[hd][1] *= al;
   }
-  float* palpha = pw + GQA * 32;
-  for (int c0 = t0; c0 < t1; c0 += 32) {
-    const int n_valid = (t1 - c0) < 32 ? (t1 - c0) : 32;
-    const bool valid = t_l < n_valid;
-    float z[NH];
+  // 4 rows at a time for every head, so that few probabilities are live at once
 #pragma unroll
-    for (int k = 0; k < NH; ++k) z[k] = 0.f;
-    if (valid) {
-      const uint4* row = reinterpret_cast<const uint4*>(kr + (int64_t)(c0 + t_l) * D);
-#pragma unroll 4
-      for (int i = 0; i < D / 8; ++i) {
-        const uint4 u = row[i];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = h2f((unsigned short)w[e]), x1 = h2f((unsigned short)(w[e] >> 16));
-#pragma unroll
-          for (int k = 0; k < NH; ++k) {
-            const int hd = half + 2 * k;
-            if (hd < GQA) z[k] += qf[hd * D + 8 * i + 2 * e] * x0 + qf[hd * D + 8 * i + 2 * e + 1] * x1;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NH; ++k) {
-      const int hd = half + 2 * k;
-      if (hd >= GQA) continue;
-      const float zz = valid ? z[k] : -INFINITY;
-      float bm = zz;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off, 32));
-      const float m_new = fmaxf(m_run[hd], bm);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[hd] - m_new);
-      const float p = valid ? __builtin_amdgcn_exp2f(zz - m_new) : 0.f;
-      l_run[hd] = l_run[hd] * alpha + p;
-      m_run[hd] = m_new;
-      pw[hd * 32 + t_l] = p;
-      if (t_l == 0) palpha[hd] = alpha;
-    }
-    wave_lds_sync();
-    // All 32 rows' Value pairs of this lane are loaded before use (rows past the
-    // chunk re-read its last row; their probabilities are 0).
-    __half2 vv[32];
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const int row = t < n_valid ? t : n_valid - 1;
-      vv[t] = *reinterpret_cast<const __half2*>(vr + (int64_t)(c0 + row) * D + 2 * lane);
-    }
+  for (int t4 = 0; t4 < 8; ++t4) {
+    __builtin_amdgcn_sched_barrier(0);
+    const float2 v[4] = {__half22float2(vv[4 * t4]), __half22float2(vv[4 * t4 + 1]),
+                         __half22float2(vv[4 * t4 + 2]), __half22float2(vv[4 * t4 + 3])};
 #pragma unroll
     for (int hd = 0; hd < GQA; ++hd) {
-      const float al = palpha[hd];
-      float s0 = acc[hd][0] * al, s1 = acc[hd][1] * al;
+      const float4 p = reinterpret_cast<const float4*>(pw + hd * 32)[t4];
+      const float pv[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        const float p = pw[hd * 32 + t];
-        s0 = fmaf(p, __low2float(vv[t]), s0);
-        s1 = fmaf(p, __high2float(vv[t]), s1);
+      for (int e = 0; e < 4; ++e) {
+        rs.acc[hd][0] = fmaf(pv[e], v[e].x, rs.acc[hd][0]);
+        rs.acc[hd][1] = fmaf(pv[e], v[e].y, rs.acc[hd][1]);
       }
-      acc[hd][0] = s0;
-      acc[hd][1] = s1;
     }
-    wave_lds_sync();
   }
+  wave_lds_sync();
+}
+
+template <int GQA>
+__device__ __forceinline__ void residual_record(const ResidState<GQA>& rs, float* comb) {
+  const int lane = threadIdx.x & 63, lo = lane & 15, j = lane >> 4;
 #pragma unroll
   for (int hd = 0; hd < GQA; ++hd) {
-    comb[hd * PSTRIDE + 2 * lane] = acc[hd][0];
-    comb[hd * PSTRIDE + 2 * lane + 1] = acc[hd][1];
-    // m_run is uniform over the lanes of the half that owns the head
-    float lsum = l_run[hd];
+    comb[hd * PSTRIDE + 2 * lane] = rs.acc[hd][0];
+    comb[hd * PSTRIDE + 2 * lane + 1] = rs.acc[hd][1];
+  }
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off, 32);
-    if (lane == (hd & 1) * 32) {
-      comb[hd * PSTRIDE + D] = m_run[hd];
-      comb[hd * PSTRIDE + D + 1] = lsum;
+  for (int i = 0; i < 4; ++i) {
+    const int hd = 4 * j + i;
+    if (hd < GQA && lo == 0) {
+      comb[hd * PSTRIDE + D] = rs.m[i];
+      comb[hd * PSTRIDE + D + 1] = rs.l[i];
     }
   }
 }
 
-// Combine the 4 per-wave results of a workgroup (or the n_parts partials of a pair)
-// in a fixed order.  src(i) returns the i-th [GQA][PSTRIDE] record.
-template <int GQA, typename Src>
-__device__ __forceinline__ void combine(int n, Src src, float* dst, int64_t dst_hstride,
-                                        bool with_ml) {
-  for (int idx = threadIdx.x; idx < GQA * D; idx += NT) {
+// Combine n [GQA][PSTRIDE] records (a workgroup's per-wave results) in a fixed order
+// into dst; src(i) returns the i-th record.  NTH threads take part.
+template <int GQA, int NTH, typename Src>
+__device__ __forceinline__ void combine(int n, Src src, float* dst) {
+  for (int idx = threadIdx.x; idx < GQA * D; idx += NTH) {
     const int hd = idx / D, c = idx % D;
     float mstar = -INFINITY;
-    for (int i = 0; i < n; ++i) mstar = fmaxf(mstar, src(i)[hd * PSTRIDE + D]);
+    for (int i = 0; i < n; ++i) {
+      const float* rec = src(i) + hd * PSTRIDE;
+      if (rec[D + 1] > 0.f) mstar = fmaxf(mstar, rec[D]);
+    }
     float l = 0.f, o = 0.f;
     if (mstar > -INFINITY) {
       for (int i = 0; i < n; ++i) {
@@ -757,31 +834,27 @@ __device__ __forceinline__ void combine(int n, Src src, float* dst, int64_t dst_
         }
       }
     }
-    if (with_ml) {
-      store_coherent(&dst[hd * dst_hstride + c], o);
-      if (c == 0) {
-        store_coherent(&dst[hd * dst_hstride + D], mstar);
-        store_coherent(&dst[hd * dst_hstride + D + 1], l);
-      }
-    } else {
-      dst[hd * dst_hstride + c] = o / l;
+    store_coherent(&dst[hd * PSTRIDE + c], o);
+    if (c == 0) {
+      store_coherent(&dst[hd * PSTRIDE + D], mstar);
+      store_coherent(&dst[hd * PSTRIDE + D + 1], l);
     }
   }
 }
 
-// Final merge by the last workgroup of a pair, 32 partials per round.  Each (partial,
+// Final merge by the last workgroup of a pair, 32 (or 16) partials per round.  Each (partial,
 // head) pair's (m, l) is loaded once, by one thread, into LDS ([head][partial]); thread
 // (head hd, channels c, c+1) loads the accumulators of every partial of the round, and
 // both kinds of loads are in flight together.  The fold has no branches: indices past
 // the last partial are clamped and weighted 0, and empty partials (l == 0) weigh 0.
 // Partials are folded in a fixed order with an online rescale.
-template <int GQA>
+template <int GQA, int NTH>
 __device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n_parts,
                                            float* __restrict__ out, float2* ml_lds) {
-  constexpr int MERGE_CH = 32;
   constexpr int ITEMS = GQA * (D / 2);
-  constexpr int IPT = (ITEMS + NT - 1) / NT;       // (head, channel pair) items per thread
-  static_assert(MERGE_CH * GQA <= NT, "one (m, l) load per thread and round");
+  constexpr int IPT = (ITEMS + NTH - 1) / NTH;     // (head, channel pair) items per thread
+  constexpr int MERGE_CH = 32 / IPT;               // partials per round
+  static_assert(MERGE_CH * GQA <= NTH, "one (m, l) load per thread and round");
   float m[IPT], l[IPT], o0[IPT], o1[IPT];
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
@@ -793,7 +866,7 @@ __device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n
     float2 ov[IPT][MERGE_CH];
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int idx = threadIdx.x + it * NT;
+      const int idx = threadIdx.x + it * NTH;
       const int hd = min(idx / (D / 2), GQA - 1), c = 2 * (idx % (D / 2));
 #pragma unroll
       for (int u = 0; u < MERGE_CH; ++u) {
@@ -810,27 +883,30 @@ __device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int idx = threadIdx.x + it * NT;
+      const int idx = threadIdx.x + it * NTH;
       const int hd = min(idx / (D / 2), GQA - 1);
-      float2 ml[MERGE_CH];
-#pragma unroll
-      for (int u = 0; u < MERGE_CH; u += 2) {
-        const float4 q = *reinterpret_cast<const float4*>(&ml_lds[hd * MERGE_CH + u]);
-        ml[u] = make_float2(q.x, q.y);
-        ml[u + 1] = make_float2(q.z, q.w);
-      }
+      const float4* mlp = reinterpret_cast<const float4*>(&ml_lds[hd * MERGE_CH]);
       float mc = m[it];
 #pragma unroll
-      for (int u = 0; u < MERGE_CH; ++u) mc = fmaxf(mc, ml[u].y > 0.f ? ml[u].x : -INFINITY);
+      for (int u = 0; u < MERGE_CH; u += 2) {
+        const float4 q = mlp[u / 2];
+        mc = fmaxf(mc, q.y > 0.f ? q.x : -INFINITY);
+        mc = fmaxf(mc, q.w > 0.f ? q.z : -INFINITY);
+      }
       const float mref = mc > -INFINITY ? mc : 0.f;
       const float wa = __builtin_amdgcn_exp2f(m[it] - mref);
       float lt = l[it] * wa, a0 = o0[it] * wa, a1 = o1[it] * wa;
 #pragma unroll
-      for (int u = 0; u < MERGE_CH; ++u) {
-        const float w = ml[u].y > 0.f ? __builtin_amdgcn_exp2f(ml[u].x - mref) : 0.f;
-        lt = fmaf(ml[u].y, w, lt);
-        a0 = fmaf(ov[it][u].x, w, a0);
-        a1 = fmaf(ov[it][u].y, w, a1);
+      for (int u = 0; u < MERGE_CH; u += 2) {
+        const float4 q = mlp[u / 2];
+        const float w0 = q.y > 0.f ? __builtin_amdgcn_exp2f(q.x - mref) : 0.f;
+        const float w1 = q.w > 0.f ? __builtin_amdgcn_exp2f(q.z - mref) : 0.f;
+        lt = fmaf(q.y, w0, lt);
+        a0 = fmaf(ov[it][u].x, w0, a0);
+        a1 = fmaf(ov[it][u].y, w0, a1);
+        lt = fmaf(q.w, w1, lt);
+        a0 = fmaf(ov[it][u + 1].x, w1, a0);
+        a1 = fmaf(ov[it][u + 1].y, w1, a1);
       }
       l[it] = lt;
       o0[it] = a0;
@@ -841,7 +917,7 @@ __device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n
   }
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
-    const int idx = threadIdx.x + it * NT;
+    const int idx = threadIdx.x + it * NTH;
     if (idx >= ITEMS) continue;
     const int hd = idx / (D / 2), c = 2 * (idx % (D / 2));
     const float inv = 1.f / l[it];
@@ -849,64 +925,76 @@ __device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n
   }
 }
 
-// Workgroups per CU that the register budget of each variant allows (the build turns
-// a missed occupancy target into an error, so this table stays true).
-constexpr int wgs_per_cu(int bits, int gqa, int G) {
-  return gqa > 4 ? 1 : (bits == 2 || G == 64) ? 3 : 2;
-}
+// ---- the kernel ---------------------------------------------------------------------
 
+// One workgroup per CU holding every wave the register budget allows there: WAVES =
+// 4 SIMDs x waves_per_simd.  Workgroup s of a pair takes a contiguous share of the
+// pair's 64-token blocks; the first workgroup also takes the float16 window, whose
+// 32-row chunks count RES_COST blocks each in the shares.  Inside a workgroup, waves
+// take window chunks, then blocks, from an LDS counter.  Each workgroup writes one
+// partial; the last to arrive merges them.
+constexpr int RES_COST = 1;
 template <int BITS, int GQA, int G>
-__global__ __launch_bounds__(NT, wgs_per_cu(BITS, GQA, G)) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_kernel(DecodeArgs a) {
   constexpr int NMT = (GQA + 3) / 4;
-  struct ResidLds {
-    float qf[GQA * D];
-    float pw[WAVES][GQA * 32 + GQA];
-  };
-  union Lds {
-    WaveLds<NMT> wave[WAVES];
-    ResidLds res;
-  };
-  __shared__ Lds lds;
-  __shared__ float comb[WAVES][GQA * PSTRIDE];
+  constexpr int WAVES = 4 * waves_per_simd(BITS, GQA, G);
+  constexpr int NTH = 64 * WAVES;
+  __shared__ WaveLds<NMT> wl[WAVES];
+  __shared__ alignas(16) float pw[WAVES][GQA * 32 + 4 * ((GQA + 3) / 4)];  // window probabilities
+  __shared__ float comb[2 * WAVES][GQA * PSTRIDE];    // [0, WAVES): blocks; then window
+  __shared__ int counter;
   __shared__ int last_flag;
 
   const int64_t P = (int64_t)a.L.B * a.L.H;
   const int64_t pair = blockIdx.x % P;
-  const int s = (int)(blockIdx.x / P);            // 0: residual rows, s >= 1: split s - 1
+  const int s = (int)(blockIdx.x / P);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_parts = a.n_split + 1;
+  const int64_t b = pair / a.L.H, h = pair % a.L.H;
 
-  if (s == 0) {
-    const int64_t b = pair / a.L.H, h = pair % a.L.H;
-    const __half* qp = a.q + (b * a.L.H * GQA + h * GQA) * D;
-    for (int i = threadIdx.x; i < GQA * D; i += NT) lds.res.qf[i] = __half2float(qp[i]) * a.qscale;
-    __syncthreads();
-    // wave w takes 32-row chunks w, w + 4, ...
-    float* cw = comb[wave];
-    for (int i = threadIdx.x & 63; i < GQA * PSTRIDE; i += 64) cw[i] = 0.f;
-    for (int hd = 0; hd < GQA; ++hd) cw[hd * PSTRIDE + D] = -INFINITY;
-    wave_lds_sync();
-    // contiguous share of rows per wave, in 32-row chunks
-    const int chunks = (a.r + 31) / 32;
-    const int c_lo = chunks * wave / WAVES, c_hi = chunks * (wave + 1) / WAVES;
-    const int t0 = 32 * c_lo, t1 = (32 * c_hi < a.r) ? 32 * c_hi : a.r;
-    if (t1 > t0) residual_wave<GQA>(a, pair, t0, t1, lds.res.qf, lds.res.pw[wave], cw);
-  } else {
-    const int split = s - 1;
-    const int64_t wb = (int64_t)a.n_split * WAVES;    // waves per pair
-    const int64_t wi = (int64_t)split * WAVES + wave;
-    const int64_t blk0 = a.nblk * wi / wb, blk1 = a.nblk * (wi + 1) / wb;
-    float* cw = comb[wave];
-    for (int i = threadIdx.x & 63; i < GQA * PSTRIDE; i += 64) cw[i] = 0.f;
-    for (int hd = 0; hd < GQA; ++hd) cw[hd * PSTRIDE + D] = -INFINITY;
-    wave_lds_sync();
-    if (blk1 > blk0) quantized_wave<BITS, GQA, G>(a, pair, blk0, blk1, lds.wave[wave], cw);
+  // this workgroup's share of the work units (window chunks first)
+  const int n_res_all = (a.r + 31) / 32;
+  const int64_t units = a.nblk + (int64_t)RES_COST * n_res_all;
+  const int64_t u_lo = units * s / a.nw, u_hi = units * (s + 1) / a.nw;
+  const int64_t res_units = (int64_t)RES_COST * n_res_all;
+  const int64_t b_lo = u_lo > res_units ? u_lo - res_units : 0;
+  const int64_t b_hi = u_hi > res_units ? u_hi - res_units : 0;
+  const int n_res = s == 0 ? n_res_all : 0;
+  const int n_items = n_res + (int)(b_hi - b_lo);
+
+  if (threadIdx.x == 0) counter = 0;
+  __syncthreads();
+
+  // window chunks
+  int item = grab_item(&counter);
+  {
+    ResidState<GQA> rs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rs.m[i] = -INFINITY;
+      rs.l[i] = 0.f;
+    }
+#pragma unroll
+    for (int hd = 0; hd < GQA; ++hd) rs.acc[hd][0] = rs.acc[hd][1] = 0.f;
+    if (item < n_res) {
+      f16x8 aq[4];
+      load_q_f16<GQA>(a.q + (b * a.L.H * GQA + h * GQA) * D, aq);
+      while (item < n_res) {
+        const int c0 = 32 * item;
+        residual_rows<GQA>(a, pair, c0, a.r - c0 < 32 ? a.r - c0 : 32, aq, pw[wave], rs);
+        item = grab_item(&counter);
+      }
+    }
+    residual_record<GQA>(rs, comb[WAVES + wave]);
   }
+  // blocks (an empty share leaves an empty record: m = -inf, l = 0)
+  quantized_items<BITS, GQA, G>(a, pair, item, n_res, n_items, b_lo, b_hi, &counter,
+                                wl[wave], comb[wave]);
   __syncthreads();
 
   // Workgroup partial -> workspace.
+  const int n_parts = a.nw;
   float* mine = a.part + ((pair * n_parts + s) * GQA) * PSTRIDE;
-  combine<GQA>(WAVES, [&](int i) { return (const float*)comb[i]; }, mine, PSTRIDE, true);
+  combine<GQA, NTH>(2 * WAVES, [&](int i) { return (const float*)comb[i]; }, mine);
 
   // Last workgroup of the pair merges all partials and resets the counter.  Every
   // thread's partial stores complete before the arrival is counted; the merging
@@ -921,9 +1009,8 @@ __global__ __launch_bounds__(NT, wgs_per_cu(BITS, GQA, G)) void decode_kernel(De
   __syncthreads();
   if (!last_flag) return;
   const float* base = a.part + (pair * n_parts * GQA) * PSTRIDE;
-  const int64_t b = pair / a.L.H, h = pair % a.L.H;
   float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
-  merge_pair<GQA>(base, n_parts, o, reinterpret_cast<float2*>(&comb[0][0]));
+  merge_pair<GQA, NTH>(base, n_parts, o, reinterpret_cast<float2*>(&comb[0][0]));
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -951,23 +1038,15 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   p.r = (int)(T - Tq);
   p.n_groups = Tq / L.G;
   const int64_t nblk = (Tq + BLK - 1) / BLK;
+  const int64_t units = nblk + (int64_t)RES_COST * ((p.r + 31) / 32);
   const int64_t pairs = (int64_t)L.B * L.H;
-  int64_t ns = n_split_req;
-  if (ns <= 0) {
-    // one round of resident workgroups on 256 CUs, at least 4 blocks per wave
-    const int per_cu = wgs_per_cu(L.bits, gqa, L.G);
-    const int64_t target_wgs = 256 * per_cu;                    // incl. one residual wg/pair
-    ns = target_wgs > 2 * pairs ? (target_wgs - pairs) / pairs : 1;
-    const int64_t cap = (nblk + 4 * WAVES - 1) / (4 * WAVES);
-    if (ns > cap) ns = cap;
-  }
-  if (ns > nblk) ns = nblk;
-  if (nblk == 0) ns = 0;
-  if (ns < 1 && nblk > 0) ns = 1;
-  p.n_split = (int)ns;
-  const int64_t n_parts = ns + 1;
+  // default: one round of CU-sized workgroups over the 256 CUs
+  int64_t nw = n_split_req > 0 ? n_split_req : kCUs / pairs;
+  if (nw > units) nw = units;
+  if (nw < 1) nw = 1;
+  p.n_split = (int)nw;
   p.ws_counters = ((size_t)pairs * sizeof(uint32_t) + 255) / 256 * 256;
-  p.ws_partials = (size_t)pairs * n_parts * gqa * PSTRIDE * sizeof(float);
+  p.ws_partials = (size_t)pairs * nw * gqa * PSTRIDE * sizeof(float);
   p.ws_partials = (p.ws_partials + 255) / 256 * 256;
   p.ws_total = p.ws_counters + p.ws_partials;
   return p;
@@ -986,13 +1065,14 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.Tq = quantized_len(T, L.R);
   a.nblk = (a.Tq + BLK - 1) / BLK;
   a.r = plan.r;
-  a.n_split = plan.n_split;
+  a.nw = plan.n_split;
   a.qscale = sm_scale * 1.4426950408889634f;
   const int64_t P = (int64_t)L.B * L.H;
-  const dim3 grid((unsigned)(P * (plan.n_split + 1)));
+  const dim3 grid((unsigned)(P * plan.n_split));
   bool ok = dispatch_decode(L.bits, gqa, L.G, [&](auto b, auto g, auto gg) {
-    hipLaunchKernelGGL((decode_kernel<decltype(b)::value, decltype(g)::value, decltype(gg)::value>),
-                       grid, dim3(NT), 0, s, a);
+    constexpr int B_ = decltype(b)::value, Q_ = decltype(g)::value, G_ = decltype(gg)::value;
+    hipLaunchKernelGGL((decode_kernel<B_, Q_, G_>), grid, dim3(256 * waves_per_simd(B_, Q_, G_)),
+                       0, s, a);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;

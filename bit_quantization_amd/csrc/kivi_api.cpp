@@ -84,15 +84,18 @@ void buffer_sizes(const kivi_dims* d, size_t out[KIVI_NUM_BUFFERS]) {
   out[5] = vmeta;
   out[6] = resid;
   out[7] = resid;
+  out[8] = unit * 2 * sizeof(float);
 }
 
 kivi_status check_cache(const kivi_cache* c) {
   if (!c) return fail(KIVI_ERR_ARG, "cache is NULL");
-  const void* p[8] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes,
-                      c->v_scale, c->v_zero,  c->k_resid, c->v_resid};
-  static const char* names[8] = {"k_codes", "k_scale", "k_zero", "v_codes",
-                                 "v_scale", "v_zero",  "k_resid", "v_resid"};
-  for (int i = 0; i < 8; ++i) {
+  const void* p[KIVI_NUM_BUFFERS] = {c->k_codes, c->k_scale, c->k_zero,
+                                     c->v_codes, c->v_scale, c->v_zero,
+                                     c->k_resid, c->v_resid, c->scale_max};
+  static const char* names[KIVI_NUM_BUFFERS] = {"k_codes", "k_scale", "k_zero",
+                                                "v_codes", "v_scale", "v_zero",
+                                                "k_resid", "v_resid", "scale_max"};
+  for (int i = 0; i < KIVI_NUM_BUFFERS; ++i) {
     if (!p[i]) return fail(KIVI_ERR_ARG, "cache.%s is NULL", names[i]);
     if (!aligned16(p[i])) return fail(KIVI_ERR_ALIGN, "cache.%s is not 16-byte aligned", names[i]);
   }
@@ -112,6 +115,7 @@ kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer) {
   L.v_zero = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->v_zero) + layer * (sz[5] / Ld));
   L.k_resid = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->k_resid) + layer * (sz[6] / Ld));
   L.v_resid = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->v_resid) + layer * (sz[7] / Ld));
+  L.scale_max = reinterpret_cast<float*>(static_cast<uint8_t*>(c->scale_max) + layer * (sz[8] / Ld));
   L.B = d->batch;
   L.H = d->kv_heads;
   L.d = d->head_dim;
@@ -293,6 +297,6 @@ kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cach
 
 const char* kivi_last_error(void) { return g_err; }
 
-int32_t kivi_abi_version(void) { return 1; }
+int32_t kivi_abi_version(void) { return 2; }
 
 }  // extern "C"

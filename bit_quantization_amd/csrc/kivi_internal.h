@@ -20,6 +20,7 @@ struct LayerView {
   __half* v_zero;
   __half* k_resid;    // [B][H][R][d]
   __half* v_resid;
+  float* scale_max;   // [B][H][2]: largest Key scale, largest Value scale
   int B, H, d, bits, G, Gv, R;
   int64_t Tmax;
 

@@ -43,6 +43,16 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits
   return p;
 }
 
+// Largest value over the wave, then raised into *p (scale maxima: non-negative floats
+// order like their bit patterns, so an unsigned atomic max is a float max).
+__device__ __forceinline__ void raise_scale_max(float* p, float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_max(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int BITS>
 __device__ __forceinline__ uint32_t quant_code(float x, const GroupParams& p) {
   constexpr float qmax = (float)((1 << BITS) - 1);
@@ -59,7 +69,8 @@ template <int BITS, int G>
 __device__ __forceinline__ void quantize_k_group(const __half* __restrict__ src,
                                                  uint8_t* __restrict__ codes,
                                                  __half* __restrict__ scale,
-                                                 __half* __restrict__ zero, uint8_t* lds) {
+                                                 __half* __restrict__ zero, uint8_t* lds,
+                                                 float* smax) {
   const int lane = threadIdx.x;
   const __half2* s2 = reinterpret_cast<const __half2*>(src);
   float x0[G], x1[G];
@@ -78,6 +89,7 @@ __device__ __forceinline__ void quantize_k_group(const __half* __restrict__ src,
   const GroupParams p1 = group_params(mn1, mx1, BITS);
   reinterpret_cast<__half2*>(scale)[lane] = __halves2half2(p0.scale, p1.scale);
   reinterpret_cast<__half2*>(zero)[lane] = __halves2half2(p0.zero, p1.zero);
+  raise_scale_max(smax, fmaxf(p0.s, p1.s));
 #pragma unroll
   for (int t = 0; t < G; ++t) {
     const uint32_t c0 = quant_code<BITS>(x0[t], p0);
@@ -85,7 +97,8 @@ __device__ __forceinline__ void quantize_k_group(const __half* __restrict__ src,
     reinterpret_cast<uint16_t*>(lds + t * D)[lane] = (uint16_t)(c0 | (c1 << 8));
   }
   __syncthreads();
-  // Pack each token row along channels, LSB-first: 32/BITS codes per 32-bit word.
+  // Pack each token row along channels: 32/BITS codes per 32-bit word, code k of a
+  // word in byte k % 4 at bit offset BITS * (k / 4).
   constexpr int CPW = 32 / BITS;
   constexpr int WPR = D / CPW;           // words per token row
   for (int w = lane; w < G * WPR; w += 64) {
@@ -93,7 +106,7 @@ __device__ __forceinline__ void quantize_k_group(const __half* __restrict__ src,
     const uint8_t* c = lds + t * D + j * CPW;
     uint32_t word = 0;
 #pragma unroll
-    for (int k = 0; k < CPW; ++k) word |= (uint32_t)c[k] << (BITS * k);
+    for (int k = 0; k < CPW; ++k) word |= (uint32_t)c[k] << (8 * (k % 4) + BITS * (k / 4));
     reinterpret_cast<uint32_t*>(codes + (int64_t)t * (D * BITS / 8))[j] = word;
   }
 }
@@ -105,7 +118,8 @@ template <int BITS, int GV>
 __device__ __forceinline__ void quantize_v_run(const __half* __restrict__ src,
                                                uint8_t* __restrict__ codes,
                                                __half* __restrict__ scale,
-                                               __half* __restrict__ zero, uint8_t* lds) {
+                                               __half* __restrict__ zero, uint8_t* lds,
+                                               float* smax) {
   const int lane = threadIdx.x;
   const int tau = lane >> 2, part = lane & 3;
   const uint4* row = reinterpret_cast<const uint4*>(src + tau * D + part * 32);
@@ -142,8 +156,13 @@ __device__ __forceinline__ void quantize_v_run(const __half* __restrict__ src,
     }
   }
   GroupParams p[NSUB];
+  float smx = 0.f;
 #pragma unroll
-  for (int k = 0; k < NSUB; ++k) p[k] = group_params(mn[k], mx[k], BITS);
+  for (int k = 0; k < NSUB; ++k) {
+    p[k] = group_params(mn[k], mx[k], BITS);
+    smx = fmaxf(smx, p[k].s);
+  }
+  raise_scale_max(smax, smx);
   constexpr int NG = D / GV;               // groups per token
   if constexpr (GV >= 32) {
     if ((part % (GV / 32)) == 0) {
@@ -163,19 +182,19 @@ __device__ __forceinline__ void quantize_v_run(const __half* __restrict__ src,
 #pragma unroll
   for (int i = 0; i < 32; ++i) myrow[i] = (uint8_t)quant_code<BITS>(x[i], p[i / SUB]);
   __syncthreads();
-  // Pack each channel's 16 tokens along tokens, LSB-first.
+  // Pack each channel's 16 tokens along tokens, in the same word order as the Keys.
   for (int c = lane; c < D; c += 64) {
     if constexpr (BITS == 2) {
       uint32_t word = 0;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) word |= (uint32_t)lds[t * D + c] << (2 * t);
+      for (int t = 0; t < 16; ++t) word |= (uint32_t)lds[t * D + c] << (8 * (t % 4) + 2 * (t / 4));
       reinterpret_cast<uint32_t*>(codes)[c] = word;
     } else {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        lo |= (uint32_t)lds[t * D + c] << (4 * t);
-        hi |= (uint32_t)lds[(t + 8) * D + c] << (4 * t);
+        lo |= (uint32_t)lds[t * D + c] << (8 * (t % 4) + 4 * (t / 4));
+        hi |= (uint32_t)lds[(t + 8) * D + c] << (8 * (t % 4) + 4 * (t / 4));
       }
       reinterpret_cast<uint2*>(codes)[c] = make_uint2(lo, hi);
     }
@@ -207,7 +226,7 @@ __global__ __launch_bounds__(64) void prefill_k_kernel(LayerView L, const __half
     quantize_k_group<BITS, G>(s + g * G * D,
                               L.k_codes + pair * L.kc_pair() + g * G * (D * BITS / 8),
                               L.k_scale + pair * L.ks_pair() + g * D,
-                              L.k_zero + pair * L.ks_pair() + g * D, lds);
+                              L.k_zero + pair * L.ks_pair() + g * D, lds, L.scale_max + 2 * pair);
   } else {
     copy_rows(s + Tq * D, L.k_resid + pair * L.rs_pair(), T - Tq);
   }
@@ -227,7 +246,8 @@ __global__ __launch_bounds__(64) void prefill_v_kernel(LayerView L, const __half
     quantize_v_run<BITS, GV>(s + j * kVRun * D,
                              L.v_codes + pair * L.vc_pair() + j * (D * kVRun * BITS / 8),
                              L.v_scale + pair * L.vs_pair() + j * kVRun * (D / GV),
-                             L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds);
+                             L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds,
+                             L.scale_max + 2 * pair + 1);
   } else {
     copy_rows(s + Tq * D, L.v_resid + pair * L.rs_pair(), T - Tq);
   }
@@ -260,7 +280,8 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
     quantize_k_group<BITS, G>(kr + (int64_t)blk * G * D,
                               L.k_codes + pair * L.kc_pair() + (t0 + blk * G) * (D * BITS / 8),
                               L.k_scale + pair * L.ks_pair() + (t0 / G + blk) * D,
-                              L.k_zero + pair * L.ks_pair() + (t0 / G + blk) * D, lds);
+                              L.k_zero + pair * L.ks_pair() + (t0 / G + blk) * D, lds,
+                              L.scale_max + 2 * pair);
     if (blk == 0) {
       __syncthreads();
       copy_rows(kn, kr, 1);
@@ -271,12 +292,19 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
                              L.v_codes + pair * L.vc_pair() +
                                  (t0 / kVRun + j) * (D * kVRun * BITS / 8),
                              L.v_scale + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV),
-                             L.v_zero + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV), lds);
+                             L.v_zero + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV), lds,
+                             L.scale_max + 2 * pair + 1);
     if (j == 0) {
       __syncthreads();
       copy_rows(vn, vr, 1);
     }
   }
+}
+
+// Entry `which` (0: Keys, 1: Values) of every (b, h) of the layer's scale_max := 0.
+__global__ __launch_bounds__(256) void reset_scale_max_kernel(float* sm, int which, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) sm[2 * i + which] = 0.f;
 }
 
 template <typename F>
@@ -304,6 +332,9 @@ bool dispatch_gv(int Gv, F&& f) {
 hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s) {
   const int64_t Tq = quantized_len(T, L.R);
+  const int pairs = L.B * L.H;
+  hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
+                     L.scale_max, 0, pairs);
   const dim3 grid((unsigned)(Tq / L.G + 1), (unsigned)(L.B * L.H));
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value>), grid, dim3(64),
@@ -317,6 +348,9 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s) {
   const int64_t Tq = quantized_len(T, L.R);
+  const int pairs = L.B * L.H;
+  hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
+                     L.scale_max, 1, pairs);
   const dim3 grid((unsigned)(Tq / kVRun + 1), (unsigned)(L.B * L.H));
   bool ok = dispatch_gv(L.Gv, [&](auto gv) {
     if (L.bits == 2)

@@ -44,7 +44,8 @@ class kivi_dims(ctypes.Structure):
                 ("max_tokens", ctypes.c_int64)]
 
 
-BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
+BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid",
+           "scale_max")
 
 
 class kivi_cache(ctypes.Structure):
@@ -129,13 +130,13 @@ class Dims:
 
 
 def kivi_cache_sizes(dims: Dims):
-    out = (ctypes.c_size_t * 8)()
+    out = (ctypes.c_size_t * len(BUFFERS))()
     _check(_lib.kivi_cache_sizes(ctypes.byref(dims.c()), out))
     return list(out)
 
 
 class Cache:
-    """The eight caller-owned device buffers of a cache, allocated with torch."""
+    """The nine caller-owned device buffers of a cache, allocated with torch."""
 
     def __init__(self, dims: Dims, device="cuda"):
         self.dims = dims
@@ -162,6 +163,8 @@ class Cache:
             return buf.view(torch.float16).view(L, B, H, T, D // d.group_v)
         if name in ("k_resid", "v_resid"):
             return buf.view(torch.float16).view(L, B, H, d.residual, D)
+        if name == "scale_max":
+            return buf.view(torch.float32).view(L, B, H, 2)
         raise KeyError(name)
 
 

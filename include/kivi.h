@@ -49,8 +49,11 @@
  *    v_zero   float16 [L][B][H_kv][T_max][d/G_v]
  *    k_resid  float16 [L][B][H_kv][R][d]               residual window rows
  *    v_resid  float16 [L][B][H_kv][R][d]
- *  Codes are packed LSB-first: code j of a packed run sits at bits
- *  [b*(j mod (8/b)), b*(j mod (8/b)) + b) of byte j / (8/b).
+ *    scale_max float32 [L][B][H_kv][2]                 largest Key scale [0] and
+ *             Value scale [1] in the quantized history (kept by the calls below)
+ *  Packed runs are little-endian 32-bit words of n = 32/b codes: code j of a run is
+ *  code e = j mod n of word j / n, which sits in byte e mod 4 of the word at bits
+ *  [b*(e / 4), b*(e / 4) + b).  (Four 2-bit or two 4-bit codes per byte.)
  *
  * Quantizer (per group of float16 values x_i; float32 arithmetic, IEEE division,
  * round-half-to-even):  x_i += 0 (so -0 becomes +0);  mn = min x_i;  mx = max x_i;
@@ -102,7 +105,11 @@ typedef struct kivi_dims {
   int64_t max_tokens;  /* T_max: token capacity per sequence, a multiple of G and 16 */
 } kivi_dims;
 
-/* The eight device buffers of a cache; layout above. */
+/* The nine device buffers of a cache; layout above.  scale_max is bookkeeping of
+ * this library: the quantize calls reset their half of a layer's entries and every
+ * quantizing call raises them to the largest scale it writes; decode reads them to
+ * fix its fixed-point exponents.  A cache restored from elsewhere must restore it
+ * too (or hold an upper bound of the scales there). */
 typedef struct kivi_cache {
   void* k_codes;
   void* k_scale;
@@ -112,11 +119,12 @@ typedef struct kivi_cache {
   void* v_zero;
   void* k_resid;
   void* v_resid;
+  void* scale_max;
 } kivi_cache;
 
-#define KIVI_NUM_BUFFERS 8
+#define KIVI_NUM_BUFFERS 9
 
-/* Byte size of each of the eight buffers, in kivi_cache field order, for all
+/* Byte size of each of the nine buffers, in kivi_cache field order, for all
  * layers.  Host-only; enqueues nothing. */
 kivi_status kivi_cache_sizes(const kivi_dims* dims, size_t bytes[KIVI_NUM_BUFFERS]);
 
@@ -126,14 +134,15 @@ kivi_status kivi_cache_sizes(const kivi_dims* dims, size_t bytes[KIVI_NUM_BUFFER
  *   k      float16 [B][H_kv][ld_tokens][d] device; tokens [0, T) are read.
  *   T      prompt length, 0 <= T <= T_max.
  *   ld     token stride of `k` (>= T).
- * Quantizes tokens [0, T_q(T)) into k_codes/k_scale/k_zero of `layer` and copies
- * tokens [T_q(T), T) into rows [0, r(T)) of k_resid. */
+ * Quantizes tokens [0, T_q(T)) into k_codes/k_scale/k_zero of `layer`, copies
+ * tokens [T_q(T), T) into rows [0, r(T)) of k_resid and sets the layer's Key entries
+ * of scale_max to the largest Key scale written (0 if none). */
 kivi_status kivi_quantize_k(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                             const void* k, int64_t T, int64_t ld_tokens, void* stream);
 
 /* Prefill quantization of the Values of one layer ("4.4 KV Cache quantization" §3.1:
  * fix a token, group along channels).  Same arguments as kivi_quantize_k, writing
- * v_codes/v_scale/v_zero and v_resid. */
+ * v_codes/v_scale/v_zero, v_resid and the Value entries of scale_max. */
 kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                             const void* v, int64_t T, int64_t ld_tokens, void* stream);
 
@@ -143,7 +152,8 @@ kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int3
  *   k_new, v_new  float16 [B][H_kv][d] device.
  * If r(T_before) == R the window is first quantized into the history at token
  * T_before - R (same arithmetic as the prefill calls); the new row then goes to row
- * r(T_before) mod R.  The cache then holds T_before + 1 tokens. */
+ * r(T_before) mod R.  The cache then holds T_before + 1 tokens; a flush raises
+ * scale_max to the largest scales it writes. */
 kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                               int64_t T_before, const void* k_new, const void* v_new,
                               void* stream);
@@ -164,17 +174,18 @@ kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t
  *              private to the library.  Zero-fill it once before its first use; it
  *              can then be reused by later calls without clearing.  Calls that may
  *              run concurrently must use distinct workspaces.
- * The result is deterministic: partial results of the token splits are combined in
- * a fixed order and no floating-point atomics are used.
+ * No floating-point atomics are used and partials are combined in a fixed order,
+ * but which wave of a workgroup takes which 64-token block varies from call to call,
+ * so repeated calls agree to float32 rounding, not bit for bit.
  * Value groups: this build's decode kernels require G_v == d (UNSUPPORTED otherwise). */
 kivi_status kivi_decode_attn(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                              int64_t T, const void* q, float sm_scale, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* As kivi_decode_attn with an explicit number of workgroups over the quantized
- * history of each (sequence, KV head) (0 = the library's choice).  The history is
- * cut into 64-token blocks and the count is clamped to the number of blocks; the
- * float16 window always gets one workgroup of its own.  Workspace size:
+/* As kivi_decode_attn with an explicit number of workgroups per (sequence, KV head)
+ * (0 = the library's choice: one round of one workgroup per CU).  The work units of a
+ * pair are the 64-token blocks of its quantized history and the 32-row chunks of its
+ * float16 window; the count is clamped to [1, units].  Workspace size:
  * kivi_decode_workspace_bytes_split. */
 kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cache,
                                    int32_t layer, int64_t T, const void* q, float sm_scale,
@@ -183,8 +194,8 @@ kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cach
 kivi_status kivi_decode_workspace_bytes_split(const kivi_dims* dims, int64_t T,
                                               int32_t n_split, size_t* bytes);
 
-/* Number of workgroups over the quantized history kivi_decode_attn uses for T
- * tokens (0 when nothing is quantized yet; host-only). */
+/* Number of workgroups per (sequence, KV head) kivi_decode_attn uses for T tokens
+ * (at least 1; host-only). */
 kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_split);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none).

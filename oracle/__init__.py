@@ -6,6 +6,6 @@ taken where the pages are silent.
 from .kivi_ref import *  # noqa: F401,F403
 from .kivi_ref import (LayerCache, attention_fp64, dequantize, dequantize_keys,  # noqa: F401
                        dequantize_values, gqa_attention_fp64, kivi_cache_bytes,
-                       kv_cache_bytes, pack_keys, pack_lsb_first, pack_values,
+                       kv_cache_bytes, pack_keys, pack_words, pack_values,
                        quantize_groups, quantize_keys, quantize_values, quantized_len,
-                       residual_len, unpack_keys, unpack_lsb_first, unpack_values)
+                       residual_len, unpack_keys, unpack_words, unpack_values)

@@ -37,11 +37,15 @@ Readings of passages the pages leave open (each is also listed in the design not
   R6  GQA: query head j reads KV head j // (H_q / H_kv).
   R7  Decode step order: append the new token (flushing first if the window is
       full), then attend over all T tokens including the new one; no mask.
-  R8  Packed layout (the pages fix neither bit order nor pack axis): codes are
-      packed LSB-first, little-endian.  Keys: per token, along channels
-      ``[T][d*b/8]``.  Values: per channel, along runs of 16 tokens
+  R8  Packed layout (the pages fix four 2-bit or two 4-bit codes per byte, but
+      neither the bit order nor the pack axis): a packed run is cut into
+      little-endian 32-bit words of n = 32/b codes, and code e of a word sits in
+      byte e mod 4 at bits [b*(e div 4), b*(e div 4) + b) ("word-interleaved"
+      order: byte k of a word holds codes k, k+4, k+8, ...).  Keys: per token,
+      along channels ``[T][d*b/8]``.  Values: per channel, along runs of 16 tokens
       ``[T/16][d][16*b/8]``.  Each product of decode attention then reduces along
-      the packed axis (Q.K^T over channels, P.V over tokens).
+      the packed axis (Q.K^T over channels, P.V over tokens), and a shift by b*k
+      and a byte mask extract codes 4k .. 4k+3 of a word in their natural order.
 """
 from __future__ import annotations
 
@@ -184,33 +188,36 @@ def dequantize_values(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray, Gv
 # 4-bit codes per byte.
 # --------------------------------------------------------------------------------------
 
-def pack_lsb_first(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Pack the last axis: code j goes to bits [b*(j % per), ...) of byte j // per."""
-    per = 8 // bits
-    *lead, n = codes.shape
-    assert n % per == 0
-    c = codes.reshape(*lead, n // per, per).astype(np.uint32)
-    out = np.zeros((*lead, n // per), np.uint32)
-    for j in range(per):
-        out |= (c[..., j] & (2 ** bits - 1)) << (bits * j)
-    return out.astype(np.uint8)
+def pack_words(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack the last axis (reading R8): 32-bit little-endian words of n = 32/b codes,
+    code e of a word in byte e % 4 at bit offset b * (e // 4)."""
+    n = 32 // bits
+    *lead, m = codes.shape
+    assert m % n == 0
+    c = codes.reshape(*lead, m // n, n).astype(np.uint32)
+    words = np.zeros((*lead, m // n), np.uint32)
+    for e in range(n):
+        words |= (c[..., e] & (2 ** bits - 1)) << (8 * (e % 4) + bits * (e // 4))
+    return np.ascontiguousarray(words.astype("<u4")).view(np.uint8).reshape(*lead, m * bits // 8)
 
 
-def unpack_lsb_first(packed: np.ndarray, bits: int) -> np.ndarray:
-    per = 8 // bits
-    p = packed.astype(np.uint32)
-    parts = [(p >> (bits * j)) & (2 ** bits - 1) for j in range(per)]
-    return np.stack(parts, axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * per) \
-        .astype(np.uint8)
+def unpack_words(packed: np.ndarray, bits: int) -> np.ndarray:
+    n = 32 // bits
+    *lead, nb = packed.shape
+    assert nb % 4 == 0
+    words = np.ascontiguousarray(packed).reshape(*lead, nb // 4, 4).view("<u4")[..., 0]
+    words = words.astype(np.uint32)
+    parts = [(words >> (8 * (e % 4) + bits * (e // 4))) & (2 ** bits - 1) for e in range(n)]
+    return np.stack(parts, axis=-1).reshape(*lead, (nb // 4) * n).astype(np.uint8)
 
 
 def pack_keys(codes: np.ndarray, bits: int) -> np.ndarray:
     """[..., T, d] codes -> [..., T, d*b/8] bytes (per token, along channels)."""
-    return pack_lsb_first(codes, bits)
+    return pack_words(codes, bits)
 
 
 def unpack_keys(packed: np.ndarray, bits: int) -> np.ndarray:
-    return unpack_lsb_first(packed, bits)
+    return unpack_words(packed, bits)
 
 
 def pack_values(codes: np.ndarray, bits: int) -> np.ndarray:
@@ -219,11 +226,11 @@ def pack_values(codes: np.ndarray, bits: int) -> np.ndarray:
     assert T % V_RUN == 0
     runs = codes.reshape(*lead, T // V_RUN, V_RUN, d)
     runs = np.swapaxes(runs, -1, -2)               # [..., T/16, d, 16]
-    return pack_lsb_first(np.ascontiguousarray(runs), bits)
+    return pack_words(np.ascontiguousarray(runs), bits)
 
 
 def unpack_values(packed: np.ndarray, bits: int) -> np.ndarray:
-    runs = unpack_lsb_first(packed, bits)          # [..., T/16, d, 16]
+    runs = unpack_words(packed, bits)              # [..., T/16, d, 16]
     runs = np.swapaxes(runs, -1, -2)               # [..., T/16, 16, d]
     *lead, nr, _, d = runs.shape
     return np.ascontiguousarray(runs).reshape(*lead, nr * V_RUN, d)

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert kv.kivi_abi_version() == 1
+    assert kv.kivi_abi_version() == 2
 
 
 def good_dims(**kw):
@@ -66,7 +66,7 @@ def test_cache_sizes_follow_the_documented_layout():
     codes = unit * d.max_tokens * d.head_dim * d.bits // 8
     assert sizes == [codes, unit * (d.max_tokens // 32) * 128 * 2, unit * (d.max_tokens // 32) * 128 * 2,
                      codes, unit * d.max_tokens * 2 * 2, unit * d.max_tokens * 2 * 2,
-                     unit * 64 * 128 * 2, unit * 64 * 128 * 2]
+                     unit * 64 * 128 * 2, unit * 64 * 128 * 2, unit * 2 * 4]
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -77,7 +77,7 @@ def test_cache_sizes_follow_the_documented_layout():
 ])
 def test_bad_dims_are_rejected(field, value, status):
     d = good_dims(**{field: value})
-    sizes = (ctypes.c_size_t * 8)()
+    sizes = (ctypes.c_size_t * len(kv.BUFFERS))()
     st, msg = call("kivi_cache_sizes", ctypes.byref(d.c()), sizes)
     assert st == status and msg
     st, msg = call("kivi_quantize_k", ctypes.byref(d.c()), ctypes.byref(fake_cache()), 0, FAKE,
@@ -98,6 +98,9 @@ def test_null_and_misaligned_pointers():
     st, msg = call("kivi_quantize_k", ctypes.byref(d), ctypes.byref(fake_cache(k_scale=0)), 0,
                    FAKE, 16, 16, None)
     assert st == 1 and "k_scale" in msg
+    st, msg = call("kivi_quantize_k", ctypes.byref(d), ctypes.byref(fake_cache(scale_max=0)), 0,
+                   FAKE, 16, 16, None)
+    assert st == 1 and "scale_max" in msg
     st, msg = call("kivi_quantize_k", ctypes.byref(d), ctypes.byref(fake_cache(v_resid=FAKE + 8)),
                    0, FAKE, 16, 16, None)
     assert st == 4 and "v_resid" in msg
@@ -110,7 +113,7 @@ def test_null_and_misaligned_pointers():
     st, _ = call("kivi_append_flush", ctypes.byref(d), ctypes.byref(fake_cache()), 0, 5, FAKE,
                  FAKE + 4, None)
     assert st == 4
-    st, _ = call("kivi_cache_sizes", None, (ctypes.c_size_t * 8)())
+    st, _ = call("kivi_cache_sizes", None, (ctypes.c_size_t * len(kv.BUFFERS))())
     assert st == 1
     st, _ = call("kivi_quantize_k", ctypes.byref(d), None, 0, FAKE, 16, 16, None)
     assert st == 1
@@ -157,11 +160,14 @@ def test_decode_argument_checks():
 
 def test_split_plan_is_clamped_and_workspace_grows_with_splits():
     d = good_dims()
-    # splits cover the quantized history in 64-token blocks; the fp16 window has its
-    # own workgroup
-    assert 1 <= kv.kivi_decode_splits(d, 300) <= (300 - 44 + 63) // 64
-    assert kv.kivi_decode_splits(d, 10) == 0          # nothing quantized yet
+    # workgroups per (sequence, KV head) share the work units: 64-token blocks of the
+    # quantized history plus 32-row chunks of the fp16 window (R = 64 here)
+    units = lambda T: (T - ((T - 1) % 64 + 1) + 63) // 64 + (((T - 1) % 64 + 1) + 31) // 32
+    assert units(300) == 4 + 2
+    assert 1 <= kv.kivi_decode_splits(d, 300) <= units(300)
+    assert kv.kivi_decode_splits(d, 10) == 1          # nothing quantized yet: the window
     a = kv.kivi_decode_workspace_bytes(d, 448, 1)
     b = kv.kivi_decode_workspace_bytes(d, 448, 4)
     assert b > a
-    assert kv.kivi_decode_workspace_bytes(d, 448, 1000) == kv.kivi_decode_workspace_bytes(d, 448, 12)
+    assert units(448) == 6 + 2
+    assert kv.kivi_decode_workspace_bytes(d, 448, 1000) == kv.kivi_decode_workspace_bytes(d, 448, 8)

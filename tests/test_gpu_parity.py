@@ -69,6 +69,12 @@ def compare_pair(cache, layer, b, h, oc, ob, oh, T):
     for name, ref in (("k_resid", oc.k_resid), ("v_resid", oc.v_resid)):
         g = bits16(cache.view(name)[layer, b, h, :r])
         assert np.array_equal(g, bits16(ref[ob, oh, :r])), name + " " + where
+    # scale_max: the largest Key and Value scale of the quantized history (0 if none)
+    sm = cache.view("scale_max")[layer, b, h].cpu().numpy()
+    ks = oc.k_scale[ob, oh, :Tq // d.group_k].astype(np.float32)
+    vs = oc.v_scale[ob, oh, :Tq].astype(np.float32)
+    assert sm[0] == (ks.max() if ks.size else 0.0), "scale_max[0] " + where
+    assert sm[1] == (vs.max() if vs.size else 0.0), "scale_max[1] " + where
 
 
 def oracle_pair(w, K, V, b, h, T, max_tokens):
@@ -231,7 +237,10 @@ def test_decode_matches_oracle(bits, G, R, B, H, g, T, n_split):
     assert_close(out, ref, f"decode bits={bits} T={T} n_split={n_split}")
 
 
-def test_decode_is_deterministic():
+def test_decode_repeats_to_float32_rounding():
+    # Waves take 64-token blocks from a queue, so the order of float additions can
+    # change from call to call; the integer parts of the sums are order-free and the
+    # float parts agree to float32 rounding.
     d, B, H, g, T = 128, 2, 2, 4, 5000
     w = W.Workload("det", 94, 1, B, H, H * g, d, T, 2, 32, d, 128)
     dims = dims_of(w, w.max_tokens())
@@ -239,8 +248,9 @@ def test_decode_is_deterministic():
     cache = gpu_prefill(w, dims, K, V, T)
     q = torch.randn((B, H * g, d), device="cuda").to(torch.float16)
     a, _ = gpu_decode(dims, cache, 0, T, q, 0.09)
-    b, _ = gpu_decode(dims, cache, 0, T, q, 0.09)
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for _ in range(3):
+        b, _ = gpu_decode(dims, cache, 0, T, q, 0.09)
+        assert np.allclose(a, b, rtol=1e-5, atol=1e-6)
 
 
 # ----------------------------------------------------------------------------------

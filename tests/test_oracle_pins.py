@@ -270,9 +270,9 @@ def test_per_token_values_contain_outlier_tokens():
 @pytest.mark.parametrize("case", _load("packing_cases.json")["cases"])
 def test_packing_hand_vectors(case):
     c = np.array(case["codes"], np.uint8)[None]
-    packed = O.pack_lsb_first(c, case["bits"])
+    packed = O.pack_words(c, case["bits"])
     assert packed[0].tolist() == case["bytes"]
-    assert np.array_equal(O.unpack_lsb_first(packed, case["bits"]), c)
+    assert np.array_equal(O.unpack_words(packed, case["bits"]), c)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
@@ -280,17 +280,22 @@ def test_key_and_value_layouts_place_each_code_where_stated(bits):
     rng = np.random.default_rng(6)
     T, d = 48, 32
     codes = rng.integers(0, 2 ** bits, size=(T, d), dtype=np.uint8)
-    per = 8 // bits
+    n = 32 // bits                                 # codes per 32-bit word
+
+    def code_at(row, j):
+        # code j of a packed run: word j // n, byte 4*(j // n) + (j % n) % 4,
+        # bit offset bits * ((j % n) // 4)
+        e = j % n
+        byte = int(row[4 * (j // n) + e % 4])
+        return (byte >> (bits * (e // 4))) & (2 ** bits - 1)
+
     pk = O.pack_keys(codes, bits)
     pv = O.pack_values(codes, bits)
     assert pk.shape == (T, d * bits // 8) and pv.shape == (T // 16, d, 16 * bits // 8)
     for t in range(T):
         for c in range(d):
-            kbyte = int(pk[t, c // per])
-            assert (kbyte >> (bits * (c % per))) & (2 ** bits - 1) == codes[t, c]
-            tau = t % 16
-            vbyte = int(pv[t // 16, c, tau // per])
-            assert (vbyte >> (bits * (tau % per))) & (2 ** bits - 1) == codes[t, c]
+            assert code_at(pk[t], c) == codes[t, c]
+            assert code_at(pv[t // 16, c], t % 16) == codes[t, c]
     assert np.array_equal(O.unpack_keys(pk, bits), codes)
     assert np.array_equal(O.unpack_values(pv, bits), codes)
 
