@@ -35,6 +35,29 @@ if ROOT not in sys.path:
 METRIC = "quantized-KV decode attention: effective HBM GB/s & % of peak; tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20
+DECODE_SOURCE = os.path.join(ROOT, "bit_quantization_amd", "csrc", "decode.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic.json")
+
+
+def source_digest(path=DECODE_SOURCE):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed PMC record (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy kernel's reading), or None when the record is
+    missing, is for another workload, or the decode source changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or rec.get("decode_source_sha256") != source_digest():
+        return None
+    return entry.get("traffic_bytes_per_launch")
 
 
 def decode_bytes(w, T):
@@ -284,7 +307,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "int8+f32",
         "data": "synthetic (seeded N(0,1) K/V/Q with x50 Key outlier channels and x100 Value "
                 "outlier tokens; no dataset or weights)",
         "config": {"workload": w.name, "batch": w1.batch, "kv_heads": w1.kv_heads,
@@ -294,13 +317,13 @@ def main():
                    "step": "append(+flush) + decode attention"},
         "tokens_per_s": round(w1.batch * args.steps / wall, 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "kivi_decode_attn (split-K + merge)",
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (work queue + merge)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(dec_per_launch),
                      "avg_launch_us": round(dec_avg_s * 1e6, 3),
                      "median_launch_us": round(dec_med_s * 1e6, 3),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
         "cpu_baseline": cpu,
         "quality": quality,
     }
