@@ -13,6 +13,7 @@
 // The arithmetic must match the definition bit for bit: float32 subtraction and
 // correctly rounded division, round-half-to-even (rintf), float32->float16 by
 // round-to-nearest-even, -0 canonicalized to +0, no contraction into FMAs.
+#include <algorithm>
 #include <type_traits>
 
 #include "kivi_internal.h"
@@ -23,10 +24,35 @@ namespace kivi {
 namespace {
 
 constexpr int D = kHeadDim;
+constexpr int V_LDS = 4 * (32 * 16 + 16);    // bytes of LDS one Value run needs
+constexpr int QW = 4;                        // waves (groups or runs) per workgroup
+
+// LDS hand-off between the lanes of one wave: LDS operations of a wave execute in
+// order, so only the compiler must be kept from moving LDS accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Lane-wise min / max of float16 pairs (exact: no rounding).  Issued directly: the
+// generic minnum lowering first canonicalizes each operand (one more instruction per
+// loaded pair) to quiet signalling NaNs, and inputs here are finite.
+__device__ __forceinline__ __half2 hmin2(__half2 a, __half2 b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(__builtin_bit_cast(uint32_t, a)),
+      "v"(__builtin_bit_cast(uint32_t, b)));
+  return __builtin_bit_cast(__half2, r);
+}
+__device__ __forceinline__ __half2 hmax2(__half2 a, __half2 b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(__builtin_bit_cast(uint32_t, a)),
+      "v"(__builtin_bit_cast(uint32_t, b)));
+  return __builtin_bit_cast(__half2, r);
+}
 
 struct GroupParams {
   float mn;      // group minimum (float32, exact float16 value)
   float s;       // float32 value of the stored float16 scale
+  float inv;     // correctly rounded 1 / s (0 when s == 0)
   __half scale;
   __half zero;
 };
@@ -40,113 +66,145 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits
   p.zero = __float2half_rn(mn);          // exact: mn is a float16 value
   p.mn = mn;
   p.s = __half2float(p.scale);
+  p.inv = p.s == 0.0f ? 0.0f : 1.0f / p.s;
   return p;
 }
 
-// Largest value over the wave, then raised into *p (scale maxima: non-negative floats
-// order like their bit patterns, so an unsigned atomic max is a float max).
-__device__ __forceinline__ void raise_scale_max(float* p, float v) {
+// Largest value over the NW waves of the workgroup, raised into *p by one atomic
+// (scale maxima: non-negative floats order like their bit patterns, so an unsigned
+// atomic max is a float max).  Every thread of the workgroup must call it.  One
+// atomic per workgroup matters: the entries of neighbouring (b, h) share a cache
+// line, and atomics on one line serialize.
+template <int NW>
+__device__ __forceinline__ void raise_scale_max(float* p, float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if constexpr (NW > 1) {
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v = fmaxf(v, red[w]);
+  }
   if (threadIdx.x == 0)
     __hip_atomic_fetch_max(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// code = clamp(rint(RN((x - mn) / s)), 0, 2^b - 1), ties to even, with RN the
+// correctly rounded float32 quotient (and code 0 when s == 0).  The quotient comes
+// without a division: with inv = RN(1/s), q0 = RN(a * inv) is within one ulp of a/s,
+// the remainder a - q0*s is exact in one FMA, and q0 + remainder*inv rounded once is
+// RN(a/s) (Markstein's theorem on correctly rounded division from a correctly
+// rounded reciprocal).  Here a = RN(x - mn) is 0 or at least 2^-24 and s a float16
+// value, so nothing is subnormal; checked against IEEE division on the CPU for every
+// positive float16 s, densely around every tie and code boundary.  With s == 0,
+// inv == 0 gives q == 0: code 0 without a branch.  s is never infinite: the range of
+// two float16 values is below 2^17, so s < 2^16.
+//
+// a = fma(x, 1, -mn) is RN(x - mn) (one rounding), with the float16 x converted inside
+// the FMA.  q >= 0, and adding 1.5 * 2^23 to min(q, qmax) rounds it to an integer,
+// ties to even, in the low mantissa bits: the low byte of the returned bit pattern
+// is the code clamp(rint(q), 0, qmax).
+constexpr float kRoundAdd = 12582912.0f;   // 1.5 * 2^23
 template <int BITS>
-__device__ __forceinline__ uint32_t quant_code(float x, const GroupParams& p) {
+__device__ __forceinline__ uint32_t quant_bits(__half x, const GroupParams& p) {
   constexpr float qmax = (float)((1 << BITS) - 1);
-  if (p.s == 0.0f) return 0u;
-  float q = rintf((x - p.mn) / p.s);     // ties to even
-  q = fminf(fmaxf(q, 0.0f), qmax);
-  return (uint32_t)q;
+  const float a = fmaf(__half2float(x), 1.0f, -p.mn);
+  const float q0 = a * p.inv;
+  const float q = fmaf(fmaf(-q0, p.s, a), p.inv, q0);
+  return __float_as_uint(fminf(q, qmax) + kRoundAdd);
 }
 
 // One wave quantizes one Key group: G tokens x D channels, rows of D float16 at
 // `src`.  Lane l owns channels 2l and 2l+1.  Writes G packed rows at `codes`
-// (row stride D*BITS/8 bytes) and D scales/zeros.  `lds` holds G*D bytes.
+// (row stride D*BITS/8 bytes) and D scales/zeros, and returns the lane's larger
+// scale.  `lds` holds G*D bytes private to the wave.  A -0 input acts as +0: only
+// the minimum and maximum can carry the sign into a result (zero, scale), and both
+// are canonicalized.
 template <int BITS, int G>
-__device__ __forceinline__ void quantize_k_group(const __half* __restrict__ src,
-                                                 uint8_t* __restrict__ codes,
-                                                 __half* __restrict__ scale,
-                                                 __half* __restrict__ zero, uint8_t* lds,
-                                                 float* smax) {
-  const int lane = threadIdx.x;
+__device__ __forceinline__ float quantize_k_group(const __half* __restrict__ src,
+                                                  uint8_t* __restrict__ codes,
+                                                  __half* __restrict__ scale,
+                                                  __half* __restrict__ zero, uint8_t* lds) {
+  const int lane = threadIdx.x & 63;
   const __half2* s2 = reinterpret_cast<const __half2*>(src);
-  float x0[G], x1[G];
-  float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+  __half2 x[G];
 #pragma unroll
-  for (int t = 0; t < G; ++t) {
-    const __half2 v = s2[t * (D / 2) + lane];
-    x0[t] = __low2float(v) + 0.0f;       // -0 -> +0
-    x1[t] = __high2float(v) + 0.0f;
-    mn0 = fminf(mn0, x0[t]);
-    mx0 = fmaxf(mx0, x0[t]);
-    mn1 = fminf(mn1, x1[t]);
-    mx1 = fmaxf(mx1, x1[t]);
+  for (int t = 0; t < G; ++t) x[t] = s2[t * (D / 2) + lane];
+  __half2 mn = x[0], mx = x[0];              // float16 min/max are exact
+#pragma unroll
+  for (int t = 1; t < G; ++t) {
+    mn = hmin2(mn, x[t]);
+    mx = hmax2(mx, x[t]);
   }
-  const GroupParams p0 = group_params(mn0, mx0, BITS);
-  const GroupParams p1 = group_params(mn1, mx1, BITS);
+  const GroupParams p0 = group_params(__low2float(mn) + 0.0f, __low2float(mx) + 0.0f, BITS);
+  const GroupParams p1 = group_params(__high2float(mn) + 0.0f, __high2float(mx) + 0.0f, BITS);
   reinterpret_cast<__half2*>(scale)[lane] = __halves2half2(p0.scale, p1.scale);
   reinterpret_cast<__half2*>(zero)[lane] = __halves2half2(p0.zero, p1.zero);
-  raise_scale_max(smax, fmaxf(p0.s, p1.s));
+  // codes into LDS as bytes, [token][channel]
 #pragma unroll
   for (int t = 0; t < G; ++t) {
-    const uint32_t c0 = quant_code<BITS>(x0[t], p0);
-    const uint32_t c1 = quant_code<BITS>(x1[t], p1);
-    reinterpret_cast<uint16_t*>(lds + t * D)[lane] = (uint16_t)(c0 | (c1 << 8));
+    const uint32_t c0 = quant_bits<BITS>(__low2half(x[t]), p0);
+    const uint32_t c1 = quant_bits<BITS>(__high2half(x[t]), p1);
+    // low bytes of c0 and c1 side by side
+    reinterpret_cast<uint16_t*>(lds + t * D)[lane] =
+        (uint16_t)__builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);
   }
-  __syncthreads();
-  // Pack each token row along channels: 32/BITS codes per 32-bit word, code k of a
-  // word in byte k % 4 at bit offset BITS * (k / 4).
-  constexpr int CPW = 32 / BITS;
-  constexpr int WPR = D / CPW;           // words per token row
-  for (int w = lane; w < G * WPR; w += 64) {
-    const int t = w / WPR, j = w % WPR;
-    const uint8_t* c = lds + t * D + j * CPW;
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < CPW; ++k) word |= (uint32_t)c[k] << (8 * (k % 4) + BITS * (k / 4));
-    reinterpret_cast<uint32_t*>(codes + (int64_t)t * (D * BITS / 8))[j] = word;
+  wave_lds_sync();
+  // Pack each token row along channels.  A 16-byte chunk holds the codes of 16
+  // consecutive channels; its dword k holds channels 4k .. 4k+3, and shifting dword
+  // k by BITS*k puts each code at bit BITS*k of its byte: 2-bit, one word per chunk
+  // (code e of the word in byte e % 4 at bit 2(e / 4)); 4-bit, two words.
+  constexpr int CHUNKS = G * (D / 16);
+  for (int i = lane; i < CHUNKS; i += 64) {
+    const int t = i / (D / 16), ch = i % (D / 16);
+    const uint4 d = *reinterpret_cast<const uint4*>(lds + t * D + 16 * ch);
+    if constexpr (BITS == 2) {
+      const uint32_t word = d.x | (d.y << 2) | (d.z << 4) | (d.w << 6);
+      reinterpret_cast<uint32_t*>(codes + (int64_t)t * (D * BITS / 8))[ch] = word;
+    } else {
+      reinterpret_cast<uint2*>(codes + (int64_t)t * (D * BITS / 8))[ch] =
+          make_uint2(d.x | (d.y << 4), d.z | (d.w << 4));
+    }
   }
+  return fmaxf(p0.s, p1.s);
 }
 
 // One wave quantizes one run of 16 Value tokens (each token in groups of GV
 // channels).  Lane l owns token l/4 and channels 32*(l%4) .. +31.  Writes the run's
-// packed codes ([D][16*BITS/8] bytes at `codes`) and 16*(D/GV) scales/zeros.
+// packed codes ([D][16*BITS/8] bytes at `codes`) and 16*(D/GV) scales/zeros, and
+// returns the largest scale among the lane's groups.  `lds` holds V_LDS bytes private
+// to the wave.  -0 is handled as in quantize_k_group.
 template <int BITS, int GV>
-__device__ __forceinline__ void quantize_v_run(const __half* __restrict__ src,
-                                               uint8_t* __restrict__ codes,
-                                               __half* __restrict__ scale,
-                                               __half* __restrict__ zero, uint8_t* lds,
-                                               float* smax) {
-  const int lane = threadIdx.x;
+__device__ __forceinline__ float quantize_v_run(const __half* __restrict__ src,
+                                                uint8_t* __restrict__ codes,
+                                                __half* __restrict__ scale,
+                                                __half* __restrict__ zero, uint8_t* lds) {
+  const int lane = threadIdx.x & 63;
   const int tau = lane >> 2, part = lane & 3;
   const uint4* row = reinterpret_cast<const uint4*>(src + tau * D + part * 32);
-  float x[32];
+  __half2 x2[16];                          // channels 2i, 2i+1 of the lane's 32
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint4 u = row[i];
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const __half2 h2 = *reinterpret_cast<const __half2*>(&w[k]);
-      x[8 * i + 2 * k] = __low2float(h2) + 0.0f;
-      x[8 * i + 2 * k + 1] = __high2float(h2) + 0.0f;
-    }
+    for (int k = 0; k < 4; ++k) x2[4 * i + k] = *reinterpret_cast<const __half2*>(&w[k]);
   }
+  auto xh = [&](int i) { return (i & 1) ? __high2half(x2[i >> 1]) : __low2half(x2[i >> 1]); };
   constexpr int SUB = GV < 32 ? GV : 32;   // channels of one group inside this lane
   constexpr int NSUB = 32 / SUB;
   float mn[NSUB], mx[NSUB];
 #pragma unroll
-  for (int k = 0; k < NSUB; ++k) {
-    mn[k] = INFINITY;
-    mx[k] = -INFINITY;
+  for (int k = 0; k < NSUB; ++k) {        // float16 min/max over pairs, then the halves
+    __half2 m2 = x2[k * SUB / 2], M2 = x2[k * SUB / 2];
 #pragma unroll
-    for (int i = 0; i < SUB; ++i) {
-      mn[k] = fminf(mn[k], x[k * SUB + i]);
-      mx[k] = fmaxf(mx[k], x[k * SUB + i]);
+    for (int i = 1; i < SUB / 2; ++i) {
+      m2 = hmin2(m2, x2[k * SUB / 2 + i]);
+      M2 = hmax2(M2, x2[k * SUB / 2 + i]);
     }
+    mn[k] = fminf(__low2float(m2), __high2float(m2));
+    mx[k] = fmaxf(__low2float(M2), __high2float(M2));
   }
   if constexpr (GV > 32) {                 // groups span GV/32 neighbouring lanes
 #pragma unroll
@@ -159,10 +217,9 @@ __device__ __forceinline__ void quantize_v_run(const __half* __restrict__ src,
   float smx = 0.f;
 #pragma unroll
   for (int k = 0; k < NSUB; ++k) {
-    p[k] = group_params(mn[k], mx[k], BITS);
+    p[k] = group_params(mn[k] + 0.0f, mx[k] + 0.0f, BITS);   // -0 -> +0
     smx = fmaxf(smx, p[k].s);
   }
-  raise_scale_max(smax, smx);
   constexpr int NG = D / GV;               // groups per token
   if constexpr (GV >= 32) {
     if ((part % (GV / 32)) == 0) {
@@ -178,27 +235,24 @@ __device__ __forceinline__ void quantize_v_run(const __half* __restrict__ src,
       zero[tau * NG + j] = p[k].zero;
     }
   }
-  uint8_t* myrow = lds + tau * D + part * 32;
+  // codes into LDS transposed, [channel][token] (16 bytes per channel, plus 16 bytes
+  // after every 32 channels so that the four lane groups' byte writes use different
+  // banks)
+  uint8_t* col = lds + part * (32 * 16 + 16) + tau;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) myrow[i] = (uint8_t)quant_code<BITS>(x[i], p[i / SUB]);
-  __syncthreads();
-  // Pack each channel's 16 tokens along tokens, in the same word order as the Keys.
+  for (int i = 0; i < 32; ++i) col[16 * i] = (uint8_t)quant_bits<BITS>(xh(i), p[i / SUB]);
+  wave_lds_sync();
+  // Pack each channel's 16 tokens: dword k of the channel's 16 bytes holds tokens
+  // 4k .. 4k+3, shifted by BITS*k into the word order of the Keys.
   for (int c = lane; c < D; c += 64) {
+    const uint4 d = *reinterpret_cast<const uint4*>(lds + (c >> 5) * (32 * 16 + 16) + (c & 31) * 16);
     if constexpr (BITS == 2) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) word |= (uint32_t)lds[t * D + c] << (8 * (t % 4) + 2 * (t / 4));
-      reinterpret_cast<uint32_t*>(codes)[c] = word;
+      reinterpret_cast<uint32_t*>(codes)[c] = d.x | (d.y << 2) | (d.z << 4) | (d.w << 6);
     } else {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        lo |= (uint32_t)lds[t * D + c] << (8 * (t % 4) + 4 * (t / 4));
-        hi |= (uint32_t)lds[(t + 8) * D + c] << (8 * (t % 4) + 4 * (t / 4));
-      }
-      reinterpret_cast<uint2*>(codes)[c] = make_uint2(lo, hi);
+      reinterpret_cast<uint2*>(codes)[c] = make_uint2(d.x | (d.y << 4), d.z | (d.w << 4));
     }
   }
+  return smx;
 }
 
 // Copy `rows` rows of D float16 from src to dst with one wave (16-byte moves).
@@ -207,50 +261,72 @@ __device__ __forceinline__ void copy_rows(const __half* __restrict__ src, __half
   const uint4* s = reinterpret_cast<const uint4*>(src);
   uint4* d = reinterpret_cast<uint4*>(dst);
   const int64_t n = rows * (D / 8);
-  for (int64_t i = threadIdx.x; i < n; i += 64) d[i] = s[i];
+  for (int64_t i = threadIdx.x & 63; i < n; i += 64) d[i] = s[i];
 }
 
 // ---- kernels ----------------------------------------------------------------------
 
-// grid = (Tq/G + 1, B*H): blocks [0, Tq/G) quantize one Key group each; the last
-// block copies the tail [Tq, T) into the residual rows.
+// Items of one (b, h): the Tq/G Key groups (or Tq/16 Value runs), then one item
+// that copies the tail [Tq, T) into the residual rows.  grid = (ceil(items /
+// (QW*npw)), B*H); workgroup x takes items QW*npw*x .. +QW*npw - 1, its waves
+// interleaved (wave w takes item QW*npw*x + QW*i + w for i < npw).
 template <int BITS, int G>
-__global__ __launch_bounds__(64) void prefill_k_kernel(LayerView L, const __half* __restrict__ src,
-                                                       int64_t ld, int64_t Tq, int64_t T) {
-  __shared__ uint8_t lds[G * D];
+__global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const __half* __restrict__ src,
+                                                            int64_t ld, int64_t Tq, int64_t T,
+                                                            int npw) {
+  __shared__ alignas(16) uint8_t lds[QW][G * D];
+  __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const __half* s = src + pair * ld * D;
   const int64_t ngroups = Tq / G;
-  const int64_t g = blockIdx.x;
-  if (g < ngroups) {
-    quantize_k_group<BITS, G>(s + g * G * D,
-                              L.k_codes + pair * L.kc_pair() + g * G * (D * BITS / 8),
-                              L.k_scale + pair * L.ks_pair() + g * D,
-                              L.k_zero + pair * L.ks_pair() + g * D, lds, L.scale_max + 2 * pair);
-  } else {
-    copy_rows(s + Tq * D, L.k_resid + pair * L.rs_pair(), T - Tq);
+  float smx = 0.f;
+  for (int i = 0; i < npw; ++i) {
+    const int64_t g = ((int64_t)blockIdx.x * npw + i) * QW + wave;
+    if (g < ngroups) {
+      smx = fmaxf(smx, quantize_k_group<BITS, G>(
+                           s + g * G * D, L.k_codes + pair * L.kc_pair() + g * G * (D * BITS / 8),
+                           L.k_scale + pair * L.ks_pair() + g * D,
+                           L.k_zero + pair * L.ks_pair() + g * D, lds[wave]));
+    } else if (g == ngroups) {
+      copy_rows(s + Tq * D, L.k_resid + pair * L.rs_pair(), T - Tq);
+    }
   }
+  raise_scale_max<QW>(L.scale_max + 2 * pair, smx, red);
 }
 
-// grid = (Tq/16 + 1, B*H): blocks [0, Tq/16) quantize one 16-token Value run each;
-// the last block copies the tail into the residual rows.
+// As prefill_k_kernel, over the Value runs.
 template <int BITS, int GV>
-__global__ __launch_bounds__(64) void prefill_v_kernel(LayerView L, const __half* __restrict__ src,
-                                                       int64_t ld, int64_t Tq, int64_t T) {
-  __shared__ uint8_t lds[kVRun * D];
+__global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const __half* __restrict__ src,
+                                                            int64_t ld, int64_t Tq, int64_t T,
+                                                            int npw) {
+  __shared__ alignas(16) uint8_t lds[QW][V_LDS];
+  __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const __half* s = src + pair * ld * D;
   const int64_t nruns = Tq / kVRun;
-  const int64_t j = blockIdx.x;
-  if (j < nruns) {
-    quantize_v_run<BITS, GV>(s + j * kVRun * D,
-                             L.v_codes + pair * L.vc_pair() + j * (D * kVRun * BITS / 8),
-                             L.v_scale + pair * L.vs_pair() + j * kVRun * (D / GV),
-                             L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds,
-                             L.scale_max + 2 * pair + 1);
-  } else {
-    copy_rows(s + Tq * D, L.v_resid + pair * L.rs_pair(), T - Tq);
+  float smx = 0.f;
+  for (int i = 0; i < npw; ++i) {
+    const int64_t j = ((int64_t)blockIdx.x * npw + i) * QW + wave;
+    if (j < nruns) {
+      smx = fmaxf(smx, quantize_v_run<BITS, GV>(
+                           s + j * kVRun * D,
+                           L.v_codes + pair * L.vc_pair() + j * (D * kVRun * BITS / 8),
+                           L.v_scale + pair * L.vs_pair() + j * kVRun * (D / GV),
+                           L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds[wave]));
+    } else if (j == nruns) {
+      copy_rows(s + Tq * D, L.v_resid + pair * L.rs_pair(), T - Tq);
+    }
   }
+  raise_scale_max<QW>(L.scale_max + 2 * pair + 1, smx, red);
+}
+
+// Items per wave so that all (b, h) together launch about kPrefillBlocks workgroups.
+constexpr int64_t kPrefillBlocks = 2048;
+int items_per_wave(int64_t items, int pairs) {
+  const int64_t blocks_per_pair = std::max<int64_t>(1, kPrefillBlocks / pairs);
+  return (int)std::max<int64_t>(1, (items + QW * blocks_per_pair - 1) / (QW * blocks_per_pair));
 }
 
 // Append one token per (b, h).  flush == 0: grid (1, B*H), the new row goes to row
@@ -262,8 +338,8 @@ template <int BITS, int G, int GV>
 __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int slot, int flush,
                                                     const __half* __restrict__ k_new,
                                                     const __half* __restrict__ v_new) {
-  constexpr int LROWS = G > kVRun ? G : kVRun;
-  __shared__ uint8_t lds[LROWS * D];
+  constexpr int LBYTES = G * D > V_LDS ? G * D : V_LDS;
+  __shared__ alignas(16) uint8_t lds[LBYTES];
   const int64_t pair = blockIdx.y;
   __half* kr = L.k_resid + pair * L.rs_pair();
   __half* vr = L.v_resid + pair * L.rs_pair();
@@ -277,23 +353,24 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
   const int nk = L.R / G;
   const int blk = blockIdx.x;
   if (blk < nk) {
-    quantize_k_group<BITS, G>(kr + (int64_t)blk * G * D,
-                              L.k_codes + pair * L.kc_pair() + (t0 + blk * G) * (D * BITS / 8),
-                              L.k_scale + pair * L.ks_pair() + (t0 / G + blk) * D,
-                              L.k_zero + pair * L.ks_pair() + (t0 / G + blk) * D, lds,
-                              L.scale_max + 2 * pair);
+    const float smx = quantize_k_group<BITS, G>(
+        kr + (int64_t)blk * G * D,
+        L.k_codes + pair * L.kc_pair() + (t0 + blk * G) * (D * BITS / 8),
+        L.k_scale + pair * L.ks_pair() + (t0 / G + blk) * D,
+        L.k_zero + pair * L.ks_pair() + (t0 / G + blk) * D, lds);
+    raise_scale_max<1>(L.scale_max + 2 * pair, smx, nullptr);
     if (blk == 0) {
       __syncthreads();
       copy_rows(kn, kr, 1);
     }
   } else {
     const int j = blk - nk;
-    quantize_v_run<BITS, GV>(vr + (int64_t)j * kVRun * D,
-                             L.v_codes + pair * L.vc_pair() +
-                                 (t0 / kVRun + j) * (D * kVRun * BITS / 8),
-                             L.v_scale + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV),
-                             L.v_zero + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV), lds,
-                             L.scale_max + 2 * pair + 1);
+    const float smx = quantize_v_run<BITS, GV>(
+        vr + (int64_t)j * kVRun * D,
+        L.v_codes + pair * L.vc_pair() + (t0 / kVRun + j) * (D * kVRun * BITS / 8),
+        L.v_scale + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV),
+        L.v_zero + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV), lds);
+    raise_scale_max<1>(L.scale_max + 2 * pair + 1, smx, nullptr);
     if (j == 0) {
       __syncthreads();
       copy_rows(vn, vr, 1);
@@ -335,10 +412,12 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
   const int pairs = L.B * L.H;
   hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
                      L.scale_max, 0, pairs);
-  const dim3 grid((unsigned)(Tq / L.G + 1), (unsigned)(L.B * L.H));
+  const int64_t items = Tq / L.G + 1;
+  const int npw = items_per_wave(items, pairs);
+  const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
-    hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value>), grid, dim3(64),
-                       0, s, L, src, ld, Tq, T);
+    hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value>), grid,
+                       dim3(64 * QW), 0, s, L, src, ld, Tq, T, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -351,14 +430,16 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
   const int pairs = L.B * L.H;
   hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
                      L.scale_max, 1, pairs);
-  const dim3 grid((unsigned)(Tq / kVRun + 1), (unsigned)(L.B * L.H));
+  const int64_t items = Tq / kVRun + 1;
+  const int npw = items_per_wave(items, pairs);
+  const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_gv(L.Gv, [&](auto gv) {
     if (L.bits == 2)
-      hipLaunchKernelGGL((prefill_v_kernel<2, decltype(gv)::value>), grid, dim3(64), 0, s, L, src,
-                         ld, Tq, T);
+      hipLaunchKernelGGL((prefill_v_kernel<2, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
+                         src, ld, Tq, T, npw);
     else
-      hipLaunchKernelGGL((prefill_v_kernel<4, decltype(gv)::value>), grid, dim3(64), 0, s, L, src,
-                         ld, Tq, T);
+      hipLaunchKernelGGL((prefill_v_kernel<4, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
+                         src, ld, Tq, T, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;

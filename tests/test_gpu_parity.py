@@ -167,6 +167,8 @@ def test_quantizer_edge_values_bit_exact(bits):
     K[0, 2] = np.float16(-0.0)
     K[0, 2, :, ::3] = np.float16(3.5)                                      # constant channels
     K[0, 2, 100:140, 7] = np.float16(0.0)
+    K[0, 2, 200:205] = np.float16(-0.0)                                    # whole rows of +-0
+    K[0, 2, 200:205, 1::2] = np.float16(0.0)
     K[0, 3] = rng.choice(np.array([-65504, 65504, 0, -0.0, 1e-7, 6e-8], np.float16), size=(T, d))
     V = K[:, ::-1].copy()
     w = W.Workload("edge", 91, 1, B, H, H, d, T, bits, G, 128, R)
