@@ -26,9 +26,12 @@
 // n_split workgroups take contiguous shares of them; the first also takes the float16
 // window rows in 32-row chunks.  Inside a workgroup the waves take chunks and blocks
 // from an LDS counter, each wave with its own online softmax (running max m, sum l),
-// so waves that run ahead take more blocks.  The waves combine in LDS in wave order;
-// the workgroups of a pair write partials, and the last one to arrive (an integer
-// arrival counter, reset by that workgroup) merges them in split order:
+// so waves that run ahead take more blocks.  The waves combine in LDS in wave order.
+// Each workgroup clears its partial slot when it starts and at the end writes its
+// partial there, every float with its lowest bit set as a "written" mark; without
+// waiting for those stores it counts its arrival on the pair's counter.  The last to
+// arrive waits until every word it needs is marked and folds the partials in split
+// order:
 //   m* = max m_s,  l* = sum l_s 2^(m_s - m*),  o = sum acc_s 2^(m_s - m*) / l*.
 // No floating-point atomics.  Which wave takes which block varies from run to run,
 // and float sums in a different order round differently, so repeated runs agree to
@@ -44,7 +47,7 @@ namespace {
 
 constexpr int D = kHeadDim;
 constexpr int BLK = 64;              // tokens per block step of a wave
-constexpr int PSTRIDE = D + 2;       // partial per head: acc[D], m, l
+constexpr int PSTRIDE = D + 4;       // partial per head: acc[D], m, l, 2 unused (16-byte rows)
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,8 +55,8 @@ struct DecodeArgs {
   LayerView L;
   const __half* q;
   float* out;
-  float* part;          // [P][n_parts][GQA][PSTRIDE]
-  unsigned* counters;   // [P], zero between calls
+  float* part;          // [P][n_parts][GQA][PSTRIDE]; slot s cleared by its owner first
+  unsigned* counters;   // [P][kCounterStride]: arrival counter, zero between calls
   int64_t Tq;           // quantized tokens
   int64_t nblk;         // 64-token blocks per pair (the last may hold 32 tokens)
   int r;                // residual tokens
@@ -68,6 +71,9 @@ constexpr int waves_per_simd(int bits, int gqa, int G) {
   return gqa > 4 ? 1 : gqa > 2 ? 2 : (bits == 2 || G == 64) ? 3 : 2;
 }
 constexpr int kCUs = 256;            // compute units of one MI355X
+// Each pair's arrival counter sits in a 256-byte slot of its own: atomics on one
+// cache line serialize.
+constexpr int kCounterStride = 64;
 
 // ---- small device helpers ---------------------------------------------------------
 
@@ -116,20 +122,17 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
-// Partials are exchanged between workgroups with system-scope relaxed stores/loads,
-// which write through / bypass the per-XCD L2, so no L2 write-back fence is needed.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-typedef __attribute__((address_space(1))) unsigned long long global_u64;
-__device__ __forceinline__ float2 load_coherent2(const float* p) {
-  const unsigned long long u = __hip_atomic_load((global_u64*)(p), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_SYSTEM);
-  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
-}
+// Partials pass between workgroups through the workspace with write-through stores and
+// L2-bypassing loads (the sc1 cache policy, device coherence across the XCDs' L2
+// caches).  A stored float carries its lowest mantissa bit set as a "written" mark
+// (at most one ulp of change; the reader clears it, which keeps 0 and -inf exact).
+// Each workgroup zeroes its own slot when it starts and waits for that before it
+// stores its partial (by then a free wait), so a reader that has seen the owner
+// arrive finds in each word either this call's value, marked, or zero: it knows a
+// word is current from the word alone, with no ordering between the partial's stores.
+constexpr int kCoherent = 16;        // sc1
+__device__ __forceinline__ uint32_t marked(float v) { return __float_as_uint(v) | 1u; }
+__device__ __forceinline__ float unmarked(uint32_t w) { return __uint_as_float(w & ~1u); }
 // Wait until this thread's global stores have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ float h2f(unsigned short h) {
@@ -811,74 +814,104 @@ __device__ __forceinline__ void residual_record(const ResidState<GQA>& rs, float
   }
 }
 
-// Combine n [GQA][PSTRIDE] records (a workgroup's per-wave results) in a fixed order
-// into dst; src(i) returns the i-th record.  NTH threads take part.
-template <int GQA, int NTH, typename Src>
-__device__ __forceinline__ void combine(int n, Src src, float* dst) {
-  for (int idx = threadIdx.x; idx < GQA * D; idx += NTH) {
-    const int hd = idx / D, c = idx % D;
-    float mstar = -INFINITY;
-    for (int i = 0; i < n; ++i) {
+// Combine N [GQA][PSTRIDE] records (a workgroup's per-wave results) in a fixed order;
+// src(i) returns the i-th record.  Thread (head hd, channels 4k .. 4k+3) calls
+// sink(hd, k, acc4, l), and the thread with k == 0 also sink_ml(hd, m, l).  Every LDS
+// read is independent of the others (no branches on loaded values), so they all go
+// out together.  NTH threads take part.
+template <int GQA, int NTH, int N, typename Src, typename Sink, typename SinkMl>
+__device__ __forceinline__ void combine(Src src, Sink sink, SinkMl sink_ml) {
+  for (int idx = threadIdx.x; idx < GQA * (D / 4); idx += NTH) {
+    const int hd = idx / (D / 4), k = idx % (D / 4);
+    float2 mli[N];
+    float4 vi[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
       const float* rec = src(i) + hd * PSTRIDE;
-      if (rec[D + 1] > 0.f) mstar = fmaxf(mstar, rec[D]);
+      mli[i] = *reinterpret_cast<const float2*>(rec + D);
+      vi[i] = *reinterpret_cast<const float4*>(rec + 4 * k);
     }
-    float l = 0.f, o = 0.f;
-    if (mstar > -INFINITY) {
-      for (int i = 0; i < n; ++i) {
-        const float* rec = src(i) + hd * PSTRIDE;
-        const float li = rec[D + 1];
-        if (li > 0.f) {
-          const float wgt = __builtin_amdgcn_exp2f(rec[D] - mstar);
-          l += li * wgt;
-          o += rec[c] * wgt;
-        }
-      }
+    float mstar = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < N; ++i) mstar = fmaxf(mstar, mli[i].y > 0.f ? mli[i].x : -INFINITY);
+    const float mref = mstar > -INFINITY ? mstar : 0.f;
+    float l = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float w = mli[i].y > 0.f ? __builtin_amdgcn_exp2f(mli[i].x - mref) : 0.f;
+      l = fmaf(mli[i].y, w, l);
+      o.x = fmaf(vi[i].x, w, o.x);
+      o.y = fmaf(vi[i].y, w, o.y);
+      o.z = fmaf(vi[i].z, w, o.z);
+      o.w = fmaf(vi[i].w, w, o.w);
     }
-    store_coherent(&dst[hd * PSTRIDE + c], o);
-    if (c == 0) {
-      store_coherent(&dst[hd * PSTRIDE + D], mstar);
-      store_coherent(&dst[hd * PSTRIDE + D + 1], l);
-    }
+    sink(hd, k, o, l);
+    if (k == 0) sink_ml(hd, mstar, l);
   }
 }
 
-// Final merge by the last workgroup of a pair, 32 (or 16) partials per round.  Each (partial,
-// head) pair's (m, l) is loaded once, by one thread, into LDS ([head][partial]); thread
-// (head hd, channels c, c+1) loads the accumulators of every partial of the round, and
-// both kinds of loads are in flight together.  The fold has no branches: indices past
-// the last partial are clamped and weighted 0, and empty partials (l == 0) weigh 0.
-// Partials are folded in a fixed order with an online rescale.
+// Final merge by the last workgroup of a pair to arrive, 32 (or 16) partials per
+// round.  A round's words count only when all carry the "written" mark; otherwise the
+// round is read again (a bounded wait: every other workgroup of the pair issued its
+// stores before it arrived, and this one waited for its own, so they become visible;
+// were the bound ever reached the output would be NaN).  Each (partial, head) pair's
+// (m, l) is loaded by one thread into LDS ([head][partial]); thread (head hd,
+// channels c, c+1) loads the accumulators of every partial of the round, all in
+// flight together.  The fold has no branches:
+// indices past the last partial are clamped and weighted 0, and empty partials
+// (l == 0) weigh 0.  Partials are folded in split order with an online rescale.
+constexpr int kMaxPolls = 1 << 20;
 template <int GQA, int NTH>
-__device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n_parts,
+__device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_parts,
                                            float* __restrict__ out, float2* ml_lds) {
   constexpr int ITEMS = GQA * (D / 2);
   constexpr int IPT = (ITEMS + NTH - 1) / NTH;     // (head, channel pair) items per thread
   constexpr int MERGE_CH = 32 / IPT;               // partials per round
   static_assert(MERGE_CH * GQA <= NTH, "one (m, l) load per thread and round");
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   float m[IPT], l[IPT], o0[IPT], o1[IPT];
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     m[it] = -INFINITY;
     l[it] = o0[it] = o1[it] = 0.f;
   }
+  bool failed = false;
   for (int i0 = 0; i0 < n_parts; i0 += MERGE_CH) {
     const int nc = n_parts - i0 < MERGE_CH ? n_parts - i0 : MERGE_CH;
     float2 ov[IPT][MERGE_CH];
+    for (int poll = 0;; ++poll) {
+      bool stale = false;
 #pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int idx = threadIdx.x + it * NTH;
-      const int hd = min(idx / (D / 2), GQA - 1), c = 2 * (idx % (D / 2));
+      for (int it = 0; it < IPT; ++it) {
+        const int idx = threadIdx.x + it * NTH;
+        const int hd = idx / (D / 2), c = 2 * (idx % (D / 2));
+        if (idx < ITEMS) {
 #pragma unroll
-      for (int u = 0; u < MERGE_CH; ++u) {
-        const int i = min(i0 + u, n_parts - 1);
-        ov[it][u] = load_coherent2(base + ((int64_t)i * GQA + hd) * PSTRIDE + c);
+          for (int u = 0; u < MERGE_CH; ++u) {
+            const int i = min(i0 + u, n_parts - 1);
+            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
+                parts, ((i * GQA + hd) * PSTRIDE + c) * 4, 0, kCoherent);
+            ov[it][u] = make_float2(unmarked(w.x), unmarked(w.y));
+            stale |= (w.x & w.y & 1u) == 0u;
+          }
+        }
       }
-    }
-    if (threadIdx.x < MERGE_CH * GQA) {
-      const int u = threadIdx.x / GQA, hd = threadIdx.x % GQA;
-      const int i = min(i0 + u, n_parts - 1);
-      const float2 ml = load_coherent2(base + ((int64_t)i * GQA + hd) * PSTRIDE + D);
-      ml_lds[hd * MERGE_CH + u] = u < nc ? ml : make_float2(-INFINITY, 0.f);
+      if (threadIdx.x < MERGE_CH * GQA) {
+        const int u = threadIdx.x / GQA, hd = threadIdx.x % GQA;
+        const int i = min(i0 + u, n_parts - 1);
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
+            parts, ((i * GQA + hd) * PSTRIDE + D) * 4, 0, kCoherent);
+        stale |= (w.x & w.y & 1u) == 0u;
+        ml_lds[hd * MERGE_CH + u] =
+            u < nc ? make_float2(unmarked(w.x), unmarked(w.y)) : make_float2(-INFINITY, 0.f);
+      }
+      if (!__syncthreads_or(stale)) break;
+      if (poll == kMaxPolls) {
+        failed = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
     __syncthreads();
 #pragma unroll
@@ -920,7 +953,7 @@ __device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n
     const int idx = threadIdx.x + it * NTH;
     if (idx >= ITEMS) continue;
     const int hd = idx / (D / 2), c = 2 * (idx % (D / 2));
-    const float inv = 1.f / l[it];
+    const float inv = failed ? __builtin_nanf("") : 1.f / l[it];
     *reinterpret_cast<float2*>(out + (int64_t)hd * D + c) = make_float2(o0[it] * inv, o1[it] * inv);
   }
 }
@@ -928,12 +961,28 @@ __device__ __forceinline__ void merge_pair(const float* __restrict__ base, int n
 // ---- the kernel ---------------------------------------------------------------------
 
 // One workgroup per CU holding every wave the register budget allows there: WAVES =
-// 4 SIMDs x waves_per_simd.  Workgroup s of a pair takes a contiguous share of the
-// pair's 64-token blocks; the first workgroup also takes the float16 window, whose
-// 32-row chunks count RES_COST blocks each in the shares.  Inside a workgroup, waves
-// take window chunks, then blocks, from an LDS counter.  Each workgroup writes one
-// partial; the last to arrive merges them.
-constexpr int RES_COST = 1;
+// 4 SIMDs x waves_per_simd.  Workgroup 0 of a pair takes the float16 window, whose
+// 32-row chunks count RES_COST blocks each (a chunk moves three blocks' bytes with fewer
+// loads in flight and takes about three blocks of wave time), and the blocks that fill
+// its fair share of the pair's work; workgroups 1 .. nw-1 split the remaining 64-token
+// blocks evenly into contiguous shares.  Inside a workgroup, waves take window chunks,
+// then blocks, from an LDS counter.  The last workgroup of the pair to arrive merges
+// the partials.
+constexpr int RES_COST = 3;
+__device__ __forceinline__ void block_share(int64_t nblk, int n_res, int nw, int s,
+                                            int64_t& b_lo, int64_t& b_hi) {
+  const int64_t fair = (nblk + (int64_t)RES_COST * n_res) / nw;
+  int64_t b0 = nw == 1 ? nblk : fair - (int64_t)RES_COST * n_res;
+  b0 = b0 < 0 ? 0 : b0 > nblk ? nblk : b0;
+  if (s == 0) {
+    b_lo = 0;
+    b_hi = b0;
+  } else {
+    const int64_t rest = nblk - b0;
+    b_lo = b0 + rest * (s - 1) / (nw - 1);
+    b_hi = b0 + rest * s / (nw - 1);
+  }
+}
 template <int BITS, int GQA, int G>
 __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_kernel(DecodeArgs a) {
   constexpr int NMT = (GQA + 3) / 4;
@@ -941,9 +990,9 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   constexpr int NTH = 64 * WAVES;
   __shared__ WaveLds<NMT> wl[WAVES];
   __shared__ alignas(16) float pw[WAVES][GQA * 32 + 4 * ((GQA + 3) / 4)];  // window probabilities
-  __shared__ float comb[2 * WAVES][GQA * PSTRIDE];    // [0, WAVES): blocks; then window
+  __shared__ alignas(16) float comb[2 * WAVES][GQA * PSTRIDE];  // [0, WAVES): blocks; then window
   __shared__ int counter;
-  __shared__ int last_flag;
+  __shared__ unsigned arrival;
 
   const int64_t P = (int64_t)a.L.B * a.L.H;
   const int64_t pair = blockIdx.x % P;
@@ -951,17 +1000,31 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t b = pair / a.L.H, h = pair % a.L.H;
 
-  // this workgroup's share of the work units (window chunks first)
+  // this workgroup's share: window chunks (workgroup 0 only), then blocks
   const int n_res_all = (a.r + 31) / 32;
-  const int64_t units = a.nblk + (int64_t)RES_COST * n_res_all;
-  const int64_t u_lo = units * s / a.nw, u_hi = units * (s + 1) / a.nw;
-  const int64_t res_units = (int64_t)RES_COST * n_res_all;
-  const int64_t b_lo = u_lo > res_units ? u_lo - res_units : 0;
-  const int64_t b_hi = u_hi > res_units ? u_hi - res_units : 0;
+  int64_t b_lo, b_hi;
+  block_share(a.nblk, n_res_all, a.nw, s, b_lo, b_hi);
   const int n_res = s == 0 ? n_res_all : 0;
   const int n_items = n_res + (int)(b_hi - b_lo);
 
   if (threadIdx.x == 0) counter = 0;
+  // Clear this workgroup's partial slot, each thread the words it stores at the end.
+  const int n_parts = a.nw;
+  const int64_t pair_floats = (int64_t)n_parts * GQA * PSTRIDE;
+  const __amdgpu_buffer_rsrc_t parts = make_rsrc(a.part + pair * pair_floats, pair_floats * 4);
+  const int my = s * GQA * PSTRIDE * 4;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  if (n_parts > 1) {
+    for (int idx = threadIdx.x; idx < GQA * (D / 4); idx += NTH) {
+      const int hd = idx / (D / 4), k = idx % (D / 4);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, parts,
+                                             my + (hd * PSTRIDE + 4 * k) * 4, 0, kCoherent);
+      if (k == 0)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, parts, my + (hd * PSTRIDE + D) * 4, 0,
+                                              kCoherent);
+    }
+  }
   __syncthreads();
 
   // window chunks
@@ -991,28 +1054,47 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
                                 wl[wave], comb[wave]);
   __syncthreads();
 
-  // Workgroup partial -> workspace.
-  const int n_parts = a.nw;
-  float* mine = a.part + ((pair * n_parts + s) * GQA) * PSTRIDE;
-  combine<GQA, NTH>(2 * WAVES, [&](int i) { return (const float*)comb[i]; }, mine);
-
-  // Last workgroup of the pair merges all partials and resets the counter.  Every
-  // thread's partial stores complete before the arrival is counted; the merging
-  // workgroup reads the partials with coherent loads after it has seen all arrivals.
+  float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
+  auto rec = [&](int i) { return (const float*)comb[i]; };
+  if (n_parts == 1) {                                 // the whole pair: straight to out
+    combine<GQA, NTH, 2 * WAVES>(
+        rec,
+        [&](int hd, int k, float4 v, float l) {
+          const float inv = 1.f / l;
+          *reinterpret_cast<float4*>(o + hd * D + 4 * k) =
+              make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+        },
+        [](int, float, float) {});
+    return;
+  }
+  // Workgroup partial -> workspace, marked, after the clear has completed; nothing
+  // waits for these stores here.
+  wait_stores();
+  combine<GQA, NTH, 2 * WAVES>(
+      rec,
+      [&](int hd, int k, float4 v, float) {
+        const u32x4 w = {marked(v.x), marked(v.y), marked(v.z), marked(v.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(w, parts, my + (hd * PSTRIDE + 4 * k) * 4, 0,
+                                               kCoherent);
+      },
+      [&](int hd, float mv, float lv) {
+        const u32x2 w = {marked(mv), marked(lv)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, parts, my + (hd * PSTRIDE + D) * 4, 0, kCoherent);
+      });
+  __syncthreads();
+  if (threadIdx.x == 0)
+    arrival = __hip_atomic_fetch_add(&a.counters[kCounterStride * pair], 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrival != (unsigned)(n_parts - 1)) return;
+  // Last to arrive: other threads read this workgroup's own words back, so its stores
+  // (issued an atomic round trip ago) must be complete first.
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&a.counters[pair], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (prev == (unsigned)(n_parts - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  const float* base = a.part + (pair * n_parts * GQA) * PSTRIDE;
-  float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
-  merge_pair<GQA, NTH>(base, n_parts, o, reinterpret_cast<float2*>(&comb[0][0]));
+  merge_pair<GQA, NTH>(parts, n_parts, o, reinterpret_cast<float2*>(&comb[0][0]));
   if (threadIdx.x == 0)
-    __hip_atomic_store(&a.counters[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.counters[kCounterStride * pair], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename F>
@@ -1038,15 +1120,15 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   p.r = (int)(T - Tq);
   p.n_groups = Tq / L.G;
   const int64_t nblk = (Tq + BLK - 1) / BLK;
-  const int64_t units = nblk + (int64_t)RES_COST * ((p.r + 31) / 32);
   const int64_t pairs = (int64_t)L.B * L.H;
-  // default: one round of CU-sized workgroups over the 256 CUs
+  // default: one round of CU-sized workgroups over the 256 CUs; at most one workgroup
+  // for the window and one per block
   int64_t nw = n_split_req > 0 ? n_split_req : kCUs / pairs;
-  if (nw > units) nw = units;
+  if (nw > 1 + nblk) nw = 1 + nblk;
   if (nw < 1) nw = 1;
   p.n_split = (int)nw;
-  p.ws_counters = ((size_t)pairs * sizeof(uint32_t) + 255) / 256 * 256;
-  p.ws_partials = (size_t)pairs * nw * gqa * PSTRIDE * sizeof(float);
+  p.ws_counters = (size_t)pairs * kCounterStride * sizeof(uint32_t);
+  p.ws_partials = nw > 1 ? (size_t)pairs * nw * gqa * PSTRIDE * sizeof(float) : 0;
   p.ws_partials = (p.ws_partials + 255) / 256 * 256;
   p.ws_total = p.ws_counters + p.ws_partials;
   return p;

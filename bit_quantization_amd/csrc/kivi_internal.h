@@ -54,7 +54,7 @@ struct DecodePlan {
   int64_t n_groups;     // quantized Key groups per (b, kv head)
   int r;                // residual tokens
   size_t ws_partials;   // bytes of partial results
-  size_t ws_counters;   // bytes of arrival counters (zero between calls)
+  size_t ws_counters;   // bytes of per-pair ticket counters and call epochs
   size_t ws_total;
 };
 DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_req);

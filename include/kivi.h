@@ -171,9 +171,11 @@ kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t
  *   out        float32 [B][H_q][d] device.
  *   T          1 <= T <= T_max.
  *   workspace  device scratch of at least kivi_decode_workspace_bytes(dims, T) bytes,
- *              private to the library.  Zero-fill it once before its first use; it
- *              can then be reused by later calls without clearing.  Calls that may
- *              run concurrently must use distinct workspaces.
+ *              private to the library.  Zero-fill it before its first use with a
+ *              given batch and kv_heads; later calls with the same batch and
+ *              kv_heads (any T, split count, q_heads or bits that fit) reuse it
+ *              without clearing.  Calls that may run concurrently must use
+ *              distinct workspaces.
  * No floating-point atomics are used and partials are combined in a fixed order,
  * but which wave of a workgroup takes which 64-token block varies from call to call,
  * so repeated calls agree to float32 rounding, not bit for bit.
@@ -183,10 +185,10 @@ kivi_status kivi_decode_attn(const kivi_dims* dims, const kivi_cache* cache, int
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* As kivi_decode_attn with an explicit number of workgroups per (sequence, KV head)
- * (0 = the library's choice: one round of one workgroup per CU).  The work units of a
- * pair are the 64-token blocks of its quantized history and the 32-row chunks of its
- * float16 window; the count is clamped to [1, units].  Workspace size:
- * kivi_decode_workspace_bytes_split. */
+ * (0 = the library's choice: one round of one workgroup per CU).  The first
+ * workgroup of a pair takes its float16 window and the others split the 64-token
+ * blocks of its quantized history, so the count is clamped to [1, 1 + blocks].
+ * Workspace size: kivi_decode_workspace_bytes_split. */
 kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cache,
                                    int32_t layer, int64_t T, const void* q, float sm_scale,
                                    float* out, void* workspace, size_t workspace_bytes,

@@ -255,6 +255,41 @@ def test_decode_repeats_to_float32_rounding():
         assert np.allclose(a, b, rtol=1e-5, atol=1e-6)
 
 
+def test_decode_workspace_reused_across_shapes():
+    # The contract: zero-fill before the first use with a given batch and kv_heads;
+    # later calls with those reuse it for any T, split count, q_heads and bits.  Its
+    # leading per-pair arrival counters (256 bytes per (sequence, KV head)) are back
+    # to zero after every call.
+    k = kv()
+    groups = [  # (B, H): [(bits, G, R, g, T, n_split), ...]
+        ((2, 3), [(2, 32, 64, 4, 1000, 0), (2, 32, 64, 4, 1000, 5), (4, 32, 32, 8, 777, 3),
+                  (2, 64, 64, 2, 1281, 0), (2, 32, 64, 4, 999, 2), (2, 32, 64, 4, 1000, 5)]),
+        ((3, 1), [(2, 64, 64, 2, 1281, 0), (4, 32, 32, 2, 300, 7), (2, 64, 64, 2, 1281, 0)]),
+    ]
+    for (B, H), cases in groups:
+        size = 0
+        for bits, G, R, g, T, n_split in cases:
+            w = W.Workload("ws", 95, 1, B, H, H * g, 128, T, bits, G, 128, R)
+            size = max(size, k.kivi_decode_workspace_bytes(dims_of(w, w.max_tokens()), T, n_split))
+        ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+        for bits, G, R, g, T, n_split in cases:
+            where = (B, H, bits, g, T, n_split)
+            print(f"[parity] shared workspace {where}", flush=True)
+            w = W.Workload("ws", 95, 1, B, H, H * g, 128, T, bits, G, 128, R)
+            dims = dims_of(w, w.max_tokens())
+            K, V = rand_kv(B, H, T, 128, seed=T + 7 * bits)
+            cache = gpu_prefill(w, dims, K, V, T)
+            q = torch.randn((B, H * g, 128), device="cuda").to(torch.float16)
+            out = torch.empty((B, H * g, 128), dtype=torch.float32, device="cuda")
+            k.kivi_decode_attn(dims, cache, 0, T, q, 0.088, out, ws, n_split=n_split)
+            torch.cuda.synchronize()
+            assert int(torch.count_nonzero(ws[:B * H * 256])) == 0, f"counters not reset {where}"
+            oc = O.LayerCache(B, H, 128, bits, G, 128, R, w.max_tokens())
+            oc.prefill(K.cpu().numpy(), V.cpu().numpy())
+            assert_close(out.cpu().numpy(), oc.attend(q.cpu().numpy(), 0.088),
+                         f"shared workspace {where}")
+
+
 # ----------------------------------------------------------------------------------
 # The workload shapes at full size (sampled pairs)
 # ----------------------------------------------------------------------------------
