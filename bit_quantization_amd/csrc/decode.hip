@@ -855,32 +855,44 @@ __device__ __forceinline__ void combine(Src src, Sink sink, SinkMl sink_ml) {
 // round.  A round's words count only when all carry the "written" mark; otherwise the
 // round is read again (a bounded wait: every other workgroup of the pair issued its
 // stores before it arrived, and this one waited for its own, so they become visible;
-// were the bound ever reached the output would be NaN).  Each (partial, head) pair's
-// (m, l) is loaded by one thread into LDS ([head][partial]); thread (head hd,
-// channels c, c+1) loads the accumulators of every partial of the round, all in
-// flight together.  The fold has no branches:
-// indices past the last partial are clamped and weighted 0, and empty partials
-// (l == 0) weigh 0.  Partials are folded in split order with an online rescale.
+// were the bound ever reached the output would be NaN).  Thread (head hd, channels
+// c, c+1) loads the accumulators of every partial of the round, all in flight
+// together; thread (partial u, head hd) loads that partial's (m, l) and, once the
+// round is complete, turns it into the partial's weight w = 2^(m - m*) and l w in LDS,
+// so the fold is multiply-adds only.  Indices past the last partial are clamped and
+// weighted 0, empty partials (l == 0) weigh 0, and rounds fold in split order with
+// an online rescale.
 constexpr int kMaxPolls = 1 << 20;
 template <int GQA, int NTH>
 __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_parts,
-                                           float* __restrict__ out, float2* ml_lds) {
+                                           float* __restrict__ out, float* lds) {
   constexpr int ITEMS = GQA * (D / 2);
   constexpr int IPT = (ITEMS + NTH - 1) / NTH;     // (head, channel pair) items per thread
   constexpr int MERGE_CH = 32 / IPT;               // partials per round
   static_assert(MERGE_CH * GQA <= NTH, "one (m, l) load per thread and round");
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  float m[IPT], l[IPT], o0[IPT], o1[IPT];
+  float2* ml_lds = reinterpret_cast<float2*>(lds);                 // [GQA][MERGE_CH] (m, l)
+  float2* wl_lds = ml_lds + GQA * MERGE_CH;                        // [GQA][MERGE_CH] (w, l w)
+  float* alpha_lds = reinterpret_cast<float*>(wl_lds + GQA * MERGE_CH);   // [GQA]
+  int* vote = reinterpret_cast<int*>(alpha_lds + GQA);             // [3]
+  const bool loader = threadIdx.x < MERGE_CH * GQA;
+  const int lu = threadIdx.x / GQA, lh = threadIdx.x % GQA;        // loader's (partial, head)
+  float m_run = -INFINITY;                                         // loader's running max
+  float l[IPT], o0[IPT], o1[IPT];
 #pragma unroll
-  for (int it = 0; it < IPT; ++it) {
-    m[it] = -INFINITY;
-    l[it] = o0[it] = o1[it] = 0.f;
-  }
+  for (int it = 0; it < IPT; ++it) l[it] = o0[it] = o1[it] = 0.f;
+  if (threadIdx.x < 3) vote[threadIdx.x] = 0;
+  __syncthreads();
   bool failed = false;
+  int poll = 0;
   for (int i0 = 0; i0 < n_parts; i0 += MERGE_CH) {
     const int nc = n_parts - i0 < MERGE_CH ? n_parts - i0 : MERGE_CH;
     float2 ov[IPT][MERGE_CH];
-    for (int poll = 0;; ++poll) {
+    float2 ml = make_float2(-INFINITY, 0.f);
+    for (;; ++poll) {
+      // vote[poll % 3] collects this pass; vote[(poll + 1) % 3], last read two passes
+      // ago, is cleared for the next one
+      if (threadIdx.x == 0) vote[(poll + 1) % 3] = 0;
       bool stale = false;
 #pragma unroll
       for (int it = 0; it < IPT; ++it) {
@@ -897,29 +909,29 @@ __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_p
           }
         }
       }
-      if (threadIdx.x < MERGE_CH * GQA) {
-        const int u = threadIdx.x / GQA, hd = threadIdx.x % GQA;
-        const int i = min(i0 + u, n_parts - 1);
+      if (loader) {
+        const int i = min(i0 + lu, n_parts - 1);
         const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
-            parts, ((i * GQA + hd) * PSTRIDE + D) * 4, 0, kCoherent);
+            parts, ((i * GQA + lh) * PSTRIDE + D) * 4, 0, kCoherent);
         stale |= (w.x & w.y & 1u) == 0u;
-        ml_lds[hd * MERGE_CH + u] =
-            u < nc ? make_float2(unmarked(w.x), unmarked(w.y)) : make_float2(-INFINITY, 0.f);
+        ml = lu < nc ? make_float2(unmarked(w.x), unmarked(w.y)) : make_float2(-INFINITY, 0.f);
+        ml_lds[lh * MERGE_CH + lu] = ml;
       }
-      if (!__syncthreads_or(stale)) break;
+      if (stale) vote[poll % 3] = 1;
+      __syncthreads();
+      const int any = vote[poll % 3];
+      if (!any) break;
       if (poll == kMaxPolls) {
         failed = true;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int idx = threadIdx.x + it * NTH;
-      const int hd = min(idx / (D / 2), GQA - 1);
-      const float4* mlp = reinterpret_cast<const float4*>(&ml_lds[hd * MERGE_CH]);
-      float mc = m[it];
+    ++poll;
+    // weights of the round's partials, one per loader thread
+    if (loader) {
+      const float4* mlp = reinterpret_cast<const float4*>(&ml_lds[lh * MERGE_CH]);
+      float mc = m_run;
 #pragma unroll
       for (int u = 0; u < MERGE_CH; u += 2) {
         const float4 q = mlp[u / 2];
@@ -927,26 +939,34 @@ __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_p
         mc = fmaxf(mc, q.w > 0.f ? q.z : -INFINITY);
       }
       const float mref = mc > -INFINITY ? mc : 0.f;
-      const float wa = __builtin_amdgcn_exp2f(m[it] - mref);
-      float lt = l[it] * wa, a0 = o0[it] * wa, a1 = o1[it] * wa;
+      const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - mref) : 0.f;
+      wl_lds[lh * MERGE_CH + lu] = make_float2(w, ml.y * w);
+      if (lu == 0) alpha_lds[lh] = __builtin_amdgcn_exp2f(m_run - mref);
+      m_run = mc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int idx = threadIdx.x + it * NTH;
+      const int hd = min(idx / (D / 2), GQA - 1);
+      const float4* wlp = reinterpret_cast<const float4*>(&wl_lds[hd * MERGE_CH]);
+      const float al = alpha_lds[hd];
+      float lt = l[it] * al, a0 = o0[it] * al, a1 = o1[it] * al;
 #pragma unroll
       for (int u = 0; u < MERGE_CH; u += 2) {
-        const float4 q = mlp[u / 2];
-        const float w0 = q.y > 0.f ? __builtin_amdgcn_exp2f(q.x - mref) : 0.f;
-        const float w1 = q.w > 0.f ? __builtin_amdgcn_exp2f(q.z - mref) : 0.f;
-        lt = fmaf(q.y, w0, lt);
-        a0 = fmaf(ov[it][u].x, w0, a0);
-        a1 = fmaf(ov[it][u].y, w0, a1);
-        lt = fmaf(q.w, w1, lt);
-        a0 = fmaf(ov[it][u + 1].x, w1, a0);
-        a1 = fmaf(ov[it][u + 1].y, w1, a1);
+        const float4 q = wlp[u / 2];
+        lt += q.y;
+        a0 = fmaf(ov[it][u].x, q.x, a0);
+        a1 = fmaf(ov[it][u].y, q.x, a1);
+        lt += q.w;
+        a0 = fmaf(ov[it][u + 1].x, q.z, a0);
+        a1 = fmaf(ov[it][u + 1].y, q.z, a1);
       }
       l[it] = lt;
       o0[it] = a0;
       o1[it] = a1;
-      m[it] = mc;
     }
-    __syncthreads();                                 // ml_lds is rewritten next round
+    __syncthreads();                                 // the LDS tables are rewritten next round
   }
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
@@ -1091,7 +1111,7 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   // (issued an atomic round trip ago) must be complete first.
   wait_stores();
   __syncthreads();
-  merge_pair<GQA, NTH>(parts, n_parts, o, reinterpret_cast<float2*>(&comb[0][0]));
+  merge_pair<GQA, NTH>(parts, n_parts, o, &comb[0][0]);
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.counters[kCounterStride * pair], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
