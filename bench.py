@@ -3,14 +3,16 @@
 
 One step = one decode step of the streaming hot path on one layer cache: append one
 float16 K/V token per sequence (flushing the residual window into the 2/4-bit store
-when it is full), then decode attention of the new query over all cached tokens.
+when it is full), then decode attention of the new query over all cached tokens,
+through kivi_append_decode (one kernel launch; flush steps add the flush launch).
+With --n-split the step is kivi_append_flush + kivi_decode_attn_split.
 Steps rotate over ``copies`` independent layer caches (like the layers of a model)
 whose total size exceeds the 256 MB last-level cache, so that each step reads its
 cache from HBM.  Inputs are resident in HBM before timing starts.
 
 Printed (one JSON line): value = algorithmic bytes of the timed steps / wall time
-(GB/s), tokens/s, the decode kernel's roofline against the HBM peak, measured with
-HIP events on the launch stream, the CPU oracle's throughput on a bounded sample,
+(GB/s), tokens/s, the step launch's roofline against the HBM peak (its algorithmic
+bytes per launch over its average duration from HIP events on the launch stream), the CPU oracle's throughput on a bounded sample,
 and the output quality against unquantized fp32 attention (reported, not gated).
 
 Algorithmic bytes of a decode launch, per (sequence, KV head): packed codes
@@ -96,6 +98,8 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0: auto)")
     p.add_argument("--n-split", type=int, default=0, help="token splits (0: library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="launch the timed steps one by one instead of as one HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
@@ -195,7 +199,8 @@ def main():
         w1 = w.replace(layers=1)
     else:
         w1 = w
-    total_steps = args.steps + args.warmup
+    # warmup, the eager loop timed per launch (roofline), then the K steps of the graph
+    total_steps = args.warmup + 2 * args.steps
     per_copy_bytes = decode_bytes(w1, w1.tokens)
     copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy_bytes))
     if w.layers > 1:
@@ -246,16 +251,22 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i, record=None):
+        # one decode step: append the token (flushing a full window) and attend; one
+        # kernel launch except on flush steps (1 in R), which add the flush launch
         c = i % copies
         T_before = Ts[c]
         j = T_before - w1.tokens
         kn, vn = news[c]
-        k.kivi_append_flush(dims, caches[c], 0, T_before, kn[j], vn[j])
         T = T_before + 1
         if record is not None:
             record[0].record(stream)
-        k.kivi_decode_attn(dims, caches[c], 0, T, qs[i % len(qs)], w1.sm_scale, out, ws,
-                           n_split=args.n_split)
+        if args.n_split:
+            k.kivi_append_flush(dims, caches[c], 0, T_before, kn[j], vn[j])
+            k.kivi_decode_attn(dims, caches[c], 0, T, qs[i % len(qs)], w1.sm_scale, out, ws,
+                               n_split=args.n_split)
+        else:
+            k.kivi_append_decode(dims, caches[c], 0, T_before, kn[j], vn[j], qs[i % len(qs)],
+                                 w1.sm_scale, out, ws)
         if record is not None:
             record[1].record(stream)
         Ts[c] = T
@@ -265,23 +276,50 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # Per-launch duration (roofline): K eager steps, each bracketed by HIP events on
+    # the launch stream.
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
-    dec_bytes = 0
-    app_bytes = 0
+    launch_bytes = 0
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         db, ab = step(args.warmup + i, events[i])
-        dec_bytes += db
-        app_bytes += ab
+        launch_bytes += db + ab          # the timed launch appends and attends
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
     dec_ms = [a.elapsed_time(b) for a, b in events]
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     dec_med_s = sorted(dec_ms)[len(dec_ms) // 2] / 1e3
-    dec_per_launch = dec_bytes / args.steps
+    dec_per_launch = launch_bytes / args.steps
+
+    # Whole-job throughput: the next K steps, launched as one HIP graph (captured with
+    # each step's own arguments, so replaying it once runs exactly those K steps and
+    # the host's per-call cost leaves the timed region), between two synchronizations.
+    dec_bytes = 0
+    app_bytes = 0
+    first = args.warmup + args.steps
+    if args.no_graph:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            db, ab = step(first + i)
+            dec_bytes += db
+            app_bytes += ab
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                db, ab = step(first + i)
+                dec_bytes += db
+                app_bytes += ab
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del graph
+    wall = t1 - t0
 
     # Quality versus unquantized fp32 attention on copy 0 (reported, not gated).
     K, V = keep
@@ -347,10 +385,13 @@ def main():
                    "q_heads": w1.q_heads, "head_dim": w1.head_dim, "tokens": w1.tokens,
                    "bits": w1.bits, "group_k": w1.group_k, "group_v": w1.group_v,
                    "residual": w1.residual, "layer_caches": copies, "n_split": n_split,
-                   "step": "append(+flush) + decode attention"},
+                   "step": "append(+flush) + decode attention",
+                   "launch": "one HIP graph of the timed steps" if not args.no_graph
+                             else "one call per step"},
         "tokens_per_s": round(w1.batch * args.steps / wall, 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel (work queue + merge)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_kernel (append fused; work queue + merge)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(dec_per_launch),

@@ -1,7 +1,8 @@
 """Build the HIP library ``libkivi.so`` in-tree for gfx950 with hipcc.
 
 Every source under ``csrc/`` is compiled into one shared library next to this file.
-Run as ``python -m bit_quantization_amd.build``.
+Run as ``python bit_quantization_amd/build.py`` (by path: importing the package loads
+the library it builds).
 """
 from __future__ import annotations
 
@@ -45,10 +46,8 @@ def hipcc() -> str:
 def build_library(verbose: bool = True) -> str:
     srcs = []
     for name in SOURCES:
-        src = os.path.join(CSRC, name)
-        # hipcc compiles .cpp sources as host C++; the API file launches through
-        # launchers defined in the .hip sources, so it needs only the HIP headers.
-        srcs += ["-x", "hip", src] if name.endswith(".hip") else ["-x", "hip", src]
+        # every source compiles as HIP (the API file includes the HIP runtime headers)
+        srcs += ["-x", "hip", os.path.join(CSRC, name)]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:

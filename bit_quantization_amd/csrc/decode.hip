@@ -62,6 +62,9 @@ struct DecodeArgs {
   int r;                // residual tokens
   int nw;               // workgroups per pair
   float qscale;         // sm_scale * log2(e)
+  const __half* k_new;  // [P][D]: window row new_slot comes from here (new_slot >= 0)
+  const __half* v_new;
+  int new_slot;         // -1: every window row is read from the cache
 };
 
 // Waves per SIMD that the register budget of each variant allows; a workgroup holds
@@ -713,7 +716,7 @@ __device__ __forceinline__ void load_q_f16(const __half* qp, f16x8 (&aq)[4]) {
 
 // Window rows [c0, c0 + n_valid), n_valid <= 32.  Every Key and Value load of the
 // chunk goes out before any is used (rows past the chunk re-read its last row; their
-// probabilities are 0).  Float16 products are exact in float32 (subnormal operands
+// probabilities are 0).  Row a.new_slot, when set, is read from the appended token.  Float16 products are exact in float32 (subnormal operands
 // aside), accumulated in float32.
 template <int GQA>
 __device__ __forceinline__ void residual_rows(const DecodeArgs& a, int64_t pair, int c0,
@@ -730,19 +733,22 @@ __device__ __forceinline__ void residual_rows(const DecodeArgs& a, int64_t pair,
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int rr = 16 * nt + lo < n_valid ? 16 * nt + lo : n_valid - 1;
+    const __half* row = c0 + rr == a.new_slot ? a.k_new + pair * D : kr + (int64_t)(c0 + rr) * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      bk[nt][ks] = *reinterpret_cast<const f16x8*>(kr + (int64_t)(c0 + rr) * D + 32 * ks + 8 * j);
+      bk[nt][ks] = *reinterpret_cast<const f16x8*>(row + 32 * ks + 8 * j);
   }
   // Value pairs, channels 2*lane, 2*lane+1 of the 32 rows (one descriptor: shared lane
   // offset, wave-uniform row offset in the scalar offset)
   const __amdgpu_buffer_rsrc_t vres = make_rsrc(vr, L.rs_pair() * 2);
+  const __amdgpu_buffer_rsrc_t vnew = make_rsrc(a.v_new ? a.v_new + pair * D : vr, D * 2);
   __half2 vv[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
     const int rr = t < n_valid ? t : n_valid - 1;
-    vv[t] = __builtin_bit_cast(__half2, __builtin_amdgcn_raw_buffer_load_b32(vres, 4 * lane,
-                                                                            (c0 + rr) * D * 2, 0));
+    const bool fresh = c0 + rr == a.new_slot;
+    vv[t] = __builtin_bit_cast(__half2, __builtin_amdgcn_raw_buffer_load_b32(
+                                            fresh ? vnew : vres, 4 * lane, fresh ? 0 : (c0 + rr) * D * 2, 0));
   }
   f32x4 d[2];
 #pragma unroll
@@ -1028,6 +1034,14 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   const int n_items = n_res + (int)(b_hi - b_lo);
 
   if (threadIdx.x == 0) counter = 0;
+  // An appended token: workgroup 0 of the pair stores its rows into the window (read
+  // by the next call; this one takes them from k_new / v_new).
+  if (a.new_slot >= 0 && s == 0 && threadIdx.x < 2 * (D / 8)) {
+    const int part = threadIdx.x / (D / 8), k = threadIdx.x % (D / 8);
+    const __half* src = (part ? a.v_new : a.k_new) + pair * D;
+    __half* dst = (part ? a.L.v_resid : a.L.k_resid) + pair * a.L.rs_pair() + (int64_t)a.new_slot * D;
+    reinterpret_cast<uint4*>(dst)[k] = reinterpret_cast<const uint4*>(src)[k];
+  }
   // Clear this workgroup's partial slot, each thread the words it stores at the end.
   const int n_parts = a.nw;
   const int64_t pair_floats = (int64_t)n_parts * GQA * PSTRIDE;
@@ -1156,7 +1170,7 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
 
 hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __half* q,
                          float sm_scale, float* out, void* ws, const DecodePlan& plan,
-                         hipStream_t s) {
+                         const NewRow* new_row, hipStream_t s) {
   const int gqa = q_heads / L.H;
   DecodeArgs a;
   a.L = L;
@@ -1169,6 +1183,9 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.r = plan.r;
   a.nw = plan.n_split;
   a.qscale = sm_scale * 1.4426950408889634f;
+  a.k_new = new_row ? new_row->k : nullptr;
+  a.v_new = new_row ? new_row->v : nullptr;
+  a.new_slot = new_row ? new_row->slot : -1;
   const int64_t P = (int64_t)L.B * L.H;
   const dim3 grid((unsigned)(P * plan.n_split));
   bool ok = dispatch_decode(L.bits, gqa, L.G, [&](auto b, auto g, auto gg) {

@@ -162,9 +162,11 @@ kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int3
   return device_status(e, keys ? "kivi_quantize_k launch" : "kivi_quantize_v launch");
 }
 
-kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+// Checks of a decode call over T tokens; fills *L and *plan.
+kivi_status decode_checks(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                           int64_t T, const void* q, float sm_scale, float* out, void* ws,
-                          size_t ws_bytes, int32_t n_split, void* stream) {
+                          size_t ws_bytes, int32_t n_split, kivi::LayerView* Lout,
+                          kivi::DecodePlan* plan_out) {
   kivi_status st = check_common(dims, cache, layer);
   if (st != KIVI_OK) return st;
   if (dims->group_v != dims->head_dim)
@@ -188,9 +190,35 @@ kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_
   if (!aligned16(ws)) return fail(KIVI_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (ws_bytes < plan.ws_total)
     return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, plan.ws_total);
+  *Lout = L;
+  *plan_out = plan;
+  return KIVI_OK;
+}
+
+kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                          int64_t T, const void* q, float sm_scale, float* out, void* ws,
+                          size_t ws_bytes, int32_t n_split, void* stream) {
+  kivi::LayerView L;
+  kivi::DecodePlan plan;
+  kivi_status st = decode_checks(dims, cache, layer, T, q, sm_scale, out, ws, ws_bytes, n_split,
+                                 &L, &plan);
+  if (st != KIVI_OK) return st;
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
-                                     out, ws, plan, static_cast<hipStream_t>(stream));
+                                     out, ws, plan, nullptr, static_cast<hipStream_t>(stream));
   return device_status(e, "kivi_decode_attn launch");
+}
+
+// Checks of an append at T_before.
+kivi_status append_checks(const kivi_dims* dims, int64_t T_before, const void* k_new,
+                          const void* v_new) {
+  if (T_before < 0) return fail(KIVI_ERR_ARG, "T_before = %lld is negative", (long long)T_before);
+  if (T_before + 1 > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T_before + 1 = %lld exceeds max_tokens = %lld",
+                (long long)(T_before + 1), (long long)dims->max_tokens);
+  if (!k_new || !v_new) return fail(KIVI_ERR_ARG, "k_new or v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(KIVI_ERR_ALIGN, "k_new or v_new is not 16-byte aligned");
+  return KIVI_OK;
 }
 
 }  // namespace
@@ -220,13 +248,8 @@ kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, in
                               void* stream) {
   kivi_status st = check_common(dims, cache, layer);
   if (st != KIVI_OK) return st;
-  if (T_before < 0) return fail(KIVI_ERR_ARG, "T_before = %lld is negative", (long long)T_before);
-  if (T_before + 1 > dims->max_tokens)
-    return fail(KIVI_ERR_CAPACITY, "T_before + 1 = %lld exceeds max_tokens = %lld",
-                (long long)(T_before + 1), (long long)dims->max_tokens);
-  if (!k_new || !v_new) return fail(KIVI_ERR_ARG, "k_new or v_new is NULL");
-  if (!aligned16(k_new) || !aligned16(v_new))
-    return fail(KIVI_ERR_ALIGN, "k_new or v_new is not 16-byte aligned");
+  st = append_checks(dims, T_before, k_new, v_new);
+  if (st != KIVI_OK) return st;
   const kivi::LayerView L = layer_view(dims, cache, layer);
   hipError_t e = kivi::launch_append_flush(L, T_before, static_cast<const __half*>(k_new),
                                            static_cast<const __half*>(v_new),
@@ -295,8 +318,40 @@ kivi_status kivi_decode_attn_split(const kivi_dims* dims, const kivi_cache* cach
                        n_split, stream);
 }
 
+kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                               int64_t T_before, const void* k_new, const void* v_new,
+                               const void* q, float sm_scale, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  st = append_checks(dims, T_before, k_new, v_new);
+  if (st != KIVI_OK) return st;
+  const int64_t T = T_before + 1;
+  kivi::LayerView L;
+  kivi::DecodePlan plan;
+  st = decode_checks(dims, cache, layer, T, q, sm_scale, out, workspace, workspace_bytes, 0, &L,
+                     &plan);
+  if (st != KIVI_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const __half* kn = static_cast<const __half*>(k_new);
+  const __half* vn = static_cast<const __half*>(v_new);
+  const int64_t r_before = kivi::residual_len(T_before, L.R);
+  if (r_before == L.R) {
+    // the window is full: flush it (and store the new row) first, then attend
+    hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, s);
+    if (e != hipSuccess) return device_status(e, "kivi_append_decode flush launch");
+    e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale, out,
+                            workspace, plan, nullptr, s);
+    return device_status(e, "kivi_append_decode launch");
+  }
+  const kivi::NewRow nr{kn, vn, (int)r_before};
+  hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
+                                     out, workspace, plan, &nr, s);
+  return device_status(e, "kivi_append_decode launch");
+}
+
 const char* kivi_last_error(void) { return g_err; }
 
-int32_t kivi_abi_version(void) { return 2; }
+int32_t kivi_abi_version(void) { return 3; }
 
 }  // extern "C"

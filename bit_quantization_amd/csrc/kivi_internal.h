@@ -54,12 +54,19 @@ struct DecodePlan {
   int64_t n_groups;     // quantized Key groups per (b, kv head)
   int r;                // residual tokens
   size_t ws_partials;   // bytes of partial results
-  size_t ws_counters;   // bytes of per-pair ticket counters and call epochs
+  size_t ws_counters;   // bytes of per-pair arrival counters
   size_t ws_total;
 };
 DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_req);
+// A token appended by the decode launch itself: its rows are read from k/v (float16
+// [B][H_kv][d]) as window row `slot`, and the launch also stores them there.
+struct NewRow {
+  const __half* k;
+  const __half* v;
+  int slot;
+};
 hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __half* q,
                          float sm_scale, float* out, void* ws, const DecodePlan& plan,
-                         hipStream_t s);
+                         const NewRow* new_row, hipStream_t s);
 
 }  // namespace kivi

@@ -24,6 +24,7 @@ STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_E
 
 EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
            "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
+           "kivi_append_decode",
            "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
            "kivi_abi_version")
 
@@ -54,7 +55,7 @@ class kivi_cache(ctypes.Structure):
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing; build it with `python -m bit_quantization_amd.build` "
+        raise ImportError(f"{path} is missing; build it with `python bit_quantization_amd/build.py` "
                           f"(the HIP path has no fallback)")
     lib = ctypes.CDLL(path)
     P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -70,6 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_decode_splits": (I32, [D, I64, ctypes.POINTER(I32)]),
         "kivi_decode_attn": (I32, [D, C, I32, I64, P, F32, P, P, SZ, P]),
         "kivi_decode_attn_split": (I32, [D, C, I32, I64, P, F32, P, P, SZ, I32, P]),
+        "kivi_append_decode": (I32, [D, C, I32, I64, P, P, P, F32, P, P, SZ, P]),
         "kivi_last_error": (ctypes.c_char_p, []),
         "kivi_abi_version": (I32, []),
     }
@@ -227,6 +229,20 @@ def kivi_decode_attn(dims: Dims, cache: Cache, layer: int, T: int, q: torch.Tens
         st = _lib.kivi_decode_attn(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, T,
                                    qp, ctypes.c_float(sm_scale), op, wp, wb, _stream(stream))
     _check(st)
+
+
+def kivi_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k_new, v_new,
+                       q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                       workspace: torch.Tensor, stream=None):
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    _check(_lib.kivi_append_decode(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                   T_before, _ptr(k_new, torch.float16, "k_new", need),
+                                   _ptr(v_new, torch.float16, "v_new", need),
+                                   _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
+                                   _ptr(out, torch.float32, "out", nq),
+                                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                   _stream(stream)))
 
 
 def kivi_abi_version() -> int:

@@ -158,6 +158,23 @@ kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, in
                               int64_t T_before, const void* k_new, const void* v_new,
                               void* stream);
 
+/* One decode step of a layer: append the new token, then attend over the
+ * T_before + 1 cached tokens ("KIVI: A Tuning-Free Asymmetric 2bit Quantization for
+ * KV Cache", "The streaming complication": new tokens enter the float16 window and
+ * the query attends over history and window).  The result, and the cache it leaves,
+ * equal kivi_append_flush(T_before, k_new, v_new) followed by
+ * kivi_decode_attn(T = T_before + 1) (outputs to float32 rounding, as between any two
+ * decode calls).  When r(T_before) < R this is one kernel launch: the attention
+ * reads the new row from k_new / v_new and stores it into the window; when the
+ * window is full it is the flush launch followed by the decode launch.
+ *   Arguments as kivi_append_flush and kivi_decode_attn; the workspace must hold
+ *   kivi_decode_workspace_bytes(dims, T_before + 1).
+ * Every check of both calls runs before anything is enqueued. */
+kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                               int64_t T_before, const void* k_new, const void* v_new,
+                               const void* q, float sm_scale, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Workspace bytes kivi_decode_attn needs for T cached tokens (host-only). */
 kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t* bytes);
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert kv.kivi_abi_version() == 2
+    assert kv.kivi_abi_version() == 3
 
 
 def good_dims(**kw):
@@ -156,6 +156,27 @@ def test_decode_argument_checks():
     d3 = good_dims(group_k=16).c()
     assert call("kivi_decode_attn", ctypes.byref(d3), c, 0, 300, FAKE, ctypes.c_float(0.1), FAKE,
                 FAKE, need, None)[0] == 2
+
+
+def test_append_decode_argument_checks():
+    d = good_dims()
+    dc = d.c()
+    c = ctypes.byref(fake_cache())
+    need = kv.kivi_decode_workspace_bytes(d, 301)
+    args = lambda Tb, kn, vn, q, out, ws, wsb: (ctypes.byref(dc), c, 0, Tb, kn, vn, q,
+                                               ctypes.c_float(0.1), out, ws, wsb, None)
+    assert call("kivi_append_decode", *args(512, FAKE, FAKE, FAKE, FAKE, FAKE, need))[0] == 3
+    assert call("kivi_append_decode", *args(-1, FAKE, FAKE, FAKE, FAKE, FAKE, need))[0] == 1
+    assert call("kivi_append_decode", *args(300, None, FAKE, FAKE, FAKE, FAKE, need))[0] == 1
+    assert call("kivi_append_decode", *args(300, FAKE, FAKE + 4, FAKE, FAKE, FAKE, need))[0] == 4
+    assert call("kivi_append_decode", *args(300, FAKE, FAKE, None, FAKE, FAKE, need))[0] == 1
+    assert call("kivi_append_decode", *args(300, FAKE, FAKE, FAKE, FAKE + 8, FAKE, need))[0] == 4
+    assert call("kivi_append_decode", *args(300, FAKE, FAKE, FAKE, FAKE, None, need))[0] == 5
+    # the workspace is sized for T_before + 1 tokens
+    assert call("kivi_append_decode", *args(300, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1))[0] == 5
+    st, msg = call("kivi_append_decode", ctypes.byref(dc), ctypes.byref(fake_cache(v_resid=0)), 0,
+                   300, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, need, None)
+    assert st == 1 and "v_resid" in msg
 
 
 def test_split_plan_is_clamped_and_workspace_grows_with_splits():

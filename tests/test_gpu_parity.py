@@ -239,6 +239,92 @@ def test_decode_matches_oracle(bits, G, R, B, H, g, T, n_split):
     assert_close(out, ref, f"decode bits={bits} T={T} n_split={n_split}")
 
 
+@pytest.mark.parametrize("bits,G,R,B,H,g", [(2, 32, 64, 2, 2, 4), (4, 64, 128, 1, 3, 2),
+                                             (2, 32, 32, 2, 1, 8)])
+def test_append_decode_equals_append_then_decode(bits, G, R, B, H, g):
+    # The fused step (one launch between flushes) against kivi_append_flush followed by
+    # kivi_decode_attn on a second cache: outputs agree to float32 rounding, the caches
+    # end bit-identical, and sampled steps match the oracle.  The stream starts
+    # mid-window and crosses several flushes.
+    k = kv()
+    d = 128
+    Tp, steps = R - 5, 2 * R + 9
+    w = W.Workload("fused", 96, 1, B, H, H * g, d, Tp + steps, bits, G, d, R)
+    Tmax = w.max_tokens()
+    dims = dims_of(w, Tmax)
+    K, V = rand_kv(B, H, Tp + steps, d, seed=R + g)
+    a = gpu_prefill(w, dims, K, V, Tp)
+    b_ = gpu_prefill(w, dims, K, V, Tp)
+    wa = k.new_workspace(dims, Tp + steps)
+    wb = k.new_workspace(dims, Tp + steps)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(g)
+    oa = torch.empty((B, H * g, d), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    for t in range(Tp, Tp + steps):
+        q = torch.randn((B, H * g, d), generator=gq, device="cuda").to(torch.float16)
+        kn, vn = K[:, :, t].contiguous(), V[:, :, t].contiguous()
+        k.kivi_append_flush(dims, a, 0, t, kn, vn)
+        k.kivi_decode_attn(dims, a, 0, t + 1, q, 0.09, oa, wa)
+        k.kivi_append_decode(dims, b_, 0, t, kn, vn, q, 0.09, ob, wb)
+        torch.cuda.synchronize()
+        assert np.allclose(oa.cpu().numpy(), ob.cpu().numpy(), rtol=1e-5, atol=1e-6), f"step {t}"
+        if t in (Tp, Tp + R - 1, Tp + steps - 1):
+            oc = O.LayerCache(B, H, d, bits, G, d, R, Tmax)
+            oc.prefill(K[:, :, :t + 1].cpu().numpy(), V[:, :, :t + 1].cpu().numpy())
+            assert_close(ob.cpu().numpy(), oc.attend(q.cpu().numpy(), 0.09), f"fused step {t}")
+    for name in k.BUFFERS:
+        assert torch.equal(a.view(name).cpu(), b_.view(name).cpu()), f"{name} differs"
+
+
+def test_decode_in_a_hip_graph_matches_eager():
+    # Replays of a captured decode step, with eager work between them, match the eager
+    # call every time (the workspace's counters are reset by each launch itself; no
+    # memset is recorded).  Then a captured run of fused append+decode steps leaves the
+    # same cache bytes as the same steps run eagerly.
+    k = kv()
+    d, B, H, g, R = 128, 2, 2, 4, 64
+    T0, steps = 3 * R - 2, R + 5
+    w = W.Workload("graph", 97, 1, B, H, H * g, d, T0 + steps, 2, 32, d, R)
+    dims = dims_of(w, w.max_tokens())
+    K, V = rand_kv(B, H, T0 + steps, d, seed=5)
+    a = gpu_prefill(w, dims, K, V, T0)
+    b_ = gpu_prefill(w, dims, K, V, T0)
+    q = torch.randn((B, H * g, d), device="cuda").to(torch.float16)
+    ws = k.new_workspace(dims, T0 + steps)
+    ref = torch.empty((B, H * g, d), dtype=torch.float32, device="cuda")
+    k.kivi_decode_attn(dims, a, 0, T0, q, 0.09, ref, ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        k.kivi_decode_attn(dims, a, 0, T0, q, 0.09, out, ws)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.allclose(out.cpu().numpy(), ref.cpu().numpy(), rtol=1e-5, atol=1e-6), f"replay {rep}"
+        k.kivi_decode_attn(dims, a, 0, T0, q, 0.09, ref, ws)      # eager work in between
+        torch.cuda.synchronize()
+    del graph
+    oa = torch.empty_like(ref)
+    wb = k.new_workspace(dims, T0 + steps)
+    for t in range(T0, T0 + steps):
+        k.kivi_append_decode(dims, a, 0, t, K[:, :, t].contiguous(), V[:, :, t].contiguous(), q,
+                             0.09, oa, ws)
+    rows = [(K[:, :, t].contiguous(), V[:, :, t].contiguous()) for t in range(T0, T0 + steps)]
+    ob = torch.empty_like(ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i, t in enumerate(range(T0, T0 + steps)):
+            k.kivi_append_decode(dims, b_, 0, t, rows[i][0], rows[i][1], q, 0.09, ob, wb)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert np.allclose(oa.cpu().numpy(), ob.cpu().numpy(), rtol=1e-5, atol=1e-6)
+    for name in k.BUFFERS:
+        assert torch.equal(a.view(name).cpu(), b_.view(name).cpu()), f"{name} differs"
+
+
 def test_decode_repeats_to_float32_rounding():
     # Waves take 64-token blocks from a queue, so the order of float additions can
     # change from call to call; the integer parts of the sums are order-free and the
