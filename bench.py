@@ -101,6 +101,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true",
                    help="launch the timed steps one by one instead of as one HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    p.add_argument("--read-ceiling", action="store_true",
+                   help="time plain reads of the decode working-set sizes (torch reductions) "
+                        "and exit: the streaming-read rate this GPU reaches at each size")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
     return p.parse_args()
@@ -116,6 +119,40 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read": 2 ** 30, "bytes_written": 2 ** 30,
                       "launches": 5}), flush=True)
+
+
+def read_ceiling():
+    """Best-of-5 HIP-event time of kivi_stream_read (a plain 16-byte-load read) over
+    the decode working-set sizes, each repeat on a slice that is not in the 256 MB
+    last-level cache."""
+    import torch
+    from bit_quantization_amd import kivi as k
+    torch.cuda.set_device(0)
+    total = 4 << 30
+    buf = torch.ones(total // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    res = {}
+    for mb in (88, 177, 1024, 4096):
+        n = mb << 20
+        slices = total // n
+        best = float("inf")
+        for rep in range(5):
+            s0 = ((rep * 3 + 1) % slices) * n
+            # a 1 GB read of another slice first: it keeps the GPU busy while the timed
+            # interval is enqueued (so the interval holds no host time) and leaves the
+            # last-level cache without the timed slice
+            o = (((s0 >> 30) + 2) % (total >> 30)) << 30
+            k.kivi_stream_read(buf[o // 4:], 1 << 30, sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            k.kivi_stream_read(buf[s0 // 4:], n, sink)
+            b.record()
+            b.synchronize()
+            best = min(best, a.elapsed_time(b) / 1e3)
+        res[f"{mb}MB"] = {"us": round(best * 1e6, 2), "GB/s": round(n / best / 1e9, 1),
+                          "pct_of_peak": round(100 * n / best / 1e9 / HBM_PEAK_GBS, 1)}
+    print(json.dumps({"read_ceiling": res, "kernel": "kivi_stream_read (8192 x 256 threads, "
+                      "16-byte loads)", "timing": "HIP events, best of 5"}), flush=True)
 
 
 def prefill_bytes(w, T):
@@ -185,6 +222,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.read_ceiling:
+        read_ceiling()
+        return
 
     import numpy as np
     import torch
@@ -250,41 +290,43 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(i, record=None):
-        # one decode step: append the token (flushing a full window) and attend; one
-        # kernel launch except on flush steps (1 in R), which add the flush launch
+    def prepare(i):
+        """Step i: one decode step (append the token, flushing a full window, then
+        attend), with its arguments marshalled now so that the timed loops only make
+        the calls; one kernel launch except on flush steps (1 in R), which add the
+        flush launch.  Returns (call, decode bytes, append bytes)."""
         c = i % copies
         T_before = Ts[c]
         j = T_before - w1.tokens
         kn, vn = news[c]
         T = T_before + 1
-        if record is not None:
-            record[0].record(stream)
-        if args.n_split:
-            k.kivi_append_flush(dims, caches[c], 0, T_before, kn[j], vn[j])
-            k.kivi_decode_attn(dims, caches[c], 0, T, qs[i % len(qs)], w1.sm_scale, out, ws,
-                               n_split=args.n_split)
-        else:
-            k.kivi_append_decode(dims, caches[c], 0, T_before, kn[j], vn[j], qs[i % len(qs)],
-                                 w1.sm_scale, out, ws)
-        if record is not None:
-            record[1].record(stream)
         Ts[c] = T
-        return decode_bytes(w1, T), append_bytes(w1, T_before)
+        q = qs[i % len(qs)]
+        if args.n_split:
+            def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
+                k.kivi_append_flush(dims, caches[c], 0, T_before, kj, vj)
+                k.kivi_decode_attn(dims, caches[c], 0, T, q, w1.sm_scale, out, ws,
+                                   n_split=args.n_split)
+        else:
+            call = k.prepare_append_decode(dims, caches[c], 0, T_before, kn[j], vn[j], q,
+                                           w1.sm_scale, out, ws)
+        return call, decode_bytes(w1, T), append_bytes(w1, T_before)
 
     for i in range(args.warmup):
-        step(i)
+        prepare(i)[0]()
     torch.cuda.synchronize()
 
     # Per-launch duration (roofline): K eager steps, each bracketed by HIP events on
     # the launch stream.
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
-    launch_bytes = 0
+    steps = [prepare(args.warmup + i) for i in range(args.steps)]
+    launch_bytes = sum(db + ab for _, db, ab in steps)   # each launch appends and attends
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        db, ab = step(args.warmup + i, events[i])
-        launch_bytes += db + ab          # the timed launch appends and attends
+    for (call, _, _), (e0, e1) in zip(steps, events):
+        e0.record(stream)
+        call()
+        e1.record(stream)
     torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in events]
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
@@ -294,25 +336,22 @@ def main():
     # Whole-job throughput: the next K steps, launched as one HIP graph (captured with
     # each step's own arguments, so replaying it once runs exactly those K steps and
     # the host's per-call cost leaves the timed region), between two synchronizations.
-    dec_bytes = 0
-    app_bytes = 0
     first = args.warmup + args.steps
     if args.no_graph:
+        steps = [prepare(first + i) for i in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            db, ab = step(first + i)
-            dec_bytes += db
-            app_bytes += ab
+        for call, _, _ in steps:
+            call()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     else:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                db, ab = step(first + i)
-                dec_bytes += db
-                app_bytes += ab
+            # the calls are marshalled inside the capture: they must use its stream
+            steps = [prepare(first + i) for i in range(args.steps)]
+            for call, _, _ in steps:
+                call()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         graph.replay()
@@ -320,6 +359,8 @@ def main():
         t1 = time.perf_counter()
         del graph
     wall = t1 - t0
+    dec_bytes = sum(db for _, db, _ in steps)
+    app_bytes = sum(ab for _, _, ab in steps)
 
     # Quality versus unquantized fp32 attention on copy 0 (reported, not gated).
     K, V = keep

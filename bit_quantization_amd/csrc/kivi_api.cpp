@@ -350,6 +350,19 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
   return device_status(e, "kivi_append_decode launch");
 }
 
+kivi_status kivi_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
+                             void* stream) {
+  if (!buf || !sink) return fail(KIVI_ERR_ARG, "buf or sink is NULL");
+  if (!aligned16(buf) || !aligned16(sink)) return fail(KIVI_ERR_ALIGN, "buf or sink is not 16-byte aligned");
+  if (bytes % 16 != 0) return fail(KIVI_ERR_ARG, "bytes = %zu is not a multiple of 16", bytes);
+  const size_t need = (size_t)kivi::kStreamReadBlocks * 256 * sizeof(unsigned);
+  if (sink_bytes < need) return fail(KIVI_ERR_WORKSPACE, "sink has %zu bytes, needs %zu", sink_bytes, need);
+  if (bytes == 0) return ok();
+  hipError_t e = kivi::launch_stream_read(buf, bytes, static_cast<unsigned*>(sink),
+                                          static_cast<hipStream_t>(stream));
+  return device_status(e, "kivi_stream_read launch");
+}
+
 const char* kivi_last_error(void) { return g_err; }
 
 int32_t kivi_abi_version(void) { return 3; }

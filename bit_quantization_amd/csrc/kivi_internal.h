@@ -69,4 +69,9 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
                          float sm_scale, float* out, void* ws, const DecodePlan& plan,
                          const NewRow* new_row, hipStream_t s);
 
+// Measurement aid: a plain read of `bytes` (a multiple of 16) with kStreamReadBlocks
+// workgroups of 256 threads; sink holds one word per thread.
+constexpr int kStreamReadBlocks = 8192;
+hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
+
 }  // namespace kivi

@@ -24,7 +24,7 @@ STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_E
 
 EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
            "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
-           "kivi_append_decode",
+           "kivi_append_decode", "kivi_stream_read",
            "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
            "kivi_abi_version")
 
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_decode_attn": (I32, [D, C, I32, I64, P, F32, P, P, SZ, P]),
         "kivi_decode_attn_split": (I32, [D, C, I32, I64, P, F32, P, P, SZ, I32, P]),
         "kivi_append_decode": (I32, [D, C, I32, I64, P, P, P, F32, P, P, SZ, P]),
+        "kivi_stream_read": (I32, [P, SZ, P, SZ, P]),
         "kivi_last_error": (ctypes.c_char_p, []),
         "kivi_abi_version": (I32, []),
     }
@@ -243,6 +244,36 @@ def kivi_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k_ne
                                    _ptr(out, torch.float32, "out", nq),
                                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                    _stream(stream)))
+
+
+def prepare_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k_new, v_new,
+                          q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                          workspace: torch.Tensor, stream=None):
+    """kivi_append_decode with its arguments checked and marshalled once: returns a
+    function of no arguments that makes the call (for loops where the host's per-call
+    cost matters; the tensors must stay alive and in place until then)."""
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    args = (ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, T_before,
+            _ptr(k_new, torch.float16, "k_new", need), _ptr(v_new, torch.float16, "v_new", need),
+            _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
+            _ptr(out, torch.float32, "out", nq), _ptr(workspace, torch.uint8, "workspace"),
+            workspace.numel(), _stream(stream))
+    fn = _lib.kivi_append_decode
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            _check(st)
+    return call
+
+
+def kivi_stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=None):
+    """Measurement aid: read nbytes of buf once (see include/kivi.h)."""
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    _check(_lib.kivi_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                 sink.numel() * sink.element_size(), _stream(stream)))
 
 
 def kivi_abi_version() -> int:

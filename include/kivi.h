@@ -221,6 +221,15 @@ kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_spli
  * Valid until the next kivi_* call on the same thread. */
 const char* kivi_last_error(void);
 
+/* Measurement aid, not part of the method: read `bytes` (a multiple of 16) of device
+ * memory at `buf` once with plain 16-byte loads (8192 workgroups of 256 threads,
+ * grid-stride) and write one XOR word per thread to `sink` (device, at least
+ * 8 MiB = 8192 * 256 * 4 bytes, else KIVI_ERR_WORKSPACE).  Timing it gives the rate at
+ * which this GPU streams a working set of that size from HBM, the reference for the
+ * decode kernels' bandwidth.  Enqueued on `stream`. */
+kivi_status kivi_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
+                             void* stream);
+
 /* ABI version of this library (bumped on any incompatible change). */
 int32_t kivi_abi_version(void);
 
