@@ -69,6 +69,32 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
                          float sm_scale, float* out, void* ws, const DecodePlan& plan,
                          const NewRow* new_row, hipStream_t s);
 
+// ---- FP8 KV codec -----------------------------------------------------------------
+// One layer of an FP8 cache: Key codes [B][H][Tmax][d], Value codes in 32-token runs
+// [B][H][Tmax/32][d][32], float32 scales per KV head.
+constexpr int kFp8Run = 32;
+struct Fp8View {
+  uint8_t* k;
+  uint8_t* v;
+  const float* k_scale;   // [H]
+  const float* v_scale;   // [H]
+  int B, H, fmt;          // fmt: 0 E4M3, 1 E5M2
+  int64_t Tmax;
+  __host__ __device__ int64_t pair_bytes() const { return Tmax * kHeadDim; }
+};
+struct Fp8Plan {
+  int n_split;            // workgroups per (sequence, KV head)
+  size_t ws_counters, ws_partials, ws_total;
+};
+hipError_t launch_fp8_quantize(const Fp8View& L, const __half* k, const __half* v, int64_t ld,
+                               int64_t T, hipStream_t s);
+hipError_t launch_fp8_append(const Fp8View& L, const __half* k_new, const __half* v_new,
+                             int64_t t, hipStream_t s);
+Fp8Plan plan_fp8_decode(int B, int H, int q_heads, int64_t T, int n_split_req);
+hipError_t launch_fp8_decode(const Fp8View& L, int q_heads, int64_t T, const __half* q,
+                             float sm_scale, float* out, void* ws, const Fp8Plan& plan,
+                             hipStream_t s);
+
 // Measurement aid: a plain read of `bytes` (a multiple of 16) with kStreamReadBlocks
 // workgroups of 256 threads; sink holds one word per thread.
 constexpr int kStreamReadBlocks = 8192;

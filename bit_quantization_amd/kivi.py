@@ -24,7 +24,9 @@ STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_E
 
 EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
            "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
-           "kivi_append_decode", "kivi_stream_read",
+           "kivi_append_decode", "kivi_stream_read", "kivi_fp8_cache_sizes",
+           "kivi_fp8_quantize", "kivi_fp8_append", "kivi_fp8_decode_workspace_bytes",
+           "kivi_fp8_decode_attn",
            "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
            "kivi_abi_version")
 
@@ -53,6 +55,21 @@ class kivi_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS]
 
 
+class kivi_fp8_dims(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("format", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64)]
+
+
+FP8_BUFFERS = ("k", "v", "k_scale", "v_scale")
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+class kivi_fp8_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in FP8_BUFFERS]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing; build it with `python bit_quantization_amd/build.py` "
@@ -73,6 +90,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_decode_attn_split": (I32, [D, C, I32, I64, P, F32, P, P, SZ, I32, P]),
         "kivi_append_decode": (I32, [D, C, I32, I64, P, P, P, F32, P, P, SZ, P]),
         "kivi_stream_read": (I32, [P, SZ, P, SZ, P]),
+        "kivi_fp8_cache_sizes": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(SZ)]),
+        "kivi_fp8_quantize": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(kivi_fp8_cache),
+                                    I32, P, P, I64, I64, P]),
+        "kivi_fp8_append": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(kivi_fp8_cache),
+                                  I32, I64, P, P, P]),
+        "kivi_fp8_decode_workspace_bytes": (I32, [ctypes.POINTER(kivi_fp8_dims), I64, I32,
+                                                  ctypes.POINTER(SZ)]),
+        "kivi_fp8_decode_attn": (I32, [ctypes.POINTER(kivi_fp8_dims),
+                                       ctypes.POINTER(kivi_fp8_cache), I32, I64, P, F32, P, P,
+                                       SZ, I32, P]),
         "kivi_last_error": (ctypes.c_char_p, []),
         "kivi_abi_version": (I32, []),
     }
@@ -274,6 +301,96 @@ def kivi_stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=
         raise ValueError("nbytes exceeds the buffer")
     _check(_lib.kivi_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(),
                                  sink.numel() * sink.element_size(), _stream(stream)))
+
+
+# ---- FP8 KV cache ----------------------------------------------------------------------
+
+@dataclass
+class Fp8Dims:
+    layers: int
+    batch: int
+    kv_heads: int
+    q_heads: int
+    head_dim: int
+    format: str          # "e4m3" or "e5m2"
+    max_tokens: int
+
+    def c(self) -> kivi_fp8_dims:
+        return kivi_fp8_dims(self.layers, self.batch, self.kv_heads, self.q_heads, self.head_dim,
+                             FP8_FORMATS[self.format], self.max_tokens)
+
+
+def kivi_fp8_cache_sizes(dims: Fp8Dims):
+    out = (ctypes.c_size_t * 4)()
+    _check(_lib.kivi_fp8_cache_sizes(ctypes.byref(dims.c()), out))
+    return list(out)
+
+
+class Fp8Cache:
+    """The four caller-owned device buffers of an FP8 cache (codes zero-filled); the
+    scales [L][H_kv] are set from k_scale / v_scale (scalars or per-head arrays)."""
+
+    def __init__(self, dims: Fp8Dims, k_scale=1.0, v_scale=1.0, device="cuda"):
+        self.dims = dims
+        sizes = kivi_fp8_cache_sizes(dims)
+        self.buffers = {n: torch.zeros(sz, dtype=torch.uint8, device=device)
+                        for n, sz in zip(FP8_BUFFERS, sizes)}
+        shape = (dims.layers, dims.kv_heads)
+        for name, val in (("k_scale", k_scale), ("v_scale", v_scale)):
+            t = torch.as_tensor(val, dtype=torch.float32).expand(shape).contiguous()
+            self.buffers[name].view(torch.float32).copy_(t.flatten().to(device))
+
+    def c(self) -> kivi_fp8_cache:
+        return kivi_fp8_cache(*[self.buffers[n].data_ptr() for n in FP8_BUFFERS])
+
+    def view(self, name: str):
+        d = self.dims
+        L, B, H, T, D = d.layers, d.batch, d.kv_heads, d.max_tokens, d.head_dim
+        if name == "k":
+            return self.buffers[name].view(L, B, H, T, D)
+        if name == "v":
+            return self.buffers[name].view(L, B, H, T // 32, D, 32)
+        return self.buffers[name].view(torch.float32).view(L, H)
+
+
+def kivi_fp8_quantize(dims: Fp8Dims, cache: Fp8Cache, layer: int, k: torch.Tensor,
+                      v: torch.Tensor, T: int, ld_tokens: int | None = None, stream=None):
+    ld = T if ld_tokens is None else ld_tokens
+    need = dims.batch * dims.kv_heads * ld * dims.head_dim if T else None
+    _check(_lib.kivi_fp8_quantize(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                  _ptr(k, torch.float16, "k", need),
+                                  _ptr(v, torch.float16, "v", need), T, ld, _stream(stream)))
+
+
+def kivi_fp8_append(dims: Fp8Dims, cache: Fp8Cache, layer: int, T_before: int, k_new, v_new,
+                    stream=None):
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    _check(_lib.kivi_fp8_append(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, T_before,
+                                _ptr(k_new, torch.float16, "k_new", need),
+                                _ptr(v_new, torch.float16, "v_new", need), _stream(stream)))
+
+
+def kivi_fp8_decode_workspace_bytes(dims: Fp8Dims, T: int, n_split: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.kivi_fp8_decode_workspace_bytes(ctypes.byref(dims.c()), T, n_split,
+                                                ctypes.byref(n)))
+    return n.value
+
+
+def new_fp8_workspace(dims: Fp8Dims, T: int, n_split: int = 0, device="cuda") -> torch.Tensor:
+    return torch.zeros(kivi_fp8_decode_workspace_bytes(dims, T, n_split), dtype=torch.uint8,
+                       device=device)
+
+
+def kivi_fp8_decode_attn(dims: Fp8Dims, cache: Fp8Cache, layer: int, T: int, q: torch.Tensor,
+                         sm_scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                         n_split: int = 0, stream=None):
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    _check(_lib.kivi_fp8_decode_attn(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, T,
+                                     _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
+                                     _ptr(out, torch.float32, "out", nq),
+                                     _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                     n_split, _stream(stream)))
 
 
 def kivi_abi_version() -> int:

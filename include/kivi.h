@@ -221,6 +221,65 @@ kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_spli
  * Valid until the next kivi_* call on the same thread. */
 const char* kivi_last_error(void);
 
+/* ==== FP8 KV cache ===================================================================
+ * The cache stored as FP8 ("09 — KV Cache Quantization", "The lazy default: FP8 KV";
+ * "4.4 KV Cache quantization" §4.1 formats, §4.2 scales): every token is coded on its
+ * own, code = the E4M3 / E5M2 value (OCP 8-bit float formats) nearest to
+ * float32(x) / s, ties to even, saturating at the largest finite value (448 / 57344),
+ * sign kept; float32 IEEE division.  s is a float32 scale per (layer, KV head) for K
+ * and one for V, set by the caller (1.0 uncalibrated; the same value for every head
+ * is a per-tensor scale).  There is no float16 window: an appended token is coded at
+ * once. */
+typedef enum { KIVI_FP8_E4M3 = 0, KIVI_FP8_E5M2 = 1 } kivi_fp8_format;
+
+typedef struct {
+  int32_t layers, batch, kv_heads, q_heads;
+  int32_t head_dim;     /* 128 */
+  int32_t format;       /* kivi_fp8_format */
+  int64_t max_tokens;   /* a positive multiple of 32 */
+} kivi_fp8_dims;
+
+/* Device buffers, caller-owned, 16-byte aligned, sizes from kivi_fp8_cache_sizes:
+ *   k        u8  [L][B][H_kv][T_max][d]: token t's codes in channel order.
+ *   v        u8  [L][B][H_kv][T_max/32][d][32]: for each 32-token run and channel, the
+ *            run's 32 codes in token order 0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15,
+ *            28-31 (the order the decode's P.V product consumes them).
+ *   k_scale, v_scale  f32 [L][H_kv]. */
+typedef struct {
+  void* k;
+  void* v;
+  void* k_scale;
+  void* v_scale;
+} kivi_fp8_cache;
+
+/* Bytes of the four buffers (host-only). */
+kivi_status kivi_fp8_cache_sizes(const kivi_fp8_dims* dims, size_t bytes[4]);
+
+/* Code tokens [0, T) of float16 k, v [B][H_kv][ld_tokens][d] into `layer` (0 <= T <=
+ * T_max).  Value codes of tokens T .. (end of T's 32-token run) are written as 0. */
+kivi_status kivi_fp8_quantize(const kivi_fp8_dims* dims, const kivi_fp8_cache* cache,
+                              int32_t layer, const void* k, const void* v, int64_t T,
+                              int64_t ld_tokens, void* stream);
+
+/* Code one new token per sequence (float16 k_new, v_new [B][H_kv][d]) at position
+ * T_before (T_before + 1 <= T_max). */
+kivi_status kivi_fp8_append(const kivi_fp8_dims* dims, const kivi_fp8_cache* cache, int32_t layer,
+                            int64_t T_before, const void* k_new, const void* v_new, void* stream);
+
+/* Workspace bytes of kivi_fp8_decode_attn over T tokens with n_split workgroups per
+ * (sequence, KV head) (0 = the library's choice; clamped to [1, ceil(T / 32)]). */
+kivi_status kivi_fp8_decode_workspace_bytes(const kivi_fp8_dims* dims, int64_t T, int32_t n_split,
+                                            size_t* bytes);
+
+/* Decode attention over the T cached FP8 tokens of `layer`: as kivi_decode_attn, with
+ * k_t = value(code) * s_K and v_t = value(code) * s_V ("4.4 KV Cache quantization"
+ * §4.5: the codes are widened to float16 exactly and attended in float32).  Workspace
+ * contract as kivi_decode_attn's. */
+kivi_status kivi_fp8_decode_attn(const kivi_fp8_dims* dims, const kivi_fp8_cache* cache,
+                                 int32_t layer, int64_t T, const void* q, float sm_scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 int32_t n_split, void* stream);
+
 /* Measurement aid, not part of the method: read `bytes` (a multiple of 16) of device
  * memory at `buf` once with plain 16-byte loads (8192 workgroups of 256 threads,
  * grid-stride) and write one XOR word per thread to `sink` (device, at least

@@ -127,8 +127,9 @@ class FP8Cache:
 
     def __init__(self, batch, kv_heads, head_dim, fmt, max_tokens, k_scale, v_scale):
         self.B, self.H, self.d, self.fmt, self.Tmax = batch, kv_heads, head_dim, fmt, max_tokens
-        self.k_scale = np.asarray(k_scale, F32).reshape(kv_heads)
-        self.v_scale = np.asarray(v_scale, F32).reshape(kv_heads)
+        # one scale per KV head; a single value is a per-tensor scale (every head)
+        self.k_scale = np.broadcast_to(np.asarray(k_scale, F32), (kv_heads,)).copy()
+        self.v_scale = np.broadcast_to(np.asarray(v_scale, F32), (kv_heads,)).copy()
         self.k = np.zeros((batch, kv_heads, max_tokens, head_dim), np.uint8)
         self.v = np.zeros((batch, kv_heads, max_tokens, head_dim), np.uint8)
         self.T = 0
