@@ -98,6 +98,9 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0: auto)")
     p.add_argument("--n-split", type=int, default=0, help="token splits (0: library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2"],
+                   help="kivi: the workload's 2/4-bit KIVI cache (default); fp8_*: the same "
+                        "workload stored as FP8 with per-head scales")
     p.add_argument("--no-graph", action="store_true",
                    help="launch the timed steps one by one instead of as one HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -213,6 +216,186 @@ def cpu_baseline(w, host_pairs, budget_s):
                        f"os.cpu_count()={os.cpu_count()}, BLAS threads={threads}")}
 
 
+def fp8_decode_bytes(w, T):
+    """Algorithmic bytes of one FP8 decode launch at T tokens: per (sequence, KV head)
+    T*d Key and T*d Value code bytes and 8 bytes of scales; q and out per query head."""
+    d = w.head_dim
+    return w.batch * w.kv_heads * (2 * T * d + 8) + w.batch * w.q_heads * d * (2 + 4)
+
+
+def fp8_append_bytes(w):
+    """k_new, v_new read (2 * 2d) and their codes written (2d), per (sequence, KV head)."""
+    return w.batch * w.kv_heads * (2 * 2 * w.head_dim + 2 * w.head_dim)
+
+
+def fp8_cpu_baseline(w, fmt, host_pairs, budget_s):
+    """The FP8 oracle's decode step (append + attend) on a bounded sample, as
+    cpu_baseline."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    one = w.replace(batch=1, kv_heads=1, q_heads=w.gqa)
+    caches = []
+    for (Kh, Vh, k_rows, v_rows, qh, T, ks, vs) in host_pairs:
+        cap = (T + len(k_rows) + 1 + 31) // 32 * 32
+        oc = O.FP8Cache(1, 1, w.head_dim, fmt, cap, ks, vs)
+        oc.prefill(Kh, Vh)
+        caches.append((oc, k_rows, v_rows, qh))
+    done_bytes, t_used, steps, T_last = 0, 0.0, 0, 0
+    while t_used < budget_s:
+        oc, k_rows, v_rows, qh = caches[steps % len(caches)]
+        j = steps // len(caches)
+        if j >= len(k_rows):
+            break
+        T = oc.T
+        t0 = time.perf_counter()
+        oc.append(k_rows[j][None, None], v_rows[j][None, None])
+        oc.attend(qh, w.sm_scale)
+        t_used += time.perf_counter() - t0
+        done_bytes += fp8_decode_bytes(one, T + 1) + fp8_append_bytes(one)
+        steps += 1
+        T_last = T + 1
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{steps} FP8 oracle decode steps (append + attend, {w.gqa} query heads, "
+                       f"~{T_last} tokens) round-robin over {len(caches)} (sequence, KV head) "
+                       f"pairs of the workload, {t_used:.1f} s of oracle time; "
+                       f"os.cpu_count()={os.cpu_count()}, BLAS threads={threads}")}
+
+
+def fp8_main(args):
+    """The workload stored as FP8: one step = kivi_fp8_append + kivi_fp8_decode_attn."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from bit_quantization_amd import kivi as k
+
+    fmt = args.codec[4:]
+    torch.cuda.set_device(0)
+    w = W.get(args.workload)
+    w1 = w.replace(layers=1) if w.layers > 1 else w
+    total_steps = args.warmup + 2 * args.steps
+    per_copy = fp8_decode_bytes(w1, w1.tokens)
+    copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy))
+    if w.layers > 1:
+        copies = args.copies or min(w.layers, max(copies, 2))
+    steps_per_copy = math.ceil(total_steps / copies) + 1
+    extra = max(steps_per_copy, 1024)
+    Tmax = (w1.tokens + steps_per_copy + 31) // 32 * 32
+    dims = k.Fp8Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, fmt, Tmax)
+    print(f"[bench] workload {w.name} as {args.codec}: {copies} layer caches x "
+          f"{per_copy / 1e6:.1f} MB decode reads, {args.warmup}+{args.steps} steps",
+          file=sys.stderr, flush=True)
+    top = 448.0 if fmt == "e4m3" else 57344.0
+    caches, Ts, news, host_pairs = [], [], [], []
+    rng = np.random.default_rng(0)
+    sample = [(int(b), int(h)) for b, h in zip(rng.integers(0, w1.batch, 6),
+                                               rng.integers(0, w1.kv_heads, 6))]
+    for c in range(copies):
+        K, V = W.make_kv(w1, c, device="cuda", total_tokens=w1.tokens + extra)
+        # per-head scales from the largest magnitude of the prompt: a calibration on the
+        # synthetic data ("4.4 KV Cache quantization" §4.2, calibrated scales)
+        ks = (K[:, :, :w1.tokens].float().abs().amax(dim=(0, 2, 3)) / top).clamp_min(1e-12)
+        vs = (V[:, :, :w1.tokens].float().abs().amax(dim=(0, 2, 3)) / top).clamp_min(1e-12)
+        cache = k.Fp8Cache(dims, ks.cpu(), vs.cpu())
+        k.kivi_fp8_quantize(dims, cache, 0, K, V, w1.tokens, K.shape[2])
+        caches.append(cache)
+        Ts.append(w1.tokens)
+        news.append((K[:, :, w1.tokens:w1.tokens + steps_per_copy].permute(2, 0, 1, 3).contiguous(),
+                     V[:, :, w1.tokens:w1.tokens + steps_per_copy].permute(2, 0, 1, 3).contiguous()))
+        if c == 0 and not args.no_cpu_baseline:
+            q0 = W.make_q(w1, 0, 0, device="cuda").cpu().numpy()
+            g = w1.gqa
+            for (b, h) in sample:
+                host_pairs.append((K[b:b + 1, h:h + 1, :w1.tokens].cpu().numpy(),
+                                   V[b:b + 1, h:h + 1, :w1.tokens].cpu().numpy(),
+                                   K[b, h, w1.tokens:].cpu().numpy(), V[b, h, w1.tokens:].cpu().numpy(),
+                                   q0[b:b + 1, h * g:(h + 1) * g], w1.tokens,
+                                   float(ks[h]), float(vs[h])))
+        del K, V
+    qs = [W.make_q(w1, 0, s_, device="cuda") for s_ in range(8)]
+    out = torch.empty((w1.batch, w1.q_heads, w1.head_dim), dtype=torch.float32, device="cuda")
+    ws = k.new_fp8_workspace(dims, Tmax, args.n_split)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def prepare(i):
+        c = i % copies
+        T_before = Ts[c]
+        j = T_before - w1.tokens
+        kn, vn = news[c]
+        T = T_before + 1
+        Ts[c] = T
+        q = qs[i % len(qs)]
+
+        def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
+            k.kivi_fp8_append(dims, caches[c], 0, T_before, kj, vj)
+            k.kivi_fp8_decode_attn(dims, caches[c], 0, T, q, w1.sm_scale, out, ws, args.n_split)
+        return call, fp8_decode_bytes(w1, T), fp8_append_bytes(w1)
+
+    for i in range(args.warmup):
+        prepare(i)[0]()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    steps = [prepare(args.warmup + i) for i in range(args.steps)]
+    launch_bytes = sum(db + ab for _, db, ab in steps)
+    torch.cuda.synchronize()
+    for (call, _, _), (e0, e1) in zip(steps, events):
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in events]
+    avg_s = sum(ms) / len(ms) / 1e3
+    first = args.warmup + args.steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps = [prepare(first + i) for i in range(args.steps)]
+        for call, _, _ in steps:
+            call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graph
+    total = sum(db + ab for _, db, ab in steps)
+    value = total / wall / 1e9
+    achieved = launch_bytes / args.steps / avg_s / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = fp8_cpu_baseline(w1, fmt, host_pairs, args.cpu_seconds)
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8+f16+f32",
+        "data": "synthetic (seeded N(0,1) K/V/Q with x50 Key outlier channels and x100 Value "
+                "outlier tokens; per-head FP8 scales from the prompt's largest magnitude)",
+        "config": {"workload": w.name, "codec": args.codec, "batch": w1.batch,
+                   "kv_heads": w1.kv_heads, "q_heads": w1.q_heads, "head_dim": w1.head_dim,
+                   "tokens": w1.tokens, "layer_caches": copies,
+                   "step": "kivi_fp8_append + kivi_fp8_decode_attn",
+                   "launch": "one HIP graph of the timed steps"},
+        "tokens_per_s": round(w1.batch * args.steps / wall, 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "fp8_decode_kernel (+ fp8_append_kernel)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": int(launch_bytes / args.steps),
+                     "avg_launch_us": round(avg_s * 1e6, 3),
+                     "median_launch_us": round(sorted(ms)[len(ms) // 2] * 1e3, 3),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -224,6 +407,9 @@ def main():
         return
     if args.read_ceiling:
         read_ceiling()
+        return
+    if args.codec != "kivi":
+        fp8_main(args)
         return
 
     import numpy as np
