@@ -46,6 +46,11 @@ Readings of passages the pages leave open (each is also listed in the design not
       ``[T/16][d][16*b/8]``.  Each product of decode attention then reduces along
       the packed axis (Q.K^T over channels, P.V over tokens), and a shift by b*k
       and a byte mask extract codes 4k .. 4k+3 of a word in their natural order.
+  R15 Sink tokens ([FORT] "Anti-patterns": the first few tokens absorb large
+      attention scores and must not be quantized; preserve the first N): with S sink
+      tokens, tokens [0, S) of a sequence stay in float16 for its lifetime and every
+      rule above (groups, window, flushes) applies to tokens S, S+1, ... counted
+      from S.  S = 0 is the plain method.
 """
 from __future__ import annotations
 
@@ -258,7 +263,7 @@ class LayerCache:
     """
 
     def __init__(self, batch, kv_heads, head_dim, bits, group_k, group_v, residual,
-                 max_tokens):
+                 max_tokens, sink: int = 0):
         assert bits in (2, 4)
         assert residual % group_k == 0 and residual % V_RUN == 0
         assert max_tokens % group_k == 0 and max_tokens % V_RUN == 0
@@ -275,7 +280,15 @@ class LayerCache:
         self.v_zero = np.zeros((B, H, max_tokens, d // group_v), F16)
         self.k_resid = np.zeros((B, H, residual, d), F16)
         self.v_resid = np.zeros((B, H, residual, d), F16)
+        self.S = sink                       # reading R15
+        self.k_sink = np.zeros((B, H, sink, d), F16)
+        self.v_sink = np.zeros((B, H, sink, d), F16)
         self.T = 0
+
+    @property
+    def Tk(self) -> int:
+        """Tokens under the KIVI rules: those after the sink (reading R15)."""
+        return max(0, self.T - self.S)
 
     # -- writes into the quantized store ------------------------------------------------
     def _store(self, K: np.ndarray, V: np.ndarray, t0: int):
@@ -299,20 +312,31 @@ class LayerCache:
         assert K.dtype == F16 and V.dtype == F16 and K.shape == V.shape
         T = K.shape[2]
         assert T + 1 <= self.T_max
-        Tq = quantized_len(T, self.R)
-        r = T - Tq
+        ns = min(T, self.S)
+        self.k_sink[:, :, :ns] = K[:, :, :ns]
+        self.v_sink[:, :, :ns] = V[:, :, :ns]
+        K, V = K[:, :, ns:], V[:, :, ns:]
+        Tk = T - ns
+        Tq = quantized_len(Tk, self.R)
+        r = Tk - Tq
         if Tq:
             self._store(K[:, :, :Tq], V[:, :, :Tq], 0)
-        self.k_resid[:, :, :r] = K[:, :, Tq:T]
-        self.v_resid[:, :, :r] = V[:, :, Tq:T]
+        self.k_resid[:, :, :r] = K[:, :, Tq:Tk]
+        self.v_resid[:, :, :r] = V[:, :, Tq:Tk]
         self.T = T
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray):
         """Add one token per sequence ([B, H, d] float16), flushing a full window first."""
         assert self.T + 1 <= self.T_max
-        r = residual_len(self.T, self.R)
+        if self.T < self.S:                  # still filling the sink
+            self.k_sink[:, :, self.T] = k_new
+            self.v_sink[:, :, self.T] = v_new
+            self.T += 1
+            return
+        Tk = self.Tk
+        r = residual_len(Tk, self.R)
         if r == self.R:
-            self._store(self.k_resid, self.v_resid, self.T - self.R)
+            self._store(self.k_resid, self.v_resid, Tk - self.R)
             r = 0
         self.k_resid[:, :, r] = k_new
         self.v_resid[:, :, r] = v_new
@@ -321,21 +345,25 @@ class LayerCache:
     # -- reads ------------------------------------------------------------------------
     def quantized_codes(self):
         """Unpacked codes of the quantized part: (k_codes, v_codes) uint8 [B,H,T_q,d]."""
-        Tq = quantized_len(self.T, self.R)
+        Tq = quantized_len(self.Tk, self.R)
         kc = unpack_keys(self.k_codes[:, :, :Tq], self.bits)
         vc = unpack_values(self.v_codes[:, :, :Tq // V_RUN], self.bits)
         return kc, vc
 
     def dequantized(self):
-        """(K_hat, V_hat) float32 [B, H, T, d]: dequantized history then the residual."""
-        Tq = quantized_len(self.T, self.R)
-        r = self.T - Tq
+        """(K_hat, V_hat) float32 [B, H, T, d]: the sink rows, the dequantized history,
+        then the residual window."""
+        ns = min(self.T, self.S)
+        Tq = quantized_len(self.Tk, self.R)
+        r = self.Tk - Tq
         kc, vc = self.quantized_codes()
         Kq = dequantize_keys(kc, self.k_scale[:, :, :Tq // self.G],
                              self.k_zero[:, :, :Tq // self.G], self.G)
         Vq = dequantize_values(vc, self.v_scale[:, :, :Tq], self.v_zero[:, :, :Tq], self.Gv)
-        Kh = np.concatenate([Kq, self.k_resid[:, :, :r].astype(F32)], axis=2)
-        Vh = np.concatenate([Vq, self.v_resid[:, :, :r].astype(F32)], axis=2)
+        Kh = np.concatenate([self.k_sink[:, :, :ns].astype(F32), Kq,
+                             self.k_resid[:, :, :r].astype(F32)], axis=2)
+        Vh = np.concatenate([self.v_sink[:, :, :ns].astype(F32), Vq,
+                             self.v_resid[:, :, :r].astype(F32)], axis=2)
         return Kh, Vh
 
     def attend(self, q: np.ndarray, sm_scale: float, pairs=None) -> np.ndarray:
@@ -360,15 +388,18 @@ class LayerCache:
 
     def dequantized_pair(self, b: int, h: int):
         """(K_hat, V_hat) float32 [T, d] for one (sequence, KV head) pair."""
-        Tq = quantized_len(self.T, self.R)
-        r = self.T - Tq
+        ns = min(self.T, self.S)
+        Tq = quantized_len(self.Tk, self.R)
+        r = self.Tk - Tq
         kc = unpack_keys(self.k_codes[b, h, :Tq], self.bits)
         vc = unpack_values(self.v_codes[b, h, :Tq // V_RUN], self.bits)
         Kq = dequantize_keys(kc, self.k_scale[b, h, :Tq // self.G],
                              self.k_zero[b, h, :Tq // self.G], self.G)
         Vq = dequantize_values(vc, self.v_scale[b, h, :Tq], self.v_zero[b, h, :Tq], self.Gv)
-        Kh = np.concatenate([Kq, self.k_resid[b, h, :r].astype(F32)], axis=0)
-        Vh = np.concatenate([Vq, self.v_resid[b, h, :r].astype(F32)], axis=0)
+        Kh = np.concatenate([self.k_sink[b, h, :ns].astype(F32), Kq,
+                             self.k_resid[b, h, :r].astype(F32)], axis=0)
+        Vh = np.concatenate([self.v_sink[b, h, :ns].astype(F32), Vq,
+                             self.v_resid[b, h, :r].astype(F32)], axis=0)
         return Kh, Vh
 
 

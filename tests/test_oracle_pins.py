@@ -512,3 +512,70 @@ def test_shift_of_logits_leaves_attention_unchanged():
     shift = q[0].astype(np.float64) / float(q[0].astype(np.float64) @ q[0]) * (30.0 / float(np.float32(sm)))
     b = O.attention_fp64(q, K + shift, V, sm)
     assert np.allclose(a, b, rtol=1e-9, atol=1e-9)
+
+
+# ---- sink tokens (reading R15) ---------------------------------------------------------
+
+def _sink_inputs(T, seed):
+    rng = np.random.default_rng(seed)
+    K = (rng.standard_normal((2, 2, T, 128)) * 2).astype(np.float16)
+    V = (rng.standard_normal((2, 2, T, 128)) * 2).astype(np.float16)
+    K[:, :, :, 5] *= 40
+    return K, V
+
+
+def test_sink_rows_are_the_inputs_exactly():
+    K, V = _sink_inputs(300, 1)
+    c = O.LayerCache(2, 2, 128, 2, 32, 128, 64, 512, sink=4)
+    c.prefill(K, V)
+    Kh, Vh = c.dequantized()
+    assert np.array_equal(Kh[:, :, :4], K[:, :, :4].astype(np.float32))
+    assert np.array_equal(Vh[:, :, :4], V[:, :, :4].astype(np.float32))
+    assert Kh.shape[2] == 300
+
+
+def test_sink_covering_every_token_is_plain_sdpa():
+    import torch
+    K, V = _sink_inputs(40, 2)
+    c = O.LayerCache(2, 2, 128, 2, 32, 128, 32, 128, sink=64)
+    c.prefill(K, V)
+    q = np.random.default_rng(3).standard_normal((2, 4, 128)).astype(np.float16)
+    got = c.attend(q, 0.088)
+    for b in range(2):
+        for j in range(4):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b, j:j + 1].astype(np.float64))[None],
+                torch.from_numpy(K[b, j // 2].astype(np.float64))[None],
+                torch.from_numpy(V[b, j // 2].astype(np.float64))[None],
+                scale=float(np.float32(0.088)))
+            assert np.allclose(got[b, j], ref[0, 0].numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_tokens_after_the_sink_follow_the_plain_method_from_s():
+    S, T = 7, 400
+    K, V = _sink_inputs(T, 4)
+    a = O.LayerCache(2, 2, 128, 4, 32, 64, 64, 512, sink=S)
+    a.prefill(K, V)
+    b = O.LayerCache(2, 2, 128, 4, 32, 64, 64, 512)
+    b.prefill(K[:, :, S:], V[:, :, S:])
+    Ka, Va = a.dequantized()
+    Kb, Vb = b.dequantized()
+    assert np.array_equal(Ka[:, :, S:], Kb) and np.array_equal(Va[:, :, S:], Vb)
+    assert np.array_equal(a.k_codes, b.k_codes) and np.array_equal(a.v_codes, b.v_codes)
+
+
+@pytest.mark.parametrize("S,T0", [(4, 0), (4, 2), (4, 4), (9, 30), (64, 50)])
+def test_sink_prefill_equals_appends(S, T0):
+    T = S + 2 * 64 + 11
+    K, V = _sink_inputs(T, 5 + S)
+    a = O.LayerCache(2, 2, 128, 2, 32, 128, 64, 512, sink=S)
+    a.prefill(K, V)
+    b = O.LayerCache(2, 2, 128, 2, 32, 128, 64, 512, sink=S)
+    b.prefill(K[:, :, :T0], V[:, :, :T0])
+    for t in range(T0, T):
+        b.append(K[:, :, t], V[:, :, t])
+    for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_sink",
+                 "v_sink"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    r = O.residual_len(T - S, 64)
+    assert np.array_equal(a.k_resid[:, :, :r], b.k_resid[:, :, :r])
