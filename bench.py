@@ -62,26 +62,34 @@ def measured_traffic(workload):
     return entry.get("traffic_bytes_per_launch")
 
 
-def decode_bytes(w, T):
+def split(T, R, S=0):
+    """(float16 rows, quantized tokens) at T tokens: the first S tokens (the sink) and
+    the window of the rest stay float16, whole windows before it are quantized."""
+    ns = min(T, S)
+    Tk = T - ns
+    r = 0 if Tk == 0 else (Tk - 1) % R + 1
+    return ns + r, Tk - r
+
+
+def decode_bytes(w, T, S=0):
     """Algorithmic bytes of one decode launch at T cached tokens (see module doc)."""
-    R = w.residual
-    r = 0 if T == 0 else (T - 1) % R + 1
-    Tq = T - r
+    rows, Tq = split(T, w.residual, S)
     d = w.head_dim
     per_pair = (2 * Tq * d * w.bits // 8            # K and V codes
                 + (Tq // w.group_k) * d * 4         # K scale + zero
                 + Tq * (d // w.group_v) * 4         # V scale + zero
-                + 2 * r * d * 2)                    # float16 residual K and V
+                + 2 * rows * d * 2)                 # float16 sink + window K and V
     pairs = w.batch * w.kv_heads
     return pairs * per_pair + w.batch * w.q_heads * d * (2 + 4)
 
 
-def append_bytes(w, T_before):
+def append_bytes(w, T_before, S=0):
     R = w.residual
     d = w.head_dim
     pairs = w.batch * w.kv_heads
     rows = pairs * 2 * d * 2 * 2                    # k_new, v_new read; residual row written
-    r = 0 if T_before == 0 else (T_before - 1) % R + 1
+    Tk = T_before - S
+    r = 0 if Tk <= 0 else (Tk - 1) % R + 1
     if r == R:                                      # flush the window
         codes = 2 * R * d * w.bits // 8
         meta = (R // w.group_k) * d * 4 + R * (d // w.group_v) * 4
@@ -98,6 +106,8 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0: auto)")
     p.add_argument("--n-split", type=int, default=0, help="token splits (0: library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sink", type=int, default=0,
+                   help="attention-sink tokens kept in float16 at the start of each sequence")
     p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2"],
                    help="kivi: the workload's 2/4-bit KIVI cache (default); fp8_*: the same "
                         "workload stored as FP8 with per-head scales")
@@ -158,21 +168,19 @@ def read_ceiling():
                       "16-byte loads)", "timing": "HIP events, best of 5"}), flush=True)
 
 
-def prefill_bytes(w, T):
+def prefill_bytes(w, T, S=0):
     """Algorithmic bytes of quantizing one layer's prompt of T tokens (a1 + a2): read
-    fp16 K and V, write codes, scales/zeros and the fp16 window rows."""
-    R = w.residual
-    r = 0 if T == 0 else (T - 1) % R + 1
-    Tq = T - r
+    fp16 K and V, write codes, scales/zeros and the fp16 sink and window rows."""
+    rows, Tq = split(T, w.residual, S)
     d = w.head_dim
     per_pair = (2 * T * d * 2                           # K and V read
                 + 2 * Tq * d * w.bits // 8              # codes written
                 + (Tq // w.group_k) * d * 4 + Tq * (d // w.group_v) * 4
-                + 2 * r * d * 2)                        # window rows written
+                + 2 * rows * d * 2)                     # float16 rows written
     return w.batch * w.kv_heads * per_pair
 
 
-def cpu_baseline(w, host_pairs, budget_s):
+def cpu_baseline(w, host_pairs, budget_s, S=0):
     """Time the CPU oracle's decode step (append + attend) on a bounded sample.
 
     A few (sequence, KV head) pairs of the workload are prefilled (untimed); then
@@ -190,7 +198,8 @@ def cpu_baseline(w, host_pairs, budget_s):
     for (Kh, Vh, k_rows, v_rows, qh, T) in host_pairs:
         m = math.lcm(16, w.group_k, w.residual)
         cap = (T + len(k_rows) + 1 + m - 1) // m * m
-        oc = O.LayerCache(1, 1, w.head_dim, w.bits, w.group_k, w.group_v, w.residual, cap)
+        oc = O.LayerCache(1, 1, w.head_dim, w.bits, w.group_k, w.group_v, w.residual, cap,
+                          sink=S)
         oc.prefill(Kh, Vh)
         caches.append((oc, k_rows, v_rows, qh))
     done_bytes, t_used, steps, T_last = 0, 0.0, 0, 0
@@ -205,7 +214,7 @@ def cpu_baseline(w, host_pairs, budget_s):
         oc.append(k_rows[j][None, None], v_rows[j][None, None])
         oc.attend(qh, w.sm_scale)
         t_used += time.perf_counter() - t0
-        done_bytes += decode_bytes(one, T + 1) + append_bytes(one, T)
+        done_bytes += decode_bytes(one, T + 1, S) + append_bytes(one, T, S)
         steps += 1
         T_last = T + 1
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads,
@@ -427,7 +436,8 @@ def main():
         w1 = w
     # warmup, the eager loop timed per launch (roofline), then the K steps of the graph
     total_steps = args.warmup + 2 * args.steps
-    per_copy_bytes = decode_bytes(w1, w1.tokens)
+    S = args.sink
+    per_copy_bytes = decode_bytes(w1, w1.tokens, S)
     copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy_bytes))
     if w.layers > 1:
         copies = args.copies or min(w.layers, max(copies, 2))
@@ -435,7 +445,7 @@ def main():
     extra_rows = max(steps_per_copy, 1024)          # rows appended on the GPU / by the oracle
     Tmax = w1.replace(stream_steps=steps_per_copy).max_tokens()
     dims = k.Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, w1.bits, w1.group_k,
-                  w1.group_v, w1.residual, Tmax)
+                  w1.group_v, w1.residual, Tmax, sink=S)
     print(f"[bench] workload {w.name}: {copies} layer caches x {per_copy_bytes / 1e6:.1f} MB "
           f"decode reads, {args.warmup}+{args.steps} steps", file=sys.stderr, flush=True)
 
@@ -496,7 +506,7 @@ def main():
         else:
             call = k.prepare_append_decode(dims, caches[c], 0, T_before, kn[j], vn[j], q,
                                            w1.sm_scale, out, ws)
-        return call, decode_bytes(w1, T), append_bytes(w1, T_before)
+        return call, decode_bytes(w1, T, S), append_bytes(w1, T_before, S)
 
     for i in range(args.warmup):
         prepare(i)[0]()
@@ -584,12 +594,12 @@ def main():
     del Kp, Vp, scratch
     prefill = {"what": "kivi_quantize_k + kivi_quantize_v of one layer's prompt",
                "tokens": w1.tokens, "us": round(pre_s * 1e6, 1),
-               "GB/s": round(prefill_bytes(w1, w1.tokens) / pre_s / 1e9, 1),
-               "bytes": prefill_bytes(w1, w1.tokens)}
+               "GB/s": round(prefill_bytes(w1, w1.tokens, S) / pre_s / 1e9, 1),
+               "bytes": prefill_bytes(w1, w1.tokens, S)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w1, host_pairs, args.cpu_seconds)
+        cpu = cpu_baseline(w1, host_pairs, args.cpu_seconds, S)
 
     total_bytes = dec_bytes + app_bytes
     value = total_bytes / wall / 1e9
@@ -611,7 +621,8 @@ def main():
         "config": {"workload": w.name, "batch": w1.batch, "kv_heads": w1.kv_heads,
                    "q_heads": w1.q_heads, "head_dim": w1.head_dim, "tokens": w1.tokens,
                    "bits": w1.bits, "group_k": w1.group_k, "group_v": w1.group_v,
-                   "residual": w1.residual, "layer_caches": copies, "n_split": n_split,
+                   "residual": w1.residual, "sink": S, "layer_caches": copies,
+                   "n_split": n_split,
                    "step": "append(+flush) + decode attention",
                    "launch": "one HIP graph of the timed steps" if not args.no_graph
                              else "one call per step"},
@@ -626,7 +637,7 @@ def main():
                      "median_launch_us": round(dec_med_s * 1e6, 3),
                      "p10_p90_launch_us": [round(sorted(dec_ms)[len(dec_ms) // 10] * 1e3, 3),
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
-                     "traffic": measured_traffic(w.name)},
+                     "traffic": measured_traffic(w.name) if S == 0 else None},
         "cpu_baseline": cpu,
         "prefill_quantize": prefill,
         "quality": quality,

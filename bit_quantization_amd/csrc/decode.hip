@@ -851,8 +851,9 @@ bool dispatch_decode(int bits, int gqa, int G, F&& f) {
 DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_req) {
   DecodePlan p{};
   const int gqa = q_heads / L.H;
-  const int64_t Tq = quantized_len(T, L.R);
-  p.r = (int)(T - Tq);
+  const TokenSplit ts = split_tokens(T, L.S, L.R);
+  const int64_t Tq = ts.Tq;
+  p.r = (int)ts.fp16_rows();          // sink rows and window rows, contiguous
   p.n_groups = Tq / L.G;
   const int64_t nblk = (Tq + BLK - 1) / BLK;
   const int64_t pairs = (int64_t)L.B * L.H;
@@ -879,7 +880,7 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.out = out;
   a.counters = reinterpret_cast<unsigned*>(ws);
   a.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + plan.ws_counters);
-  a.Tq = quantized_len(T, L.R);
+  a.Tq = split_tokens(T, L.S, L.R).Tq;
   a.nblk = (a.Tq + BLK - 1) / BLK;
   a.r = plan.r;
   a.nw = plan.n_split;

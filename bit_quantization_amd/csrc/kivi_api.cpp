@@ -62,7 +62,8 @@ kivi_status check_dims(const kivi_dims* d) {
   if (d->residual < 1 || d->residual % d->group_k != 0 || d->residual % kivi::kVRun != 0)
     return fail(KIVI_ERR_ARG, "residual = %d must be a positive multiple of group_k (%d) and 16",
                 d->residual, d->group_k);
-  if (d->reserved != 0) return fail(KIVI_ERR_ARG, "dims.reserved must be 0");
+  if (d->sink < 0 || d->sink > 1024)
+    return fail(KIVI_ERR_ARG, "sink = %d outside [0, 1024]", d->sink);
   if (d->max_tokens < 1 || d->max_tokens % d->group_k != 0 || d->max_tokens % kivi::kVRun != 0)
     return fail(KIVI_ERR_ARG, "max_tokens = %lld must be a positive multiple of group_k and 16",
                 (long long)d->max_tokens);
@@ -75,7 +76,7 @@ void buffer_sizes(const kivi_dims* d, size_t out[KIVI_NUM_BUFFERS]) {
   const size_t codes = unit * T * d->head_dim * d->bits / 8;
   const size_t kmeta = unit * (T / d->group_k) * d->head_dim * 2;
   const size_t vmeta = unit * T * (d->head_dim / d->group_v) * 2;
-  const size_t resid = unit * d->residual * d->head_dim * 2;
+  const size_t resid = unit * (size_t)(d->sink + d->residual) * d->head_dim * 2;
   out[0] = codes;
   out[1] = kmeta;
   out[2] = kmeta;
@@ -123,6 +124,7 @@ kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer) {
   L.G = d->group_k;
   L.Gv = d->group_v;
   L.R = d->residual;
+  L.S = d->sink;
   L.Tmax = d->max_tokens;
   return L;
 }
@@ -428,6 +430,7 @@ kivi_status kivi_decode_workspace_bytes_split(const kivi_dims* dims, int64_t T, 
   L.G = dims->group_k;
   L.Gv = dims->group_v;
   L.R = dims->residual;
+  L.S = dims->sink;
   L.Tmax = dims->max_tokens;
   *bytes = kivi::plan_decode(L, dims->q_heads, T, n_split).ws_total;
   return ok();
@@ -452,6 +455,7 @@ kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_spli
   L.G = dims->group_k;
   L.Gv = dims->group_v;
   L.R = dims->residual;
+  L.S = dims->sink;
   L.Tmax = dims->max_tokens;
   *n_split = kivi::plan_decode(L, dims->q_heads, T, 0).n_split;
   return ok();
@@ -489,8 +493,8 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const __half* kn = static_cast<const __half*>(k_new);
   const __half* vn = static_cast<const __half*>(v_new);
-  const int64_t r_before = kivi::residual_len(T_before, L.R);
-  if (r_before == L.R) {
+  const kivi::AppendPlan ap = kivi::plan_append(T_before, L.S, L.R);
+  if (ap.flush) {
     // the window is full: flush it (and store the new row) first, then attend
     hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, s);
     if (e != hipSuccess) return device_status(e, "kivi_append_decode flush launch");
@@ -498,7 +502,7 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
                             workspace, plan, nullptr, s);
     return device_status(e, "kivi_append_decode launch");
   }
-  const kivi::NewRow nr{kn, vn, (int)r_before};
+  const kivi::NewRow nr{kn, vn, ap.slot};
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
                                      out, workspace, plan, &nr, s);
   return device_status(e, "kivi_append_decode launch");

@@ -18,10 +18,11 @@ struct LayerView {
   uint8_t* v_codes;   // [B][H][Tmax/16][d][16*b/8]
   __half* v_scale;    // [B][H][Tmax][d/Gv]
   __half* v_zero;
-  __half* k_resid;    // [B][H][R][d]
+  __half* k_resid;    // [B][H][S + R][d]: rows [0, S) the sink tokens, then the window
   __half* v_resid;
   float* scale_max;   // [B][H][2]: largest Key scale, largest Value scale
   int B, H, d, bits, G, Gv, R;
+  int S;              // sink tokens kept in float16 (tokens [0, S) of each sequence)
   int64_t Tmax;
 
   // Per-(b, h) element strides of each buffer.
@@ -29,16 +30,47 @@ struct LayerView {
   __host__ __device__ int64_t ks_pair() const { return (Tmax / G) * d; }
   __host__ __device__ int64_t vc_pair() const { return Tmax * (d * bits / 8); }
   __host__ __device__ int64_t vs_pair() const { return Tmax * (d / Gv); }
-  __host__ __device__ int64_t rs_pair() const { return (int64_t)R * d; }
+  __host__ __device__ int64_t rs_pair() const { return (int64_t)(S + R) * d; }
 };
 
 inline int64_t residual_len(int64_t T, int R) { return T == 0 ? 0 : (T - 1) % R + 1; }
 inline int64_t quantized_len(int64_t T, int R) { return T - residual_len(T, R); }
 
+// T cached tokens with S sink tokens: the first min(T, S) stay in float16 (residual
+// rows [0, S)); the rest follow the window rules counted from S: Tq of them are in
+// the quantized history, r in the window (residual rows [S, S + r)).
+struct TokenSplit {
+  int64_t ns, Tq, r;
+  int64_t fp16_rows() const { return ns + r; }   // rows [0, ns) and [S, S + r) (ns == S if r > 0)
+};
+inline TokenSplit split_tokens(int64_t T, int S, int R) {
+  TokenSplit t;
+  t.ns = T < S ? T : S;
+  const int64_t Tk = T - t.ns;
+  t.Tq = quantized_len(Tk, R);
+  t.r = Tk - t.Tq;
+  return t;
+}
+
+// Where an appended token goes: the sink row T_before while the sink fills; else the
+// window, after flushing it into the history at token t0 when it is full.
+struct AppendPlan {
+  int flush;      // 1: quantize the full window into the history first
+  int slot;       // residual row of the new token
+  int64_t t0;     // history token of window row 0 (flush only)
+};
+inline AppendPlan plan_append(int64_t T_before, int S, int R) {
+  if (T_before < S) return AppendPlan{0, (int)T_before, 0};
+  const int64_t Tk = T_before - S;
+  const int64_t r = residual_len(Tk, R);
+  if (r == R) return AppendPlan{1, S, Tk - R};
+  return AppendPlan{0, (int)(S + r), 0};
+}
+
 // ---- launchers (return hipGetLastError() of the launch) -------------------------
 
-// Prefill: quantize tokens [0, Tq) of src ([B][H][ld][d]) and copy [Tq, T) to the
-// residual rows [0, T - Tq).
+// Prefill of T tokens of src ([B][H][ld][d]): the sink tokens to residual rows
+// [0, ns), the history tokens [S, S + Tq) quantized, the last r to rows [S, S + r).
 hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s);
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,

@@ -266,19 +266,21 @@ __device__ __forceinline__ void copy_rows(const __half* __restrict__ src, __half
 
 // ---- kernels ----------------------------------------------------------------------
 
-// Items of one (b, h): the Tq/G Key groups (or Tq/16 Value runs), then one item
-// that copies the tail [Tq, T) into the residual rows.  grid = (ceil(items /
+// Items of one (b, h): the Tq/G Key groups (or Tq/16 Value runs) of the tokens after
+// the sink, then one item that copies the sink tokens and the r window tokens into
+// the residual rows.  grid = (ceil(items /
 // (QW*npw)), B*H); workgroup x takes items QW*npw*x .. +QW*npw - 1, its waves
 // interleaved (wave w takes item QW*npw*x + QW*i + w for i < npw).
 template <int BITS, int G>
 __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const __half* __restrict__ src,
-                                                            int64_t ld, int64_t Tq, int64_t T,
-                                                            int npw) {
+                                                            int64_t ld, int64_t Tq, int64_t r,
+                                                            int64_t ns, int npw) {
   __shared__ alignas(16) uint8_t lds[QW][G * D];
   __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const __half* s = src + pair * ld * D;
+  const __half* s0 = src + pair * ld * D;
+  const __half* s = s0 + (int64_t)L.S * D;        // the tokens after the sink
   const int64_t ngroups = Tq / G;
   float smx = 0.f;
   for (int i = 0; i < npw; ++i) {
@@ -289,7 +291,8 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
                            L.k_scale + pair * L.ks_pair() + g * D,
                            L.k_zero + pair * L.ks_pair() + g * D, lds[wave]));
     } else if (g == ngroups) {
-      copy_rows(s + Tq * D, L.k_resid + pair * L.rs_pair(), T - Tq);
+      copy_rows(s0, L.k_resid + pair * L.rs_pair(), ns);
+      copy_rows(s + Tq * D, L.k_resid + pair * L.rs_pair() + (int64_t)L.S * D, r);
     }
   }
   raise_scale_max<QW>(L.scale_max + 2 * pair, smx, red);
@@ -298,13 +301,14 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
 // As prefill_k_kernel, over the Value runs.
 template <int BITS, int GV>
 __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const __half* __restrict__ src,
-                                                            int64_t ld, int64_t Tq, int64_t T,
-                                                            int npw) {
+                                                            int64_t ld, int64_t Tq, int64_t r,
+                                                            int64_t ns, int npw) {
   __shared__ alignas(16) uint8_t lds[QW][V_LDS];
   __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const __half* s = src + pair * ld * D;
+  const __half* s0 = src + pair * ld * D;
+  const __half* s = s0 + (int64_t)L.S * D;        // the tokens after the sink
   const int64_t nruns = Tq / kVRun;
   float smx = 0.f;
   for (int i = 0; i < npw; ++i) {
@@ -316,7 +320,8 @@ __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const _
                            L.v_scale + pair * L.vs_pair() + j * kVRun * (D / GV),
                            L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds[wave]));
     } else if (j == nruns) {
-      copy_rows(s + Tq * D, L.v_resid + pair * L.rs_pair(), T - Tq);
+      copy_rows(s0, L.v_resid + pair * L.rs_pair(), ns);
+      copy_rows(s + Tq * D, L.v_resid + pair * L.rs_pair() + (int64_t)L.S * D, r);
     }
   }
   raise_scale_max<QW>(L.scale_max + 2 * pair + 1, smx, red);
@@ -329,11 +334,11 @@ int items_per_wave(int64_t items, int pairs) {
   return (int)std::max<int64_t>(1, (items + QW * blocks_per_pair - 1) / (QW * blocks_per_pair));
 }
 
-// Append one token per (b, h).  flush == 0: grid (1, B*H), the new row goes to row
-// `slot`.  flush == 1: grid (R/G + R/16, B*H); blocks [0, R/G) quantize the Key
-// groups of the window and blocks [R/G, R/G + R/16) its Value runs, into the history
-// at token t0 = T_before - R.  The blocks that read window row 0 (Key group 0 and
-// Value run 0) then store the new row in row 0 after their reads.
+// Append one token per (b, h).  flush == 0: grid (1, B*H), the new row goes to
+// residual row `slot`.  flush == 1: grid (R/G + R/16, B*H); blocks [0, R/G) quantize
+// the Key groups of the window (residual rows [S, S + R)) and blocks [R/G, R/G + R/16)
+// its Value runs, into the history at token t0.  The blocks that read window row 0
+// (Key group 0 and Value run 0) then store the new row there after their reads.
 template <int BITS, int G, int GV>
 __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int slot, int flush,
                                                     const __half* __restrict__ k_new,
@@ -341,15 +346,15 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
   constexpr int LBYTES = G * D > V_LDS ? G * D : V_LDS;
   __shared__ alignas(16) uint8_t lds[LBYTES];
   const int64_t pair = blockIdx.y;
-  __half* kr = L.k_resid + pair * L.rs_pair();
-  __half* vr = L.v_resid + pair * L.rs_pair();
   const __half* kn = k_new + pair * D;
   const __half* vn = v_new + pair * D;
   if (!flush) {
-    copy_rows(kn, kr + (int64_t)slot * D, 1);
-    copy_rows(vn, vr + (int64_t)slot * D, 1);
+    copy_rows(kn, L.k_resid + pair * L.rs_pair() + (int64_t)slot * D, 1);
+    copy_rows(vn, L.v_resid + pair * L.rs_pair() + (int64_t)slot * D, 1);
     return;
   }
+  __half* kr = L.k_resid + pair * L.rs_pair() + (int64_t)L.S * D;     // the window
+  __half* vr = L.v_resid + pair * L.rs_pair() + (int64_t)L.S * D;
   const int nk = L.R / G;
   const int blk = blockIdx.x;
   if (blk < nk) {
@@ -408,7 +413,8 @@ bool dispatch_gv(int Gv, F&& f) {
 
 hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s) {
-  const int64_t Tq = quantized_len(T, L.R);
+  const TokenSplit ts = split_tokens(T, L.S, L.R);
+  const int64_t Tq = ts.Tq;
   const int pairs = L.B * L.H;
   hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
                      L.scale_max, 0, pairs);
@@ -417,7 +423,7 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
   const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value>), grid,
-                       dim3(64 * QW), 0, s, L, src, ld, Tq, T, npw);
+                       dim3(64 * QW), 0, s, L, src, ld, Tq, ts.r, ts.ns, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -426,7 +432,8 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
 
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s) {
-  const int64_t Tq = quantized_len(T, L.R);
+  const TokenSplit ts = split_tokens(T, L.S, L.R);
+  const int64_t Tq = ts.Tq;
   const int pairs = L.B * L.H;
   hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
                      L.scale_max, 1, pairs);
@@ -436,10 +443,10 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
   bool ok = dispatch_gv(L.Gv, [&](auto gv) {
     if (L.bits == 2)
       hipLaunchKernelGGL((prefill_v_kernel<2, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, Tq, T, npw);
+                         src, ld, Tq, ts.r, ts.ns, npw);
     else
       hipLaunchKernelGGL((prefill_v_kernel<4, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, Tq, T, npw);
+                         src, ld, Tq, ts.r, ts.ns, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -448,10 +455,9 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
 
 hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __half* k_new,
                                const __half* v_new, hipStream_t s) {
-  const int64_t r = residual_len(T_before, L.R);
-  const int flush = (r == L.R) ? 1 : 0;
-  const int slot = flush ? 0 : (int)r;
-  const int64_t t0 = T_before - L.R;
+  const AppendPlan ap = plan_append(T_before, L.S, L.R);
+  const int flush = ap.flush, slot = ap.slot;
+  const int64_t t0 = ap.t0;
   const dim3 grid(flush ? (unsigned)(L.R / L.G + L.R / kVRun) : 1u, (unsigned)(L.B * L.H));
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     return dispatch_gv(L.Gv, [&](auto gv) {

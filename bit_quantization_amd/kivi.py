@@ -43,7 +43,7 @@ class kivi_dims(ctypes.Structure):
                 ("kv_heads", ctypes.c_int32), ("q_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group_k", ctypes.c_int32), ("group_v", ctypes.c_int32),
-                ("residual", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("residual", ctypes.c_int32), ("sink", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64)]
 
 
@@ -152,10 +152,11 @@ class Dims:
     group_v: int
     residual: int
     max_tokens: int
+    sink: int = 0        # tokens kept in float16 at the start of every sequence
 
     def c(self) -> kivi_dims:
         return kivi_dims(self.layers, self.batch, self.kv_heads, self.q_heads, self.head_dim,
-                         self.bits, self.group_k, self.group_v, self.residual, 0,
+                         self.bits, self.group_k, self.group_v, self.residual, self.sink,
                          self.max_tokens)
 
 
@@ -192,7 +193,7 @@ class Cache:
         if name in ("v_scale", "v_zero"):
             return buf.view(torch.float16).view(L, B, H, T, D // d.group_v)
         if name in ("k_resid", "v_resid"):
-            return buf.view(torch.float16).view(L, B, H, d.residual, D)
+            return buf.view(torch.float16).view(L, B, H, d.sink + d.residual, D)
         if name == "scale_max":
             return buf.view(torch.float32).view(L, B, H, 2)
         raise KeyError(name)

@@ -47,8 +47,8 @@
  *    v_codes  uint8   [L][B][H_kv][T_max/16][d][2*b]   per channel, runs of 16 tokens
  *    v_scale  float16 [L][B][H_kv][T_max][d/G_v]       per (token, Value group)
  *    v_zero   float16 [L][B][H_kv][T_max][d/G_v]
- *    k_resid  float16 [L][B][H_kv][R][d]               residual window rows
- *    v_resid  float16 [L][B][H_kv][R][d]
+ *    k_resid  float16 [L][B][H_kv][S + R][d]           rows [0, S): the sink tokens;
+ *    v_resid  float16 [L][B][H_kv][S + R][d]           rows [S, S + R): the window
  *    scale_max float32 [L][B][H_kv][2]                 largest Key scale [0] and
  *             Value scale [1] in the quantized history (kept by the calls below)
  *  Packed runs are little-endian 32-bit words of n = 32/b codes: code j of a run is
@@ -90,7 +90,15 @@ typedef enum kivi_status {
 } kivi_status;
 
 /* Problem statement of one cache ("4.4 KV Cache quantization" §1 and §3: layers,
- * batch, KV heads, head_dim, bits, group size, residual length). */
+ * batch, KV heads, head_dim, bits, group size, residual length).
+ *
+ * Sink tokens ("09 — KV Cache Quantization", "Anti-patterns": the first tokens of a
+ * sequence absorb large attention scores and must not be quantized; preserve the
+ * first N): with sink = S, tokens [0, S) of every sequence stay in float16 for its
+ * lifetime (residual rows [0, S)), and every rule of this header — groups, window,
+ * flushes, T_q and r — applies to the tokens after them, counted from S:
+ * T_q(T) and r(T) below mean T_q(T - S) and r(T - S) for T > S (0 for T <= S), and
+ * history token i is token S + i of the sequence. */
 typedef struct kivi_dims {
   int32_t layers;      /* L >= 1 */
   int32_t batch;       /* B >= 1 */
@@ -101,7 +109,8 @@ typedef struct kivi_dims {
   int32_t group_k;     /* G: tokens per Key group, in {16, 32, 64} */
   int32_t group_v;     /* G_v: channels per Value group, divides d, in {16, 32, 64, 128} */
   int32_t residual;    /* R: residual window, a multiple of G and of 16 */
-  int32_t reserved;    /* must be 0 */
+  int32_t sink;        /* S in [0, 1024]: tokens kept in float16 at the start of every
+                          sequence (0: none); see "Sink tokens" above */
   int64_t max_tokens;  /* T_max: token capacity per sequence, a multiple of G and 16 */
 } kivi_dims;
 
@@ -134,9 +143,10 @@ kivi_status kivi_cache_sizes(const kivi_dims* dims, size_t bytes[KIVI_NUM_BUFFER
  *   k      float16 [B][H_kv][ld_tokens][d] device; tokens [0, T) are read.
  *   T      prompt length, 0 <= T <= T_max.
  *   ld     token stride of `k` (>= T).
- * Quantizes tokens [0, T_q(T)) into k_codes/k_scale/k_zero of `layer`, copies
- * tokens [T_q(T), T) into rows [0, r(T)) of k_resid and sets the layer's Key entries
- * of scale_max to the largest Key scale written (0 if none). */
+ * Copies tokens [0, min(T, S)) into rows [0, S) of k_resid, quantizes the next T_q(T)
+ * tokens into k_codes/k_scale/k_zero of `layer`, copies the last r(T) tokens into
+ * rows [S, S + r(T)) of k_resid and sets the layer's Key entries of scale_max to the
+ * largest Key scale written (0 if none). */
 kivi_status kivi_quantize_k(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                             const void* k, int64_t T, int64_t ld_tokens, void* stream);
 
@@ -150,10 +160,11 @@ kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int3
  * streaming complication"; "4.4 KV Cache quantization" §3.2).
  *   T_before   tokens cached before this call (0 <= T_before, T_before + 1 <= T_max).
  *   k_new, v_new  float16 [B][H_kv][d] device.
- * If r(T_before) == R the window is first quantized into the history at token
- * T_before - R (same arithmetic as the prefill calls); the new row then goes to row
- * r(T_before) mod R.  The cache then holds T_before + 1 tokens; a flush raises
- * scale_max to the largest scales it writes. */
+ * While T_before < S the new row goes to sink row T_before.  Otherwise, if
+ * r(T_before) == R the window is first quantized into the history at history token
+ * T_q(T_before) (same arithmetic as the prefill calls); the new row then goes to
+ * window row r(T_before) mod R.  The cache then holds T_before + 1 tokens; a flush
+ * raises scale_max to the largest scales it writes. */
 kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                               int64_t T_before, const void* k_new, const void* v_new,
                               void* stream);

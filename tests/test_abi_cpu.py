@@ -85,12 +85,23 @@ def test_bad_dims_are_rejected(field, value, status):
     assert st == status and msg
 
 
-def test_reserved_field_must_be_zero():
+@pytest.mark.parametrize("sink", [-1, 1025])
+def test_sink_out_of_range_is_rejected(sink):
     c = good_dims().c()
-    c.reserved = 1
-    st, _ = call("kivi_quantize_v", ctypes.byref(c), ctypes.byref(fake_cache()), 0, FAKE, 16, 16,
-                 None)
-    assert st == 1
+    c.sink = sink
+    st, msg = call("kivi_quantize_v", ctypes.byref(c), ctypes.byref(fake_cache()), 0, FAKE, 16, 16,
+                   None)
+    assert st == 1 and "sink" in msg
+
+
+def test_sink_rows_extend_the_float16_buffers():
+    d = good_dims(bits=4, group_v=64)
+    d.sink = 7
+    sizes = kv.kivi_cache_sizes(d)
+    unit = d.layers * d.batch * d.kv_heads
+    assert sizes[6] == sizes[7] == unit * (7 + 64) * 128 * 2
+    d.sink = 0
+    assert kv.kivi_cache_sizes(d)[6] == unit * 64 * 128 * 2
 
 
 def test_null_and_misaligned_pointers():
