@@ -51,6 +51,14 @@ Readings of passages the pages leave open (each is also listed in the design not
       tokens, tokens [0, S) of a sequence stay in float16 for its lifetime and every
       rule above (groups, window, flushes) applies to tokens S, S+1, ... counted
       from S.  S = 0 is the plain method.
+  R16 Group-wise aging of the window ([ZSM] "The streaming complication": as the
+      window fills, a completed group of keys is quantized once and frozen, and the
+      newest tokens stay in float16 until they age out).  Variant of R5, selected
+      per cache: the window holds at most R tokens; a token that arrives at a full
+      window first sends only the oldest G window tokens (one Key group; their
+      Values token by token) into the history, and the newest R - G stay.  Hence
+      r(T) = T for T <= R and R - G + ((T - R - 1) mod G) + 1 after, so the window
+      always keeps at least the R - G + 1 most recent tokens.  G = R is R5.
 """
 from __future__ import annotations
 
@@ -84,6 +92,15 @@ def residual_len(T: int, R: int) -> int:
 
 def quantized_len(T: int, R: int) -> int:
     return T - residual_len(T, R)
+
+
+def residual_len_grouped(T: int, R: int, G: int) -> int:
+    """Window tokens after T tokens when the window ages one Key group at a time
+    (reading R16)."""
+    return T if T <= R else R - G + (T - R - 1) % G + 1
+
+
+AGING = ("window", "group")
 
 
 def kivi_cache_bytes(layers: int, batch: int, tokens: int, kv_heads: int, head_dim: int,
@@ -263,8 +280,8 @@ class LayerCache:
     """
 
     def __init__(self, batch, kv_heads, head_dim, bits, group_k, group_v, residual,
-                 max_tokens, sink: int = 0):
-        assert bits in (2, 4)
+                 max_tokens, sink: int = 0, aging: str = "window"):
+        assert bits in (2, 4) and aging in AGING
         assert residual % group_k == 0 and residual % V_RUN == 0
         assert max_tokens % group_k == 0 and max_tokens % V_RUN == 0
         assert head_dim % group_v == 0
@@ -281,6 +298,7 @@ class LayerCache:
         self.k_resid = np.zeros((B, H, residual, d), F16)
         self.v_resid = np.zeros((B, H, residual, d), F16)
         self.S = sink                       # reading R15
+        self.aging = aging                  # reading R5 ("window") or R16 ("group")
         self.k_sink = np.zeros((B, H, sink, d), F16)
         self.v_sink = np.zeros((B, H, sink, d), F16)
         self.T = 0
@@ -289,6 +307,17 @@ class LayerCache:
     def Tk(self) -> int:
         """Tokens under the KIVI rules: those after the sink (reading R15)."""
         return max(0, self.T - self.S)
+
+    def window_len(self, Tk: int) -> int:
+        """r: window tokens when Tk tokens follow the sink (readings R5 and R16)."""
+        if self.aging == "group":
+            return residual_len_grouped(Tk, self.R, self.G)
+        return residual_len(Tk, self.R)
+
+    @property
+    def Tq(self) -> int:
+        """Tokens in the quantized history."""
+        return self.Tk - self.window_len(self.Tk)
 
     # -- writes into the quantized store ------------------------------------------------
     def _store(self, K: np.ndarray, V: np.ndarray, t0: int):
@@ -317,8 +346,8 @@ class LayerCache:
         self.v_sink[:, :, :ns] = V[:, :, :ns]
         K, V = K[:, :, ns:], V[:, :, ns:]
         Tk = T - ns
-        Tq = quantized_len(Tk, self.R)
-        r = Tk - Tq
+        r = self.window_len(Tk)
+        Tq = Tk - r
         if Tq:
             self._store(K[:, :, :Tq], V[:, :, :Tq], 0)
         self.k_resid[:, :, :r] = K[:, :, Tq:Tk]
@@ -334,10 +363,15 @@ class LayerCache:
             self.T += 1
             return
         Tk = self.Tk
-        r = residual_len(Tk, self.R)
+        r = self.window_len(Tk)
         if r == self.R:
-            self._store(self.k_resid, self.v_resid, Tk - self.R)
-            r = 0
+            # the window is full: its oldest n tokens go to the history (all R of them,
+            # reading R5; one Key group, reading R16), the rest move to its front
+            n = self.G if self.aging == "group" else self.R
+            self._store(self.k_resid[:, :, :n], self.v_resid[:, :, :n], Tk - self.R)
+            self.k_resid[:, :, :r - n] = self.k_resid[:, :, n:r].copy()
+            self.v_resid[:, :, :r - n] = self.v_resid[:, :, n:r].copy()
+            r -= n
         self.k_resid[:, :, r] = k_new
         self.v_resid[:, :, r] = v_new
         self.T += 1
@@ -345,7 +379,7 @@ class LayerCache:
     # -- reads ------------------------------------------------------------------------
     def quantized_codes(self):
         """Unpacked codes of the quantized part: (k_codes, v_codes) uint8 [B,H,T_q,d]."""
-        Tq = quantized_len(self.Tk, self.R)
+        Tq = self.Tq
         kc = unpack_keys(self.k_codes[:, :, :Tq], self.bits)
         vc = unpack_values(self.v_codes[:, :, :Tq // V_RUN], self.bits)
         return kc, vc
@@ -354,7 +388,7 @@ class LayerCache:
         """(K_hat, V_hat) float32 [B, H, T, d]: the sink rows, the dequantized history,
         then the residual window."""
         ns = min(self.T, self.S)
-        Tq = quantized_len(self.Tk, self.R)
+        Tq = self.Tq
         r = self.Tk - Tq
         kc, vc = self.quantized_codes()
         Kq = dequantize_keys(kc, self.k_scale[:, :, :Tq // self.G],
@@ -389,7 +423,7 @@ class LayerCache:
     def dequantized_pair(self, b: int, h: int):
         """(K_hat, V_hat) float32 [T, d] for one (sequence, KV head) pair."""
         ns = min(self.T, self.S)
-        Tq = quantized_len(self.Tk, self.R)
+        Tq = self.Tq
         r = self.Tk - Tq
         kc = unpack_keys(self.k_codes[b, h, :Tq], self.bits)
         vc = unpack_values(self.v_codes[b, h, :Tq // V_RUN], self.bits)

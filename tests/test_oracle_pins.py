@@ -579,3 +579,94 @@ def test_sink_prefill_equals_appends(S, T0):
         assert np.array_equal(getattr(a, name), getattr(b, name)), name
     r = O.residual_len(T - S, 64)
     assert np.array_equal(a.k_resid[:, :, :r], b.k_resid[:, :, :r])
+
+
+# ---- group-wise aging of the window (reading R16) --------------------------------------
+
+def test_grouped_window_length_table():
+    # R = 64, G = 16: the window fills to 64, then each arriving token at a full
+    # window sends one group of 16 out: 65 -> 49, 80 -> 64, 81 -> 49; 200 -> 48 + 8
+    table = {0: 0, 1: 1, 63: 63, 64: 64, 65: 49, 66: 50, 79: 63, 80: 64, 81: 49, 200: 56}
+    for T, r in table.items():
+        assert O.residual_len_grouped(T, 64, 16) == r, T
+    for T in range(0, 300):
+        assert O.residual_len_grouped(T, 32, 32) == O.residual_len(T, 32)
+        if T > 64:
+            r = O.residual_len_grouped(T, 64, 16)
+            assert 49 <= r <= 64 and (T - r) % 16 == 0
+
+
+def _aging_stream(R, G, S, T, seed, bits=2, Gv=128):
+    K, V = _sink_inputs(T, seed)
+    c = O.LayerCache(2, 2, 128, bits, G, Gv, R, 512, sink=S, aging="group")
+    return K, V, c
+
+
+def test_grouped_aging_flushes_one_group_at_a_time():
+    R, G, T = 64, 16, 170
+    K, V, c = _aging_stream(R, G, 0, T, 21)
+    grew = []
+    for t in range(T):
+        before = c.Tq
+        c.append(K[:, :, t], V[:, :, t])
+        if c.Tq != before:
+            grew.append((t, c.Tq - before))
+        r = c.Tk - c.Tq
+        # the window is the r most recent tokens, exactly, oldest first
+        assert np.array_equal(c.k_resid[:, :, :r], K[:, :, t + 1 - r:t + 1])
+        assert np.array_equal(c.v_resid[:, :, :r], V[:, :, t + 1 - r:t + 1])
+    assert grew == [(t, 16) for t in range(64, T, 16)]
+
+
+@pytest.mark.parametrize("R,G,S,T0,bits", [(64, 16, 0, 0, 2), (64, 32, 0, 40, 4),
+                                           (128, 32, 5, 3, 2), (96, 32, 0, 200, 4)])
+def test_grouped_aging_prefill_equals_appends(R, G, S, T0, bits):
+    T = S + 3 * R + 13
+    K, V, a = _aging_stream(R, G, S, T, 30 + G, bits)
+    a.prefill(K, V)
+    _, _, b = _aging_stream(R, G, S, T, 30 + G, bits)
+    b.prefill(K[:, :, :T0], V[:, :, :T0])
+    for t in range(T0, T):
+        b.append(K[:, :, t], V[:, :, t])
+    for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_sink",
+                 "v_sink"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    r = a.Tk - a.Tq
+    assert r == b.Tk - b.Tq == O.residual_len_grouped(T - S, R, G)
+    assert np.array_equal(a.k_resid[:, :, :r], b.k_resid[:, :, :r])
+    assert np.array_equal(a.v_resid[:, :, :r], b.v_resid[:, :, :r])
+
+
+def test_grouped_aging_with_one_group_windows_is_the_window_rule():
+    T = 3 * 32 + 9
+    K, V = _sink_inputs(T, 40)
+    a = O.LayerCache(2, 2, 128, 2, 32, 128, 32, 256, aging="group")
+    b = O.LayerCache(2, 2, 128, 2, 32, 128, 32, 256)
+    for t in range(T):
+        a.append(K[:, :, t], V[:, :, t])
+        b.append(K[:, :, t], V[:, :, t])
+    for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "k_resid",
+                 "v_resid"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+
+
+@pytest.mark.parametrize("T", [64, 65, 100, 129, 200, 257])
+def test_grouped_history_matches_window_history_on_the_common_prefix(T):
+    # groups are quantized on their own, so the history of either rule holds the same
+    # codes, scales and zeros for every token both have quantized
+    K, V = _sink_inputs(T, 50)
+    a = O.LayerCache(2, 2, 128, 4, 16, 64, 64, 512, aging="group")
+    b = O.LayerCache(2, 2, 128, 4, 16, 64, 64, 512)
+    a.prefill(K, V)
+    b.prefill(K, V)
+    n = min(a.Tq, b.Tq)
+    assert a.Tq == T - O.residual_len_grouped(T, 64, 16) and b.Tq == O.quantized_len(T, 64)
+    assert np.array_equal(a.k_codes[:, :, :n], b.k_codes[:, :, :n])
+    assert np.array_equal(a.k_scale[:, :, :n // 16], b.k_scale[:, :, :n // 16])
+    assert np.array_equal(a.k_zero[:, :, :n // 16], b.k_zero[:, :, :n // 16])
+    assert np.array_equal(a.v_codes[:, :, :n // 16], b.v_codes[:, :, :n // 16])
+    assert np.array_equal(a.v_scale[:, :, :n], b.v_scale[:, :, :n])
+    Kh, Vh = a.dequantized()
+    r = T - a.Tq
+    assert np.array_equal(Kh[:, :, T - r:], K[:, :, T - r:].astype(np.float32))
+    assert np.array_equal(Vh[:, :, T - r:], V[:, :, T - r:].astype(np.float32))
