@@ -62,18 +62,29 @@ def measured_traffic(workload):
     return entry.get("traffic_bytes_per_launch")
 
 
-def split(T, R, S=0):
+AGING = "window"     # "group" with --aging group
+
+
+def window_len(Tk, R, G):
+    if Tk == 0:
+        return 0
+    if AGING == "group":
+        return Tk if Tk <= R else R - G + (Tk - R - 1) % G + 1
+    return (Tk - 1) % R + 1
+
+
+def split(T, R, S=0, G=32):
     """(float16 rows, quantized tokens) at T tokens: the first S tokens (the sink) and
-    the window of the rest stay float16, whole windows before it are quantized."""
+    the window of the rest stay float16, the tokens before the window are quantized."""
     ns = min(T, S)
     Tk = T - ns
-    r = 0 if Tk == 0 else (Tk - 1) % R + 1
+    r = window_len(Tk, R, G)
     return ns + r, Tk - r
 
 
 def decode_bytes(w, T, S=0):
     """Algorithmic bytes of one decode launch at T cached tokens (see module doc)."""
-    rows, Tq = split(T, w.residual, S)
+    rows, Tq = split(T, w.residual, S, w.group_k)
     d = w.head_dim
     per_pair = (2 * Tq * d * w.bits // 8            # K and V codes
                 + (Tq // w.group_k) * d * 4         # K scale + zero
@@ -89,11 +100,12 @@ def append_bytes(w, T_before, S=0):
     pairs = w.batch * w.kv_heads
     rows = pairs * 2 * d * 2 * 2                    # k_new, v_new read; residual row written
     Tk = T_before - S
-    r = 0 if Tk <= 0 else (Tk - 1) % R + 1
-    if r == R:                                      # flush the window
-        codes = 2 * R * d * w.bits // 8
-        meta = (R // w.group_k) * d * 4 + R * (d // w.group_v) * 4
-        rows += pairs * (2 * R * d * 2 + codes + meta)
+    r = 0 if Tk <= 0 else window_len(Tk, R, w.group_k)
+    if r == R:                                      # flush the window (or its oldest group)
+        n = w.group_k if AGING == "group" else R
+        codes = 2 * n * d * w.bits // 8
+        meta = (n // w.group_k) * d * 4 + n * (d // w.group_v) * 4
+        rows += pairs * (2 * n * d * 2 + codes + meta)
     return rows
 
 
@@ -108,6 +120,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sink", type=int, default=0,
                    help="attention-sink tokens kept in float16 at the start of each sequence")
+    p.add_argument("--aging", default="window", choices=["window", "group"],
+                   help="a full window flushes whole (window) or its oldest Key group (group)")
     p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2"],
                    help="kivi: the workload's 2/4-bit KIVI cache (default); fp8_*: the same "
                         "workload stored as FP8 with per-head scales")
@@ -171,7 +185,7 @@ def read_ceiling():
 def prefill_bytes(w, T, S=0):
     """Algorithmic bytes of quantizing one layer's prompt of T tokens (a1 + a2): read
     fp16 K and V, write codes, scales/zeros and the fp16 sink and window rows."""
-    rows, Tq = split(T, w.residual, S)
+    rows, Tq = split(T, w.residual, S, w.group_k)
     d = w.head_dim
     per_pair = (2 * T * d * 2                           # K and V read
                 + 2 * Tq * d * w.bits // 8              # codes written
@@ -199,7 +213,7 @@ def cpu_baseline(w, host_pairs, budget_s, S=0):
         m = math.lcm(16, w.group_k, w.residual)
         cap = (T + len(k_rows) + 1 + m - 1) // m * m
         oc = O.LayerCache(1, 1, w.head_dim, w.bits, w.group_k, w.group_v, w.residual, cap,
-                          sink=S)
+                          sink=S, aging=AGING)
         oc.prefill(Kh, Vh)
         caches.append((oc, k_rows, v_rows, qh))
     done_bytes, t_used, steps, T_last = 0, 0.0, 0, 0
@@ -437,6 +451,8 @@ def main():
     # warmup, the eager loop timed per launch (roofline), then the K steps of the graph
     total_steps = args.warmup + 2 * args.steps
     S = args.sink
+    global AGING
+    AGING = args.aging
     per_copy_bytes = decode_bytes(w1, w1.tokens, S)
     copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy_bytes))
     if w.layers > 1:
@@ -445,7 +461,7 @@ def main():
     extra_rows = max(steps_per_copy, 1024)          # rows appended on the GPU / by the oracle
     Tmax = w1.replace(stream_steps=steps_per_copy).max_tokens()
     dims = k.Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, w1.bits, w1.group_k,
-                  w1.group_v, w1.residual, Tmax, sink=S)
+                  w1.group_v, w1.residual, Tmax, sink=S, aging=AGING)
     print(f"[bench] workload {w.name}: {copies} layer caches x {per_copy_bytes / 1e6:.1f} MB "
           f"decode reads, {args.warmup}+{args.steps} steps", file=sys.stderr, flush=True)
 
@@ -621,7 +637,8 @@ def main():
         "config": {"workload": w.name, "batch": w1.batch, "kv_heads": w1.kv_heads,
                    "q_heads": w1.q_heads, "head_dim": w1.head_dim, "tokens": w1.tokens,
                    "bits": w1.bits, "group_k": w1.group_k, "group_v": w1.group_v,
-                   "residual": w1.residual, "sink": S, "layer_caches": copies,
+                   "residual": w1.residual, "sink": S, "aging": AGING,
+                   "layer_caches": copies,
                    "n_split": n_split,
                    "step": "append(+flush) + decode attention",
                    "launch": "one HIP graph of the timed steps" if not args.no_graph
@@ -637,7 +654,8 @@ def main():
                      "median_launch_us": round(dec_med_s * 1e6, 3),
                      "p10_p90_launch_us": [round(sorted(dec_ms)[len(dec_ms) // 10] * 1e3, 3),
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
-                     "traffic": measured_traffic(w.name) if S == 0 else None},
+                     "traffic": measured_traffic(w.name) if S == 0 and AGING == "window"
+                                else None},
         "cpu_baseline": cpu,
         "prefill_quantize": prefill,
         "quality": quality,

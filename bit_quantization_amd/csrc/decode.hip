@@ -57,7 +57,8 @@ struct DecodeArgs {
   unsigned* counters;   // [P][kCounterStride]: arrival counter, zero between calls
   int64_t Tq;           // quantized tokens
   int64_t nblk;         // 64-token blocks per pair (the last may hold 32 tokens)
-  int r;                // residual tokens
+  int r;                // float16 tokens: sink rows, then the window
+  int ring;             // window ring start: window token i is in row S + (ring + i) mod R
   int nw;               // workgroups per pair
   float qscale;         // sm_scale * log2(e)
   const __half* k_new;  // [P][D]: window row new_slot comes from here (new_slot >= 0)
@@ -629,7 +630,14 @@ __device__ __forceinline__ void load_q_f16(const __half* qp, f16x8 (&aq)[4]) {
   }
 }
 
-// Window rows [c0, c0 + n_valid), n_valid <= 32.  Every Key and Value load of the
+// Residual row of float16 token i (i < a.r): the sink rows, then the window's ring.
+__device__ __forceinline__ int fp16_row(const DecodeArgs& a, int i) {
+  if (i < a.L.S) return i;
+  const int p = i + a.ring;
+  return p >= a.L.S + a.L.R ? p - a.L.R : p;
+}
+
+// Float16 tokens [c0, c0 + n_valid), n_valid <= 32.  Every Key and Value load of the
 // chunk goes out before any is used (rows past the chunk re-read its last row; their
 // probabilities are 0).  Row a.new_slot, when set, is read from the appended token.  Float16 products are exact in float32 (subnormal operands
 // aside), accumulated in float32.
@@ -648,7 +656,8 @@ __device__ __forceinline__ void residual_rows(const DecodeArgs& a, int64_t pair,
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int rr = 16 * nt + lo < n_valid ? 16 * nt + lo : n_valid - 1;
-    const __half* row = c0 + rr == a.new_slot ? a.k_new + pair * D : kr + (int64_t)(c0 + rr) * D;
+    const int pr = fp16_row(a, c0 + rr);
+    const __half* row = pr == a.new_slot ? a.k_new + pair * D : kr + (int64_t)pr * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       bk[nt][ks] = *reinterpret_cast<const f16x8*>(row + 32 * ks + 8 * j);
@@ -661,9 +670,10 @@ __device__ __forceinline__ void residual_rows(const DecodeArgs& a, int64_t pair,
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
     const int rr = t < n_valid ? t : n_valid - 1;
-    const bool fresh = c0 + rr == a.new_slot;
+    const int pr = fp16_row(a, c0 + rr);
+    const bool fresh = pr == a.new_slot;
     vv[t] = __builtin_bit_cast(__half2, __builtin_amdgcn_raw_buffer_load_b32(
-                                            fresh ? vnew : vres, 4 * lane, fresh ? 0 : (c0 + rr) * D * 2, 0));
+                                            fresh ? vnew : vres, 4 * lane, fresh ? 0 : pr * D * 2, 0));
   }
   f32x4 d[2];
 #pragma unroll
@@ -851,9 +861,10 @@ bool dispatch_decode(int bits, int gqa, int G, F&& f) {
 DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_req) {
   DecodePlan p{};
   const int gqa = q_heads / L.H;
-  const TokenSplit ts = split_tokens(T, L.S, L.R);
+  const TokenSplit ts = split_tokens(L, T);
   const int64_t Tq = ts.Tq;
-  p.r = (int)ts.fp16_rows();          // sink rows and window rows, contiguous
+  p.r = (int)ts.fp16_rows();          // sink rows and window tokens
+  p.ring = ts.ring;
   p.n_groups = Tq / L.G;
   const int64_t nblk = (Tq + BLK - 1) / BLK;
   const int64_t pairs = (int64_t)L.B * L.H;
@@ -880,9 +891,10 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.out = out;
   a.counters = reinterpret_cast<unsigned*>(ws);
   a.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + plan.ws_counters);
-  a.Tq = split_tokens(T, L.S, L.R).Tq;
+  a.Tq = split_tokens(L, T).Tq;
   a.nblk = (a.Tq + BLK - 1) / BLK;
   a.r = plan.r;
+  a.ring = plan.ring;
   a.nw = plan.n_split;
   a.qscale = sm_scale * 1.4426950408889634f;
   a.k_new = new_row ? new_row->k : nullptr;

@@ -64,6 +64,10 @@ kivi_status check_dims(const kivi_dims* d) {
                 d->residual, d->group_k);
   if (d->sink < 0 || d->sink > 1024)
     return fail(KIVI_ERR_ARG, "sink = %d outside [0, 1024]", d->sink);
+  if (d->aging != KIVI_AGING_WINDOW && d->aging != KIVI_AGING_GROUP)
+    return fail(KIVI_ERR_ARG, "aging = %d; expected KIVI_AGING_WINDOW (0) or KIVI_AGING_GROUP (1)",
+                d->aging);
+  if (d->reserved != 0) return fail(KIVI_ERR_ARG, "reserved = %d must be 0", d->reserved);
   if (d->max_tokens < 1 || d->max_tokens % d->group_k != 0 || d->max_tokens % kivi::kVRun != 0)
     return fail(KIVI_ERR_ARG, "max_tokens = %lld must be a positive multiple of group_k and 16",
                 (long long)d->max_tokens);
@@ -103,10 +107,26 @@ kivi_status check_cache(const kivi_cache* c) {
   return KIVI_OK;
 }
 
+// The dims of a layer, no buffers (planning).
+kivi::LayerView shape_view(const kivi_dims* d) {
+  kivi::LayerView L{};
+  L.B = d->batch;
+  L.H = d->kv_heads;
+  L.d = d->head_dim;
+  L.bits = d->bits;
+  L.G = d->group_k;
+  L.Gv = d->group_v;
+  L.R = d->residual;
+  L.S = d->sink;
+  L.aging = d->aging;
+  L.Tmax = d->max_tokens;
+  return L;
+}
+
 kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer) {
   size_t sz[KIVI_NUM_BUFFERS];
   buffer_sizes(d, sz);
-  kivi::LayerView L;
+  kivi::LayerView L = shape_view(d);
   const size_t Ld = (size_t)d->layers;
   L.k_codes = static_cast<uint8_t*>(c->k_codes) + layer * (sz[0] / Ld);
   L.k_scale = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->k_scale) + layer * (sz[1] / Ld));
@@ -117,15 +137,6 @@ kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer) {
   L.k_resid = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->k_resid) + layer * (sz[6] / Ld));
   L.v_resid = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->v_resid) + layer * (sz[7] / Ld));
   L.scale_max = reinterpret_cast<float*>(static_cast<uint8_t*>(c->scale_max) + layer * (sz[8] / Ld));
-  L.B = d->batch;
-  L.H = d->kv_heads;
-  L.d = d->head_dim;
-  L.bits = d->bits;
-  L.G = d->group_k;
-  L.Gv = d->group_v;
-  L.R = d->residual;
-  L.S = d->sink;
-  L.Tmax = d->max_tokens;
   return L;
 }
 
@@ -422,16 +433,7 @@ kivi_status kivi_decode_workspace_bytes_split(const kivi_dims* dims, int64_t T, 
     return fail(T < 1 ? KIVI_ERR_ARG : KIVI_ERR_CAPACITY, "T = %lld outside [1, max_tokens]",
                 (long long)T);
   if (n_split < 0) return fail(KIVI_ERR_ARG, "n_split = %d is negative", n_split);
-  kivi::LayerView L{};
-  L.B = dims->batch;
-  L.H = dims->kv_heads;
-  L.d = dims->head_dim;
-  L.bits = dims->bits;
-  L.G = dims->group_k;
-  L.Gv = dims->group_v;
-  L.R = dims->residual;
-  L.S = dims->sink;
-  L.Tmax = dims->max_tokens;
+  const kivi::LayerView L = shape_view(dims);
   *bytes = kivi::plan_decode(L, dims->q_heads, T, n_split).ws_total;
   return ok();
 }
@@ -447,16 +449,7 @@ kivi_status kivi_decode_splits(const kivi_dims* dims, int64_t T, int32_t* n_spli
   if (T < 1 || T > dims->max_tokens)
     return fail(T < 1 ? KIVI_ERR_ARG : KIVI_ERR_CAPACITY, "T = %lld outside [1, max_tokens]",
                 (long long)T);
-  kivi::LayerView L{};
-  L.B = dims->batch;
-  L.H = dims->kv_heads;
-  L.d = dims->head_dim;
-  L.bits = dims->bits;
-  L.G = dims->group_k;
-  L.Gv = dims->group_v;
-  L.R = dims->residual;
-  L.S = dims->sink;
-  L.Tmax = dims->max_tokens;
+  const kivi::LayerView L = shape_view(dims);
   *n_split = kivi::plan_decode(L, dims->q_heads, T, 0).n_split;
   return ok();
 }
@@ -493,7 +486,7 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const __half* kn = static_cast<const __half*>(k_new);
   const __half* vn = static_cast<const __half*>(v_new);
-  const kivi::AppendPlan ap = kivi::plan_append(T_before, L.S, L.R);
+  const kivi::AppendPlan ap = kivi::plan_append(L, T_before);
   if (ap.flush) {
     // the window is full: flush it (and store the new row) first, then attend
     hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, s);
@@ -523,6 +516,6 @@ kivi_status kivi_stream_read(const void* buf, size_t bytes, void* sink, size_t s
 
 const char* kivi_last_error(void) { return g_err; }
 
-int32_t kivi_abi_version(void) { return 3; }
+int32_t kivi_abi_version(void) { return 4; }
 
 }  // extern "C"

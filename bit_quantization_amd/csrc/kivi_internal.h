@@ -23,6 +23,7 @@ struct LayerView {
   float* scale_max;   // [B][H][2]: largest Key scale, largest Value scale
   int B, H, d, bits, G, Gv, R;
   int S;              // sink tokens kept in float16 (tokens [0, S) of each sequence)
+  int aging;          // 0: a full window is flushed whole; 1: only its oldest Key group
   int64_t Tmax;
 
   // Per-(b, h) element strides of each buffer.
@@ -33,50 +34,67 @@ struct LayerView {
   __host__ __device__ int64_t rs_pair() const { return (int64_t)(S + R) * d; }
 };
 
-inline int64_t residual_len(int64_t T, int R) { return T == 0 ? 0 : (T - 1) % R + 1; }
-inline int64_t quantized_len(int64_t T, int R) { return T - residual_len(T, R); }
+// Window tokens after Tk tokens (those after the sink): the full window flushes
+// whole, so r = ((Tk - 1) mod R) + 1; with group aging only its oldest G tokens
+// leave, so r = Tk up to R and R - G + ((Tk - R - 1) mod G) + 1 after.
+inline int64_t window_len(int64_t Tk, int R, int G, int aging) {
+  if (Tk == 0) return 0;
+  if (!aging) return (Tk - 1) % R + 1;
+  return Tk <= R ? Tk : R - G + (Tk - R - 1) % G + 1;
+}
 
 // T cached tokens with S sink tokens: the first min(T, S) stay in float16 (residual
 // rows [0, S)); the rest follow the window rules counted from S: Tq of them are in
-// the quantized history, r in the window (residual rows [S, S + r)).
+// the quantized history, r in the window.  The window is a ring over residual rows
+// [S, S + R): token i after the sink sits in row S + (i mod R), so its r tokens
+// start at row S + ring and wrap after row S + R - 1 (ring = Tq mod R, a multiple
+// of G; 0 when the full window flushes).
 struct TokenSplit {
   int64_t ns, Tq, r;
-  int64_t fp16_rows() const { return ns + r; }   // rows [0, ns) and [S, S + r) (ns == S if r > 0)
+  int ring;
+  int64_t fp16_rows() const { return ns + r; }   // sink rows and window tokens
 };
-inline TokenSplit split_tokens(int64_t T, int S, int R) {
+inline TokenSplit split_tokens(const LayerView& L, int64_t T) {
   TokenSplit t;
-  t.ns = T < S ? T : S;
+  t.ns = T < L.S ? T : L.S;
   const int64_t Tk = T - t.ns;
-  t.Tq = quantized_len(Tk, R);
-  t.r = Tk - t.Tq;
+  t.r = window_len(Tk, L.R, L.G, L.aging);
+  t.Tq = Tk - t.r;
+  t.ring = (int)(t.Tq % L.R);
   return t;
 }
 
-// Where an appended token goes: the sink row T_before while the sink fills; else the
-// window, after flushing it into the history at token t0 when it is full.
+// Where an appended token goes: the sink row T_before while the sink fills; else its
+// ring row in the window, after flushing the oldest n window tokens (rows
+// [first, first + n), never wrapping) into the history at token t0 when the window
+// is full.  The new token then takes row `first`.
 struct AppendPlan {
-  int flush;      // 1: quantize the full window into the history first
+  int flush;      // 1: quantize n window tokens into the history first
+  int n;          // tokens flushed: R, or G with group aging
+  int first;      // residual row of the oldest window token (flush only)
   int slot;       // residual row of the new token
-  int64_t t0;     // history token of window row 0 (flush only)
+  int64_t t0;     // history token of the oldest window token (flush only)
 };
-inline AppendPlan plan_append(int64_t T_before, int S, int R) {
-  if (T_before < S) return AppendPlan{0, (int)T_before, 0};
-  const int64_t Tk = T_before - S;
-  const int64_t r = residual_len(Tk, R);
-  if (r == R) return AppendPlan{1, S, Tk - R};
-  return AppendPlan{0, (int)(S + r), 0};
+inline AppendPlan plan_append(const LayerView& L, int64_t T_before) {
+  if (T_before < L.S) return AppendPlan{0, 0, 0, (int)T_before, 0};
+  const int64_t Tk = T_before - L.S;
+  const int64_t r = window_len(Tk, L.R, L.G, L.aging);
+  const int slot = L.S + (int)(Tk % L.R);
+  if (r < L.R) return AppendPlan{0, 0, 0, slot, 0};
+  const int64_t Tq = Tk - r;
+  return AppendPlan{1, L.aging ? L.G : L.R, L.S + (int)(Tq % L.R), slot, Tq};
 }
 
 // ---- launchers (return hipGetLastError() of the launch) -------------------------
 
 // Prefill of T tokens of src ([B][H][ld][d]): the sink tokens to residual rows
-// [0, ns), the history tokens [S, S + Tq) quantized, the last r to rows [S, S + r).
+// [0, ns), the history tokens [S, S + Tq) quantized, the last r to their ring rows.
 hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s);
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s);
 
-// Append one row; flush the full window first when r(T_before) == R.
+// Append one row; when the window is full, flush its oldest tokens first (plan_append).
 hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __half* k_new,
                                const __half* v_new, hipStream_t s);
 
@@ -84,7 +102,8 @@ hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __hal
 struct DecodePlan {
   int n_split;          // token splits per (b, kv head)
   int64_t n_groups;     // quantized Key groups per (b, kv head)
-  int r;                // residual tokens
+  int r;                // float16 tokens: sink rows and window
+  int ring;             // window ring start (split_tokens)
   size_t ws_partials;   // bytes of partial results
   size_t ws_counters;   // bytes of per-pair arrival counters
   size_t ws_total;

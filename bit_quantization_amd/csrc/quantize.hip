@@ -264,17 +264,30 @@ __device__ __forceinline__ void copy_rows(const __half* __restrict__ src, __half
   for (int64_t i = threadIdx.x & 63; i < n; i += 64) d[i] = s[i];
 }
 
+// The float16 rows of one (b, h) after a prefill: the ns sink tokens (the first rows
+// of the sequence s0) to residual rows [0, ns), and the r window tokens (w, the
+// tokens after the quantized history) to their ring rows S + ring .. wrapping after
+// row S + R - 1.
+__device__ __forceinline__ void store_fp16_rows(const LayerView& L, const __half* s0,
+                                                const __half* w, __half* resid, int64_t ns,
+                                                int64_t r, int ring) {
+  copy_rows(s0, resid, ns);
+  const int64_t n1 = r < L.R - ring ? r : L.R - ring;
+  copy_rows(w, resid + (int64_t)(L.S + ring) * D, n1);
+  copy_rows(w + n1 * D, resid + (int64_t)L.S * D, r - n1);
+}
+
 // ---- kernels ----------------------------------------------------------------------
 
 // Items of one (b, h): the Tq/G Key groups (or Tq/16 Value runs) of the tokens after
 // the sink, then one item that copies the sink tokens and the r window tokens into
-// the residual rows.  grid = (ceil(items /
+// their residual rows.  grid = (ceil(items /
 // (QW*npw)), B*H); workgroup x takes items QW*npw*x .. +QW*npw - 1, its waves
 // interleaved (wave w takes item QW*npw*x + QW*i + w for i < npw).
 template <int BITS, int G>
 __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const __half* __restrict__ src,
                                                             int64_t ld, int64_t Tq, int64_t r,
-                                                            int64_t ns, int npw) {
+                                                            int64_t ns, int ring, int npw) {
   __shared__ alignas(16) uint8_t lds[QW][G * D];
   __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
@@ -291,8 +304,7 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
                            L.k_scale + pair * L.ks_pair() + g * D,
                            L.k_zero + pair * L.ks_pair() + g * D, lds[wave]));
     } else if (g == ngroups) {
-      copy_rows(s0, L.k_resid + pair * L.rs_pair(), ns);
-      copy_rows(s + Tq * D, L.k_resid + pair * L.rs_pair() + (int64_t)L.S * D, r);
+      store_fp16_rows(L, s0, s + Tq * D, L.k_resid + pair * L.rs_pair(), ns, r, ring);
     }
   }
   raise_scale_max<QW>(L.scale_max + 2 * pair, smx, red);
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
 template <int BITS, int GV>
 __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const __half* __restrict__ src,
                                                             int64_t ld, int64_t Tq, int64_t r,
-                                                            int64_t ns, int npw) {
+                                                            int64_t ns, int ring, int npw) {
   __shared__ alignas(16) uint8_t lds[QW][V_LDS];
   __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
@@ -320,8 +332,7 @@ __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const _
                            L.v_scale + pair * L.vs_pair() + j * kVRun * (D / GV),
                            L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds[wave]));
     } else if (j == nruns) {
-      copy_rows(s0, L.v_resid + pair * L.rs_pair(), ns);
-      copy_rows(s + Tq * D, L.v_resid + pair * L.rs_pair() + (int64_t)L.S * D, r);
+      store_fp16_rows(L, s0, s + Tq * D, L.v_resid + pair * L.rs_pair(), ns, r, ring);
     }
   }
   raise_scale_max<QW>(L.scale_max + 2 * pair + 1, smx, red);
@@ -334,13 +345,14 @@ int items_per_wave(int64_t items, int pairs) {
   return (int)std::max<int64_t>(1, (items + QW * blocks_per_pair - 1) / (QW * blocks_per_pair));
 }
 
-// Append one token per (b, h).  flush == 0: grid (1, B*H), the new row goes to
-// residual row `slot`.  flush == 1: grid (R/G + R/16, B*H); blocks [0, R/G) quantize
-// the Key groups of the window (residual rows [S, S + R)) and blocks [R/G, R/G + R/16)
-// its Value runs, into the history at token t0.  The blocks that read window row 0
-// (Key group 0 and Value run 0) then store the new row there after their reads.
+// Append one token per (b, h).  n == 0: grid (1, B*H), the new row goes to residual
+// row `slot`.  n > 0 (the window is full): grid (n/G + n/16, B*H); blocks [0, n/G)
+// quantize the Key groups of the n oldest window tokens (residual rows [first,
+// first + n)) and blocks [n/G, n/G + n/16) their Value runs, into the history at token
+// t0.  The blocks that read row `first` (Key group 0 and Value run 0) then store the
+// new row there (slot == first) after their reads.
 template <int BITS, int G, int GV>
-__global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int slot, int flush,
+__global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int slot, int n,
                                                     const __half* __restrict__ k_new,
                                                     const __half* __restrict__ v_new) {
   constexpr int LBYTES = G * D > V_LDS ? G * D : V_LDS;
@@ -348,14 +360,14 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
   const int64_t pair = blockIdx.y;
   const __half* kn = k_new + pair * D;
   const __half* vn = v_new + pair * D;
-  if (!flush) {
-    copy_rows(kn, L.k_resid + pair * L.rs_pair() + (int64_t)slot * D, 1);
-    copy_rows(vn, L.v_resid + pair * L.rs_pair() + (int64_t)slot * D, 1);
+  __half* kr = L.k_resid + pair * L.rs_pair() + (int64_t)slot * D;
+  __half* vr = L.v_resid + pair * L.rs_pair() + (int64_t)slot * D;
+  if (n == 0) {
+    copy_rows(kn, kr, 1);
+    copy_rows(vn, vr, 1);
     return;
   }
-  __half* kr = L.k_resid + pair * L.rs_pair() + (int64_t)L.S * D;     // the window
-  __half* vr = L.v_resid + pair * L.rs_pair() + (int64_t)L.S * D;
-  const int nk = L.R / G;
+  const int nk = n / G;
   const int blk = blockIdx.x;
   if (blk < nk) {
     const float smx = quantize_k_group<BITS, G>(
@@ -413,7 +425,7 @@ bool dispatch_gv(int Gv, F&& f) {
 
 hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s) {
-  const TokenSplit ts = split_tokens(T, L.S, L.R);
+  const TokenSplit ts = split_tokens(L, T);
   const int64_t Tq = ts.Tq;
   const int pairs = L.B * L.H;
   hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
@@ -423,7 +435,7 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
   const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value>), grid,
-                       dim3(64 * QW), 0, s, L, src, ld, Tq, ts.r, ts.ns, npw);
+                       dim3(64 * QW), 0, s, L, src, ld, Tq, ts.r, ts.ns, ts.ring, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -432,7 +444,7 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
 
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              hipStream_t s) {
-  const TokenSplit ts = split_tokens(T, L.S, L.R);
+  const TokenSplit ts = split_tokens(L, T);
   const int64_t Tq = ts.Tq;
   const int pairs = L.B * L.H;
   hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
@@ -443,10 +455,10 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
   bool ok = dispatch_gv(L.Gv, [&](auto gv) {
     if (L.bits == 2)
       hipLaunchKernelGGL((prefill_v_kernel<2, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, Tq, ts.r, ts.ns, npw);
+                         src, ld, Tq, ts.r, ts.ns, ts.ring, npw);
     else
       hipLaunchKernelGGL((prefill_v_kernel<4, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, Tq, ts.r, ts.ns, npw);
+                         src, ld, Tq, ts.r, ts.ns, ts.ring, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -455,15 +467,16 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
 
 hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __half* k_new,
                                const __half* v_new, hipStream_t s) {
-  const AppendPlan ap = plan_append(T_before, L.S, L.R);
-  const int flush = ap.flush, slot = ap.slot;
+  const AppendPlan ap = plan_append(L, T_before);
+  const int n = ap.flush ? ap.n : 0;
+  const int slot = ap.slot;
   const int64_t t0 = ap.t0;
-  const dim3 grid(flush ? (unsigned)(L.R / L.G + L.R / kVRun) : 1u, (unsigned)(L.B * L.H));
+  const dim3 grid(n ? (unsigned)(n / L.G + n / kVRun) : 1u, (unsigned)(L.B * L.H));
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     return dispatch_gv(L.Gv, [&](auto gv) {
       hipLaunchKernelGGL(
           (append_kernel<decltype(b)::value, decltype(g)::value, decltype(gv)::value>), grid,
-          dim3(64), 0, s, L, t0, slot, flush, k_new, v_new);
+          dim3(64), 0, s, L, t0, slot, n, k_new, v_new);
       return true;
     });
   });

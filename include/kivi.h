@@ -48,7 +48,7 @@
  *    v_scale  float16 [L][B][H_kv][T_max][d/G_v]       per (token, Value group)
  *    v_zero   float16 [L][B][H_kv][T_max][d/G_v]
  *    k_resid  float16 [L][B][H_kv][S + R][d]           rows [0, S): the sink tokens;
- *    v_resid  float16 [L][B][H_kv][S + R][d]           rows [S, S + R): the window
+ *    v_resid  float16 [L][B][H_kv][S + R][d]           rows [S, S + R): the window ring
  *    scale_max float32 [L][B][H_kv][2]                 largest Key scale [0] and
  *             Value scale [1] in the quantized history (kept by the calls below)
  *  Packed runs are little-endian 32-bit words of n = 32/b codes: code j of a run is
@@ -61,11 +61,18 @@
  *  s = float(scale);  code_i = s == 0 ? 0 : clamp(rint((x_i - mn) / s), 0, 2^b - 1).
  *  Dequantized value: code * scale + zero.
  *
- * Residual window: after T tokens it holds r(T) = T == 0 ? 0 : ((T - 1) mod R) + 1
- * tokens and the quantized history holds T_q(T) = T - r(T) tokens.  Appending when
- * r == R first quantizes the R window rows into the history at token T - R, then
- * stores the new token in row 0.  Prefill of T tokens gives the same bytes as T
- * appends.  All sequences of a batch share T.
+ * Residual window: after T tokens it holds r(T) tokens and the quantized history
+ * holds T_q(T) = T - r(T).  With aging = KIVI_AGING_WINDOW (default),
+ * r(T) = T == 0 ? 0 : ((T - 1) mod R) + 1: an append at r == R first quantizes all R
+ * window tokens into the history.  With aging = KIVI_AGING_GROUP ("KIVI: A
+ * Tuning-Free ...", "The streaming complication": a completed Key group is quantized
+ * once, the newest tokens stay float16 until they age out), r(T) = T for T <= R and
+ * R - G + ((T - R - 1) mod G) + 1 after: an append at r == R first quantizes only
+ * the oldest G window tokens.  The window is a ring over its R rows: token T_q + i
+ * (i < r) sits in window row (T_q + i) mod R, so the flushed tokens' rows are
+ * reused by the newest ones; under KIVI_AGING_WINDOW T_q is a multiple of R and
+ * token T_q + i is in row i.  Prefill of T tokens gives the same bytes as T appends.
+ * All sequences of a batch share T.
  *
  * Grouped-query attention: query head j reads KV head j / (H_q / H_kv).
  */
@@ -89,6 +96,9 @@ typedef enum kivi_status {
   KIVI_ERR_DEVICE = 6        /* the HIP runtime rejected a launch */
 } kivi_status;
 
+#define KIVI_AGING_WINDOW 0   /* a full window is flushed whole */
+#define KIVI_AGING_GROUP 1    /* a full window sends only its oldest Key group out */
+
 /* Problem statement of one cache ("4.4 KV Cache quantization" §1 and §3: layers,
  * batch, KV heads, head_dim, bits, group size, residual length).
  *
@@ -111,6 +121,8 @@ typedef struct kivi_dims {
   int32_t residual;    /* R: residual window, a multiple of G and of 16 */
   int32_t sink;        /* S in [0, 1024]: tokens kept in float16 at the start of every
                           sequence (0: none); see "Sink tokens" above */
+  int32_t aging;       /* KIVI_AGING_WINDOW or KIVI_AGING_GROUP; see "Residual window" */
+  int32_t reserved;    /* must be 0 */
   int64_t max_tokens;  /* T_max: token capacity per sequence, a multiple of G and 16 */
 } kivi_dims;
 
@@ -161,9 +173,10 @@ kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int3
  *   T_before   tokens cached before this call (0 <= T_before, T_before + 1 <= T_max).
  *   k_new, v_new  float16 [B][H_kv][d] device.
  * While T_before < S the new row goes to sink row T_before.  Otherwise, if
- * r(T_before) == R the window is first quantized into the history at history token
- * T_q(T_before) (same arithmetic as the prefill calls); the new row then goes to
- * window row r(T_before) mod R.  The cache then holds T_before + 1 tokens; a flush
+ * r(T_before) == R the oldest R (KIVI_AGING_WINDOW) or G (KIVI_AGING_GROUP) window
+ * tokens are first quantized into the history at history token T_q(T_before) (same
+ * arithmetic as the prefill calls); the new row then goes to window row
+ * (T_before - S) mod R.  The cache then holds T_before + 1 tokens; a flush
  * raises scale_max to the largest scales it writes. */
 kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                               int64_t T_before, const void* k_new, const void* v_new,
@@ -194,7 +207,7 @@ kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t
  * attention kernel"; "KV Cache Quantization (KIVI & FP4)" §2 and §4):
  *   out[b][j][:] = softmax_t(sm_scale * q[b][j] . k_t) v_t over the T cached tokens of
  *   sequence b and KV head j / (H_q / H_kv); k_t, v_t are dequantized codes for the
- *   T_q(T) history tokens and the float16 window rows for the last r(T).
+ *   T_q(T) history tokens and the float16 rows for the sink and the last r(T).
  *   q          float16 [B][H_q][d] device.
  *   out        float32 [B][H_q][d] device.
  *   T          1 <= T <= T_max.

@@ -25,9 +25,9 @@ def kv():
     return kivi
 
 
-def sink_dims(bits, G, Gv, R, S, B, H, g, Tmax):
+def sink_dims(bits, G, Gv, R, S, B, H, g, Tmax, aging="window"):
     return kv().Dims(layers=1, batch=B, kv_heads=H, q_heads=H * g, head_dim=D, bits=bits,
-                     group_k=G, group_v=Gv, residual=R, max_tokens=Tmax, sink=S)
+                     group_k=G, group_v=Gv, residual=R, max_tokens=Tmax, sink=S, aging=aging)
 
 
 def capacity(T, R):
@@ -43,19 +43,23 @@ def prefill(dims, K, V, T):
 
 
 def compare_sink_cache(cache, oc, T):
-    """Every byte the oracle defines at T tokens, for all pairs."""
+    """Every byte the oracle defines at T tokens, for all pairs.  The oracle keeps its
+    window oldest first; the GPU keeps window token Tq + i in ring row (Tq + i) mod R
+    after the S sink rows."""
     d = cache.dims
-    S = d.sink
+    S, R = d.sink, d.residual
+    assert oc.T == T and oc.aging == d.aging
     ns = min(T, S)
-    Tq = O.quantized_len(T - ns, d.residual)
+    Tq = oc.Tq
     r = T - ns - Tq
-    where = f"S={S} T={T}"
+    where = f"S={S} T={T} aging={d.aging}"
+    ring = torch.from_numpy(S + (Tq + np.arange(r, dtype=np.int64)) % R)
     for name, sink_ref, win_ref in (("k_resid", oc.k_sink, oc.k_resid),
                                     ("v_resid", oc.v_sink, oc.v_resid)):
-        rows = cache.view(name)[0]
+        rows = cache.view(name)[0].cpu()
         assert np.array_equal(bits16(rows[:, :, :ns]), bits16(sink_ref[:, :, :ns])), \
             f"{name} sink rows {where}"
-        assert np.array_equal(bits16(rows[:, :, S:S + r]), bits16(win_ref[:, :, :r])), \
+        assert np.array_equal(bits16(rows[:, :, ring]), bits16(win_ref[:, :, :r])), \
             f"{name} window rows {where}"
     g = cache.view("k_codes")[0, :, :, :Tq].cpu().numpy()
     assert np.array_equal(g, oc.k_codes[:, :, :Tq]), "k_codes " + where
@@ -74,9 +78,9 @@ def compare_sink_cache(cache, oc, T):
     assert np.array_equal(sm[..., 1], ref_v), "scale_max[1] " + where
 
 
-def oracle_cache(bits, G, Gv, R, S, K, V, T, Tmax):
+def oracle_cache(bits, G, Gv, R, S, K, V, T, Tmax, aging="window"):
     B, H = K.shape[0], K.shape[1]
-    oc = O.LayerCache(B, H, D, bits, G, Gv, R, Tmax, sink=S)
+    oc = O.LayerCache(B, H, D, bits, G, Gv, R, Tmax, sink=S, aging=aging)
     oc.prefill(K[:, :, :T].cpu().numpy(), V[:, :, :T].cpu().numpy())
     return oc
 
