@@ -120,6 +120,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sink", type=int, default=0,
                    help="attention-sink tokens kept in float16 at the start of each sequence")
+    p.add_argument("--ragged", action="store_true",
+                   help="a ragged batch: sequence b holds tokens * (b + 1) / batch tokens")
     p.add_argument("--aging", default="window", choices=["window", "group"],
                    help="a full window flushes whole (window) or its oldest Key group (group)")
     p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2"],
@@ -453,7 +455,17 @@ def main():
     S = args.sink
     global AGING
     AGING = args.aging
-    per_copy_bytes = decode_bytes(w1, w1.tokens, S)
+    one = w1.replace(batch=1)
+    # prompt length of each sequence: all w1.tokens, or tokens * (b + 1) / batch
+    base = [w1.tokens * (b + 1) // w1.batch if args.ragged else w1.tokens
+            for b in range(w1.batch)]
+
+    def step_bytes(T_before):
+        """(decode bytes, append bytes) of the step that appends at T_before + j."""
+        return (sum(decode_bytes(one, t + 1, S) for t in T_before),
+                sum(append_bytes(one, t, S) for t in T_before))
+
+    per_copy_bytes = step_bytes(base)[0]
     copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy_bytes))
     if w.layers > 1:
         copies = args.copies or min(w.layers, max(copies, 2))
@@ -471,33 +483,45 @@ def main():
     rng = np.random.default_rng(0)
     sample_pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, w1.batch, 64),
                                                       rng.integers(0, w1.kv_heads, 64))]
+    T_hi = max(base)
+    base_t = torch.tensor(base, dtype=torch.int32, device="cuda")
+    # per-sequence token counts before step j of a copy (ragged calls read them on the GPU)
+    lens_steps = torch.stack([base_t + j for j in range(steps_per_copy)]).contiguous()
+
+    def rows_from(X, j0, n):
+        """X[b, :, base[b] + j0 + t] for t < n, as [n, B, H, d] (contiguous per step)."""
+        return torch.stack([X[b, :, base[b] + j0:base[b] + j0 + n] for b in range(w1.batch)]) \
+            .permute(2, 0, 1, 3).contiguous()
+
     for c in range(copies):
         K, V = W.make_kv(w1, c, device="cuda", total_tokens=w1.tokens + extra_rows)
         cache = k.Cache(dims)
-        k.kivi_quantize_k(dims, cache, 0, K, w1.tokens, K.shape[2])
-        k.kivi_quantize_v(dims, cache, 0, V, w1.tokens, V.shape[2])
+        if args.ragged:
+            k.kivi_quantize_k_varlen(dims, cache, 0, K, base_t, T_hi, K.shape[2])
+            k.kivi_quantize_v_varlen(dims, cache, 0, V, base_t, T_hi, V.shape[2])
+        else:
+            k.kivi_quantize_k(dims, cache, 0, K, w1.tokens, K.shape[2])
+            k.kivi_quantize_v(dims, cache, 0, V, w1.tokens, V.shape[2])
         caches.append(cache)
-        Ts.append(w1.tokens)
-        # new rows per step, [steps, B, H, d] so that each step's rows are contiguous
-        news.append((K[:, :, w1.tokens:w1.tokens + steps_per_copy].permute(2, 0, 1, 3).contiguous(),
-                     V[:, :, w1.tokens:w1.tokens + steps_per_copy].permute(2, 0, 1, 3).contiguous()))
+        Ts.append(0)                                # steps taken on this copy
+        news.append((rows_from(K, 0, steps_per_copy), rows_from(V, 0, steps_per_copy)))
         if c == 0:
             keep = (K, V)
             if not args.no_cpu_baseline:
                 q0 = W.make_q(w1, 0, 0, device="cuda").cpu().numpy()
                 g = w1.gqa
                 for (b, h) in sample_pairs[:6]:
-                    host_pairs.append((K[b:b + 1, h:h + 1, :w1.tokens].cpu().numpy(),
-                                       V[b:b + 1, h:h + 1, :w1.tokens].cpu().numpy(),
-                                       K[b, h, w1.tokens:].cpu().numpy(),
-                                       V[b, h, w1.tokens:].cpu().numpy(),
-                                       q0[b:b + 1, h * g:(h + 1) * g], w1.tokens))
+                    t = base[b]
+                    host_pairs.append((K[b:b + 1, h:h + 1, :t].cpu().numpy(),
+                                       V[b:b + 1, h:h + 1, :t].cpu().numpy(),
+                                       K[b, h, t:].cpu().numpy(), V[b, h, t:].cpu().numpy(),
+                                       q0[b:b + 1, h * g:(h + 1) * g], t))
         else:
             del K, V
     qs = [W.make_q(w1, 0, s, device="cuda") for s in range(8)]
     out = torch.empty((w1.batch, w1.q_heads, w1.head_dim), dtype=torch.float32, device="cuda")
     ws = k.new_workspace(dims, Tmax, args.n_split)
-    n_split = args.n_split or k.kivi_decode_splits(dims, w1.tokens)
+    n_split = args.n_split or k.kivi_decode_splits(dims, T_hi)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -508,13 +532,17 @@ def main():
         the calls; one kernel launch except on flush steps (1 in R), which add the
         flush launch.  Returns (call, decode bytes, append bytes)."""
         c = i % copies
-        T_before = Ts[c]
-        j = T_before - w1.tokens
-        kn, vn = news[c]
+        j = Ts[c]
+        Ts[c] = j + 1
+        T_before = T_hi + j                         # the longest sequence's count
         T = T_before + 1
-        Ts[c] = T
+        kn, vn = news[c]
         q = qs[i % len(qs)]
-        if args.n_split:
+        db, ab = step_bytes([t + j for t in base])
+        if args.ragged:
+            call = k.prepare_append_decode_varlen(dims, caches[c], 0, lens_steps[j], T_before,
+                                                  kn[j], vn[j], q, w1.sm_scale, out, ws)
+        elif args.n_split:
             def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
                 k.kivi_append_flush(dims, caches[c], 0, T_before, kj, vj)
                 k.kivi_decode_attn(dims, caches[c], 0, T, q, w1.sm_scale, out, ws,
@@ -522,7 +550,7 @@ def main():
         else:
             call = k.prepare_append_decode(dims, caches[c], 0, T_before, kn[j], vn[j], q,
                                            w1.sm_scale, out, ws)
-        return call, decode_bytes(w1, T, S), append_bytes(w1, T_before, S)
+        return call, db, ab
 
     for i in range(args.warmup):
         prepare(i)[0]()
@@ -576,42 +604,50 @@ def main():
 
     # Quality versus unquantized fp32 attention on copy 0 (reported, not gated).
     K, V = keep
-    Tq = Ts[0]
-    qq = qs[0]
-    k.kivi_decode_attn(dims, caches[0], 0, Tq, qq, w1.sm_scale, out, ws, n_split=args.n_split)
-    g = w1.gqa
-    Kf = K[:, :, :Tq].float()
-    Vf = V[:, :, :Tq].float()
-    qf = qq.float().view(w1.batch, w1.kv_heads, g, w1.head_dim)
-    logits = torch.matmul(qf, Kf.transpose(-1, -2).contiguous()) * float(np.float32(w1.sm_scale))
-    ref = torch.matmul(torch.softmax(logits, dim=-1), Vf).view_as(out)
-    o = out.double()
-    rd = ref.double()
-    quality = {"vs": "unquantized fp32 attention on the same float16 K/V",
-               "rel_l2": float((o - rd).norm() / rd.norm()),
-               "cosine": float(torch.nn.functional.cosine_similarity(o.flatten(), rd.flatten(),
-                                                                     dim=0)),
-               "max_abs": float((o - rd).abs().max())}
-    del K, V, Kf, Vf, keep
+    quality = None
+    if not args.ragged:
+        Tq = w1.tokens + Ts[0]
+        qq = qs[0]
+        k.kivi_decode_attn(dims, caches[0], 0, Tq, qq, w1.sm_scale, out, ws,
+                           n_split=args.n_split)
+        g = w1.gqa
+        Kf = K[:, :, :Tq].float()
+        Vf = V[:, :, :Tq].float()
+        qf = qq.float().view(w1.batch, w1.kv_heads, g, w1.head_dim)
+        logits = torch.matmul(qf, Kf.transpose(-1, -2).contiguous()) * float(np.float32(w1.sm_scale))
+        ref = torch.matmul(torch.softmax(logits, dim=-1), Vf).view_as(out)
+        o = out.double()
+        rd = ref.double()
+        quality = {"vs": "unquantized fp32 attention on the same float16 K/V",
+                   "rel_l2": float((o - rd).norm() / rd.norm()),
+                   "cosine": float(torch.nn.functional.cosine_similarity(o.flatten(),
+                                                                         rd.flatten(), dim=0)),
+                   "max_abs": float((o - rd).abs().max())}
+        del Kf, Vf
+    del K, V, keep
 
     # Secondary: prefill quantization (a1 + a2) of one layer's prompt, re-run on
     # copy 0's fp16 K/V into a scratch cache (HIP events, best of 3).
-    Kp, Vp = W.make_kv(w1, 0, device="cuda", total_tokens=w1.tokens)
+    Kp, Vp = W.make_kv(w1, 0, device="cuda", total_tokens=T_hi)
     scratch = k.Cache(dims)
     pre_s = float("inf")
     for _ in range(3):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        k.kivi_quantize_k(dims, scratch, 0, Kp, w1.tokens, Kp.shape[2])
-        k.kivi_quantize_v(dims, scratch, 0, Vp, w1.tokens, Vp.shape[2])
+        if args.ragged:
+            k.kivi_quantize_k_varlen(dims, scratch, 0, Kp, base_t, T_hi, Kp.shape[2])
+            k.kivi_quantize_v_varlen(dims, scratch, 0, Vp, base_t, T_hi, Vp.shape[2])
+        else:
+            k.kivi_quantize_k(dims, scratch, 0, Kp, w1.tokens, Kp.shape[2])
+            k.kivi_quantize_v(dims, scratch, 0, Vp, w1.tokens, Vp.shape[2])
         b.record()
         b.synchronize()
         pre_s = min(pre_s, a.elapsed_time(b) / 1e3)
     del Kp, Vp, scratch
+    pre_bytes = sum(prefill_bytes(one, t, S) for t in base)
     prefill = {"what": "kivi_quantize_k + kivi_quantize_v of one layer's prompt",
-               "tokens": w1.tokens, "us": round(pre_s * 1e6, 1),
-               "GB/s": round(prefill_bytes(w1, w1.tokens, S) / pre_s / 1e9, 1),
-               "bytes": prefill_bytes(w1, w1.tokens, S)}
+               "tokens": sum(base), "us": round(pre_s * 1e6, 1),
+               "GB/s": round(pre_bytes / pre_s / 1e9, 1), "bytes": pre_bytes}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -638,6 +674,8 @@ def main():
                    "q_heads": w1.q_heads, "head_dim": w1.head_dim, "tokens": w1.tokens,
                    "bits": w1.bits, "group_k": w1.group_k, "group_v": w1.group_v,
                    "residual": w1.residual, "sink": S, "aging": AGING,
+                   "lengths": ("tokens * (b + 1) / batch: " + ",".join(map(str, base))
+                               if args.ragged else "uniform"),
                    "layer_caches": copies,
                    "n_split": n_split,
                    "step": "append(+flush) + decode attention",
@@ -654,8 +692,8 @@ def main():
                      "median_launch_us": round(dec_med_s * 1e6, 3),
                      "p10_p90_launch_us": [round(sorted(dec_ms)[len(dec_ms) // 10] * 1e3, 3),
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
-                     "traffic": measured_traffic(w.name) if S == 0 and AGING == "window"
-                                else None},
+                     "traffic": measured_traffic(w.name)
+                                if S == 0 and AGING == "window" and not args.ragged else None},
         "cpu_baseline": cpu,
         "prefill_quantize": prefill,
         "quality": quality,

@@ -64,7 +64,26 @@ struct DecodeArgs {
   const __half* k_new;  // [P][D]: window row new_slot comes from here (new_slot >= 0)
   const __half* v_new;
   int new_slot;         // -1: every window row is read from the cache
+  Lens lens;            // ragged batch: per-sequence counts (the fields above are for T)
 };
+
+// A ragged batch: the token split of sequence b (and its new row's slot), computed by
+// each workgroup for its own pair.
+__device__ __forceinline__ void ragged_split(DecodeArgs& a, int64_t b) {
+  int64_t T;
+  if (a.new_slot >= 0) {
+    const int64_t T_before = a.lens.get(b, 0);
+    a.new_slot = plan_append(a.L, T_before).slot;
+    T = T_before + 1;
+  } else {
+    T = a.lens.get(b, 1);
+  }
+  const TokenSplit ts = split_tokens(a.L, T);
+  a.Tq = ts.Tq;
+  a.nblk = (ts.Tq + BLK - 1) / BLK;
+  a.r = (int)ts.fp16_rows();
+  a.ring = ts.ring;
+}
 
 // Waves per SIMD that the register budget of each variant allows; a workgroup holds
 // 4 SIMDs' worth.  The build turns a kernel that misses this occupancy into an error
@@ -771,7 +790,7 @@ __device__ __forceinline__ void block_share(int64_t nblk, int n_res, int nw, int
   }
 }
 template <int BITS, int GQA, int G>
-__global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_kernel(DecodeArgs args) {
   constexpr int NMT = (GQA + 3) / 4;
   constexpr int WAVES = 4 * waves_per_simd(BITS, GQA, G);
   constexpr int NTH = 64 * WAVES;
@@ -780,11 +799,13 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   __shared__ alignas(16) float comb[2 * WAVES][GQA * PSTRIDE];  // [0, WAVES): blocks; then window
   __shared__ int counter;
 
-  const int64_t P = (int64_t)a.L.B * a.L.H;
+  const int64_t P = (int64_t)args.L.B * args.L.H;
   const int64_t pair = blockIdx.x % P;
   const int s = (int)(blockIdx.x / P);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t b = pair / a.L.H, h = pair % a.L.H;
+  const int64_t b = pair / args.L.H, h = pair % args.L.H;
+  DecodeArgs a = args;
+  if (a.lens.p) ragged_split(a, b);
 
   // this workgroup's share: window chunks (workgroup 0 only), then blocks
   const int n_res_all = (a.r + 31) / 32;
@@ -883,7 +904,7 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
 
 hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __half* q,
                          float sm_scale, float* out, void* ws, const DecodePlan& plan,
-                         const NewRow* new_row, hipStream_t s) {
+                         const NewRow* new_row, Lens lens, hipStream_t s) {
   const int gqa = q_heads / L.H;
   DecodeArgs a;
   a.L = L;
@@ -900,6 +921,7 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.k_new = new_row ? new_row->k : nullptr;
   a.v_new = new_row ? new_row->v : nullptr;
   a.new_slot = new_row ? new_row->slot : -1;
+  a.lens = lens;
   const int64_t P = (int64_t)L.B * L.H;
   const dim3 grid((unsigned)(P * plan.n_split));
   bool ok = dispatch_decode(L.bits, gqa, L.G, [&](auto b, auto g, auto gg) {

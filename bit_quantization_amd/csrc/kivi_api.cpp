@@ -155,8 +155,19 @@ kivi_status device_status(hipError_t e, const char* what) {
   return fail(KIVI_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A ragged batch's per-sequence counts (device int32 [B]); nullptr is accepted only
+// where the caller passes no array.
+kivi_status check_lens(const int32_t* lens) {
+  if (!lens) return fail(KIVI_ERR_ARG, "lens is NULL");
+  if ((reinterpret_cast<uintptr_t>(lens) & 3u) != 0)
+    return fail(KIVI_ERR_ALIGN, "lens is not 4-byte aligned");
+  return KIVI_OK;
+}
+
+// lens == nullptr: every sequence has T tokens; else sequence b has lens[b] <= T.
 kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
-                            const void* x, int64_t T, int64_t ld, void* stream, bool keys) {
+                            const void* x, int64_t T, int64_t ld, void* stream, bool keys,
+                            const int32_t* lens = nullptr) {
   kivi_status st = check_common(dims, cache, layer);
   if (st != KIVI_OK) return st;
   if (T < 0) return fail(KIVI_ERR_ARG, "T = %lld is negative", (long long)T);
@@ -168,9 +179,10 @@ kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int3
   if (!x) return fail(KIVI_ERR_ARG, "%s input is NULL", keys ? "key" : "value");
   if (!aligned16(x)) return fail(KIVI_ERR_ALIGN, "%s input is not 16-byte aligned", keys ? "key" : "value");
   const kivi::LayerView L = layer_view(dims, cache, layer);
-  hipError_t e = keys ? kivi::launch_quantize_k(L, static_cast<const __half*>(x), ld, T,
+  const kivi::Lens ln{lens, T};
+  hipError_t e = keys ? kivi::launch_quantize_k(L, static_cast<const __half*>(x), ld, T, ln,
                                                 static_cast<hipStream_t>(stream))
-                      : kivi::launch_quantize_v(L, static_cast<const __half*>(x), ld, T,
+                      : kivi::launch_quantize_v(L, static_cast<const __half*>(x), ld, T, ln,
                                                 static_cast<hipStream_t>(stream));
   return device_status(e, keys ? "kivi_quantize_k launch" : "kivi_quantize_v launch");
 }
@@ -210,14 +222,16 @@ kivi_status decode_checks(const kivi_dims* dims, const kivi_cache* cache, int32_
 
 kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                           int64_t T, const void* q, float sm_scale, float* out, void* ws,
-                          size_t ws_bytes, int32_t n_split, void* stream) {
+                          size_t ws_bytes, int32_t n_split, void* stream,
+                          const int32_t* lens = nullptr) {
   kivi::LayerView L;
   kivi::DecodePlan plan;
   kivi_status st = decode_checks(dims, cache, layer, T, q, sm_scale, out, ws, ws_bytes, n_split,
                                  &L, &plan);
   if (st != KIVI_OK) return st;
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
-                                     out, ws, plan, nullptr, static_cast<hipStream_t>(stream));
+                                     out, ws, plan, nullptr, kivi::Lens{lens, T},
+                                     static_cast<hipStream_t>(stream));
   return device_status(e, "kivi_decode_attn launch");
 }
 
@@ -410,9 +424,9 @@ kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int3
   return quantize_common(dims, cache, layer, v, T, ld_tokens, stream, false);
 }
 
-kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
-                              int64_t T_before, const void* k_new, const void* v_new,
-                              void* stream) {
+kivi_status append_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                          int64_t T_before, const void* k_new, const void* v_new, void* stream,
+                          const int32_t* lens) {
   kivi_status st = check_common(dims, cache, layer);
   if (st != KIVI_OK) return st;
   st = append_checks(dims, T_before, k_new, v_new);
@@ -420,8 +434,15 @@ kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, in
   const kivi::LayerView L = layer_view(dims, cache, layer);
   hipError_t e = kivi::launch_append_flush(L, T_before, static_cast<const __half*>(k_new),
                                            static_cast<const __half*>(v_new),
+                                           kivi::Lens{lens, T_before}, false,
                                            static_cast<hipStream_t>(stream));
   return device_status(e, "kivi_append_flush launch");
+}
+
+kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                              int64_t T_before, const void* k_new, const void* v_new,
+                              void* stream) {
+  return append_common(dims, cache, layer, T_before, k_new, v_new, stream, nullptr);
 }
 
 kivi_status kivi_decode_workspace_bytes_split(const kivi_dims* dims, int64_t T, int32_t n_split,
@@ -487,18 +508,85 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
   const __half* kn = static_cast<const __half*>(k_new);
   const __half* vn = static_cast<const __half*>(v_new);
   const kivi::AppendPlan ap = kivi::plan_append(L, T_before);
+  const kivi::Lens none{nullptr, 0};
   if (ap.flush) {
     // the window is full: flush it (and store the new row) first, then attend
-    hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, s);
+    hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, none, false, s);
     if (e != hipSuccess) return device_status(e, "kivi_append_decode flush launch");
     e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale, out,
-                            workspace, plan, nullptr, s);
+                            workspace, plan, nullptr, none, s);
     return device_status(e, "kivi_append_decode launch");
   }
   const kivi::NewRow nr{kn, vn, ap.slot};
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
-                                     out, workspace, plan, &nr, s);
+                                     out, workspace, plan, &nr, none, s);
   return device_status(e, "kivi_append_decode launch");
+}
+
+// ---- ragged batches ------------------------------------------------------------------
+
+kivi_status kivi_quantize_k_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                                   const void* k, const int32_t* lens, int64_t T_hi,
+                                   int64_t ld_tokens, void* stream) {
+  kivi_status st = check_lens(lens);
+  if (st != KIVI_OK) return st;
+  return quantize_common(dims, cache, layer, k, T_hi, ld_tokens, stream, true, lens);
+}
+
+kivi_status kivi_quantize_v_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                                   const void* v, const int32_t* lens, int64_t T_hi,
+                                   int64_t ld_tokens, void* stream) {
+  kivi_status st = check_lens(lens);
+  if (st != KIVI_OK) return st;
+  return quantize_common(dims, cache, layer, v, T_hi, ld_tokens, stream, false, lens);
+}
+
+kivi_status kivi_append_flush_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                     int32_t layer, const int32_t* T_before, int64_t T_hi,
+                                     const void* k_new, const void* v_new, void* stream) {
+  kivi_status st = check_lens(T_before);
+  if (st != KIVI_OK) return st;
+  return append_common(dims, cache, layer, T_hi, k_new, v_new, stream, T_before);
+}
+
+kivi_status kivi_decode_attn_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                    int32_t layer, const int32_t* lens, int64_t T_hi,
+                                    const void* q, float sm_scale, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  kivi_status st = check_lens(lens);
+  if (st != KIVI_OK) return st;
+  return decode_common(dims, cache, layer, T_hi, q, sm_scale, out, workspace, workspace_bytes,
+                       0, stream, lens);
+}
+
+kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                      int32_t layer, const int32_t* T_before, int64_t T_hi,
+                                      const void* k_new, const void* v_new, const void* q,
+                                      float sm_scale, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  kivi_status st = check_lens(T_before);
+  if (st != KIVI_OK) return st;
+  st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  st = append_checks(dims, T_hi, k_new, v_new);
+  if (st != KIVI_OK) return st;
+  kivi::LayerView L;
+  kivi::DecodePlan plan;
+  st = decode_checks(dims, cache, layer, T_hi + 1, q, sm_scale, out, workspace, workspace_bytes,
+                     0, &L, &plan);
+  if (st != KIVI_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const __half* kn = static_cast<const __half*>(k_new);
+  const __half* vn = static_cast<const __half*>(v_new);
+  const kivi::Lens ln{T_before, T_hi};
+  // the sequences whose window is full flush first (the others' blocks return at once);
+  // the decode launch then stores every new row and attends
+  hipError_t e = kivi::launch_append_flush(L, T_hi, kn, vn, ln, true, s);
+  if (e != hipSuccess) return device_status(e, "kivi_append_decode_varlen flush launch");
+  const kivi::NewRow nr{kn, vn, kivi::plan_append(L, T_hi).slot};
+  e = kivi::launch_decode(L, dims->q_heads, T_hi + 1, static_cast<const __half*>(q), sm_scale,
+                          out, workspace, plan, &nr, ln, s);
+  return device_status(e, "kivi_append_decode_varlen launch");
 }
 
 kivi_status kivi_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes,

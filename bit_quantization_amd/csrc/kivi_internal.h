@@ -37,7 +37,7 @@ struct LayerView {
 // Window tokens after Tk tokens (those after the sink): the full window flushes
 // whole, so r = ((Tk - 1) mod R) + 1; with group aging only its oldest G tokens
 // leave, so r = Tk up to R and R - G + ((Tk - R - 1) mod G) + 1 after.
-inline int64_t window_len(int64_t Tk, int R, int G, int aging) {
+__host__ __device__ inline int64_t window_len(int64_t Tk, int R, int G, int aging) {
   if (Tk == 0) return 0;
   if (!aging) return (Tk - 1) % R + 1;
   return Tk <= R ? Tk : R - G + (Tk - R - 1) % G + 1;
@@ -52,9 +52,9 @@ inline int64_t window_len(int64_t Tk, int R, int G, int aging) {
 struct TokenSplit {
   int64_t ns, Tq, r;
   int ring;
-  int64_t fp16_rows() const { return ns + r; }   // sink rows and window tokens
+  __host__ __device__ int64_t fp16_rows() const { return ns + r; }   // sink rows and window tokens
 };
-inline TokenSplit split_tokens(const LayerView& L, int64_t T) {
+__host__ __device__ inline TokenSplit split_tokens(const LayerView& L, int64_t T) {
   TokenSplit t;
   t.ns = T < L.S ? T : L.S;
   const int64_t Tk = T - t.ns;
@@ -75,7 +75,7 @@ struct AppendPlan {
   int slot;       // residual row of the new token
   int64_t t0;     // history token of the oldest window token (flush only)
 };
-inline AppendPlan plan_append(const LayerView& L, int64_t T_before) {
+__host__ __device__ inline AppendPlan plan_append(const LayerView& L, int64_t T_before) {
   if (T_before < L.S) return AppendPlan{0, 0, 0, (int)T_before, 0};
   const int64_t Tk = T_before - L.S;
   const int64_t r = window_len(Tk, L.R, L.G, L.aging);
@@ -85,18 +85,35 @@ inline AppendPlan plan_append(const LayerView& L, int64_t T_before) {
   return AppendPlan{1, L.aging ? L.G : L.R, L.S + (int)(Tq % L.R), slot, Tq};
 }
 
+// Per-sequence token counts of a ragged batch: device int32 [B] holding T_b (or T_b
+// - 1 for a decode step that appends), clamped on the device into [lo, hi] so that
+// every access stays inside the cache whatever the array holds.
+struct Lens {
+  const int32_t* p;     // nullptr: every sequence has the call's uniform T
+  int64_t hi;           // upper bound the launch was planned for
+  __device__ int64_t get(int64_t b, int64_t lo) const {
+    const int64_t t = p[b];
+    return t < lo ? lo : t > hi ? hi : t;
+  }
+};
+
 // ---- launchers (return hipGetLastError() of the launch) -------------------------
 
 // Prefill of T tokens of src ([B][H][ld][d]): the sink tokens to residual rows
 // [0, ns), the history tokens [S, S + Tq) quantized, the last r to their ring rows.
+// With lens.p set, sequence b has lens.get(b, 0) tokens and T is lens.hi.
 hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
-                             hipStream_t s);
+                             Lens lens, hipStream_t s);
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
-                             hipStream_t s);
+                             Lens lens, hipStream_t s);
 
 // Append one row; when the window is full, flush its oldest tokens first (plan_append).
+// With lens.p set, sequence b appends at T_before = lens.get(b, 0) (T_before is
+// lens.hi), and flush_only leaves the new row of a sequence that does not flush to the
+// decode launch that follows.
 hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __half* k_new,
-                               const __half* v_new, hipStream_t s);
+                               const __half* v_new, Lens lens, bool flush_only,
+                               hipStream_t s);
 
 // Decode attention: split-K partials + fixed-order merge.
 struct DecodePlan {
@@ -116,9 +133,12 @@ struct NewRow {
   const __half* v;
   int slot;
 };
+// With lens.p set, sequence b attends over lens.get(b, 1) tokens (T = lens.hi), or,
+// with new_row set, appends at T_before = lens.get(b, 0) and attends over T_before + 1
+// (T = lens.hi + 1); new_row->slot is then found per sequence.
 hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __half* q,
                          float sm_scale, float* out, void* ws, const DecodePlan& plan,
-                         const NewRow* new_row, hipStream_t s);
+                         const NewRow* new_row, Lens lens, hipStream_t s);
 
 // ---- FP8 KV codec -----------------------------------------------------------------
 // One layer of an FP8 cache: Key codes [B][H][Tmax][d], Value codes in 32-token runs

@@ -282,16 +282,20 @@ __device__ __forceinline__ void store_fp16_rows(const LayerView& L, const __half
 // Items of one (b, h): the Tq/G Key groups (or Tq/16 Value runs) of the tokens after
 // the sink, then one item that copies the sink tokens and the r window tokens into
 // their residual rows.  grid = (ceil(items /
-// (QW*npw)), B*H); workgroup x takes items QW*npw*x .. +QW*npw - 1, its waves
-// interleaved (wave w takes item QW*npw*x + QW*i + w for i < npw).
+// (QW*npw)), B*H) for the items of T tokens; workgroup x takes items QW*npw*x ..
+// +QW*npw - 1, its waves interleaved (wave w takes item QW*npw*x + QW*i + w for
+// i < npw).  A ragged batch gives sequence b lens.get(b, 0) <= T tokens, so its pairs
+// have no more items than the grid covers.
 template <int BITS, int G>
 __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const __half* __restrict__ src,
-                                                            int64_t ld, int64_t Tq, int64_t r,
-                                                            int64_t ns, int ring, int npw) {
+                                                            int64_t ld, int64_t T, Lens lens,
+                                                            int npw) {
   __shared__ alignas(16) uint8_t lds[QW][G * D];
   __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const TokenSplit ts = split_tokens(L, lens.p ? lens.get(pair / L.H, 0) : T);
+  const int64_t Tq = ts.Tq;
   const __half* s0 = src + pair * ld * D;
   const __half* s = s0 + (int64_t)L.S * D;        // the tokens after the sink
   const int64_t ngroups = Tq / G;
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
                            L.k_scale + pair * L.ks_pair() + g * D,
                            L.k_zero + pair * L.ks_pair() + g * D, lds[wave]));
     } else if (g == ngroups) {
-      store_fp16_rows(L, s0, s + Tq * D, L.k_resid + pair * L.rs_pair(), ns, r, ring);
+      store_fp16_rows(L, s0, s + Tq * D, L.k_resid + pair * L.rs_pair(), ts.ns, ts.r, ts.ring);
     }
   }
   raise_scale_max<QW>(L.scale_max + 2 * pair, smx, red);
@@ -313,12 +317,14 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
 // As prefill_k_kernel, over the Value runs.
 template <int BITS, int GV>
 __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const __half* __restrict__ src,
-                                                            int64_t ld, int64_t Tq, int64_t r,
-                                                            int64_t ns, int ring, int npw) {
+                                                            int64_t ld, int64_t T, Lens lens,
+                                                            int npw) {
   __shared__ alignas(16) uint8_t lds[QW][V_LDS];
   __shared__ float red[QW];
   const int64_t pair = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const TokenSplit ts = split_tokens(L, lens.p ? lens.get(pair / L.H, 0) : T);
+  const int64_t Tq = ts.Tq;
   const __half* s0 = src + pair * ld * D;
   const __half* s = s0 + (int64_t)L.S * D;        // the tokens after the sink
   const int64_t nruns = Tq / kVRun;
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const _
                            L.v_scale + pair * L.vs_pair() + j * kVRun * (D / GV),
                            L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds[wave]));
     } else if (j == nruns) {
-      store_fp16_rows(L, s0, s + Tq * D, L.v_resid + pair * L.rs_pair(), ns, r, ring);
+      store_fp16_rows(L, s0, s + Tq * D, L.v_resid + pair * L.rs_pair(), ts.ns, ts.r, ts.ring);
     }
   }
   raise_scale_max<QW>(L.scale_max + 2 * pair + 1, smx, red);
@@ -350,14 +356,25 @@ int items_per_wave(int64_t items, int pairs) {
 // quantize the Key groups of the n oldest window tokens (residual rows [first,
 // first + n)) and blocks [n/G, n/G + n/16) their Value runs, into the history at token
 // t0.  The blocks that read row `first` (Key group 0 and Value run 0) then store the
-// new row there (slot == first) after their reads.
+// new row there (slot == first) after their reads.  A ragged batch (lens.p set) plans
+// each sequence on the device: the grid has the blocks of the largest flush, blocks a
+// sequence does not need return at once, and with flush_only a sequence that does
+// not flush leaves its new row to the decode launch that follows.
 template <int BITS, int G, int GV>
 __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int slot, int n,
                                                     const __half* __restrict__ k_new,
-                                                    const __half* __restrict__ v_new) {
+                                                    const __half* __restrict__ v_new, Lens lens,
+                                                    int flush_only) {
   constexpr int LBYTES = G * D > V_LDS ? G * D : V_LDS;
   __shared__ alignas(16) uint8_t lds[LBYTES];
   const int64_t pair = blockIdx.y;
+  if (lens.p) {
+    const AppendPlan ap = plan_append(L, lens.get(pair / L.H, 0));
+    n = ap.flush ? ap.n : 0;
+    slot = ap.slot;
+    t0 = ap.t0;
+    if (n == 0 ? (flush_only || blockIdx.x > 0) : (int)blockIdx.x >= n / G + n / kVRun) return;
+  }
   const __half* kn = k_new + pair * D;
   const __half* vn = v_new + pair * D;
   __half* kr = L.k_resid + pair * L.rs_pair() + (int64_t)slot * D;
@@ -424,7 +441,7 @@ bool dispatch_gv(int Gv, F&& f) {
 }  // namespace
 
 hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, int64_t T,
-                             hipStream_t s) {
+                             Lens lens, hipStream_t s) {
   const TokenSplit ts = split_tokens(L, T);
   const int64_t Tq = ts.Tq;
   const int pairs = L.B * L.H;
@@ -435,7 +452,7 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
   const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value>), grid,
-                       dim3(64 * QW), 0, s, L, src, ld, Tq, ts.r, ts.ns, ts.ring, npw);
+                       dim3(64 * QW), 0, s, L, src, ld, T, lens, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -443,7 +460,7 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
 }
 
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
-                             hipStream_t s) {
+                             Lens lens, hipStream_t s) {
   const TokenSplit ts = split_tokens(L, T);
   const int64_t Tq = ts.Tq;
   const int pairs = L.B * L.H;
@@ -455,10 +472,10 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
   bool ok = dispatch_gv(L.Gv, [&](auto gv) {
     if (L.bits == 2)
       hipLaunchKernelGGL((prefill_v_kernel<2, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, Tq, ts.r, ts.ns, ts.ring, npw);
+                         src, ld, T, lens, npw);
     else
       hipLaunchKernelGGL((prefill_v_kernel<4, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, Tq, ts.r, ts.ns, ts.ring, npw);
+                         src, ld, T, lens, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -466,17 +483,19 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
 }
 
 hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __half* k_new,
-                               const __half* v_new, hipStream_t s) {
+                               const __half* v_new, Lens lens, bool flush_only,
+                               hipStream_t s) {
   const AppendPlan ap = plan_append(L, T_before);
-  const int n = ap.flush ? ap.n : 0;
+  int n = ap.flush ? ap.n : 0;
   const int slot = ap.slot;
   const int64_t t0 = ap.t0;
+  if (lens.p) n = L.aging ? L.G : L.R;           // room for any sequence's flush
   const dim3 grid(n ? (unsigned)(n / L.G + n / kVRun) : 1u, (unsigned)(L.B * L.H));
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     return dispatch_gv(L.Gv, [&](auto gv) {
       hipLaunchKernelGGL(
           (append_kernel<decltype(b)::value, decltype(g)::value, decltype(gv)::value>), grid,
-          dim3(64), 0, s, L, t0, slot, n, k_new, v_new);
+          dim3(64), 0, s, L, t0, slot, n, k_new, v_new, lens, flush_only ? 1 : 0);
       return true;
     });
   });

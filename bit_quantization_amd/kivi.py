@@ -24,7 +24,9 @@ STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_E
 
 EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
            "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
-           "kivi_append_decode", "kivi_stream_read", "kivi_fp8_cache_sizes",
+           "kivi_append_decode", "kivi_quantize_k_varlen", "kivi_quantize_v_varlen",
+           "kivi_append_flush_varlen", "kivi_decode_attn_varlen", "kivi_append_decode_varlen",
+           "kivi_stream_read", "kivi_fp8_cache_sizes",
            "kivi_fp8_quantize", "kivi_fp8_append", "kivi_fp8_decode_workspace_bytes",
            "kivi_fp8_decode_attn",
            "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
@@ -91,6 +93,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_decode_attn": (I32, [D, C, I32, I64, P, F32, P, P, SZ, P]),
         "kivi_decode_attn_split": (I32, [D, C, I32, I64, P, F32, P, P, SZ, I32, P]),
         "kivi_append_decode": (I32, [D, C, I32, I64, P, P, P, F32, P, P, SZ, P]),
+        "kivi_quantize_k_varlen": (I32, [D, C, I32, P, P, I64, I64, P]),
+        "kivi_quantize_v_varlen": (I32, [D, C, I32, P, P, I64, I64, P]),
+        "kivi_append_flush_varlen": (I32, [D, C, I32, P, I64, P, P, P]),
+        "kivi_decode_attn_varlen": (I32, [D, C, I32, P, I64, P, F32, P, P, SZ, P]),
+        "kivi_append_decode_varlen": (I32, [D, C, I32, P, I64, P, P, P, F32, P, P, SZ, P]),
         "kivi_stream_read": (I32, [P, SZ, P, SZ, P]),
         "kivi_fp8_cache_sizes": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(SZ)]),
         "kivi_fp8_quantize": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(kivi_fp8_cache),
@@ -275,6 +282,80 @@ def kivi_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k_ne
                                    _ptr(out, torch.float32, "out", nq),
                                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                    _stream(stream)))
+
+
+# ---- ragged batches: per-sequence token counts in a device int32 [B] tensor ----------
+
+def _lens(lens, dims):
+    return _ptr(lens, torch.int32, "lens", dims.batch)
+
+
+def kivi_quantize_k_varlen(dims: Dims, cache: Cache, layer: int, k: torch.Tensor,
+                           lens: torch.Tensor, T_hi: int, ld_tokens: int | None = None,
+                           stream=None):
+    ld = T_hi if ld_tokens is None else ld_tokens
+    need = dims.batch * dims.kv_heads * ld * dims.head_dim if T_hi else None
+    _check(_lib.kivi_quantize_k_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                       _ptr(k, torch.float16, "k", need), _lens(lens, dims),
+                                       T_hi, ld, _stream(stream)))
+
+
+def kivi_quantize_v_varlen(dims: Dims, cache: Cache, layer: int, v: torch.Tensor,
+                           lens: torch.Tensor, T_hi: int, ld_tokens: int | None = None,
+                           stream=None):
+    ld = T_hi if ld_tokens is None else ld_tokens
+    need = dims.batch * dims.kv_heads * ld * dims.head_dim if T_hi else None
+    _check(_lib.kivi_quantize_v_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                       _ptr(v, torch.float16, "v", need), _lens(lens, dims),
+                                       T_hi, ld, _stream(stream)))
+
+
+def kivi_append_flush_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
+                             T_hi: int, k_new, v_new, stream=None):
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    _check(_lib.kivi_append_flush_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                         _lens(T_before, dims), T_hi,
+                                         _ptr(k_new, torch.float16, "k_new", need),
+                                         _ptr(v_new, torch.float16, "v_new", need),
+                                         _stream(stream)))
+
+
+def kivi_decode_attn_varlen(dims: Dims, cache: Cache, layer: int, lens: torch.Tensor, T_hi: int,
+                            q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                            workspace: torch.Tensor, stream=None):
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    _check(_lib.kivi_decode_attn_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                        _lens(lens, dims), T_hi, _ptr(q, torch.float16, "q", nq),
+                                        ctypes.c_float(sm_scale),
+                                        _ptr(out, torch.float32, "out", nq),
+                                        _ptr(workspace, torch.uint8, "workspace"),
+                                        workspace.numel(), _stream(stream)))
+
+
+def prepare_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
+                                 T_hi: int, k_new, v_new, q: torch.Tensor, sm_scale: float,
+                                 out: torch.Tensor, workspace: torch.Tensor, stream=None):
+    """kivi_append_decode_varlen with its arguments marshalled once (see
+    prepare_append_decode)."""
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    args = (ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, _lens(T_before, dims), T_hi,
+            _ptr(k_new, torch.float16, "k_new", need), _ptr(v_new, torch.float16, "v_new", need),
+            _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
+            _ptr(out, torch.float32, "out", nq), _ptr(workspace, torch.uint8, "workspace"),
+            workspace.numel(), _stream(stream))
+    fn = _lib.kivi_append_decode_varlen
+
+    def call():
+        _check(fn(*args))
+    return call
+
+
+def kivi_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
+                              T_hi: int, k_new, v_new, q: torch.Tensor, sm_scale: float,
+                              out: torch.Tensor, workspace: torch.Tensor, stream=None):
+    prepare_append_decode_varlen(dims, cache, layer, T_before, T_hi, k_new, v_new, q, sm_scale,
+                                 out, workspace, stream)()
 
 
 def prepare_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k_new, v_new,

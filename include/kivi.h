@@ -199,6 +199,53 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
                                const void* q, float sm_scale, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Ragged batches ("KV Cache Quantization (KIVI & FP4)" §6: serving engines hold
+ * sequences of different lengths in one batch).  Each call below is the call of the
+ * same name without _varlen, with sequence b holding its own token count:
+ *   lens / T_before  device int32 [B]: tokens of sequence b (decode: 1 <= lens[b];
+ *                    prefill: 0 <= lens[b]), or tokens before its append.
+ *   T_hi             host upper bound of every entry: the capacity checks, the
+ *                    workspace size and the launch are those of the uniform call at
+ *                    T = T_hi (appends: T_before = T_hi).
+ * The arrays are read on the device: the host cannot check them, so each entry is
+ * clamped into its valid range ([0, T_hi], decode [1, T_hi]) before use; every access
+ * stays inside the cache, and a sequence whose entry was out of range gets an
+ * unspecified result.  All heads of a sequence share its count.  The arrays must stay
+ * valid until the stream has passed the call; the caller updates them (an append
+ * leaves T_before + 1 tokens). */
+
+/* kivi_quantize_k for a ragged batch: sequence b's first lens[b] tokens of k
+ * ([B][H_kv][ld_tokens][d], ld_tokens >= T_hi). */
+kivi_status kivi_quantize_k_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                                   const void* k, const int32_t* lens, int64_t T_hi,
+                                   int64_t ld_tokens, void* stream);
+/* kivi_quantize_v for a ragged batch. */
+kivi_status kivi_quantize_v_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                                   const void* v, const int32_t* lens, int64_t T_hi,
+                                   int64_t ld_tokens, void* stream);
+/* kivi_append_flush for a ragged batch: sequence b appends at T_before[b], flushing
+ * its own window when that is full.  One launch sized for a flush of every sequence. */
+kivi_status kivi_append_flush_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                     int32_t layer, const int32_t* T_before, int64_t T_hi,
+                                     const void* k_new, const void* v_new, void* stream);
+/* kivi_decode_attn for a ragged batch: sequence b attends over its lens[b] tokens.
+ * Workspace: kivi_decode_workspace_bytes(dims, T_hi).  The launch has the workgroups
+ * of a batch of T_hi tokens; each (sequence, KV head) splits its own blocks among
+ * them, so short sequences finish early. */
+kivi_status kivi_decode_attn_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                    int32_t layer, const int32_t* lens, int64_t T_hi,
+                                    const void* q, float sm_scale, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+/* kivi_append_decode for a ragged batch: two launches (the flushes of the sequences
+ * whose window is full, then decode attention that stores every new row); equal to
+ * kivi_append_flush_varlen followed by kivi_decode_attn_varlen over T_before[b] + 1.
+ * Workspace: kivi_decode_workspace_bytes(dims, T_hi + 1). */
+kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                      int32_t layer, const int32_t* T_before, int64_t T_hi,
+                                      const void* k_new, const void* v_new, const void* q,
+                                      float sm_scale, float* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* Workspace bytes kivi_decode_attn needs for T cached tokens (host-only). */
 kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t* bytes);
 

@@ -1,0 +1,247 @@
+"""GPU parity of ragged batches: every sequence of the batch has its own token count,
+held in a device int32 array (the *_varlen entry points).
+
+The oracle of a ragged batch is one oracle cache per sequence (oracle/kivi_ref.py,
+LayerCache with batch 1): sequences share nothing.  Bar: every cache byte of every
+sequence bit-exact, attention within |gpu - ref| <= 2e-3 + 1e-3 |ref|.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.test_gpu_parity import assert_close, rand_kv
+from tests.test_gpu_sink import capacity, compare_sink_cache, sink_dims
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def kv():
+    from bit_quantization_amd import kivi
+    return kivi
+
+
+def lens_tensor(lens):
+    return torch.tensor(lens, dtype=torch.int32, device="cuda")
+
+
+def seq_oracle(dims, K, V, b, T):
+    oc = O.LayerCache(1, dims.kv_heads, D, dims.bits, dims.group_k, dims.group_v, dims.residual,
+                      dims.max_tokens, sink=dims.sink, aging=dims.aging)
+    oc.prefill(K[b:b + 1, :, :T].cpu().numpy(), V[b:b + 1, :, :T].cpu().numpy())
+    return oc
+
+
+def varlen_prefill(dims, K, V, lens):
+    k = kv()
+    cache = k.Cache(dims)
+    T_hi = max(lens)
+    lt = lens_tensor(lens)
+    k.kivi_quantize_k_varlen(dims, cache, 0, K, lt, T_hi, K.shape[2])
+    k.kivi_quantize_v_varlen(dims, cache, 0, V, lt, T_hi, V.shape[2])
+    return cache
+
+
+def check_all(cache, K, V, lens):
+    torch.cuda.synchronize()
+    for b, T in enumerate(lens):
+        compare_sink_cache(cache, seq_oracle(cache.dims, K, V, b, T), T, seq=b)
+
+
+CASES = [
+    # bits, G, R, S, aging, lens
+    (2, 32, 128, 0, "window", [1000, 37, 129, 256, 1, 0]),
+    (4, 64, 128, 4, "window", [700, 3, 4, 5, 131, 1301]),
+    (2, 32, 128, 0, "group", [1000, 129, 97, 160, 161]),
+    (4, 32, 64, 7, "group", [7, 300, 71, 72, 0]),
+]
+
+
+@pytest.mark.parametrize("bits,G,R,S,aging,lens", CASES)
+def test_varlen_prefill_is_bit_exact(bits, G, R, S, aging, lens):
+    B, H = len(lens), 2
+    T_hi = max(lens)
+    dims = sink_dims(bits, G, 128, R, S, B, H, 1, capacity(T_hi, R), aging)
+    K, V = rand_kv(B, H, T_hi + 5, D, seed=T_hi + B)
+    check_all(varlen_prefill(dims, K, V, lens), K, V, lens)
+
+
+@pytest.mark.parametrize("bits,G,R,S,aging,lens", CASES[:3])
+def test_varlen_appends_equal_per_sequence_prefill(bits, G, R, S, aging, lens):
+    # every sequence appends from its own length; the sequences cross their flushes at
+    # different steps
+    k = kv()
+    B, H = len(lens), 2
+    steps = R + 2 * G + 3
+    T_end = max(lens) + steps
+    dims = sink_dims(bits, G, 128, R, S, B, H, 1, capacity(T_end, R), aging)
+    K, V = rand_kv(B, H, T_end, D, seed=steps + B)
+    cache = varlen_prefill(dims, K, V, lens)
+    cur = list(lens)
+    for _ in range(steps):
+        lt = lens_tensor(cur)
+        kn = torch.stack([K[b, :, cur[b]] for b in range(B)]).contiguous()
+        vn = torch.stack([V[b, :, cur[b]] for b in range(B)]).contiguous()
+        k.kivi_append_flush_varlen(dims, cache, 0, lt, max(cur), kn, vn)
+        cur = [t + 1 for t in cur]
+    check_all(cache, K, V, cur)
+
+
+DECODE = [
+    # bits, G, R, S, aging, g, lens
+    (2, 32, 128, 0, "window", 4, [1000, 37, 129, 256, 1, 2048]),
+    (4, 64, 128, 4, "window", 2, [700, 3, 4, 5, 131, 1301]),
+    (2, 32, 128, 0, "group", 8, [1000, 129, 97, 160, 161]),
+    (4, 32, 64, 7, "group", 1, [7, 3000, 71, 72]),
+    (2, 32, 128, 0, "window", 4, [4096, 1]),
+]
+
+
+@pytest.mark.parametrize("bits,G,R,S,aging,g,lens", DECODE)
+def test_varlen_decode_matches_oracle(bits, G, R, S, aging, g, lens):
+    k = kv()
+    B, H = len(lens), 2
+    T_hi = max(lens)
+    dims = sink_dims(bits, G, 128, R, S, B, H, g, capacity(T_hi, R), aging)
+    K, V = rand_kv(B, H, T_hi, D, seed=T_hi + g, scale=3.0)
+    K[:, :, :, 11] *= 25
+    cache = varlen_prefill(dims, K, V, lens)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(B + g)
+    q = torch.randn((B, H * g, D), generator=gq, device="cuda").to(torch.float16)
+    out = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
+    ws = k.new_workspace(dims, T_hi)
+    sm = 1 / math.sqrt(D)
+    k.kivi_decode_attn_varlen(dims, cache, 0, lens_tensor(lens), T_hi, q, sm, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    qn = q.cpu().numpy()
+    for b, T in enumerate(lens):
+        ref = seq_oracle(dims, K, V, b, T).attend(qn[b:b + 1], sm)
+        assert_close(got[b:b + 1], ref, f"varlen decode sequence {b} T={T}")
+    assert int(torch.count_nonzero(ws[:B * H * 256])) == 0, "arrival counters not reset"
+
+
+def test_varlen_sequence_of_uniform_lengths_equals_uniform_call():
+    # a ragged call whose lengths are all equal writes the uniform call's bytes and
+    # outputs (to float32 rounding)
+    k = kv()
+    B, H, g, T = 3, 2, 4, 777
+    dims = sink_dims(2, 32, 128, 128, 0, B, H, g, capacity(T, 128))
+    K, V = rand_kv(B, H, T, D, seed=1)
+    a = varlen_prefill(dims, K, V, [T] * B)
+    b_ = k.Cache(dims)
+    k.kivi_quantize_k(dims, b_, 0, K, T, T)
+    k.kivi_quantize_v(dims, b_, 0, V, T, T)
+    torch.cuda.synchronize()
+    for name in k.BUFFERS:
+        assert torch.equal(a.view(name).cpu(), b_.view(name).cpu()), name
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(5)
+    q = torch.randn((B, H * g, D), generator=gq, device="cuda").to(torch.float16)
+    oa = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    k.kivi_decode_attn_varlen(dims, a, 0, lens_tensor([T] * B), T, q, 0.1, oa,
+                              k.new_workspace(dims, T))
+    k.kivi_decode_attn(dims, b_, 0, T, q, 0.1, ob, k.new_workspace(dims, T))
+    torch.cuda.synchronize()
+    assert np.allclose(oa.cpu().numpy(), ob.cpu().numpy(), rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("aging,S", [("window", 0), ("group", 5)])
+def test_varlen_append_decode_matches_oracle(aging, S):
+    # the ragged decode step against append_flush_varlen + decode_attn_varlen on a
+    # second cache (outputs to float32 rounding, caches bit-identical) and against the
+    # oracle at sampled steps
+    k = kv()
+    bits, G, R, g = 2, 32, 64, 4
+    lens = [2, 70, 63, 64, 200]
+    B, H = len(lens), 2
+    steps = R + G + 4
+    T_end = max(lens) + steps
+    dims = sink_dims(bits, G, 128, R, S, B, H, g, capacity(T_end, R), aging)
+    K, V = rand_kv(B, H, T_end, D, seed=7 + S)
+    a = varlen_prefill(dims, K, V, lens)
+    b_ = varlen_prefill(dims, K, V, lens)
+    wa = k.new_workspace(dims, T_end)
+    wb = k.new_workspace(dims, T_end)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(11)
+    oa = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    cur = list(lens)
+    for step in range(steps):
+        q = torch.randn((B, H * g, D), generator=gq, device="cuda").to(torch.float16)
+        lt = lens_tensor(cur)
+        kn = torch.stack([K[b, :, cur[b]] for b in range(B)]).contiguous()
+        vn = torch.stack([V[b, :, cur[b]] for b in range(B)]).contiguous()
+        k.kivi_append_decode_varlen(dims, a, 0, lt, max(cur), kn, vn, q, 0.09, oa, wa)
+        k.kivi_append_flush_varlen(dims, b_, 0, lt, max(cur), kn, vn)
+        after = lens_tensor([t + 1 for t in cur])
+        k.kivi_decode_attn_varlen(dims, b_, 0, after, max(cur) + 1, q, 0.09, ob, wb)
+        torch.cuda.synchronize()
+        assert np.allclose(oa.cpu().numpy(), ob.cpu().numpy(), rtol=1e-5, atol=1e-6), step
+        cur = [t + 1 for t in cur]
+        if step in (0, R - 2, steps - 1):
+            got = oa.cpu().numpy()
+            for b, T in enumerate(cur):
+                ref = seq_oracle(dims, K, V, b, T).attend(q[b:b + 1].cpu().numpy(), 0.09)
+                assert_close(got[b:b + 1], ref, f"varlen step {step} sequence {b}")
+    for name in k.BUFFERS:
+        assert torch.equal(a.view(name).cpu(), b_.view(name).cpu()), f"{name} differs"
+    check_all(a, K, V, cur)
+
+
+def test_varlen_out_of_range_entries_stay_inside_the_cache():
+    # entries beyond T_hi (or negative) are clamped on the device: the call completes
+    # and the in-range sequences are unaffected
+    k = kv()
+    lens = [300, 77, 5]
+    B, H, g = 3, 1, 2
+    T_hi = max(lens)
+    dims = sink_dims(2, 32, 128, 128, 0, B, H, g, capacity(T_hi, 128))
+    K, V = rand_kv(B, H, T_hi, D, seed=3)
+    cache = varlen_prefill(dims, K, V, lens)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(6)
+    q = torch.randn((B, H * g, D), generator=gq, device="cuda").to(torch.float16)
+    out = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
+    bad = lens_tensor([300, 1 << 30, -5])
+    k.kivi_decode_attn_varlen(dims, cache, 0, bad, T_hi, q, 0.1, out, k.new_workspace(dims, T_hi))
+    torch.cuda.synchronize()
+    ref = seq_oracle(dims, K, V, 0, 300).attend(q[0:1].cpu().numpy(), 0.1)
+    assert_close(out[0:1].cpu().numpy(), ref, "in-range sequence")
+    assert np.all(np.isfinite(out.cpu().numpy()))
+
+
+def test_varlen_workload_8b_length_mix_sampled():
+    # the 8B-shaped 32k workload as a ragged batch: sequence b holds
+    # 4096 * (b + 1) tokens (4k .. 32k); sampled pairs recomputed by the oracle
+    k = kv()
+    w = W.get("llama8b_32k")
+    print("[parity] varlen workload llama8b_32k 4k..32k", flush=True)
+    lens = [4096 * (b + 1) for b in range(w.batch)]
+    T_hi = max(lens)
+    dims = k.Dims(1, w.batch, w.kv_heads, w.q_heads, w.head_dim, w.bits, w.group_k, w.group_v,
+                  w.residual, w.max_tokens())
+    Kd, Vd = W.make_kv(w, 0, device="cuda", total_tokens=T_hi)
+    cache = varlen_prefill(dims, Kd, Vd, lens)
+    q = W.make_q(w, 0, 0, device="cuda")
+    out = torch.empty((w.batch, w.q_heads, D), dtype=torch.float32, device="cuda")
+    ws = k.new_workspace(dims, T_hi)
+    k.kivi_decode_attn_varlen(dims, cache, 0, lens_tensor(lens), T_hi, q, w.sm_scale, out, ws)
+    torch.cuda.synchronize()
+    g = w.gqa
+    for b, h in [(0, 1), (3, 4), (7, 6)]:
+        T = lens[b]
+        oc = O.LayerCache(1, 1, D, w.bits, w.group_k, w.group_v, w.residual, w.max_tokens())
+        oc.prefill(Kd[b:b + 1, h:h + 1, :T].cpu().numpy(), Vd[b:b + 1, h:h + 1, :T].cpu().numpy())
+        Tq = oc.Tq
+        assert np.array_equal(cache.view("k_codes")[0, b, h, :Tq].cpu().numpy(), oc.k_codes[0, 0, :Tq])
+        ref = oc.attend(q[b:b + 1, h * g:(h + 1) * g].cpu().numpy(), w.sm_scale)
+        assert_close(out[b, h * g:(h + 1) * g].cpu().numpy(), ref[0], f"varlen pair {(b, h)} T={T}")

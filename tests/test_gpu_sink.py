@@ -42,11 +42,17 @@ def prefill(dims, K, V, T):
     return cache
 
 
-def compare_sink_cache(cache, oc, T):
-    """Every byte the oracle defines at T tokens, for all pairs.  The oracle keeps its
-    window oldest first; the GPU keeps window token Tq + i in ring row (Tq + i) mod R
-    after the S sink rows."""
+def compare_sink_cache(cache, oc, T, seq=None):
+    """Every byte the oracle defines at T tokens, for all pairs (or, with ``seq``, for
+    sequence ``seq`` of the GPU cache against a one-sequence oracle).  The oracle keeps
+    its window oldest first; the GPU keeps window token Tq + i in ring row
+    (Tq + i) mod R after the S sink rows."""
     d = cache.dims
+    sel = slice(None) if seq is None else slice(seq, seq + 1)
+
+    def view(name):
+        return cache.view(name)[0, sel]
+
     S, R = d.sink, d.residual
     assert oc.T == T and oc.aging == d.aging
     ns = min(T, S)
@@ -56,20 +62,20 @@ def compare_sink_cache(cache, oc, T):
     ring = torch.from_numpy(S + (Tq + np.arange(r, dtype=np.int64)) % R)
     for name, sink_ref, win_ref in (("k_resid", oc.k_sink, oc.k_resid),
                                     ("v_resid", oc.v_sink, oc.v_resid)):
-        rows = cache.view(name)[0].cpu()
+        rows = view(name).cpu()
         assert np.array_equal(bits16(rows[:, :, :ns]), bits16(sink_ref[:, :, :ns])), \
             f"{name} sink rows {where}"
         assert np.array_equal(bits16(rows[:, :, ring]), bits16(win_ref[:, :, :r])), \
             f"{name} window rows {where}"
-    g = cache.view("k_codes")[0, :, :, :Tq].cpu().numpy()
+    g = view("k_codes")[:, :, :Tq].cpu().numpy()
     assert np.array_equal(g, oc.k_codes[:, :, :Tq]), "k_codes " + where
-    g = cache.view("v_codes")[0, :, :, :Tq // 16].cpu().numpy()
+    g = view("v_codes")[:, :, :Tq // 16].cpu().numpy()
     assert np.array_equal(g, oc.v_codes[:, :, :Tq // 16]), "v_codes " + where
     for name, n in (("k_scale", Tq // d.group_k), ("k_zero", Tq // d.group_k),
                     ("v_scale", Tq), ("v_zero", Tq)):
-        g = bits16(cache.view(name)[0, :, :, :n])
+        g = bits16(view(name)[:, :, :n])
         assert np.array_equal(g, bits16(getattr(oc, name)[:, :, :n])), f"{name} {where}"
-    sm = cache.view("scale_max")[0].cpu().numpy()
+    sm = view("scale_max").cpu().numpy()
     ks = oc.k_scale[:, :, :Tq // d.group_k].astype(np.float32)
     vs = oc.v_scale[:, :, :Tq].astype(np.float32)
     ref_k = ks.max(axis=(2, 3)) if ks.shape[2] else np.zeros(sm.shape[:2], np.float32)
