@@ -122,6 +122,8 @@ def parse():
                    help="attention-sink tokens kept in float16 at the start of each sequence")
     p.add_argument("--ragged", action="store_true",
                    help="a ragged batch: sequence b holds tokens * (b + 1) / batch tokens")
+    p.add_argument("--paged", type=int, default=0, metavar="P",
+                   help="a paged cache with pages of P tokens in a shuffled pool (0: contiguous)")
     p.add_argument("--aging", default="window", choices=["window", "group"],
                    help="a full window flushes whole (window) or its oldest Key group (group)")
     p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2"],
@@ -485,6 +487,17 @@ def main():
                                                       rng.integers(0, w1.kv_heads, 64))]
     T_hi = max(base)
     base_t = torch.tensor(base, dtype=torch.int32, device="cuda")
+    varlen = args.ragged or args.paged > 0
+    paging = None
+    if args.paged:
+        # every sequence's pages drawn from one shuffled pool (a seeded permutation)
+        per_seq = -(-Tmax // args.paged)
+        perm = np.random.default_rng(0).permutation(w1.batch * per_seq).astype(np.int32)
+        paging = k.Paging(args.paged, per_seq, w1.batch * per_seq,
+                          torch.from_numpy(perm.reshape(w1.batch, per_seq)).cuda())
+
+    def new_cache():
+        return k.PagedCache(dims, paging) if paging else k.Cache(dims)
     # per-sequence token counts before step j of a copy (ragged calls read them on the GPU)
     lens_steps = torch.stack([base_t + j for j in range(steps_per_copy)]).contiguous()
 
@@ -495,10 +508,10 @@ def main():
 
     for c in range(copies):
         K, V = W.make_kv(w1, c, device="cuda", total_tokens=w1.tokens + extra_rows)
-        cache = k.Cache(dims)
-        if args.ragged:
-            k.kivi_quantize_k_varlen(dims, cache, 0, K, base_t, T_hi, K.shape[2])
-            k.kivi_quantize_v_varlen(dims, cache, 0, V, base_t, T_hi, V.shape[2])
+        cache = new_cache()
+        if varlen:
+            k.kivi_quantize_k_varlen(dims, cache, 0, K, base_t, T_hi, K.shape[2], paging=paging)
+            k.kivi_quantize_v_varlen(dims, cache, 0, V, base_t, T_hi, V.shape[2], paging=paging)
         else:
             k.kivi_quantize_k(dims, cache, 0, K, w1.tokens, K.shape[2])
             k.kivi_quantize_v(dims, cache, 0, V, w1.tokens, V.shape[2])
@@ -539,9 +552,10 @@ def main():
         kn, vn = news[c]
         q = qs[i % len(qs)]
         db, ab = step_bytes([t + j for t in base])
-        if args.ragged:
+        if varlen:
             call = k.prepare_append_decode_varlen(dims, caches[c], 0, lens_steps[j], T_before,
-                                                  kn[j], vn[j], q, w1.sm_scale, out, ws)
+                                                  kn[j], vn[j], q, w1.sm_scale, out, ws,
+                                                  paging=paging)
         elif args.n_split:
             def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
                 k.kivi_append_flush(dims, caches[c], 0, T_before, kj, vj)
@@ -605,7 +619,7 @@ def main():
     # Quality versus unquantized fp32 attention on copy 0 (reported, not gated).
     K, V = keep
     quality = None
-    if not args.ragged:
+    if not varlen:
         Tq = w1.tokens + Ts[0]
         qq = qs[0]
         k.kivi_decode_attn(dims, caches[0], 0, Tq, qq, w1.sm_scale, out, ws,
@@ -629,14 +643,16 @@ def main():
     # Secondary: prefill quantization (a1 + a2) of one layer's prompt, re-run on
     # copy 0's fp16 K/V into a scratch cache (HIP events, best of 3).
     Kp, Vp = W.make_kv(w1, 0, device="cuda", total_tokens=T_hi)
-    scratch = k.Cache(dims)
+    scratch = new_cache()
     pre_s = float("inf")
     for _ in range(3):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        if args.ragged:
-            k.kivi_quantize_k_varlen(dims, scratch, 0, Kp, base_t, T_hi, Kp.shape[2])
-            k.kivi_quantize_v_varlen(dims, scratch, 0, Vp, base_t, T_hi, Vp.shape[2])
+        if varlen:
+            k.kivi_quantize_k_varlen(dims, scratch, 0, Kp, base_t, T_hi, Kp.shape[2],
+                                     paging=paging)
+            k.kivi_quantize_v_varlen(dims, scratch, 0, Vp, base_t, T_hi, Vp.shape[2],
+                                     paging=paging)
         else:
             k.kivi_quantize_k(dims, scratch, 0, Kp, w1.tokens, Kp.shape[2])
             k.kivi_quantize_v(dims, scratch, 0, Vp, w1.tokens, Vp.shape[2])
@@ -676,6 +692,8 @@ def main():
                    "residual": w1.residual, "sink": S, "aging": AGING,
                    "lengths": ("tokens * (b + 1) / batch: " + ",".join(map(str, base))
                                if args.ragged else "uniform"),
+                   "paged": (f"pages of {args.paged} tokens, shuffled pool" if args.paged
+                             else "contiguous"),
                    "layer_caches": copies,
                    "n_split": n_split,
                    "step": "append(+flush) + decode attention",
@@ -693,7 +711,7 @@ def main():
                      "p10_p90_launch_us": [round(sorted(dec_ms)[len(dec_ms) // 10] * 1e3, 3),
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
                      "traffic": measured_traffic(w.name)
-                                if S == 0 and AGING == "window" and not args.ragged else None},
+                                if S == 0 and AGING == "window" and not varlen else None},
         "cpu_baseline": cpu,
         "prefill_quantize": prefill,
         "quality": quality,

@@ -481,8 +481,8 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
 // Processes the block items handed out by the queue, starting with `item` (>= n_res),
 // and writes comb[GQA][PSTRIDE] (acc with the Value-zero term folded in, m, l).  The
 // fixed-point exponents come from the pair's largest Key/Value scale, so they hold for
-// any block of the pair.
-template <int BITS, int GQA, int G>
+// any block of the pair.  PAGED: the history is paged (a.L.table is set).
+template <int BITS, int GQA, int G, bool PAGED>
 __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pair, int item, int n_res,
                                 int n_items, int64_t b_lo, int64_t b_hi, int* counter,
                                 WaveLds<(GQA + 3) / 4>& lds, float* comb) {
@@ -495,12 +495,20 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
   constexpr int KB = D * BITS / 8;
   constexpr int VRB = kVRun * BITS / 8;             // Value code bytes per (run, channel)
   PairBufs pb;
-  pb.kc = make_rsrc(L.k_codes + pair * L.kc_pair(), L.kc_pair());
-  pb.ksc = make_rsrc(L.k_scale + pair * L.ks_pair(), L.ks_pair() * 2);
-  pb.kze = make_rsrc(L.k_zero + pair * L.ks_pair(), L.ks_pair() * 2);
-  pb.vc = make_rsrc(L.v_codes + pair * L.vc_pair(), L.vc_pair());
-  pb.vsc = make_rsrc(L.v_scale + pair * L.vs_pair(), L.vs_pair() * 2);
-  pb.vze = make_rsrc(L.v_zero + pair * L.vs_pair(), L.vs_pair() * 2);
+  // the pair's history section; block loads address it with hist(t) (a paged cache
+  // maps each 64-token block through the page table)
+  // (the section geometry of LayerView, with PAGED known at compile time; decode has
+  // G_v == d, so Value scales are one per token)
+  const int64_t sec = PAGED ? pair % L.H : pair;
+  const int64_t rows = PAGED ? L.pages << L.page_log2 : L.Tmax;
+  const int64_t kc = rows * KB, ks = (rows / G) * D;
+  pb.kc = make_rsrc(L.k_codes + sec * kc, kc);
+  pb.ksc = make_rsrc(L.k_scale + sec * ks, ks * 2);
+  pb.kze = make_rsrc(L.k_zero + sec * ks, ks * 2);
+  pb.vc = make_rsrc(L.v_codes + sec * kc, kc);
+  pb.vsc = make_rsrc(L.v_scale + sec * rows, rows * 2);
+  pb.vze = make_rsrc(L.v_zero + sec * rows, rows * 2);
+  auto hist = [&](int64_t t) { return PAGED ? L.hist_token(b, t) : t; };
   pb.off_k = 2 * lo * KB + j * (KB / 4);
   pb.off_v = j * D * VRB + 8 * lo * VRB;
   pb.off_ks = 16 * lo;
@@ -520,7 +528,7 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
   // The first block's loads go out before the exponent set-up so that both overlap.
   BlockRegs<BITS> R;
   if (item < n_items && item != partial_item)
-    load_block<BITS, G, true>(R, pb, block_of(item) * BLK, BLK, j);
+    load_block<BITS, G, true>(R, pb, hist(block_of(item) * BLK), BLK, j);
 
   // Query values of this lane: head 4mt + j, channels 8lo .. 8lo+7.
   float qraw[NMT][8];
@@ -579,10 +587,10 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
   if (item == partial_item) {
     const int64_t blk = a.nblk - 1;
     const int nv = (int)(a.Tq - blk * BLK);
-    load_block<BITS, G, false>(R, pb, blk * BLK, nv, j);
+    load_block<BITS, G, false>(R, pb, hist(blk * BLK), nv, j);
     process_block<BITS, GQA, G, false, false>(R, nv, qk, lc, lds, st, lo, j, pb, 0);
     item = grab_item(counter);
-    if (item < n_items) load_block<BITS, G, true>(R, pb, block_of(item) * BLK, BLK, j);
+    if (item < n_items) load_block<BITS, G, true>(R, pb, hist(block_of(item) * BLK), BLK, j);
   }
   int nxt = item < n_items ? grab_item(counter) : n_items;
   int done = 0;
@@ -590,7 +598,7 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
     const int after = nxt < n_items ? grab_item(counter) : n_items;
     const int64_t blk = block_of(item);
     const int64_t nb = nxt < n_items ? block_of(nxt) : blk;
-    process_block<BITS, GQA, G, true, true>(R, BLK, qk, lc, lds, st, lo, j, pb, nb * BLK);
+    process_block<BITS, GQA, G, true, true>(R, BLK, qk, lc, lds, st, lo, j, pb, hist(nb * BLK));
     if ((++done & 1023) == 0) {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) fold_acc(st, mt, 1.f);
@@ -789,7 +797,9 @@ __device__ __forceinline__ void block_share(int64_t nblk, int n_res, int nw, int
     b_hi = b0 + rest * s / (nw - 1);
   }
 }
-template <int BITS, int GQA, int G>
+// PAGED: a paged cache (args.L.table set); its own instantiation, so that the block
+// loop of a contiguous cache carries no page-table lookup.
+template <int BITS, int GQA, int G, bool PAGED>
 __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_kernel(DecodeArgs args) {
   constexpr int NMT = (GQA + 3) / 4;
   constexpr int WAVES = 4 * waves_per_simd(BITS, GQA, G);
@@ -854,8 +864,8 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
     residual_record<GQA>(rs, comb[WAVES + wave]);
   }
   // blocks (an empty share leaves an empty record: m = -inf, l = 0)
-  quantized_items<BITS, GQA, G>(a, pair, item, n_res, n_items, b_lo, b_hi, &counter,
-                                wl[wave], comb[wave]);
+  quantized_items<BITS, GQA, G, PAGED>(a, pair, item, n_res, n_items, b_lo, b_hi, &counter,
+                                       wl[wave], comb[wave]);
   __syncthreads();
 
   float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
@@ -926,8 +936,12 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   const dim3 grid((unsigned)(P * plan.n_split));
   bool ok = dispatch_decode(L.bits, gqa, L.G, [&](auto b, auto g, auto gg) {
     constexpr int B_ = decltype(b)::value, Q_ = decltype(g)::value, G_ = decltype(gg)::value;
-    hipLaunchKernelGGL((decode_kernel<B_, Q_, G_>), grid, dim3(256 * waves_per_simd(B_, Q_, G_)),
-                       0, s, a);
+    if (L.table)
+      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, true>), grid,
+                         dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, false>), grid,
+                         dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;

@@ -74,12 +74,15 @@ kivi_status check_dims(const kivi_dims* d) {
   return KIVI_OK;
 }
 
-void buffer_sizes(const kivi_dims* d, size_t out[KIVI_NUM_BUFFERS]) {
+// pg == nullptr: contiguous history, one section of max_tokens per (b, h); else one
+// section per KV head holding the page pool.
+void buffer_sizes(const kivi_dims* d, const kivi_paging* pg, size_t out[KIVI_NUM_BUFFERS]) {
   const size_t unit = (size_t)d->layers * d->batch * d->kv_heads;
-  const size_t T = (size_t)d->max_tokens;
-  const size_t codes = unit * T * d->head_dim * d->bits / 8;
-  const size_t kmeta = unit * (T / d->group_k) * d->head_dim * 2;
-  const size_t vmeta = unit * T * (d->head_dim / d->group_v) * 2;
+  const size_t sections = pg ? (size_t)d->layers * d->kv_heads : unit;
+  const size_t T = pg ? (size_t)pg->pages * pg->page_tokens : (size_t)d->max_tokens;
+  const size_t codes = sections * T * d->head_dim * d->bits / 8;
+  const size_t kmeta = sections * (T / d->group_k) * d->head_dim * 2;
+  const size_t vmeta = sections * T * (d->head_dim / d->group_v) * 2;
   const size_t resid = unit * (size_t)(d->sink + d->residual) * d->head_dim * 2;
   out[0] = codes;
   out[1] = kmeta;
@@ -123,10 +126,17 @@ kivi::LayerView shape_view(const kivi_dims* d) {
   return L;
 }
 
-kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer) {
+kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer,
+                           const kivi_paging* pg = nullptr) {
   size_t sz[KIVI_NUM_BUFFERS];
-  buffer_sizes(d, sz);
+  buffer_sizes(d, pg, sz);
   kivi::LayerView L = shape_view(d);
+  if (pg) {
+    L.table = pg->block_table;
+    L.page_log2 = __builtin_ctz((unsigned)pg->page_tokens);
+    L.pages_per_seq = pg->pages_per_seq;
+    L.pages = pg->pages;
+  }
   const size_t Ld = (size_t)d->layers;
   L.k_codes = static_cast<uint8_t*>(c->k_codes) + layer * (sz[0] / Ld);
   L.k_scale = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->k_scale) + layer * (sz[1] / Ld));
@@ -138,6 +148,33 @@ kivi::LayerView layer_view(const kivi_dims* d, const kivi_cache* c, int layer) {
   L.v_resid = reinterpret_cast<__half*>(static_cast<uint8_t*>(c->v_resid) + layer * (sz[7] / Ld));
   L.scale_max = reinterpret_cast<float*>(static_cast<uint8_t*>(c->scale_max) + layer * (sz[8] / Ld));
   return L;
+}
+
+// A paged cache: pages of a power-of-two number of tokens (>= 64, so that a decode
+// block never straddles two), enough pages per sequence for max_tokens, and a page
+// pool whose per-head byte offsets fit the 32-bit buffer offsets of the kernels.
+kivi_status check_page_geometry(const kivi_dims* d, const kivi_paging* pg) {
+  const int32_t P = pg->page_tokens;
+  if (P < 64 || P > (1 << 20) || (P & (P - 1)) != 0)
+    return fail(KIVI_ERR_ARG, "page_tokens = %d must be a power of two in [64, 2^20]", P);
+  if (pg->pages < 1 || pg->pages_per_seq < 1)
+    return fail(KIVI_ERR_ARG, "pages and pages_per_seq must be >= 1");
+  if ((int64_t)pg->pages_per_seq * P < d->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "pages_per_seq * page_tokens = %lld < max_tokens = %lld",
+                (long long)pg->pages_per_seq * P, (long long)d->max_tokens);
+  if (pg->pages * P * (int64_t)(d->head_dim * d->bits / 8) >= ((int64_t)1 << 31))
+    return fail(KIVI_ERR_UNSUPPORTED, "a KV head's page pool holds 2^31 bytes or more");
+  return KIVI_OK;
+}
+
+kivi_status check_paging(const kivi_dims* d, const kivi_paging* pg) {
+  if (!pg) return KIVI_OK;
+  kivi_status st = check_page_geometry(d, pg);
+  if (st != KIVI_OK) return st;
+  if (!pg->block_table) return fail(KIVI_ERR_ARG, "block_table is NULL");
+  if ((reinterpret_cast<uintptr_t>(pg->block_table) & 3u) != 0)
+    return fail(KIVI_ERR_ALIGN, "block_table is not 4-byte aligned");
+  return KIVI_OK;
 }
 
 kivi_status check_common(const kivi_dims* d, const kivi_cache* c, int32_t layer) {
@@ -167,8 +204,10 @@ kivi_status check_lens(const int32_t* lens) {
 // lens == nullptr: every sequence has T tokens; else sequence b has lens[b] <= T.
 kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                             const void* x, int64_t T, int64_t ld, void* stream, bool keys,
-                            const int32_t* lens = nullptr) {
+                            const int32_t* lens = nullptr, const kivi_paging* pg = nullptr) {
   kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  st = check_paging(dims, pg);
   if (st != KIVI_OK) return st;
   if (T < 0) return fail(KIVI_ERR_ARG, "T = %lld is negative", (long long)T);
   if (T > dims->max_tokens)
@@ -178,7 +217,7 @@ kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int3
   if (T == 0) return ok();
   if (!x) return fail(KIVI_ERR_ARG, "%s input is NULL", keys ? "key" : "value");
   if (!aligned16(x)) return fail(KIVI_ERR_ALIGN, "%s input is not 16-byte aligned", keys ? "key" : "value");
-  const kivi::LayerView L = layer_view(dims, cache, layer);
+  const kivi::LayerView L = layer_view(dims, cache, layer, pg);
   const kivi::Lens ln{lens, T};
   hipError_t e = keys ? kivi::launch_quantize_k(L, static_cast<const __half*>(x), ld, T, ln,
                                                 static_cast<hipStream_t>(stream))
@@ -191,8 +230,10 @@ kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int3
 kivi_status decode_checks(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                           int64_t T, const void* q, float sm_scale, float* out, void* ws,
                           size_t ws_bytes, int32_t n_split, kivi::LayerView* Lout,
-                          kivi::DecodePlan* plan_out) {
+                          kivi::DecodePlan* plan_out, const kivi_paging* pg = nullptr) {
   kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  st = check_paging(dims, pg);
   if (st != KIVI_OK) return st;
   if (dims->group_v != dims->head_dim)
     return fail(KIVI_ERR_UNSUPPORTED, "decode requires group_v == head_dim (got %d)",
@@ -209,7 +250,7 @@ kivi_status decode_checks(const kivi_dims* dims, const kivi_cache* cache, int32_
   if (!aligned16(q) || !aligned16(out)) return fail(KIVI_ERR_ALIGN, "q or out is not 16-byte aligned");
   if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
     return fail(KIVI_ERR_ARG, "sm_scale is not finite");
-  const kivi::LayerView L = layer_view(dims, cache, layer);
+  const kivi::LayerView L = layer_view(dims, cache, layer, pg);
   const kivi::DecodePlan plan = kivi::plan_decode(L, dims->q_heads, T, n_split);
   if (!ws) return fail(KIVI_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(ws)) return fail(KIVI_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -223,11 +264,11 @@ kivi_status decode_checks(const kivi_dims* dims, const kivi_cache* cache, int32_
 kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                           int64_t T, const void* q, float sm_scale, float* out, void* ws,
                           size_t ws_bytes, int32_t n_split, void* stream,
-                          const int32_t* lens = nullptr) {
+                          const int32_t* lens = nullptr, const kivi_paging* pg = nullptr) {
   kivi::LayerView L;
   kivi::DecodePlan plan;
   kivi_status st = decode_checks(dims, cache, layer, T, q, sm_scale, out, ws, ws_bytes, n_split,
-                                 &L, &plan);
+                                 &L, &plan, pg);
   if (st != KIVI_OK) return st;
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
                                      out, ws, plan, nullptr, kivi::Lens{lens, T},
@@ -410,7 +451,19 @@ kivi_status kivi_cache_sizes(const kivi_dims* dims, size_t bytes[KIVI_NUM_BUFFER
   kivi_status st = check_dims(dims);
   if (st != KIVI_OK) return st;
   if (!bytes) return fail(KIVI_ERR_ARG, "bytes is NULL");
-  buffer_sizes(dims, bytes);
+  buffer_sizes(dims, nullptr, bytes);
+  return ok();
+}
+
+kivi_status kivi_paged_cache_sizes(const kivi_dims* dims, const kivi_paging* paging,
+                                   size_t bytes[KIVI_NUM_BUFFERS]) {
+  kivi_status st = check_dims(dims);
+  if (st != KIVI_OK) return st;
+  if (!paging) return fail(KIVI_ERR_ARG, "paging is NULL");
+  if (!bytes) return fail(KIVI_ERR_ARG, "bytes is NULL");
+  st = check_page_geometry(dims, paging);          // the table is not needed for sizes
+  if (st != KIVI_OK) return st;
+  buffer_sizes(dims, paging, bytes);
   return ok();
 }
 
@@ -426,12 +479,14 @@ kivi_status kivi_quantize_v(const kivi_dims* dims, const kivi_cache* cache, int3
 
 kivi_status append_common(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                           int64_t T_before, const void* k_new, const void* v_new, void* stream,
-                          const int32_t* lens) {
+                          const int32_t* lens, const kivi_paging* pg = nullptr) {
   kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  st = check_paging(dims, pg);
   if (st != KIVI_OK) return st;
   st = append_checks(dims, T_before, k_new, v_new);
   if (st != KIVI_OK) return st;
-  const kivi::LayerView L = layer_view(dims, cache, layer);
+  const kivi::LayerView L = layer_view(dims, cache, layer, pg);
   hipError_t e = kivi::launch_append_flush(L, T_before, static_cast<const __half*>(k_new),
                                            static_cast<const __half*>(v_new),
                                            kivi::Lens{lens, T_before}, false,
@@ -525,45 +580,50 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
 
 // ---- ragged batches ------------------------------------------------------------------
 
-kivi_status kivi_quantize_k_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
-                                   const void* k, const int32_t* lens, int64_t T_hi,
-                                   int64_t ld_tokens, void* stream) {
+kivi_status kivi_quantize_k_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                   const kivi_paging* paging, int32_t layer, const void* k,
+                                   const int32_t* lens, int64_t T_hi, int64_t ld_tokens,
+                                   void* stream) {
   kivi_status st = check_lens(lens);
   if (st != KIVI_OK) return st;
-  return quantize_common(dims, cache, layer, k, T_hi, ld_tokens, stream, true, lens);
+  return quantize_common(dims, cache, layer, k, T_hi, ld_tokens, stream, true, lens, paging);
 }
 
-kivi_status kivi_quantize_v_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
-                                   const void* v, const int32_t* lens, int64_t T_hi,
-                                   int64_t ld_tokens, void* stream) {
+kivi_status kivi_quantize_v_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                   const kivi_paging* paging, int32_t layer, const void* v,
+                                   const int32_t* lens, int64_t T_hi, int64_t ld_tokens,
+                                   void* stream) {
   kivi_status st = check_lens(lens);
   if (st != KIVI_OK) return st;
-  return quantize_common(dims, cache, layer, v, T_hi, ld_tokens, stream, false, lens);
+  return quantize_common(dims, cache, layer, v, T_hi, ld_tokens, stream, false, lens, paging);
 }
 
 kivi_status kivi_append_flush_varlen(const kivi_dims* dims, const kivi_cache* cache,
-                                     int32_t layer, const int32_t* T_before, int64_t T_hi,
-                                     const void* k_new, const void* v_new, void* stream) {
+                                     const kivi_paging* paging, int32_t layer,
+                                     const int32_t* T_before, int64_t T_hi, const void* k_new,
+                                     const void* v_new, void* stream) {
   kivi_status st = check_lens(T_before);
   if (st != KIVI_OK) return st;
-  return append_common(dims, cache, layer, T_hi, k_new, v_new, stream, T_before);
+  return append_common(dims, cache, layer, T_hi, k_new, v_new, stream, T_before, paging);
 }
 
 kivi_status kivi_decode_attn_varlen(const kivi_dims* dims, const kivi_cache* cache,
-                                    int32_t layer, const int32_t* lens, int64_t T_hi,
-                                    const void* q, float sm_scale, float* out, void* workspace,
+                                    const kivi_paging* paging, int32_t layer,
+                                    const int32_t* lens, int64_t T_hi, const void* q,
+                                    float sm_scale, float* out, void* workspace,
                                     size_t workspace_bytes, void* stream) {
   kivi_status st = check_lens(lens);
   if (st != KIVI_OK) return st;
   return decode_common(dims, cache, layer, T_hi, q, sm_scale, out, workspace, workspace_bytes,
-                       0, stream, lens);
+                       0, stream, lens, paging);
 }
 
 kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* cache,
-                                      int32_t layer, const int32_t* T_before, int64_t T_hi,
-                                      const void* k_new, const void* v_new, const void* q,
-                                      float sm_scale, float* out, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      const kivi_paging* paging, int32_t layer,
+                                      const int32_t* T_before, int64_t T_hi, const void* k_new,
+                                      const void* v_new, const void* q, float sm_scale,
+                                      float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
   kivi_status st = check_lens(T_before);
   if (st != KIVI_OK) return st;
   st = check_common(dims, cache, layer);
@@ -573,7 +633,7 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
   kivi::LayerView L;
   kivi::DecodePlan plan;
   st = decode_checks(dims, cache, layer, T_hi + 1, q, sm_scale, out, workspace, workspace_bytes,
-                     0, &L, &plan);
+                     0, &L, &plan, paging);
   if (st != KIVI_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const __half* kn = static_cast<const __half*>(k_new);
@@ -604,6 +664,6 @@ kivi_status kivi_stream_read(const void* buf, size_t bytes, void* sink, size_t s
 
 const char* kivi_last_error(void) { return g_err; }
 
-int32_t kivi_abi_version(void) { return 4; }
+int32_t kivi_abi_version(void) { return 5; }
 
 }  // extern "C"

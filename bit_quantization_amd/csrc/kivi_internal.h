@@ -10,13 +10,17 @@ namespace kivi {
 constexpr int kHeadDim = 128;   // head_dim this build's kernels are written for
 constexpr int kVRun = 16;       // tokens per packed Value run
 
-// Device pointers of one layer, already offset to that layer, plus the dims.
+// Device pointers of one layer, already offset to that layer, plus the dims.  The
+// history buffers hold one section per (b, h) pair of Tmax tokens, or, for a paged
+// cache, one section per KV head: a pool of `pages` pages of P = 2^page_log2 tokens,
+// table[b * pages_per_seq + i] naming the page of sequence b's history tokens
+// [iP, (i+1)P).
 struct LayerView {
-  uint8_t* k_codes;   // [B][H][Tmax][d*b/8]
-  __half* k_scale;    // [B][H][Tmax/G][d]
+  uint8_t* k_codes;   // [sections][rows][d*b/8]
+  __half* k_scale;    // [sections][rows/G][d]
   __half* k_zero;
-  uint8_t* v_codes;   // [B][H][Tmax/16][d][16*b/8]
-  __half* v_scale;    // [B][H][Tmax][d/Gv]
+  uint8_t* v_codes;   // [sections][rows/16][d][16*b/8]
+  __half* v_scale;    // [sections][rows][d/Gv]
   __half* v_zero;
   __half* k_resid;    // [B][H][S + R][d]: rows [0, S) the sink tokens, then the window
   __half* v_resid;
@@ -25,12 +29,28 @@ struct LayerView {
   int S;              // sink tokens kept in float16 (tokens [0, S) of each sequence)
   int aging;          // 0: a full window is flushed whole; 1: only its oldest Key group
   int64_t Tmax;
+  const int32_t* table;   // nullptr: contiguous history, one section per pair
+  int page_log2;
+  int pages_per_seq;
+  int64_t pages;
 
-  // Per-(b, h) element strides of each buffer.
-  __host__ __device__ int64_t kc_pair() const { return Tmax * (d * bits / 8); }
-  __host__ __device__ int64_t ks_pair() const { return (Tmax / G) * d; }
-  __host__ __device__ int64_t vc_pair() const { return Tmax * (d * bits / 8); }
-  __host__ __device__ int64_t vs_pair() const { return Tmax * (d / Gv); }
+  // Tokens of one history section, the section of a (b, h) pair, and where history
+  // token t of sequence b sits in its section (a page-table entry outside [0, pages)
+  // is clamped, so every access stays inside the pool).
+  __host__ __device__ int64_t rows() const { return table ? pages << page_log2 : Tmax; }
+  __host__ __device__ int64_t section(int64_t pair) const { return table ? pair % H : pair; }
+  __device__ int64_t hist_token(int64_t b, int64_t t) const {
+    if (!table) return t;
+    int64_t pg = table[b * pages_per_seq + (t >> page_log2)];
+    pg = pg < 0 ? 0 : pg >= pages ? pages - 1 : pg;
+    return (pg << page_log2) + (t & ((int64_t(1) << page_log2) - 1));
+  }
+
+  // Per-section element strides of each history buffer; per-pair of the window.
+  __host__ __device__ int64_t kc_pair() const { return rows() * (d * bits / 8); }
+  __host__ __device__ int64_t ks_pair() const { return (rows() / G) * d; }
+  __host__ __device__ int64_t vc_pair() const { return rows() * (d * bits / 8); }
+  __host__ __device__ int64_t vs_pair() const { return rows() * (d / Gv); }
   __host__ __device__ int64_t rs_pair() const { return (int64_t)(S + R) * d; }
 };
 

@@ -303,10 +303,11 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
   for (int i = 0; i < npw; ++i) {
     const int64_t g = ((int64_t)blockIdx.x * npw + i) * QW + wave;
     if (g < ngroups) {
+      const int64_t ht = L.hist_token(pair / L.H, g * G), sec = L.section(pair);
       smx = fmaxf(smx, quantize_k_group<BITS, G>(
-                           s + g * G * D, L.k_codes + pair * L.kc_pair() + g * G * (D * BITS / 8),
-                           L.k_scale + pair * L.ks_pair() + g * D,
-                           L.k_zero + pair * L.ks_pair() + g * D, lds[wave]));
+                           s + g * G * D, L.k_codes + sec * L.kc_pair() + ht * (D * BITS / 8),
+                           L.k_scale + sec * L.ks_pair() + (ht / G) * D,
+                           L.k_zero + sec * L.ks_pair() + (ht / G) * D, lds[wave]));
     } else if (g == ngroups) {
       store_fp16_rows(L, s0, s + Tq * D, L.k_resid + pair * L.rs_pair(), ts.ns, ts.r, ts.ring);
     }
@@ -332,11 +333,12 @@ __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const _
   for (int i = 0; i < npw; ++i) {
     const int64_t j = ((int64_t)blockIdx.x * npw + i) * QW + wave;
     if (j < nruns) {
+      const int64_t ht = L.hist_token(pair / L.H, j * kVRun), sec = L.section(pair);
       smx = fmaxf(smx, quantize_v_run<BITS, GV>(
                            s + j * kVRun * D,
-                           L.v_codes + pair * L.vc_pair() + j * (D * kVRun * BITS / 8),
-                           L.v_scale + pair * L.vs_pair() + j * kVRun * (D / GV),
-                           L.v_zero + pair * L.vs_pair() + j * kVRun * (D / GV), lds[wave]));
+                           L.v_codes + sec * L.vc_pair() + (ht / kVRun) * (D * kVRun * BITS / 8),
+                           L.v_scale + sec * L.vs_pair() + ht * (D / GV),
+                           L.v_zero + sec * L.vs_pair() + ht * (D / GV), lds[wave]));
     } else if (j == nruns) {
       store_fp16_rows(L, s0, s + Tq * D, L.v_resid + pair * L.rs_pair(), ts.ns, ts.r, ts.ring);
     }
@@ -386,12 +388,13 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
   }
   const int nk = n / G;
   const int blk = blockIdx.x;
+  const int64_t sec = L.section(pair);
   if (blk < nk) {
+    const int64_t ht = L.hist_token(pair / L.H, t0 + (int64_t)blk * G);
     const float smx = quantize_k_group<BITS, G>(
-        kr + (int64_t)blk * G * D,
-        L.k_codes + pair * L.kc_pair() + (t0 + blk * G) * (D * BITS / 8),
-        L.k_scale + pair * L.ks_pair() + (t0 / G + blk) * D,
-        L.k_zero + pair * L.ks_pair() + (t0 / G + blk) * D, lds);
+        kr + (int64_t)blk * G * D, L.k_codes + sec * L.kc_pair() + ht * (D * BITS / 8),
+        L.k_scale + sec * L.ks_pair() + (ht / G) * D, L.k_zero + sec * L.ks_pair() + (ht / G) * D,
+        lds);
     raise_scale_max<1>(L.scale_max + 2 * pair, smx, nullptr);
     if (blk == 0) {
       __syncthreads();
@@ -399,11 +402,12 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
     }
   } else {
     const int j = blk - nk;
+    const int64_t ht = L.hist_token(pair / L.H, t0 + (int64_t)j * kVRun);
     const float smx = quantize_v_run<BITS, GV>(
         vr + (int64_t)j * kVRun * D,
-        L.v_codes + pair * L.vc_pair() + (t0 / kVRun + j) * (D * kVRun * BITS / 8),
-        L.v_scale + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV),
-        L.v_zero + pair * L.vs_pair() + (t0 + j * kVRun) * (D / GV), lds);
+        L.v_codes + sec * L.vc_pair() + (ht / kVRun) * (D * kVRun * BITS / 8),
+        L.v_scale + sec * L.vs_pair() + ht * (D / GV), L.v_zero + sec * L.vs_pair() + ht * (D / GV),
+        lds);
     raise_scale_max<1>(L.scale_max + 2 * pair + 1, smx, nullptr);
     if (j == 0) {
       __syncthreads();

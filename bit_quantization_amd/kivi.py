@@ -24,7 +24,8 @@ STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_E
 
 EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
            "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
-           "kivi_append_decode", "kivi_quantize_k_varlen", "kivi_quantize_v_varlen",
+           "kivi_append_decode", "kivi_paged_cache_sizes", "kivi_quantize_k_varlen",
+           "kivi_quantize_v_varlen",
            "kivi_append_flush_varlen", "kivi_decode_attn_varlen", "kivi_append_decode_varlen",
            "kivi_stream_read", "kivi_fp8_cache_sizes",
            "kivi_fp8_quantize", "kivi_fp8_append", "kivi_fp8_decode_workspace_bytes",
@@ -59,6 +60,11 @@ class kivi_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS]
 
 
+class kivi_paging(ctypes.Structure):
+    _fields_ = [("page_tokens", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32),
+                ("pages", ctypes.c_int64), ("block_table", ctypes.c_void_p)]
+
+
 class kivi_fp8_dims(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("q_heads", ctypes.c_int32),
@@ -82,6 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
     D, C = ctypes.POINTER(kivi_dims), ctypes.POINTER(kivi_cache)
+    PG = ctypes.POINTER(kivi_paging)
     sig = {
         "kivi_cache_sizes": (I32, [D, ctypes.POINTER(SZ)]),
         "kivi_quantize_k": (I32, [D, C, I32, P, I64, I64, P]),
@@ -93,11 +100,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_decode_attn": (I32, [D, C, I32, I64, P, F32, P, P, SZ, P]),
         "kivi_decode_attn_split": (I32, [D, C, I32, I64, P, F32, P, P, SZ, I32, P]),
         "kivi_append_decode": (I32, [D, C, I32, I64, P, P, P, F32, P, P, SZ, P]),
-        "kivi_quantize_k_varlen": (I32, [D, C, I32, P, P, I64, I64, P]),
-        "kivi_quantize_v_varlen": (I32, [D, C, I32, P, P, I64, I64, P]),
-        "kivi_append_flush_varlen": (I32, [D, C, I32, P, I64, P, P, P]),
-        "kivi_decode_attn_varlen": (I32, [D, C, I32, P, I64, P, F32, P, P, SZ, P]),
-        "kivi_append_decode_varlen": (I32, [D, C, I32, P, I64, P, P, P, F32, P, P, SZ, P]),
+        "kivi_paged_cache_sizes": (I32, [D, PG, ctypes.POINTER(SZ)]),
+        "kivi_quantize_k_varlen": (I32, [D, C, PG, I32, P, P, I64, I64, P]),
+        "kivi_quantize_v_varlen": (I32, [D, C, PG, I32, P, P, I64, I64, P]),
+        "kivi_append_flush_varlen": (I32, [D, C, PG, I32, P, I64, P, P, P]),
+        "kivi_decode_attn_varlen": (I32, [D, C, PG, I32, P, I64, P, F32, P, P, SZ, P]),
+        "kivi_append_decode_varlen": (I32, [D, C, PG, I32, P, I64, P, P, P, F32, P, P, SZ, P]),
         "kivi_stream_read": (I32, [P, SZ, P, SZ, P]),
         "kivi_fp8_cache_sizes": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(SZ)]),
         "kivi_fp8_quantize": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(kivi_fp8_cache),
@@ -209,6 +217,60 @@ class Cache:
         raise KeyError(name)
 
 
+@dataclass
+class Paging:
+    """A paged cache's page geometry and block table (device int32 [B][pages_per_seq])."""
+    page_tokens: int
+    pages_per_seq: int
+    pages: int
+    block_table: torch.Tensor | None = None
+
+    def c(self, dims: Dims | None = None) -> kivi_paging:
+        bt = None
+        if self.block_table is not None:
+            need = dims.batch * self.pages_per_seq if dims is not None else None
+            bt = _ptr(self.block_table, torch.int32, "block_table", need)
+        return kivi_paging(self.page_tokens, self.pages_per_seq, self.pages, bt)
+
+
+def kivi_paged_cache_sizes(dims: Dims, paging: Paging):
+    out = (ctypes.c_size_t * len(BUFFERS))()
+    _check(_lib.kivi_paged_cache_sizes(ctypes.byref(dims.c()), ctypes.byref(paging.c()), out))
+    return list(out)
+
+
+class PagedCache(Cache):
+    """The nine buffers of a paged cache: the history buffers hold per layer and KV head
+    a pool of pages; the window buffers and scale_max are per (sequence, KV head)."""
+
+    def __init__(self, dims: Dims, paging: Paging, device="cuda"):
+        self.dims = dims
+        self.paging = paging
+        self.buffers = {name: torch.zeros(nbytes, dtype=torch.uint8, device=device)
+                        for name, nbytes in zip(BUFFERS, kivi_paged_cache_sizes(dims, paging))}
+
+    def view(self, name: str):
+        d, pg = self.dims, self.paging
+        L, H, N, P, D = d.layers, d.kv_heads, pg.pages, pg.page_tokens, d.head_dim
+        buf = self.buffers[name]
+        if name == "k_codes":
+            return buf.view(L, H, N, P, D * d.bits // 8)
+        if name in ("k_scale", "k_zero"):
+            return buf.view(torch.float16).view(L, H, N, P // d.group_k, D)
+        if name == "v_codes":
+            return buf.view(L, H, N, P // 16, D, 16 * d.bits // 8)
+        if name in ("v_scale", "v_zero"):
+            return buf.view(torch.float16).view(L, H, N, P, D // d.group_v)
+        return super().view(name)
+
+    def sequence_view(self, name: str, layer: int, b: int):
+        """History buffer `name` of sequence b in token order: the pages its block-table
+        row names, concatenated ([H][pages_per_seq * rows per page][...])."""
+        pages = self.paging.block_table[b].long()
+        v = self.view(name)[layer][:, pages]
+        return v.reshape(v.shape[0], -1, *v.shape[3:])
+
+
 def kivi_quantize_k(dims: Dims, cache: Cache, layer: int, k: torch.Tensor, T: int,
                     ld_tokens: int | None = None, stream=None):
     ld = T if ld_tokens is None else ld_tokens
@@ -290,30 +352,37 @@ def _lens(lens, dims):
     return _ptr(lens, torch.int32, "lens", dims.batch)
 
 
+def _paging(paging, dims):
+    return None if paging is None else ctypes.byref(paging.c(dims))
+
+
 def kivi_quantize_k_varlen(dims: Dims, cache: Cache, layer: int, k: torch.Tensor,
                            lens: torch.Tensor, T_hi: int, ld_tokens: int | None = None,
-                           stream=None):
+                           stream=None, paging: Paging | None = None):
     ld = T_hi if ld_tokens is None else ld_tokens
     need = dims.batch * dims.kv_heads * ld * dims.head_dim if T_hi else None
-    _check(_lib.kivi_quantize_k_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+    _check(_lib.kivi_quantize_k_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                       _paging(paging, dims), layer,
                                        _ptr(k, torch.float16, "k", need), _lens(lens, dims),
                                        T_hi, ld, _stream(stream)))
 
 
 def kivi_quantize_v_varlen(dims: Dims, cache: Cache, layer: int, v: torch.Tensor,
                            lens: torch.Tensor, T_hi: int, ld_tokens: int | None = None,
-                           stream=None):
+                           stream=None, paging: Paging | None = None):
     ld = T_hi if ld_tokens is None else ld_tokens
     need = dims.batch * dims.kv_heads * ld * dims.head_dim if T_hi else None
-    _check(_lib.kivi_quantize_v_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+    _check(_lib.kivi_quantize_v_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                       _paging(paging, dims), layer,
                                        _ptr(v, torch.float16, "v", need), _lens(lens, dims),
                                        T_hi, ld, _stream(stream)))
 
 
 def kivi_append_flush_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
-                             T_hi: int, k_new, v_new, stream=None):
+                             T_hi: int, k_new, v_new, stream=None, paging: Paging | None = None):
     need = dims.batch * dims.kv_heads * dims.head_dim
-    _check(_lib.kivi_append_flush_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+    _check(_lib.kivi_append_flush_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                         _paging(paging, dims), layer,
                                          _lens(T_before, dims), T_hi,
                                          _ptr(k_new, torch.float16, "k_new", need),
                                          _ptr(v_new, torch.float16, "v_new", need),
@@ -322,9 +391,10 @@ def kivi_append_flush_varlen(dims: Dims, cache: Cache, layer: int, T_before: tor
 
 def kivi_decode_attn_varlen(dims: Dims, cache: Cache, layer: int, lens: torch.Tensor, T_hi: int,
                             q: torch.Tensor, sm_scale: float, out: torch.Tensor,
-                            workspace: torch.Tensor, stream=None):
+                            workspace: torch.Tensor, stream=None, paging: Paging | None = None):
     nq = dims.batch * dims.q_heads * dims.head_dim
-    _check(_lib.kivi_decode_attn_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+    _check(_lib.kivi_decode_attn_varlen(ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+                                        _paging(paging, dims), layer,
                                         _lens(lens, dims), T_hi, _ptr(q, torch.float16, "q", nq),
                                         ctypes.c_float(sm_scale),
                                         _ptr(out, torch.float32, "out", nq),
@@ -334,12 +404,15 @@ def kivi_decode_attn_varlen(dims: Dims, cache: Cache, layer: int, lens: torch.Te
 
 def prepare_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
                                  T_hi: int, k_new, v_new, q: torch.Tensor, sm_scale: float,
-                                 out: torch.Tensor, workspace: torch.Tensor, stream=None):
+                                 out: torch.Tensor, workspace: torch.Tensor, stream=None,
+                                 paging: Paging | None = None):
     """kivi_append_decode_varlen with its arguments marshalled once (see
     prepare_append_decode)."""
     need = dims.batch * dims.kv_heads * dims.head_dim
     nq = dims.batch * dims.q_heads * dims.head_dim
-    args = (ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, _lens(T_before, dims), T_hi,
+    pg = None if paging is None else paging.c(dims)    # kept alive by the closure
+    args = (ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+            None if pg is None else ctypes.byref(pg), layer, _lens(T_before, dims), T_hi,
             _ptr(k_new, torch.float16, "k_new", need), _ptr(v_new, torch.float16, "v_new", need),
             _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
             _ptr(out, torch.float32, "out", nq), _ptr(workspace, torch.uint8, "workspace"),
@@ -353,9 +426,10 @@ def prepare_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before:
 
 def kivi_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
                               T_hi: int, k_new, v_new, q: torch.Tensor, sm_scale: float,
-                              out: torch.Tensor, workspace: torch.Tensor, stream=None):
+                              out: torch.Tensor, workspace: torch.Tensor, stream=None,
+                              paging: Paging | None = None):
     prepare_append_decode_varlen(dims, cache, layer, T_before, T_hi, k_new, v_new, q, sm_scale,
-                                 out, workspace, stream)()
+                                 out, workspace, stream, paging)()
 
 
 def prepare_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k_new, v_new,

@@ -199,6 +199,33 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
                                const void* q, float sm_scale, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Paged caches ("KV Cache Quantization (KIVI & FP4)" §6: PagedAttention allocates the
+ * cache in fixed pages, and under KIVI a page of the same bytes holds more tokens).
+ * The quantized history of every sequence lives in pages of P tokens taken from a
+ * pool; the float16 sink and window rows and scale_max stay per (sequence, KV head)
+ * as in the contiguous layout.  Each history buffer holds, per layer and KV head, the
+ * pool's pages in order, each page laid out like a P-token history:
+ *    k_codes  uint8   [L][H_kv][pages][P][d*b/8]
+ *    k_scale  float16 [L][H_kv][pages][P/G][d]        k_zero likewise
+ *    v_codes  uint8   [L][H_kv][pages][P/16][d][2*b]
+ *    v_scale  float16 [L][H_kv][pages][P][d/G_v]      v_zero likewise
+ * History token t of sequence b (all its KV heads and layers) is token t mod P of page
+ * block_table[b][t / P].  The table is read on the device; an entry outside
+ * [0, pages) is clamped into it (every access stays inside the pool; the result is
+ * then unspecified).  Pages may be shared by several sequences only where their
+ * history is identical; each append writes the page that holds its flushed tokens. */
+typedef struct kivi_paging {
+  int32_t page_tokens;         /* P: a power of two in [64, 2^20] */
+  int32_t pages_per_seq;       /* columns of block_table; pages_per_seq * P >= max_tokens */
+  int64_t pages;               /* pages in the pool (per layer and KV head) */
+  const int32_t* block_table;  /* device int32 [B][pages_per_seq] */
+} kivi_paging;
+
+/* Byte sizes of the nine buffers of a paged cache (layout above; the window buffers
+ * and scale_max as in kivi_cache_sizes).  Host-only; block_table is not read. */
+kivi_status kivi_paged_cache_sizes(const kivi_dims* dims, const kivi_paging* paging,
+                                   size_t bytes[KIVI_NUM_BUFFERS]);
+
 /* Ragged batches ("KV Cache Quantization (KIVI & FP4)" §6: serving engines hold
  * sequences of different lengths in one batch).  Each call below is the call of the
  * same name without _varlen, with sequence b holding its own token count:
@@ -207,6 +234,8 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
  *   T_hi             host upper bound of every entry: the capacity checks, the
  *                    workspace size and the launch are those of the uniform call at
  *                    T = T_hi (appends: T_before = T_hi).
+ *   paging           NULL: the cache has the contiguous layout (kivi_cache_sizes);
+ *                    else a paged cache (kivi_paged_cache_sizes) and its block table.
  * The arrays are read on the device: the host cannot check them, so each entry is
  * clamped into its valid range ([0, T_hi], decode [1, T_hi]) before use; every access
  * stays inside the cache, and a sequence whose entry was out of range gets an
@@ -216,35 +245,40 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
 
 /* kivi_quantize_k for a ragged batch: sequence b's first lens[b] tokens of k
  * ([B][H_kv][ld_tokens][d], ld_tokens >= T_hi). */
-kivi_status kivi_quantize_k_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
-                                   const void* k, const int32_t* lens, int64_t T_hi,
-                                   int64_t ld_tokens, void* stream);
+kivi_status kivi_quantize_k_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                   const kivi_paging* paging, int32_t layer, const void* k,
+                                   const int32_t* lens, int64_t T_hi, int64_t ld_tokens,
+                                   void* stream);
 /* kivi_quantize_v for a ragged batch. */
-kivi_status kivi_quantize_v_varlen(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
-                                   const void* v, const int32_t* lens, int64_t T_hi,
-                                   int64_t ld_tokens, void* stream);
+kivi_status kivi_quantize_v_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                   const kivi_paging* paging, int32_t layer, const void* v,
+                                   const int32_t* lens, int64_t T_hi, int64_t ld_tokens,
+                                   void* stream);
 /* kivi_append_flush for a ragged batch: sequence b appends at T_before[b], flushing
  * its own window when that is full.  One launch sized for a flush of every sequence. */
 kivi_status kivi_append_flush_varlen(const kivi_dims* dims, const kivi_cache* cache,
-                                     int32_t layer, const int32_t* T_before, int64_t T_hi,
-                                     const void* k_new, const void* v_new, void* stream);
+                                     const kivi_paging* paging, int32_t layer,
+                                     const int32_t* T_before, int64_t T_hi, const void* k_new,
+                                     const void* v_new, void* stream);
 /* kivi_decode_attn for a ragged batch: sequence b attends over its lens[b] tokens.
  * Workspace: kivi_decode_workspace_bytes(dims, T_hi).  The launch has the workgroups
  * of a batch of T_hi tokens; each (sequence, KV head) splits its own blocks among
  * them, so short sequences finish early. */
 kivi_status kivi_decode_attn_varlen(const kivi_dims* dims, const kivi_cache* cache,
-                                    int32_t layer, const int32_t* lens, int64_t T_hi,
-                                    const void* q, float sm_scale, float* out, void* workspace,
+                                    const kivi_paging* paging, int32_t layer,
+                                    const int32_t* lens, int64_t T_hi, const void* q,
+                                    float sm_scale, float* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 /* kivi_append_decode for a ragged batch: two launches (the flushes of the sequences
  * whose window is full, then decode attention that stores every new row); equal to
  * kivi_append_flush_varlen followed by kivi_decode_attn_varlen over T_before[b] + 1.
  * Workspace: kivi_decode_workspace_bytes(dims, T_hi + 1). */
 kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* cache,
-                                      int32_t layer, const int32_t* T_before, int64_t T_hi,
-                                      const void* k_new, const void* v_new, const void* q,
-                                      float sm_scale, float* out, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+                                      const kivi_paging* paging, int32_t layer,
+                                      const int32_t* T_before, int64_t T_hi, const void* k_new,
+                                      const void* v_new, const void* q, float sm_scale,
+                                      float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* Workspace bytes kivi_decode_attn needs for T cached tokens (host-only). */
 kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t* bytes);

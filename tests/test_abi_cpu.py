@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert kv.kivi_abi_version() == 4
+    assert kv.kivi_abi_version() == 5
 
 
 def good_dims(**kw):
@@ -213,3 +213,43 @@ def test_aging_and_reserved_fields_are_checked(field, value):
     st, msg = call("kivi_quantize_k", ctypes.byref(c), ctypes.byref(fake_cache()), 0, FAKE, 16, 16,
                    None)
     assert st == 1 and field in msg
+
+
+def test_paged_cache_sizes_follow_the_documented_layout():
+    d = good_dims(bits=4, group_v=64)
+    pg = kv.Paging(page_tokens=128, pages_per_seq=d.max_tokens // 128 + 1, pages=37)
+    sizes = kv.kivi_paged_cache_sizes(d, pg)
+    sec = d.layers * d.kv_heads
+    unit = d.layers * d.batch * d.kv_heads
+    rows = 37 * 128
+    codes = sec * rows * d.head_dim * d.bits // 8
+    assert sizes == [codes, sec * (rows // 32) * 128 * 2, sec * (rows // 32) * 128 * 2,
+                     codes, sec * rows * 2 * 2, sec * rows * 2 * 2,
+                     unit * 64 * 128 * 2, unit * 64 * 128 * 2, unit * 2 * 4]
+
+
+@pytest.mark.parametrize("P,per_seq,pages,status", [
+    (100, 64, 8, 1), (32, 64, 8, 1), (128, 64, 0, 1), (128, 0, 8, 1),
+    (128, 1, 8, 3),                       # 128 tokens per sequence < max_tokens
+    (1 << 20, 1, 1 << 12, 2),             # a head's pool beyond 2^31 bytes
+])
+def test_bad_paging_is_rejected(P, per_seq, pages, status):
+    d = good_dims()
+    pg = kv.kivi_paging(P, per_seq, pages, FAKE)
+    sizes = (ctypes.c_size_t * len(kv.BUFFERS))()
+    st, msg = call("kivi_paged_cache_sizes", ctypes.byref(d.c()), ctypes.byref(pg), sizes)
+    assert st == status and msg
+    lens = FAKE
+    st, msg = call("kivi_quantize_k_varlen", ctypes.byref(d.c()), ctypes.byref(fake_cache()),
+                   ctypes.byref(pg), 0, FAKE, lens, 16, 16, None)
+    assert st == status and msg
+
+
+def test_paged_calls_check_the_block_table_pointer():
+    d = good_dims()
+    for table, status in ((None, 1), (FAKE + 2, 4)):
+        pg = kv.kivi_paging(128, d.max_tokens // 128 + 1, 8, table)
+        st, msg = call("kivi_decode_attn_varlen", ctypes.byref(d.c()), ctypes.byref(fake_cache()),
+                       ctypes.byref(pg), 0, FAKE, 16, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                       1 << 20, None)
+        assert st == status and "block_table" in msg
