@@ -67,6 +67,46 @@ struct DecodeArgs {
   Lens lens;            // ragged batch: per-sequence counts (the fields above are for T)
 };
 
+// A ragged batch: the tokens sequence b attends over.
+__device__ __forceinline__ int64_t ragged_tokens(const DecodeArgs& a, int64_t b) {
+  return a.new_slot >= 0 ? a.lens.get(b, 0) + 1 : a.lens.get(b, 1);
+}
+
+// A ragged batch shares out the workgroups of each KV head's slice of the grid (B * nw
+// of them) among the sequences in proportion to their token counts, at least one
+// each, so that a long sequence gets more workgroups than a short one (the spare
+// workgroups beyond one each are cut at the rounded cumulative token shares, so all
+// of them are used).  Sets the workgroup's pair, its index s among the pair's nw
+// workgroups and the pair's first partial slot; returns false if none is left for it.
+struct RaggedSlot {
+  int64_t pair, slot0;
+  int s, nw;
+};
+__device__ __forceinline__ bool ragged_assign(const DecodeArgs& a, RaggedSlot& out) {
+  const int B = a.L.B, H = a.L.H;
+  const int64_t per_head = gridDim.x / H;
+  const int64_t h = blockIdx.x / per_head, i = blockIdx.x % per_head;
+  int64_t sum = 0;
+  for (int b = 0; b < B; ++b) sum += ragged_tokens(a, b);
+  const int64_t spare = per_head - B;
+  int64_t acc = 0, cum = 0, cut = 0;
+  for (int b = 0; b < B; ++b) {
+    cum += ragged_tokens(a, b);
+    const int64_t next_cut = spare * cum / sum;
+    const int64_t w = 1 + next_cut - cut;
+    cut = next_cut;
+    if (i < acc + w) {
+      out.pair = (int64_t)b * H + h;
+      out.s = (int)(i - acc);
+      out.nw = (int)w;
+      out.slot0 = h * per_head + acc;
+      return true;
+    }
+    acc += w;
+  }
+  return false;
+}
+
 // A ragged batch: the token split of sequence b (and its new row's slot), computed by
 // each workgroup for its own pair.
 __device__ __forceinline__ void ragged_split(DecodeArgs& a, int64_t b) {
@@ -594,11 +634,32 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
   }
   int nxt = item < n_items ? grab_item(counter) : n_items;
   int done = 0;
+  // Paged: the refill target of the next iteration is looked up one block ahead, with
+  // a vector load issued before this block's refill loads and read after the block,
+  // so that its latency hides behind the block (a scalar load would be waited for at
+  // the block's first LDS wait).
+  const __amdgpu_buffer_rsrc_t tbl =
+      make_rsrc(PAGED ? L.table + b * L.pages_per_seq : nullptr, PAGED ? L.pages_per_seq * 4 : 0);
+  int64_t tgt_next = 0;
+  if constexpr (PAGED)
+    if (item < n_items) tgt_next = hist((nxt < n_items ? block_of(nxt) : block_of(item)) * BLK);
   while (item < n_items) {
     const int after = nxt < n_items ? grab_item(counter) : n_items;
     const int64_t blk = block_of(item);
     const int64_t nb = nxt < n_items ? block_of(nxt) : blk;
-    process_block<BITS, GQA, G, true, true>(R, BLK, qk, lc, lds, st, lo, j, pb, hist(nb * BLK));
+    int64_t tgt = nb * BLK, na = 0;
+    int page_v = 0;
+    if constexpr (PAGED) {
+      tgt = tgt_next;
+      na = (after < n_items ? block_of(after) : nb) * BLK;
+      page_v = (int)__builtin_amdgcn_raw_buffer_load_b32(tbl, 0, (int)((na >> L.page_log2) * 4), 0);
+    }
+    process_block<BITS, GQA, G, true, true>(R, BLK, qk, lc, lds, st, lo, j, pb, tgt);
+    if constexpr (PAGED) {
+      int64_t pg = __builtin_amdgcn_readfirstlane(page_v);
+      pg = pg < 0 ? 0 : pg >= L.pages ? L.pages - 1 : pg;
+      tgt_next = (pg << L.page_log2) + (na & ((int64_t(1) << L.page_log2) - 1));
+    }
     if ((++done & 1023) == 0) {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) fold_acc(st, mt, 1.f);
@@ -809,12 +870,24 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   __shared__ alignas(16) float comb[2 * WAVES][GQA * PSTRIDE];  // [0, WAVES): blocks; then window
   __shared__ int counter;
 
+  // workgroup -> (pair, s): uniform T: pair blockIdx.x mod P, nw workgroups a pair;
+  // a ragged batch: ragged_assign
   const int64_t P = (int64_t)args.L.B * args.L.H;
-  const int64_t pair = blockIdx.x % P;
-  const int s = (int)(blockIdx.x / P);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t b = pair / args.L.H, h = pair % args.L.H;
+  int64_t pair = blockIdx.x % P, slot0;
+  int s = (int)(blockIdx.x / P);
   DecodeArgs a = args;
+  if (a.lens.p) {
+    RaggedSlot rsl;
+    if (!ragged_assign(a, rsl)) return;
+    pair = rsl.pair;
+    s = rsl.s;
+    a.nw = rsl.nw;
+    slot0 = rsl.slot0;
+  } else {
+    slot0 = pair * a.nw;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b = pair / a.L.H, h = pair % a.L.H;
   if (a.lens.p) ragged_split(a, b);
 
   // this workgroup's share: window chunks (workgroup 0 only), then blocks
@@ -836,7 +909,8 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   // Clear this workgroup's partial slot (each thread the words it stores at the end).
   const int n_parts = a.nw;
   const int64_t pair_floats = (int64_t)n_parts * GQA * PSTRIDE;
-  const __amdgpu_buffer_rsrc_t parts = make_rsrc(a.part + pair * pair_floats, pair_floats * 4);
+  const __amdgpu_buffer_rsrc_t parts =
+      make_rsrc(a.part + slot0 * GQA * PSTRIDE, pair_floats * 4);
   const int my = s * GQA * PSTRIDE * 4;
   if (n_parts > 1) clear_partial<GQA, NTH>(parts, my);
   __syncthreads();
