@@ -126,9 +126,9 @@ def parse():
                    help="a paged cache with pages of P tokens in a shuffled pool (0: contiguous)")
     p.add_argument("--aging", default="window", choices=["window", "group"],
                    help="a full window flushes whole (window) or its oldest Key group (group)")
-    p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2"],
+    p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2", "mxfp4"],
                    help="kivi: the workload's 2/4-bit KIVI cache (default); fp8_*: the same "
-                        "workload stored as FP8 with per-head scales")
+                        "workload stored as FP8 with per-head scales; mxfp4: stored as MXFP4")
     p.add_argument("--no-graph", action="store_true",
                    help="launch the timed steps one by one instead of as one HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -255,6 +255,19 @@ def fp8_append_bytes(w):
     return w.batch * w.kv_heads * (2 * 2 * w.head_dim + 2 * w.head_dim)
 
 
+def mx_decode_bytes(w, T):
+    """Algorithmic bytes of one MXFP4 decode launch at T tokens: per (sequence, KV head)
+    and token d/2 Key and d/2 Value code bytes and d/32 scale bytes each; q and out."""
+    d = w.head_dim
+    return w.batch * w.kv_heads * T * 2 * (d // 2 + d // 32) + w.batch * w.q_heads * d * (2 + 4)
+
+
+def mx_append_bytes(w):
+    """k_new, v_new read (2 * 2d) and their codes and scales written."""
+    d = w.head_dim
+    return w.batch * w.kv_heads * (2 * 2 * d + 2 * (d // 2 + d // 32))
+
+
 def fp8_cpu_baseline(w, fmt, host_pairs, budget_s):
     """The FP8 oracle's decode step (append + attend) on a bounded sample, as
     cpu_baseline."""
@@ -266,9 +279,11 @@ def fp8_cpu_baseline(w, fmt, host_pairs, budget_s):
         threads = 1
     one = w.replace(batch=1, kv_heads=1, q_heads=w.gqa)
     caches = []
+    mx = fmt == "mxfp4"
     for (Kh, Vh, k_rows, v_rows, qh, T, ks, vs) in host_pairs:
         cap = (T + len(k_rows) + 1 + 31) // 32 * 32
-        oc = O.FP8Cache(1, 1, w.head_dim, fmt, cap, ks, vs)
+        oc = (O.MXFP4Cache(1, 1, w.head_dim, cap) if mx
+              else O.FP8Cache(1, 1, w.head_dim, fmt, cap, ks, vs))
         oc.prefill(Kh, Vh)
         caches.append((oc, k_rows, v_rows, qh))
     done_bytes, t_used, steps, T_last = 0, 0.0, 0, 0
@@ -282,38 +297,44 @@ def fp8_cpu_baseline(w, fmt, host_pairs, budget_s):
         oc.append(k_rows[j][None, None], v_rows[j][None, None])
         oc.attend(qh, w.sm_scale)
         t_used += time.perf_counter() - t0
-        done_bytes += fp8_decode_bytes(one, T + 1) + fp8_append_bytes(one)
+        done_bytes += (mx_decode_bytes(one, T + 1) + mx_append_bytes(one) if mx
+                       else fp8_decode_bytes(one, T + 1) + fp8_append_bytes(one))
         steps += 1
         T_last = T + 1
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"{steps} FP8 oracle decode steps (append + attend, {w.gqa} query heads, "
+            "sample": (f"{steps} {'MXFP4' if mx else 'FP8'} oracle decode steps (append + attend, {w.gqa} query heads, "
                        f"~{T_last} tokens) round-robin over {len(caches)} (sequence, KV head) "
                        f"pairs of the workload, {t_used:.1f} s of oracle time; "
                        f"os.cpu_count()={os.cpu_count()}, BLAS threads={threads}")}
 
 
 def fp8_main(args):
-    """The workload stored as FP8: one step = kivi_fp8_append + kivi_fp8_decode_attn."""
+    """The workload stored as FP8 (one step = kivi_fp8_append + kivi_fp8_decode_attn) or
+    as MXFP4 (kivi_mxfp4_append + kivi_mxfp4_decode_attn)."""
     import numpy as np
     import torch
 
     import workloads as W
     from bit_quantization_amd import kivi as k
 
-    fmt = args.codec[4:]
+    mx = args.codec == "mxfp4"
+    fmt = "mxfp4" if mx else args.codec[4:]
+    dec_bytes = mx_decode_bytes if mx else fp8_decode_bytes
+    app_bytes = mx_append_bytes if mx else fp8_append_bytes
     torch.cuda.set_device(0)
     w = W.get(args.workload)
     w1 = w.replace(layers=1) if w.layers > 1 else w
     total_steps = args.warmup + 2 * args.steps
-    per_copy = fp8_decode_bytes(w1, w1.tokens)
+    per_copy = dec_bytes(w1, w1.tokens)
     copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy))
     if w.layers > 1:
         copies = args.copies or min(w.layers, max(copies, 2))
     steps_per_copy = math.ceil(total_steps / copies) + 1
     extra = max(steps_per_copy, 1024)
     Tmax = (w1.tokens + steps_per_copy + 31) // 32 * 32
-    dims = k.Fp8Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, fmt, Tmax)
+    dims = (k.MxDims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, Tmax) if mx
+            else k.Fp8Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, fmt, Tmax))
     print(f"[bench] workload {w.name} as {args.codec}: {copies} layer caches x "
           f"{per_copy / 1e6:.1f} MB decode reads, {args.warmup}+{args.steps} steps",
           file=sys.stderr, flush=True)
@@ -328,8 +349,12 @@ def fp8_main(args):
         # synthetic data ("4.4 KV Cache quantization" §4.2, calibrated scales)
         ks = (K[:, :, :w1.tokens].float().abs().amax(dim=(0, 2, 3)) / top).clamp_min(1e-12)
         vs = (V[:, :, :w1.tokens].float().abs().amax(dim=(0, 2, 3)) / top).clamp_min(1e-12)
-        cache = k.Fp8Cache(dims, ks.cpu(), vs.cpu())
-        k.kivi_fp8_quantize(dims, cache, 0, K, V, w1.tokens, K.shape[2])
+        if mx:                  # MXFP4 needs no calibration: every block has its own scale
+            cache = k.MxCache(dims)
+            k.kivi_mxfp4_quantize(dims, cache, 0, K, V, w1.tokens, K.shape[2])
+        else:
+            cache = k.Fp8Cache(dims, ks.cpu(), vs.cpu())
+            k.kivi_fp8_quantize(dims, cache, 0, K, V, w1.tokens, K.shape[2])
         caches.append(cache)
         Ts.append(w1.tokens)
         news.append((K[:, :, w1.tokens:w1.tokens + steps_per_copy].permute(2, 0, 1, 3).contiguous(),
@@ -346,7 +371,7 @@ def fp8_main(args):
         del K, V
     qs = [W.make_q(w1, 0, s_, device="cuda") for s_ in range(8)]
     out = torch.empty((w1.batch, w1.q_heads, w1.head_dim), dtype=torch.float32, device="cuda")
-    ws = k.new_fp8_workspace(dims, Tmax, args.n_split)
+    ws = (k.new_mxfp4_workspace if mx else k.new_fp8_workspace)(dims, Tmax, args.n_split)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -359,10 +384,20 @@ def fp8_main(args):
         Ts[c] = T
         q = qs[i % len(qs)]
 
-        def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
-            k.kivi_fp8_append(dims, caches[c], 0, T_before, kj, vj)
-            k.kivi_fp8_decode_attn(dims, caches[c], 0, T, q, w1.sm_scale, out, ws, args.n_split)
-        return call, fp8_decode_bytes(w1, T), fp8_append_bytes(w1)
+        if mx and not args.n_split:
+            call = k.prepare_mxfp4_step(dims, caches[c], 0, T_before, kn[j], vn[j], q,
+                                        w1.sm_scale, out, ws)
+        elif mx:
+            def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
+                k.kivi_mxfp4_append(dims, caches[c], 0, T_before, kj, vj)
+                k.kivi_mxfp4_decode_attn(dims, caches[c], 0, T, q, w1.sm_scale, out, ws,
+                                         args.n_split)
+        else:
+            def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
+                k.kivi_fp8_append(dims, caches[c], 0, T_before, kj, vj)
+                k.kivi_fp8_decode_attn(dims, caches[c], 0, T, q, w1.sm_scale, out, ws,
+                                       args.n_split)
+        return call, dec_bytes(w1, T), app_bytes(w1)
 
     for i in range(args.warmup):
         prepare(i)[0]()
@@ -401,17 +436,20 @@ def fp8_main(args):
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8+f16+f32",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4+f16+f32" if mx else "fp8+f16+f32",
         "data": "synthetic (seeded N(0,1) K/V/Q with x50 Key outlier channels and x100 Value "
-                "outlier tokens; per-head FP8 scales from the prompt's largest magnitude)",
+                "outlier tokens; " + ("MXFP4 block scales from the data)" if mx else
+                                      "per-head FP8 scales from the prompt's largest magnitude)"),
         "config": {"workload": w.name, "codec": args.codec, "batch": w1.batch,
                    "kv_heads": w1.kv_heads, "q_heads": w1.q_heads, "head_dim": w1.head_dim,
                    "tokens": w1.tokens, "layer_caches": copies,
-                   "step": "kivi_fp8_append + kivi_fp8_decode_attn",
+                   "step": ("kivi_mxfp4_append + kivi_mxfp4_decode_attn" if mx
+                            else "kivi_fp8_append + kivi_fp8_decode_attn"),
                    "launch": "one HIP graph of the timed steps"},
         "tokens_per_s": round(w1.batch * args.steps / wall, 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "fp8_decode_kernel (+ fp8_append_kernel)",
+        "roofline": {"bound": "hbm", "kernel": ("mx_decode_kernel (+ mx_append_kernel)" if mx
+                                                else "fp8_decode_kernel (+ fp8_append_kernel)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(launch_bytes / args.steps),

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libkivi.so")
 
-SOURCES = ["kivi_api.cpp", "quantize.hip", "decode.hip", "fp8.hip", "read_probe.hip"]
+SOURCES = ["kivi_api.cpp", "quantize.hip", "decode.hip", "fp8.hip", "mxfp4.hip", "read_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

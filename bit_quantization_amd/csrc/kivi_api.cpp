@@ -355,9 +355,145 @@ kivi::Fp8View fp8_view(const kivi_fp8_dims* d, const kivi_fp8_cache* c, int laye
   return L;
 }
 
+// ---- MXFP4 codec -------------------------------------------------------------------
+
+kivi_status check_mx_dims(const kivi_mxfp4_dims* d) {
+  if (!d) return fail(KIVI_ERR_ARG, "dims is NULL");
+  if (d->reserved != 0) return fail(KIVI_ERR_ARG, "reserved = %d must be 0", d->reserved);
+  const kivi_fp8_dims f{d->layers, d->batch, d->kv_heads, d->q_heads, d->head_dim, KIVI_FP8_E4M3,
+                        d->max_tokens};
+  return check_fp8_dims(&f);                       // the same shape rules
+}
+
+void mx_sizes(const kivi_mxfp4_dims* d, size_t out[4]) {
+  const size_t unit = (size_t)d->layers * d->batch * d->kv_heads * (size_t)d->max_tokens;
+  out[0] = unit * (d->head_dim / 2);                 // k
+  out[1] = unit * (d->head_dim / 32);                // k_scale
+  out[2] = out[0];                                   // v
+  out[3] = out[1];                                   // v_scale
+}
+
+kivi_status check_mx_common(const kivi_mxfp4_dims* d, const kivi_mxfp4_cache* c, int32_t layer) {
+  kivi_status st = check_mx_dims(d);
+  if (st != KIVI_OK) return st;
+  if (!c) return fail(KIVI_ERR_ARG, "cache is NULL");
+  const void* p[4] = {c->k, c->k_scale, c->v, c->v_scale};
+  static const char* names[4] = {"k", "k_scale", "v", "v_scale"};
+  for (int i = 0; i < 4; ++i) {
+    if (!p[i]) return fail(KIVI_ERR_ARG, "cache.%s is NULL", names[i]);
+    if (!aligned16(p[i])) return fail(KIVI_ERR_ALIGN, "cache.%s is not 16-byte aligned", names[i]);
+  }
+  if (layer < 0 || layer >= d->layers)
+    return fail(KIVI_ERR_ARG, "layer = %d outside [0, %d)", layer, d->layers);
+  return KIVI_OK;
+}
+
+kivi::MxView mx_view(const kivi_mxfp4_dims* d, const kivi_mxfp4_cache* c, int layer) {
+  size_t sz[4];
+  mx_sizes(d, sz);
+  const size_t Ld = (size_t)d->layers;
+  kivi::MxView L;
+  L.k = static_cast<uint8_t*>(c->k) + layer * (sz[0] / Ld);
+  L.k_scale = static_cast<uint8_t*>(c->k_scale) + layer * (sz[1] / Ld);
+  L.v = static_cast<uint8_t*>(c->v) + layer * (sz[2] / Ld);
+  L.v_scale = static_cast<uint8_t*>(c->v_scale) + layer * (sz[3] / Ld);
+  L.B = d->batch;
+  L.H = d->kv_heads;
+  L.Tmax = d->max_tokens;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
+
+kivi_status kivi_mxfp4_cache_sizes(const kivi_mxfp4_dims* dims, size_t bytes[4]) {
+  kivi_status st = check_mx_dims(dims);
+  if (st != KIVI_OK) return st;
+  if (!bytes) return fail(KIVI_ERR_ARG, "bytes is NULL");
+  mx_sizes(dims, bytes);
+  return ok();
+}
+
+kivi_status kivi_mxfp4_quantize(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                                int32_t layer, const void* k, const void* v, int64_t T,
+                                int64_t ld_tokens, void* stream) {
+  kivi_status st = check_mx_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  if (T < 0) return fail(KIVI_ERR_ARG, "T = %lld is negative", (long long)T);
+  if (T > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T = %lld exceeds max_tokens = %lld", (long long)T,
+                (long long)dims->max_tokens);
+  if (ld_tokens < T)
+    return fail(KIVI_ERR_ARG, "ld_tokens = %lld < T = %lld", (long long)ld_tokens, (long long)T);
+  if (T == 0) return ok();
+  if (!k || !v) return fail(KIVI_ERR_ARG, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(KIVI_ERR_ALIGN, "k or v is not 16-byte aligned");
+  hipError_t e = kivi::launch_mx_quantize(mx_view(dims, cache, layer), static_cast<const __half*>(k),
+                                          static_cast<const __half*>(v), ld_tokens, T,
+                                          static_cast<hipStream_t>(stream));
+  return device_status(e, "kivi_mxfp4_quantize launch");
+}
+
+kivi_status kivi_mxfp4_append(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                              int32_t layer, int64_t T_before, const void* k_new,
+                              const void* v_new, void* stream) {
+  kivi_status st = check_mx_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  if (T_before < 0) return fail(KIVI_ERR_ARG, "T_before = %lld is negative", (long long)T_before);
+  if (T_before + 1 > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T_before + 1 = %lld exceeds max_tokens = %lld",
+                (long long)(T_before + 1), (long long)dims->max_tokens);
+  if (!k_new || !v_new) return fail(KIVI_ERR_ARG, "k_new or v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(KIVI_ERR_ALIGN, "k_new or v_new is not 16-byte aligned");
+  hipError_t e = kivi::launch_mx_append(mx_view(dims, cache, layer),
+                                        static_cast<const __half*>(k_new),
+                                        static_cast<const __half*>(v_new), T_before,
+                                        static_cast<hipStream_t>(stream));
+  return device_status(e, "kivi_mxfp4_append launch");
+}
+
+kivi_status kivi_mxfp4_decode_workspace_bytes(const kivi_mxfp4_dims* dims, int64_t T,
+                                              int32_t n_split, size_t* bytes) {
+  kivi_status st = check_mx_dims(dims);
+  if (st != KIVI_OK) return st;
+  if (!bytes) return fail(KIVI_ERR_ARG, "bytes is NULL");
+  if (T < 1 || T > dims->max_tokens)
+    return fail(T < 1 ? KIVI_ERR_ARG : KIVI_ERR_CAPACITY, "T = %lld outside [1, max_tokens]",
+                (long long)T);
+  if (n_split < 0) return fail(KIVI_ERR_ARG, "n_split = %d is negative", n_split);
+  *bytes = kivi::plan_fp8_decode(dims->batch, dims->kv_heads, dims->q_heads, T, n_split).ws_total;
+  return ok();
+}
+
+kivi_status kivi_mxfp4_decode_attn(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                                   int32_t layer, int64_t T, const void* q, float sm_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   int32_t n_split, void* stream) {
+  kivi_status st = check_mx_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  if (T < 1) return fail(KIVI_ERR_ARG, "T = %lld must be >= 1", (long long)T);
+  if (T > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T = %lld exceeds max_tokens = %lld", (long long)T,
+                (long long)dims->max_tokens);
+  if (n_split < 0) return fail(KIVI_ERR_ARG, "n_split = %d is negative", n_split);
+  if (!q || !out) return fail(KIVI_ERR_ARG, "q or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(KIVI_ERR_ALIGN, "q or out is not 16-byte aligned");
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(KIVI_ERR_ARG, "sm_scale is not finite");
+  const kivi::Fp8Plan plan =
+      kivi::plan_fp8_decode(dims->batch, dims->kv_heads, dims->q_heads, T, n_split);
+  if (!workspace) return fail(KIVI_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(KIVI_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < plan.ws_total)
+    return fail(KIVI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                plan.ws_total);
+  hipError_t e = kivi::launch_mx_decode(mx_view(dims, cache, layer), dims->q_heads, T,
+                                        static_cast<const __half*>(q), sm_scale, out, workspace,
+                                        plan, static_cast<hipStream_t>(stream));
+  return device_status(e, "kivi_mxfp4_decode_attn launch");
+}
 
 kivi_status kivi_fp8_cache_sizes(const kivi_fp8_dims* dims, size_t bytes[4]) {
   kivi_status st = check_fp8_dims(dims);

@@ -186,6 +186,31 @@ hipError_t launch_fp8_decode(const Fp8View& L, int q_heads, int64_t T, const __h
                              float sm_scale, float* out, void* ws, const Fp8Plan& plan,
                              hipStream_t s);
 
+// ---- MXFP4 KV codec ---------------------------------------------------------------
+// One layer of an MXFP4 cache, per (sequence, KV head): Key codes [Tmax][d/2] bytes and
+// scales [Tmax][d/32]; Value codes in 32-token runs [Tmax/32][d][16] bytes and scales
+// [Tmax/32][d/32][32] (E8M0 codes).
+struct MxView {
+  uint8_t* k;
+  uint8_t* k_scale;
+  uint8_t* v;
+  uint8_t* v_scale;
+  int B, H;
+  int64_t Tmax;
+  __host__ __device__ int64_t k_pair() const { return Tmax * (kHeadDim / 2); }
+  __host__ __device__ int64_t ks_pair() const { return Tmax * (kHeadDim / 32); }
+  __host__ __device__ int64_t v_pair() const { return Tmax * (kHeadDim / 2); }
+  __host__ __device__ int64_t vs_pair() const { return Tmax * (kHeadDim / 32); }
+};
+hipError_t launch_mx_quantize(const MxView& L, const __half* k, const __half* v, int64_t ld,
+                              int64_t T, hipStream_t s);
+hipError_t launch_mx_append(const MxView& L, const __half* k_new, const __half* v_new, int64_t t,
+                            hipStream_t s);
+// Planned as the FP8 decode (32-token blocks): plan_fp8_decode.
+hipError_t launch_mx_decode(const MxView& L, int q_heads, int64_t T, const __half* q,
+                            float sm_scale, float* out, void* ws, const Fp8Plan& plan,
+                            hipStream_t s);
+
 // Measurement aid: a plain read of `bytes` (a multiple of 16) with kStreamReadBlocks
 // workgroups of 256 threads; sink holds one word per thread.
 constexpr int kStreamReadBlocks = 8192;

@@ -30,6 +30,8 @@ EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_appen
            "kivi_stream_read", "kivi_fp8_cache_sizes",
            "kivi_fp8_quantize", "kivi_fp8_append", "kivi_fp8_decode_workspace_bytes",
            "kivi_fp8_decode_attn",
+           "kivi_mxfp4_cache_sizes", "kivi_mxfp4_quantize", "kivi_mxfp4_append",
+           "kivi_mxfp4_decode_workspace_bytes", "kivi_mxfp4_decode_attn",
            "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
            "kivi_abi_version")
 
@@ -80,6 +82,20 @@ class kivi_fp8_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in FP8_BUFFERS]
 
 
+class kivi_mxfp4_dims(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64)]
+
+
+MX_BUFFERS = ("k", "k_scale", "v", "v_scale")
+
+
+class kivi_mxfp4_cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in MX_BUFFERS]
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing; build it with `python bit_quantization_amd/build.py` "
@@ -89,6 +105,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                             ctypes.c_size_t)
     D, C = ctypes.POINTER(kivi_dims), ctypes.POINTER(kivi_cache)
     PG = ctypes.POINTER(kivi_paging)
+    MD, MC = ctypes.POINTER(kivi_mxfp4_dims), ctypes.POINTER(kivi_mxfp4_cache)
     sig = {
         "kivi_cache_sizes": (I32, [D, ctypes.POINTER(SZ)]),
         "kivi_quantize_k": (I32, [D, C, I32, P, I64, I64, P]),
@@ -117,6 +134,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_fp8_decode_attn": (I32, [ctypes.POINTER(kivi_fp8_dims),
                                        ctypes.POINTER(kivi_fp8_cache), I32, I64, P, F32, P, P,
                                        SZ, I32, P]),
+        "kivi_mxfp4_cache_sizes": (I32, [MD, ctypes.POINTER(SZ)]),
+        "kivi_mxfp4_quantize": (I32, [MD, MC, I32, P, P, I64, I64, P]),
+        "kivi_mxfp4_append": (I32, [MD, MC, I32, I64, P, P, P]),
+        "kivi_mxfp4_decode_workspace_bytes": (I32, [MD, I64, I32, ctypes.POINTER(SZ)]),
+        "kivi_mxfp4_decode_attn": (I32, [MD, MC, I32, I64, P, F32, P, P, SZ, I32, P]),
         "kivi_last_error": (ctypes.c_char_p, []),
         "kivi_abi_version": (I32, []),
     }
@@ -550,6 +572,114 @@ def kivi_fp8_decode_attn(dims: Fp8Dims, cache: Fp8Cache, layer: int, T: int, q: 
                                      _ptr(out, torch.float32, "out", nq),
                                      _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                      n_split, _stream(stream)))
+
+
+# ---- MXFP4 KV cache --------------------------------------------------------------------
+
+@dataclass
+class MxDims:
+    layers: int
+    batch: int
+    kv_heads: int
+    q_heads: int
+    head_dim: int
+    max_tokens: int
+
+    def c(self) -> kivi_mxfp4_dims:
+        return kivi_mxfp4_dims(self.layers, self.batch, self.kv_heads, self.q_heads,
+                               self.head_dim, 0, self.max_tokens)
+
+
+def kivi_mxfp4_cache_sizes(dims: MxDims):
+    out = (ctypes.c_size_t * 4)()
+    _check(_lib.kivi_mxfp4_cache_sizes(ctypes.byref(dims.c()), out))
+    return list(out)
+
+
+class MxCache:
+    """The four caller-owned device buffers of an MXFP4 cache (zero-filled)."""
+
+    def __init__(self, dims: MxDims, device="cuda"):
+        self.dims = dims
+        self.buffers = {n: torch.zeros(sz, dtype=torch.uint8, device=device)
+                        for n, sz in zip(MX_BUFFERS, kivi_mxfp4_cache_sizes(dims))}
+
+    def c(self) -> kivi_mxfp4_cache:
+        return kivi_mxfp4_cache(*[self.buffers[n].data_ptr() for n in MX_BUFFERS])
+
+    def view(self, name: str):
+        d = self.dims
+        L, B, H, T, D = d.layers, d.batch, d.kv_heads, d.max_tokens, d.head_dim
+        buf = self.buffers[name]
+        if name == "k":
+            return buf.view(L, B, H, T, D // 2)
+        if name == "k_scale":
+            return buf.view(L, B, H, T, D // 32)
+        if name == "v":
+            return buf.view(L, B, H, T // 32, D, 16)
+        return buf.view(L, B, H, T // 32, D // 32, 32)
+
+
+def kivi_mxfp4_quantize(dims: MxDims, cache: MxCache, layer: int, k: torch.Tensor,
+                        v: torch.Tensor, T: int, ld_tokens: int | None = None, stream=None):
+    ld = T if ld_tokens is None else ld_tokens
+    need = dims.batch * dims.kv_heads * ld * dims.head_dim if T else None
+    _check(_lib.kivi_mxfp4_quantize(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                    _ptr(k, torch.float16, "k", need),
+                                    _ptr(v, torch.float16, "v", need), T, ld, _stream(stream)))
+
+
+def kivi_mxfp4_append(dims: MxDims, cache: MxCache, layer: int, T_before: int, k_new, v_new,
+                      stream=None):
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    _check(_lib.kivi_mxfp4_append(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                  T_before, _ptr(k_new, torch.float16, "k_new", need),
+                                  _ptr(v_new, torch.float16, "v_new", need), _stream(stream)))
+
+
+def kivi_mxfp4_decode_workspace_bytes(dims: MxDims, T: int, n_split: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.kivi_mxfp4_decode_workspace_bytes(ctypes.byref(dims.c()), T, n_split,
+                                                  ctypes.byref(n)))
+    return n.value
+
+
+def new_mxfp4_workspace(dims: MxDims, T: int, n_split: int = 0, device="cuda") -> torch.Tensor:
+    return torch.zeros(kivi_mxfp4_decode_workspace_bytes(dims, T, n_split), dtype=torch.uint8,
+                       device=device)
+
+
+def kivi_mxfp4_decode_attn(dims: MxDims, cache: MxCache, layer: int, T: int, q: torch.Tensor,
+                           sm_scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                           n_split: int = 0, stream=None):
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    _check(_lib.kivi_mxfp4_decode_attn(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                       T, _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
+                                       _ptr(out, torch.float32, "out", nq),
+                                       _ptr(workspace, torch.uint8, "workspace"),
+                                       workspace.numel(), n_split, _stream(stream)))
+
+
+def prepare_mxfp4_step(dims: MxDims, cache: MxCache, layer: int, T_before: int, k_new, v_new,
+                       q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                       workspace: torch.Tensor, stream=None):
+    """One decode step (append, then attend over T_before + 1 tokens) with its
+    arguments marshalled once; returns a function of no arguments making the calls."""
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    d, c = ctypes.byref(dims.c()), ctypes.byref(cache.c())
+    st = _stream(stream)
+    a1 = (d, c, layer, T_before, _ptr(k_new, torch.float16, "k_new", need),
+          _ptr(v_new, torch.float16, "v_new", need), st)
+    a2 = (d, c, layer, T_before + 1, _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
+          _ptr(out, torch.float32, "out", nq), _ptr(workspace, torch.uint8, "workspace"),
+          workspace.numel(), 0, st)
+    f1, f2 = _lib.kivi_mxfp4_append, _lib.kivi_mxfp4_decode_attn
+
+    def call():
+        _check(f1(*a1))
+        _check(f2(*a2))
+    return call
 
 
 def kivi_abi_version() -> int:

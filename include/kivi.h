@@ -385,6 +385,67 @@ kivi_status kivi_fp8_decode_attn(const kivi_fp8_dims* dims, const kivi_fp8_cache
                                  float* out, void* workspace, size_t workspace_bytes,
                                  int32_t n_split, void* stream);
 
+/* ---- MXFP4 codec ----------------------------------------------------------------
+ * "KV Cache Quantization (KIVI & FP4)" §4, "Hardware Micro-Scaling": four-bit E2M1
+ * values (1 sign, 2 exponent, 1 mantissa bit) in blocks sharing an 8-bit scale.  This
+ * is the OCP MXFP4 format the page names: blocks of 32 consecutive channels of one
+ * token (Keys and Values alike) share the scale X = 2^s, stored as the E8M0 code
+ * s + 127, with s = floor(log2(max |x|)) - 2 (a block of zeros: s = -127); element
+ * code = the E2M1 value nearest to x / X (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6),
+ * ties to the even code, saturating at 6, sign kept.  Every token is coded on its own
+ * (no float16 window).  Decoding: value(code) * X. */
+typedef struct {
+  int32_t layers, batch, kv_heads, q_heads;
+  int32_t head_dim;     /* 128 */
+  int32_t reserved;     /* must be 0 */
+  int64_t max_tokens;   /* a positive multiple of 32 */
+} kivi_mxfp4_dims;
+
+/* Device buffers, caller-owned, 16-byte aligned, sizes from kivi_mxfp4_cache_sizes:
+ *   k        u8 [L][B][H_kv][T_max][d/2]: token t's codes, channel 2i in the low
+ *            nibble of byte i, 2i+1 in the high nibble.
+ *   k_scale  u8 [L][B][H_kv][T_max][d/32]: E8M0 codes of token t's blocks.
+ *   v        u8 [L][B][H_kv][T_max/32][d][16]: for each 32-token run and channel, the
+ *            run's 32 codes (two per byte, low nibble first) in token order 0-3,
+ *            16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31.
+ *   v_scale  u8 [L][B][H_kv][T_max/32][d/32][32]: E8M0 codes of each run's tokens per
+ *            block, in the same token order. */
+typedef struct {
+  void* k;
+  void* k_scale;
+  void* v;
+  void* v_scale;
+} kivi_mxfp4_cache;
+
+/* Bytes of the four buffers (host-only). */
+kivi_status kivi_mxfp4_cache_sizes(const kivi_mxfp4_dims* dims, size_t bytes[4]);
+
+/* Code tokens [0, T) of float16 k, v [B][H_kv][ld_tokens][d] into `layer` (0 <= T <=
+ * T_max).  Codes and scales of tokens T .. (end of T's 32-token run) are written as 0. */
+kivi_status kivi_mxfp4_quantize(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                                int32_t layer, const void* k, const void* v, int64_t T,
+                                int64_t ld_tokens, void* stream);
+
+/* Code one new token per sequence (float16 k_new, v_new [B][H_kv][d]) at position
+ * T_before (T_before + 1 <= T_max); the run's other tokens keep their codes. */
+kivi_status kivi_mxfp4_append(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                              int32_t layer, int64_t T_before, const void* k_new,
+                              const void* v_new, void* stream);
+
+/* Workspace bytes of kivi_mxfp4_decode_attn (as kivi_fp8_decode_workspace_bytes). */
+kivi_status kivi_mxfp4_decode_workspace_bytes(const kivi_mxfp4_dims* dims, int64_t T,
+                                              int32_t n_split, size_t* bytes);
+
+/* Decode attention over the T cached MXFP4 tokens of `layer`: as kivi_decode_attn,
+ * with k_t and v_t the decoded values.  The values are widened to float16 with their
+ * block scale (exact while the scaled value is a float16 number: always for blocks
+ * whose largest magnitude is 2^-20 or more) and attended on the float16 matrix cores
+ * in float32.  Workspace contract as kivi_decode_attn's. */
+kivi_status kivi_mxfp4_decode_attn(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                                   int32_t layer, int64_t T, const void* q, float sm_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   int32_t n_split, void* stream);
+
 /* Measurement aid, not part of the method: read `bytes` (a multiple of 16) of device
  * memory at `buf` once with plain 16-byte loads (8192 workgroups of 256 threads,
  * grid-stride) and write one XOR word per thread to `sink` (device, at least

@@ -79,12 +79,18 @@ def e2m1_decode(codes: np.ndarray) -> np.ndarray:
     return lut[np.asarray(codes, np.uint8)]
 
 
+def block_exponents(blocks: np.ndarray) -> np.ndarray:
+    """s of each block (last axis) of float16 values (reading R17): floor(log2 amax)
+    is frexp's exponent minus one (exact)."""
+    amax = np.max(np.abs(np.asarray(blocks, np.float64)), axis=-1)
+    _, e = np.frexp(amax)
+    s = np.clip(e.astype(np.int64) - 1 - EMAX_ELEM, -127, 127)
+    return np.where(amax == 0.0, -127, s)
+
+
 def block_exponent(block: np.ndarray) -> int:
     """s of one block of float16 values (reading R17)."""
-    amax = float(np.max(np.abs(np.asarray(block, np.float64))))
-    if amax == 0.0:
-        return -127
-    return int(np.clip(np.floor(np.log2(amax)) - EMAX_ELEM, -127, 127))
+    return int(block_exponents(np.asarray(block)[None])[0])
 
 
 def quantize_mx(x: np.ndarray):
@@ -93,9 +99,7 @@ def quantize_mx(x: np.ndarray):
     x = np.asarray(x, np.float16)
     *lead, n = x.shape
     blocks = x.reshape(*lead, n // BLOCK, BLOCK)
-    s = np.zeros((*lead, n // BLOCK), np.int64)
-    for idx in np.ndindex(*s.shape):
-        s[idx] = block_exponent(blocks[idx])
+    s = block_exponents(blocks)
     y = blocks.astype(F32) / np.exp2(s.astype(np.float64))[..., None].astype(F32)
     codes = e2m1_encode(y).reshape(*lead, n)
     return codes, (s + 127).astype(np.uint8)
