@@ -467,10 +467,14 @@ kivi_status kivi_mxfp4_decode_workspace_bytes(const kivi_mxfp4_dims* dims, int64
   return ok();
 }
 
-kivi_status kivi_mxfp4_decode_attn(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
-                                   int32_t layer, int64_t T, const void* q, float sm_scale,
-                                   float* out, void* workspace, size_t workspace_bytes,
-                                   int32_t n_split, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kivi_status mx_decode_common(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                             int32_t layer, int64_t T, const void* q, float sm_scale, float* out,
+                             void* workspace, size_t workspace_bytes, int32_t n_split,
+                             const void* k_new, const void* v_new, void* stream) {
   kivi_status st = check_mx_common(dims, cache, layer);
   if (st != KIVI_OK) return st;
   if (T < 1) return fail(KIVI_ERR_ARG, "T = %lld must be >= 1", (long long)T);
@@ -491,8 +495,40 @@ kivi_status kivi_mxfp4_decode_attn(const kivi_mxfp4_dims* dims, const kivi_mxfp4
                 plan.ws_total);
   hipError_t e = kivi::launch_mx_decode(mx_view(dims, cache, layer), dims->q_heads, T,
                                         static_cast<const __half*>(q), sm_scale, out, workspace,
-                                        plan, static_cast<hipStream_t>(stream));
-  return device_status(e, "kivi_mxfp4_decode_attn launch");
+                                        plan, static_cast<const __half*>(k_new),
+                                        static_cast<const __half*>(v_new),
+                                        static_cast<hipStream_t>(stream));
+  return device_status(e, "kivi_mxfp4 decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_mxfp4_decode_attn(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                                   int32_t layer, int64_t T, const void* q, float sm_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   int32_t n_split, void* stream) {
+  return mx_decode_common(dims, cache, layer, T, q, sm_scale, out, workspace, workspace_bytes,
+                          n_split, nullptr, nullptr, stream);
+}
+
+kivi_status kivi_mxfp4_append_decode(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                                     int32_t layer, int64_t T_before, const void* k_new,
+                                     const void* v_new, const void* q, float sm_scale,
+                                     float* out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  kivi_status st = check_mx_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  if (T_before < 0) return fail(KIVI_ERR_ARG, "T_before = %lld is negative", (long long)T_before);
+  if (T_before + 1 > dims->max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "T_before + 1 = %lld exceeds max_tokens = %lld",
+                (long long)(T_before + 1), (long long)dims->max_tokens);
+  if (!k_new || !v_new) return fail(KIVI_ERR_ARG, "k_new or v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(KIVI_ERR_ALIGN, "k_new or v_new is not 16-byte aligned");
+  return mx_decode_common(dims, cache, layer, T_before + 1, q, sm_scale, out, workspace,
+                          workspace_bytes, 0, k_new, v_new, stream);
 }
 
 kivi_status kivi_fp8_cache_sizes(const kivi_fp8_dims* dims, size_t bytes[4]) {

@@ -206,10 +206,11 @@ hipError_t launch_mx_quantize(const MxView& L, const __half* k, const __half* v,
                               int64_t T, hipStream_t s);
 hipError_t launch_mx_append(const MxView& L, const __half* k_new, const __half* v_new, int64_t t,
                             hipStream_t s);
-// Planned as the FP8 decode (32-token blocks): plan_fp8_decode.
+// Planned as the FP8 decode (32-token blocks): plan_fp8_decode.  With k_new / v_new
+// (float16 [B][H][d]) set, the launch also codes token T - 1 from them before reading it.
 hipError_t launch_mx_decode(const MxView& L, int q_heads, int64_t T, const __half* q,
                             float sm_scale, float* out, void* ws, const Fp8Plan& plan,
-                            hipStream_t s);
+                            const __half* k_new, const __half* v_new, hipStream_t s);
 
 // Measurement aid: a plain read of `bytes` (a multiple of 16) with kStreamReadBlocks
 // workgroups of 256 threads; sink holds one word per thread.

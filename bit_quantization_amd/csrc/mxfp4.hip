@@ -17,7 +17,8 @@
 // cores, probabilities kept in registers).  The E2M1 values widen to float16 exactly;
 // a Key lane's 32 channels are one MX block of one token, so its scale is applied by
 // the widening itself (v_cvt_scalef32_pk_f16_fp4); a Value lane holds 8 tokens of one
-// channel, each with its own scale, applied with v_ldexp_f16.  Both are exact while
+// channel, each with its own scale, applied by a packed float16 multiply (v_ldexp_f16
+// when a scale is below float16's normal range).  Both are exact while
 // the scaled value is a float16 number: always for the largest values of a block
 // (s <= 13 for float16 inputs), and the values that fall below float16's range belong
 // to blocks whose largest magnitude is under 2^-20.
@@ -133,13 +134,13 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(MxView L, const __half
         reinterpret_cast<const uint32_t*>(&vscale[0][0])[threadIdx.x];
 }
 
-// grid = B*H, 64 threads: token t of each (sequence, KV head); lane l codes channels
-// 2l, 2l+1 (16 lanes per MX block).  The Value nibbles are merged into their bytes,
-// whose other nibble belongs to the run's neighbouring position.
-__global__ __launch_bounds__(64) void mx_append_kernel(MxView L, const __half* __restrict__ kn,
-                                                       const __half* __restrict__ vn, int64_t t) {
-  const int64_t pair = blockIdx.x;
-  const int lane = threadIdx.x;
+// Token t of one (sequence, KV head), coded by one wave: lane l codes channels 2l, 2l+1
+// (16 lanes per MX block).  The Value nibbles are merged into their bytes, whose other
+// nibble belongs to the run's neighbouring position.
+__device__ __forceinline__ void mx_code_token(const MxView& L, int64_t pair,
+                                              const __half* __restrict__ kn,
+                                              const __half* __restrict__ vn, int64_t t) {
+  const int lane = threadIdx.x & 63;
   const __half2 k2 = reinterpret_cast<const __half2*>(kn + pair * D)[lane];
   const __half2 v2 = reinterpret_cast<const __half2*>(vn + pair * D)[lane];
   const float k0 = __low2float(k2), k1 = __high2float(k2);
@@ -169,6 +170,12 @@ __global__ __launch_bounds__(64) void mx_append_kernel(MxView L, const __half* _
   }
 }
 
+// grid = B*H, 64 threads: token t of each (sequence, KV head).
+__global__ __launch_bounds__(64) void mx_append_kernel(MxView L, const __half* __restrict__ kn,
+                                                       const __half* __restrict__ vn, int64_t t) {
+  mx_code_token(L, blockIdx.x, kn, vn, t);
+}
+
 // ---- decode ---------------------------------------------------------------------------
 
 struct MxDecodeArgs {
@@ -181,9 +188,20 @@ struct MxDecodeArgs {
   int64_t nblk;         // 32-token runs per pair
   int nw;               // workgroups per pair
   float qscale;         // sm_scale * log2(e)
+  const __half* k_new;  // [P][D]: token new_t is coded by this launch (new_t >= 0)
+  const __half* v_new;
+  int64_t new_t;
 };
 
 constexpr int kMxWavesPerSimd = 4;
+
+// The loads of one 32-token run of one lane.
+struct MxRun {
+  u32x4 kw[2];          // Key codes: tile nt, token t0 + 16nt + lo, MX block j (16 bytes)
+  uint32_t ksc[2];      // that token's 4 Key scale codes
+  uint32_t vw[8];       // Value codes: channel 16mt + lo, run positions 8j .. 8j+7
+  u32x2 vsc[kNBlk];     // Value scale codes of positions 8j .. 8j+7, per MX block
+};
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -194,6 +212,16 @@ __device__ __forceinline__ f16x8 widen8_scaled(uint32_t w, float scale) {
   const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2);
   const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3);
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The scales 2^s of two Value positions as a float16 pair, from a word holding their
+// E8M0 codes in bytes b and b + 1 (b = 0 or 2): the fields code - 112 shifted into the
+// exponent bits.  Valid for codes 113 .. 142 (s in [-14, 15], the float16-normal
+// powers of two); float16 inputs give codes of at most 140 (s <= 13).
+template <int B>
+__device__ __forceinline__ f16x2 pow2_pair(uint32_t codes) {
+  const uint32_t spread = __builtin_amdgcn_perm(0u, codes, B == 0 ? 0x0C010C00u : 0x0C030C02u);
+  return __builtin_bit_cast(f16x2, (spread - 0x00700070u) << 10);
 }
 
 // Token of the run that k-slot e (0..7) of lane group j supplies to P.V.
@@ -220,6 +248,9 @@ __global__ __launch_bounds__(256 * kMxWavesPerSimd, 1) void mx_decode_kernel(MxD
   const int64_t b_lo = a.nblk * s / a.nw, b_hi = a.nblk * (s + 1) / a.nw;
 
   if (threadIdx.x == 0) counter = 0;
+  // An appended token: its run is the pair's last, which only the last workgroup
+  // reads; one of its waves codes the token before the barrier below.
+  if (a.new_t >= 0 && s == a.nw - 1 && wave == 0) mx_code_token(L, pair, a.k_new, a.v_new, a.new_t);
   const int n_parts = a.nw;
   const int64_t pair_floats = (int64_t)n_parts * GQA * PSTRIDE;
   const __amdgpu_buffer_rsrc_t parts = make_rsrc(a.part + pair * pair_floats, pair_floats * 4);
@@ -247,30 +278,34 @@ __global__ __launch_bounds__(256 * kMxWavesPerSimd, 1) void mx_decode_kernel(MxD
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int item = grab_item(&counter); b_lo + item < b_hi; item = grab_item(&counter)) {
-    const int64_t blk = b_lo + item;
+  auto load_run = [&](int64_t blk, MxRun& R) {
     const int64_t t0 = blk * kMxRun;
-    // Key codes: tile nt, token t0 + 16nt + lo, MX block j (16 bytes), and its scale
-    u32x4 kw[2];
-    uint32_t ksc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int64_t tok = t0 + 16 * nt + lo;
-      kw[nt] = __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(tok * kKRow + 16 * j), 0, 0);
-      ksc[nt] = __builtin_amdgcn_raw_buffer_load_b32(ksres, (int)(tok * kNBlk), 0, 0);
+      R.kw[nt] = __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(tok * kKRow + 16 * j), 0, 0);
+      R.ksc[nt] = __builtin_amdgcn_raw_buffer_load_b32(ksres, (int)(tok * kNBlk), 0, 0);
     }
-    // Value codes: channel 16mt + lo, run positions 8j .. 8j+7 (4 bytes); scales of
-    // those positions for MX block mt / 2 (8 bytes)
-    uint32_t vw[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-      vw[mt] = __builtin_amdgcn_raw_buffer_load_b32(
+      R.vw[mt] = __builtin_amdgcn_raw_buffer_load_b32(
           vres, (int)(blk * D * (kMxRun / 2) + (16 * mt + lo) * (kMxRun / 2) + 4 * j), 0, 0);
-    u32x2 vsc[kNBlk];
 #pragma unroll
     for (int q = 0; q < kNBlk; ++q)
-      vsc[q] = __builtin_amdgcn_raw_buffer_load_b64(
+      R.vsc[q] = __builtin_amdgcn_raw_buffer_load_b64(
           vsres, (int)(blk * kNBlk * kMxRun + q * kMxRun + 8 * j), 0, 0);
+  };
+  // (Loading the next run before computing this one, at three waves per SIMD for the
+  // registers, measured slower: 84.6 against 77.1 us per 32k step.)
+  for (int item = grab_item(&counter); b_lo + item < b_hi; item = grab_item(&counter)) {
+    const int64_t blk = b_lo + item;
+    const int64_t t0 = blk * kMxRun;
+    MxRun cur;
+    load_run(blk, cur);
+    const u32x4* kw = cur.kw;
+    const uint32_t* ksc = cur.ksc;
+    const uint32_t* vw = cur.vw;
+    const u32x2* vsc = cur.vsc;
 
     // S^T = K q^T for the two 16-token tiles
     f32x4 d[2];
@@ -313,17 +348,35 @@ __global__ __launch_bounds__(256 * kMxWavesPerSimd, 1) void mx_decode_kernel(MxD
     }
     l = l * alpha + psum;
     // O^T += V^T P^T for the eight 16-channel tiles; a Value's scale is its token's
-    // (positions past T hold code 0 and scale code 0: value 0)
+    // (positions past T hold code 0 and scale code 0: value 0).  Scale codes of 113 or
+    // more (s >= -14, every block whose largest magnitude is 2^-12 or more) become
+    // float16 pairs multiplied in packed form; a run with a smaller one anywhere in the
+    // wave scales each value with v_ldexp_f16 instead (exact down to float16's
+    // subnormals).  The rescale by alpha is skipped when no head's maximum moved.
+    bool fast = true;
+#pragma unroll
+    for (int q = 0; q < kNBlk; ++q)
+      fast &= (((vsc[q][0] + 0x0F0F0F0Fu) & (vsc[q][1] + 0x0F0F0F0Fu) & 0x80808080u) == 0x80808080u);
+    const bool all_fast = __builtin_amdgcn_ballot_w64(!fast) == 0;
+    const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       f16x8 vf = widen8_scaled(vw[mt], 1.f);
       const u32x2 sw = vsc[mt / 2];
+      if (all_fast) {
+        const f16x2 s0 = pow2_pair<0>(sw[0]), s1 = pow2_pair<2>(sw[0]);
+        const f16x2 s2 = pow2_pair<0>(sw[1]), s3 = pow2_pair<2>(sw[1]);
+        const f16x2 v0 = f16x2{vf[0], vf[1]} * s0, v1 = f16x2{vf[2], vf[3]} * s1;
+        const f16x2 v2 = f16x2{vf[4], vf[5]} * s2, v3 = f16x2{vf[6], vf[7]} * s3;
+        vf = f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sc = (int)((sw[e / 4] >> (8 * (e % 4))) & 0xFF) - 127;
-        vf[e] = __builtin_amdgcn_ldexph(vf[e], sc);
+        for (int e = 0; e < 8; ++e) {
+          const int sc = (int)((sw[e / 4] >> (8 * (e % 4))) & 0xFF) - 127;
+          vf[e] = __builtin_amdgcn_ldexph(vf[e], sc);
+        }
       }
-      acc[mt] = acc[mt] * alpha;
+      if (rescale) acc[mt] = acc[mt] * alpha;
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, acc[mt], 0, 0, 0);
     }
@@ -367,7 +420,7 @@ hipError_t launch_mx_append(const MxView& L, const __half* k_new, const __half* 
 
 hipError_t launch_mx_decode(const MxView& L, int q_heads, int64_t T, const __half* q,
                             float sm_scale, float* out, void* ws, const Fp8Plan& plan,
-                            hipStream_t s) {
+                            const __half* k_new, const __half* v_new, hipStream_t s) {
   MxDecodeArgs a;
   a.L = L;
   a.q = q;
@@ -378,6 +431,9 @@ hipError_t launch_mx_decode(const MxView& L, int q_heads, int64_t T, const __hal
   a.nblk = (T + kMxRun - 1) / kMxRun;
   a.nw = plan.n_split;
   a.qscale = sm_scale * 1.4426950408889634f;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_t = k_new ? T - 1 : -1;
   const int gqa = q_heads / L.H;
   const dim3 grid((unsigned)((int64_t)L.B * L.H * plan.n_split));
   const dim3 block(256 * kMxWavesPerSimd);

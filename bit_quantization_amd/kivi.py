@@ -32,6 +32,7 @@ EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_appen
            "kivi_fp8_decode_attn",
            "kivi_mxfp4_cache_sizes", "kivi_mxfp4_quantize", "kivi_mxfp4_append",
            "kivi_mxfp4_decode_workspace_bytes", "kivi_mxfp4_decode_attn",
+           "kivi_mxfp4_append_decode",
            "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
            "kivi_abi_version")
 
@@ -139,6 +140,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_mxfp4_append": (I32, [MD, MC, I32, I64, P, P, P]),
         "kivi_mxfp4_decode_workspace_bytes": (I32, [MD, I64, I32, ctypes.POINTER(SZ)]),
         "kivi_mxfp4_decode_attn": (I32, [MD, MC, I32, I64, P, F32, P, P, SZ, I32, P]),
+        "kivi_mxfp4_append_decode": (I32, [MD, MC, I32, I64, P, P, P, F32, P, P, SZ, P]),
         "kivi_last_error": (ctypes.c_char_p, []),
         "kivi_abi_version": (I32, []),
     }
@@ -663,23 +665,27 @@ def kivi_mxfp4_decode_attn(dims: MxDims, cache: MxCache, layer: int, T: int, q: 
 def prepare_mxfp4_step(dims: MxDims, cache: MxCache, layer: int, T_before: int, k_new, v_new,
                        q: torch.Tensor, sm_scale: float, out: torch.Tensor,
                        workspace: torch.Tensor, stream=None):
-    """One decode step (append, then attend over T_before + 1 tokens) with its
-    arguments marshalled once; returns a function of no arguments making the calls."""
+    """kivi_mxfp4_append_decode (one decode step, one launch) with its arguments
+    marshalled once; returns a function of no arguments making the call."""
     need = dims.batch * dims.kv_heads * dims.head_dim
     nq = dims.batch * dims.q_heads * dims.head_dim
-    d, c = ctypes.byref(dims.c()), ctypes.byref(cache.c())
-    st = _stream(stream)
-    a1 = (d, c, layer, T_before, _ptr(k_new, torch.float16, "k_new", need),
-          _ptr(v_new, torch.float16, "v_new", need), st)
-    a2 = (d, c, layer, T_before + 1, _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
-          _ptr(out, torch.float32, "out", nq), _ptr(workspace, torch.uint8, "workspace"),
-          workspace.numel(), 0, st)
-    f1, f2 = _lib.kivi_mxfp4_append, _lib.kivi_mxfp4_decode_attn
+    args = (ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer, T_before,
+            _ptr(k_new, torch.float16, "k_new", need), _ptr(v_new, torch.float16, "v_new", need),
+            _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
+            _ptr(out, torch.float32, "out", nq), _ptr(workspace, torch.uint8, "workspace"),
+            workspace.numel(), _stream(stream))
+    fn = _lib.kivi_mxfp4_append_decode
 
     def call():
-        _check(f1(*a1))
-        _check(f2(*a2))
+        _check(fn(*args))
     return call
+
+
+def kivi_mxfp4_append_decode(dims: MxDims, cache: MxCache, layer: int, T_before: int, k_new,
+                             v_new, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                             workspace: torch.Tensor, stream=None):
+    prepare_mxfp4_step(dims, cache, layer, T_before, k_new, v_new, q, sm_scale, out, workspace,
+                       stream)()
 
 
 def kivi_abi_version() -> int:

@@ -446,6 +446,18 @@ kivi_status kivi_mxfp4_decode_attn(const kivi_mxfp4_dims* dims, const kivi_mxfp4
                                    float* out, void* workspace, size_t workspace_bytes,
                                    int32_t n_split, void* stream);
 
+/* One MXFP4 decode step in one launch: code the new token (as kivi_mxfp4_append) and
+ * attend over the T_before + 1 tokens (as kivi_mxfp4_decode_attn with the library's
+ * split); the last workgroup of each (sequence, KV head), the only one that reads the
+ * new token's run, codes it before reading.  Cache and output equal those of the two
+ * calls (outputs to float32 rounding).  Workspace: kivi_mxfp4_decode_workspace_bytes(
+ * dims, T_before + 1, 0). */
+kivi_status kivi_mxfp4_append_decode(const kivi_mxfp4_dims* dims, const kivi_mxfp4_cache* cache,
+                                     int32_t layer, int64_t T_before, const void* k_new,
+                                     const void* v_new, const void* q, float sm_scale,
+                                     float* out, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* Measurement aid, not part of the method: read `bytes` (a multiple of 16) of device
  * memory at `buf` once with plain 16-byte loads (8192 workgroups of 256 threads,
  * grid-stride) and write one XOR word per thread to `sink` (device, at least

@@ -158,3 +158,32 @@ def test_mxfp4_workload_32k_sampled_pairs():
                               O.pack_value_scales(oc.vs[0, 0]))
         ref = oc.attend(q[b:b + 1, h * g:(h + 1) * g].cpu().numpy(), w.sm_scale)
         assert_close(out[b, h * g:(h + 1) * g].cpu().numpy(), ref[0], f"mxfp4 32k pair {(b, h)}")
+
+
+def test_mxfp4_append_decode_equals_append_then_decode():
+    # the one-launch step against kivi_mxfp4_append + kivi_mxfp4_decode_attn on a second
+    # cache: outputs to float32 rounding, caches bit-identical; across run boundaries and
+    # with several workgroups per pair
+    k = kv()
+    B, H, g = 2, 2, 4
+    T0, steps = 61, 40
+    dims, _, _, K, V = build(B, H, g, T0 + steps, seed=13)
+    Kt, Vt = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
+    a, b_ = k.MxCache(dims), k.MxCache(dims)
+    for c in (a, b_):
+        k.kivi_mxfp4_quantize(dims, c, 0, Kt[:, :, :T0].contiguous(), Vt[:, :, :T0].contiguous(), T0)
+    wa, wb = k.new_mxfp4_workspace(dims, T0 + steps), k.new_mxfp4_workspace(dims, T0 + steps)
+    oa = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(2)
+    for t in range(T0, T0 + steps):
+        q = torch.randn((B, H * g, D), generator=gq, device="cuda").to(torch.float16)
+        kn, vn = Kt[:, :, t].contiguous(), Vt[:, :, t].contiguous()
+        k.kivi_mxfp4_append_decode(dims, a, 0, t, kn, vn, q, 0.1, oa, wa)
+        k.kivi_mxfp4_append(dims, b_, 0, t, kn, vn)
+        k.kivi_mxfp4_decode_attn(dims, b_, 0, t + 1, q, 0.1, ob, wb)
+        torch.cuda.synchronize()
+        assert np.allclose(oa.cpu().numpy(), ob.cpu().numpy(), rtol=1e-5, atol=1e-6), t
+    for name in k.MX_BUFFERS:
+        assert torch.equal(a.view(name).cpu(), b_.view(name).cpu()), name
