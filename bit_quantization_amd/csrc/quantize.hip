@@ -279,6 +279,19 @@ __device__ __forceinline__ void store_fp16_rows(const LayerView& L, const __half
 
 // ---- kernels ----------------------------------------------------------------------
 
+// LayerView's history geometry with PAGED (a page table is set) known at compile time,
+// so that the contiguous kernels carry no page-table branches: the section of a pair,
+// its rows, and where history token t of sequence b sits in it.
+template <bool PAGED>
+struct Hist {
+  int64_t sec, rows;
+  __device__ Hist(const LayerView& L, int64_t pair)
+      : sec(PAGED ? pair % L.H : pair), rows(PAGED ? L.pages << L.page_log2 : L.Tmax) {}
+  __device__ int64_t token(const LayerView& L, int64_t b, int64_t t) const {
+    return PAGED ? L.hist_token(b, t) : t;
+  }
+};
+
 // Items of one (b, h): the Tq/G Key groups (or Tq/16 Value runs) of the tokens after
 // the sink, then one item that copies the sink tokens and the r window tokens into
 // their residual rows.  grid = (ceil(items /
@@ -286,7 +299,7 @@ __device__ __forceinline__ void store_fp16_rows(const LayerView& L, const __half
 // +QW*npw - 1, its waves interleaved (wave w takes item QW*npw*x + QW*i + w for
 // i < npw).  A ragged batch gives sequence b lens.get(b, 0) <= T tokens, so its pairs
 // have no more items than the grid covers.
-template <int BITS, int G>
+template <int BITS, int G, bool PAGED>
 __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const __half* __restrict__ src,
                                                             int64_t ld, int64_t T, Lens lens,
                                                             int npw) {
@@ -303,11 +316,12 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
   for (int i = 0; i < npw; ++i) {
     const int64_t g = ((int64_t)blockIdx.x * npw + i) * QW + wave;
     if (g < ngroups) {
-      const int64_t ht = L.hist_token(pair / L.H, g * G), sec = L.section(pair);
+      const Hist<PAGED> hs(L, pair);
+      const int64_t ht = hs.token(L, pair / L.H, g * G);
+      const int64_t kc = hs.sec * hs.rows * (D * BITS / 8), ks = hs.sec * (hs.rows / G) * D;
       smx = fmaxf(smx, quantize_k_group<BITS, G>(
-                           s + g * G * D, L.k_codes + sec * L.kc_pair() + ht * (D * BITS / 8),
-                           L.k_scale + sec * L.ks_pair() + (ht / G) * D,
-                           L.k_zero + sec * L.ks_pair() + (ht / G) * D, lds[wave]));
+                           s + g * G * D, L.k_codes + kc + ht * (D * BITS / 8),
+                           L.k_scale + ks + (ht / G) * D, L.k_zero + ks + (ht / G) * D, lds[wave]));
     } else if (g == ngroups) {
       store_fp16_rows(L, s0, s + Tq * D, L.k_resid + pair * L.rs_pair(), ts.ns, ts.r, ts.ring);
     }
@@ -316,7 +330,7 @@ __global__ __launch_bounds__(64 * QW) void prefill_k_kernel(LayerView L, const _
 }
 
 // As prefill_k_kernel, over the Value runs.
-template <int BITS, int GV>
+template <int BITS, int GV, bool PAGED>
 __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const __half* __restrict__ src,
                                                             int64_t ld, int64_t T, Lens lens,
                                                             int npw) {
@@ -333,12 +347,14 @@ __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const _
   for (int i = 0; i < npw; ++i) {
     const int64_t j = ((int64_t)blockIdx.x * npw + i) * QW + wave;
     if (j < nruns) {
-      const int64_t ht = L.hist_token(pair / L.H, j * kVRun), sec = L.section(pair);
+      const Hist<PAGED> hs(L, pair);
+      const int64_t ht = hs.token(L, pair / L.H, j * kVRun);
+      const int64_t vc = hs.sec * hs.rows * (D * BITS / 8), vs = hs.sec * hs.rows * (D / GV);
       smx = fmaxf(smx, quantize_v_run<BITS, GV>(
                            s + j * kVRun * D,
-                           L.v_codes + sec * L.vc_pair() + (ht / kVRun) * (D * kVRun * BITS / 8),
-                           L.v_scale + sec * L.vs_pair() + ht * (D / GV),
-                           L.v_zero + sec * L.vs_pair() + ht * (D / GV), lds[wave]));
+                           L.v_codes + vc + (ht / kVRun) * (D * kVRun * BITS / 8),
+                           L.v_scale + vs + ht * (D / GV), L.v_zero + vs + ht * (D / GV),
+                           lds[wave]));
     } else if (j == nruns) {
       store_fp16_rows(L, s0, s + Tq * D, L.v_resid + pair * L.rs_pair(), ts.ns, ts.r, ts.ring);
     }
@@ -455,8 +471,12 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
   const int npw = items_per_wave(items, pairs);
   const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
-    hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value>), grid,
-                       dim3(64 * QW), 0, s, L, src, ld, T, lens, npw);
+    if (L.table)
+      hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value, true>), grid,
+                         dim3(64 * QW), 0, s, L, src, ld, T, lens, npw);
+    else
+      hipLaunchKernelGGL((prefill_k_kernel<decltype(b)::value, decltype(g)::value, false>), grid,
+                         dim3(64 * QW), 0, s, L, src, ld, T, lens, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
@@ -474,12 +494,20 @@ hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, 
   const int npw = items_per_wave(items, pairs);
   const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_gv(L.Gv, [&](auto gv) {
-    if (L.bits == 2)
-      hipLaunchKernelGGL((prefill_v_kernel<2, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, T, lens, npw);
+    constexpr int GV = decltype(gv)::value;
+    const bool paged = L.table != nullptr;
+    if (L.bits == 2 && !paged)
+      hipLaunchKernelGGL((prefill_v_kernel<2, GV, false>), grid, dim3(64 * QW), 0, s, L, src, ld,
+                         T, lens, npw);
+    else if (L.bits == 2)
+      hipLaunchKernelGGL((prefill_v_kernel<2, GV, true>), grid, dim3(64 * QW), 0, s, L, src, ld,
+                         T, lens, npw);
+    else if (!paged)
+      hipLaunchKernelGGL((prefill_v_kernel<4, GV, false>), grid, dim3(64 * QW), 0, s, L, src, ld,
+                         T, lens, npw);
     else
-      hipLaunchKernelGGL((prefill_v_kernel<4, decltype(gv)::value>), grid, dim3(64 * QW), 0, s, L,
-                         src, ld, T, lens, npw);
+      hipLaunchKernelGGL((prefill_v_kernel<4, GV, true>), grid, dim3(64 * QW), 0, s, L, src, ld,
+                         T, lens, npw);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;
