@@ -129,7 +129,7 @@ __device__ __forceinline__ void ragged_split(DecodeArgs& a, int64_t b) {
 // 4 SIMDs' worth.  The build turns a kernel that misses this occupancy into an error
 // (launch bounds of one workgroup per CU with a register limit derived from it).
 constexpr int waves_per_simd(int bits, int gqa, int G) {
-  return gqa > 4 ? 1 : gqa > 2 ? 2 : (bits == 2 || G == 64) ? 3 : 2;
+  return gqa > 2 ? 2 : (bits == 2 || G == 64) ? 3 : 2;
 }
 
 __device__ __forceinline__ float h2f(unsigned short h) {
@@ -521,7 +521,8 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
 // Processes the block items handed out by the queue, starting with `item` (>= n_res),
 // and writes comb[GQA][PSTRIDE] (acc with the Value-zero term folded in, m, l).  The
 // fixed-point exponents come from the pair's largest Key/Value scale, so they hold for
-// any block of the pair.  PAGED: the history is paged (a.L.table is set).
+// any block of the pair.  PAGED: the history is paged (a.L.table is set).  comb may
+// overlay lds: it is written after the last block.
 template <int BITS, int GQA, int G, bool PAGED>
 __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pair, int item, int n_res,
                                 int n_items, int64_t b_lo, int64_t b_hi, int* counter,
@@ -669,7 +670,9 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
   }
 
   // Finish: fold the integer accumulators and the Value-zero term, undo 2^Ev (and the
-  // lane's 2^-vshift on l and the zero term).
+  // lane's 2^-vshift on l and the zero term).  comb may overlay lds, which the blocks
+  // read through other types: no store below may move above those reads.
+  asm volatile("" ::: "memory");
   const float vsh = __builtin_amdgcn_ldexpf(1.f, lc.vshift);
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
@@ -810,6 +813,10 @@ __device__ __forceinline__ void residual_rows(const DecodeArgs& a, int64_t pair,
         rs.acc[hd][0] = fmaf(pv[e], v[e].x, rs.acc[hd][0]);
         rs.acc[hd][1] = fmaf(pv[e], v[e].y, rs.acc[hd][1]);
       }
+      // The compiler would otherwise sink these multiply-adds below the whole loop
+      // and keep every probability read live until then (4 registers per head and
+      // 4 rows).
+      asm volatile("" : "+v"(rs.acc[hd][0]), "+v"(rs.acc[hd][1]));
     }
   }
   wave_lds_sync();
@@ -865,9 +872,11 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   constexpr int NMT = (GQA + 3) / 4;
   constexpr int WAVES = 4 * waves_per_simd(BITS, GQA, G);
   constexpr int NTH = 64 * WAVES;
+  // A wave's record of its blocks is written over its own WaveLds after its last block.
   __shared__ WaveLds<NMT> wl[WAVES];
+  static_assert(sizeof(WaveLds<NMT>) >= GQA * PSTRIDE * sizeof(float), "block record in WaveLds");
   __shared__ alignas(16) float pw[WAVES][GQA * 32 + 4 * ((GQA + 3) / 4)];  // window probabilities
-  __shared__ alignas(16) float comb[2 * WAVES][GQA * PSTRIDE];  // [0, WAVES): blocks; then window
+  __shared__ alignas(16) float comb[WAVES][GQA * PSTRIDE];      // window records
   __shared__ int counter;
 
   // workgroup -> (pair, s): uniform T: pair blockIdx.x mod P, nw workgroups a pair;
@@ -935,16 +944,19 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
         item = grab_item(&counter);
       }
     }
-    residual_record<GQA>(rs, comb[WAVES + wave]);
+    residual_record<GQA>(rs, comb[wave]);
   }
   // blocks (an empty share leaves an empty record: m = -inf, l = 0)
   quantized_items<BITS, GQA, G, PAGED>(a, pair, item, n_res, n_items, b_lo, b_hi, &counter,
-                                       wl[wave], comb[wave]);
+                                       wl[wave], reinterpret_cast<float*>(&wl[wave]));
   __syncthreads();
 
   float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
-  finish_pair<GQA, NTH, 2 * WAVES>([&](int i) { return (const float*)comb[i]; }, parts, my,
-                                   n_parts, a.counters + kCounterStride * pair, o, &comb[0][0]);
+  finish_pair<GQA, NTH, 2 * WAVES>(
+      [&](int i) {
+        return i < WAVES ? reinterpret_cast<const float*>(&wl[i]) : (const float*)comb[i - WAVES];
+      },
+      parts, my, n_parts, a.counters + kCounterStride * pair, o, &comb[0][0]);
 }
 
 template <typename F>
