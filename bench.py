@@ -577,6 +577,8 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    flushes = {}                                    # step i -> does it flush a window
+
     def prepare(i):
         """Step i: one decode step (append the token, flushing a full window, then
         attend), with its arguments marshalled now so that the timed loops only make
@@ -585,6 +587,8 @@ def main():
         c = i % copies
         j = Ts[c]
         Ts[c] = j + 1
+        flushes[i] = any(t + j - S > 0 and window_len(t + j - S, w1.residual, w1.group_k)
+                         == w1.residual for t in base)
         T_before = T_hi + j                         # the longest sequence's count
         T = T_before + 1
         kn, vn = news[c]
@@ -621,6 +625,12 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in events]
+    # per-launch times of steps that flush a window (two launches) and of the others
+    kinds = {}
+    for name, want in (("flush", True), ("plain", False)):
+        ms = [t for i, t in enumerate(dec_ms) if flushes[args.warmup + i] == want]
+        if ms:
+            kinds[name] = {"steps": len(ms), "avg_us": round(sum(ms) / len(ms) * 1e3, 3)}
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     dec_med_s = sorted(dec_ms)[len(dec_ms) // 2] / 1e3
     dec_per_launch = launch_bytes / args.steps
@@ -749,7 +759,8 @@ def main():
                      "p10_p90_launch_us": [round(sorted(dec_ms)[len(dec_ms) // 10] * 1e3, 3),
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
                      "traffic": measured_traffic(w.name)
-                                if S == 0 and AGING == "window" and not varlen else None},
+                                if S == 0 and AGING == "window" and not varlen else None,
+                     "step_kinds": kinds},
         "cpu_baseline": cpu,
         "prefill_quantize": prefill,
         "quality": quality,
