@@ -985,14 +985,27 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   p.n_groups = Tq / L.G;
   const int64_t nblk = (Tq + BLK - 1) / BLK;
   const int64_t pairs = (int64_t)L.B * L.H;
-  // default: one round of CU-sized workgroups over the 256 CUs; at most one workgroup
-  // for the window and one per block
-  int64_t nw = n_split_req > 0 ? n_split_req : kCUs / pairs;
-  if (nw > 1 + nblk) nw = 1 + nblk;
+  // default: one round of CU-sized workgroups over the 256 CUs, but no more workgroups
+  // per pair than keep every wave busy with a block or window chunk (a chunk counting
+  // RES_COST blocks): a small pair is cheaper in one workgroup than merged from
+  // several.  At most one workgroup for the window and one per block.
+  // The workspace holds partials for the count without that limit, which grows with T,
+  // so a workspace sized for T serves every smaller T (the limited count does not: a
+  // flush trades many window rows for a few blocks).
+  int64_t room = n_split_req > 0 ? n_split_req : kCUs / pairs;
+  if (room > 1 + nblk) room = 1 + nblk;
+  if (room < 1) room = 1;
+  int64_t nw = room;
+  if (n_split_req <= 0) {
+    const int64_t waves = 4 * waves_per_simd(L.bits, gqa, L.G);
+    const int64_t items = nblk + (int64_t)RES_COST * ((p.r + 31) / 32);
+    const int64_t busy = (items + waves - 1) / waves;
+    if (nw > busy) nw = busy;
+  }
   if (nw < 1) nw = 1;
   p.n_split = (int)nw;
   p.ws_counters = (size_t)pairs * kCounterStride * sizeof(uint32_t);
-  p.ws_partials = nw > 1 ? (size_t)pairs * nw * gqa * PSTRIDE * sizeof(float) : 0;
+  p.ws_partials = room > 1 ? (size_t)pairs * room * gqa * PSTRIDE * sizeof(float) : 0;
   p.ws_partials = (p.ws_partials + 255) / 256 * 256;
   p.ws_total = p.ws_counters + p.ws_partials;
   return p;

@@ -307,7 +307,8 @@ kivi_status kivi_decode_attn(const kivi_dims* dims, const kivi_cache* cache, int
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* As kivi_decode_attn with an explicit number of workgroups per (sequence, KV head)
- * (0 = the library's choice: one round of one workgroup per CU).  The first
+ * (0 = the library's choice: one round of one workgroup per CU, or fewer when that
+ * would leave waves without a 64-token block or float16 chunk to do).  The first
  * workgroup of a pair takes its float16 window and the others split the 64-token
  * blocks of its quantized history, so the count is clamped to [1, 1 + blocks].
  * Workspace size: kivi_decode_workspace_bytes_split. */

@@ -253,3 +253,34 @@ def test_paged_calls_check_the_block_table_pointer():
                        ctypes.byref(pg), 0, FAKE, 16, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
                        1 << 20, None)
         assert st == status and "block_table" in msg
+
+
+def test_default_split_keeps_every_wave_busy():
+    """The default split count is one workgroup per CU (256 / pairs) unless the pair's
+    work (64-token blocks, float16 chunks counted as 3 blocks) would leave some of a
+    workgroup's waves (12 at g <= 2 and 2 bits, 8 at g = 4) without an item."""
+    big = dict(layers=1, max_tokens=140000, head_dim=128, bits=2, group_k=32, group_v=128,
+               residual=128)
+    d = kv.Dims(batch=8, kv_heads=8, q_heads=32, **big)          # 64 pairs, 8 waves
+    assert kv.kivi_decode_splits(d, 32769) == 4                   # 256 / 64
+    # T = 300: 256 quantized tokens (4 blocks) + 44 float16 rows (2 chunks) = 10 items
+    assert kv.kivi_decode_splits(d, 300) == 2
+    d = kv.Dims(batch=1, kv_heads=1, q_heads=1, **big)            # 1 pair, 12 waves
+    # T = 257: 4 blocks + one chunk = 7 items: one workgroup, no merge
+    assert kv.kivi_decode_splits(d, 257) == 1
+    # T = 131073: 2048 blocks + one chunk = 2051 items -> 171 workgroups of 12 waves
+    assert kv.kivi_decode_splits(d, 131073) == 171
+    d = kv.Dims(batch=1, kv_heads=8, q_heads=32, **big)           # 8 pairs
+    assert kv.kivi_decode_splits(d, 131073) == 32                 # 256 / 8
+
+
+def test_workspace_for_T_serves_every_smaller_T():
+    """kivi_decode_attn checks the workspace against the size for its own T: the size
+    must never fall as T grows (across flushes the default split count does)."""
+    for g, bits in ((4, 2), (2, 4), (8, 2)):
+        d = kv.Dims(layers=1, batch=2, kv_heads=2, q_heads=2 * g, head_dim=128, bits=bits,
+                    group_k=32, group_v=128, residual=128, max_tokens=4096)
+        sizes = [kv.kivi_decode_workspace_bytes(d, T) for T in range(1, 1400)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+        splits = [kv.kivi_decode_splits(d, T) for T in range(1, 1400)]
+        assert any(a > b for a, b in zip(splits, splits[1:]))   # the count itself does fall
