@@ -332,6 +332,14 @@ Fp8Plan plan_fp8_decode(int B, int H, int q_heads, int64_t T, int n_split_req) {
   const int64_t nblk = (T + kFp8Run - 1) / kFp8Run;
   const int64_t pairs = (int64_t)B * H;
   int64_t nw = n_split_req > 0 ? n_split_req : kCUs / pairs;
+  if (n_split_req <= 0) {
+    // by default no more workgroups than keep every wave busy with a 32-token run:
+    // beyond that they only add partials to merge (the count still grows with T, so a
+    // workspace sized for T serves every smaller T)
+    const int64_t waves = 4 * kFp8WavesPerSimd;
+    const int64_t busy = (nblk + waves - 1) / waves;
+    if (nw > busy) nw = busy;
+  }
   if (nw > nblk) nw = nblk;
   if (nw < 1) nw = 1;
   p.n_split = (int)nw;
