@@ -59,6 +59,15 @@ Readings of passages the pages leave open (each is also listed in the design not
       Values token by token) into the history, and the newest R - G stay.  Hence
       r(T) = T for T <= R and R - G + ((T - R - 1) mod G) + 1 after, so the window
       always keeps at least the R - G + 1 most recent tokens.  G = R is R5.
+  R21 Per-token Value window ([INFRA] §3.2: a Value needs no group to fill, and its
+      residual keeps only the most recent tokens, each arrival pushing the oldest
+      one out after quantizing it, like a sliding window).  Variant selected per
+      cache (``v_window="token"``; the default "flush" moves Values with the Keys as
+      in R5/R16): the Value window holds exactly the min(T_k, R) most recent tokens
+      after the sink, and a token that arrives at a full Value window first
+      quantizes the oldest one (on its own, G_v-channel groups) into history
+      position T_k - R.  Keys keep their rule.  Tokens in [T_k - R, T_k - r) then
+      have quantized Keys and float16 Values.
 """
 from __future__ import annotations
 
@@ -101,6 +110,7 @@ def residual_len_grouped(T: int, R: int, G: int) -> int:
 
 
 AGING = ("window", "group")
+V_WINDOW = ("flush", "token")
 
 
 def kivi_cache_bytes(layers: int, batch: int, tokens: int, kv_heads: int, head_dim: int,
@@ -280,8 +290,8 @@ class LayerCache:
     """
 
     def __init__(self, batch, kv_heads, head_dim, bits, group_k, group_v, residual,
-                 max_tokens, sink: int = 0, aging: str = "window"):
-        assert bits in (2, 4) and aging in AGING
+                 max_tokens, sink: int = 0, aging: str = "window", v_window: str = "flush"):
+        assert bits in (2, 4) and aging in AGING and v_window in V_WINDOW
         assert residual % group_k == 0 and residual % V_RUN == 0
         assert max_tokens % group_k == 0 and max_tokens % V_RUN == 0
         assert head_dim % group_v == 0
@@ -299,6 +309,10 @@ class LayerCache:
         self.v_resid = np.zeros((B, H, residual, d), F16)
         self.S = sink                       # reading R15
         self.aging = aging                  # reading R5 ("window") or R16 ("group")
+        self.v_window = v_window            # reading R21 ("token") or with the Keys
+        # R21: the unpacked Value codes of the history (a token's codes are written
+        # on their own and its 16-token run is packed again)
+        self.v_code_vals = np.zeros((B, H, max_tokens, d), np.uint8)
         self.k_sink = np.zeros((B, H, sink, d), F16)
         self.v_sink = np.zeros((B, H, sink, d), F16)
         self.T = 0
@@ -316,21 +330,40 @@ class LayerCache:
 
     @property
     def Tq(self) -> int:
-        """Tokens in the quantized history."""
+        """Tokens in the quantized Key history (and Value history unless R21)."""
         return self.Tk - self.window_len(self.Tk)
+
+    @property
+    def Tqv(self) -> int:
+        """Tokens in the quantized Value history."""
+        if self.v_window == "token":
+            return max(0, self.Tk - self.R)
+        return self.Tq
 
     # -- writes into the quantized store ------------------------------------------------
     def _store(self, K: np.ndarray, V: np.ndarray, t0: int):
-        """Quantize tokens K/V [B, H, n, d] (n a multiple of R) into offset t0."""
+        """Quantize tokens K/V [B, H, n, d] (n a multiple of G) into offset t0."""
+        self._store_k(K, t0)
+        self._store_v(V, t0)
+
+    def _store_k(self, K: np.ndarray, t0: int):
         n = K.shape[2]
         kc, ks, kz = quantize_keys(K, self.G, self.bits)
         self.k_codes[:, :, t0:t0 + n] = pack_keys(kc, self.bits)
         self.k_scale[:, :, t0 // self.G:(t0 + n) // self.G] = ks
         self.k_zero[:, :, t0 // self.G:(t0 + n) // self.G] = kz
+
+    def _store_v(self, V: np.ndarray, t0: int):
+        """Quantize Value tokens [B, H, n, d] into history positions t0 .. t0 + n - 1;
+        any n (each token is coded on its own), its runs packed again."""
+        n = V.shape[2]
         vc, vs, vz = quantize_values(V, self.Gv, self.bits)
-        self.v_codes[:, :, t0 // V_RUN:(t0 + n) // V_RUN] = pack_values(vc, self.bits)
+        self.v_code_vals[:, :, t0:t0 + n] = vc
         self.v_scale[:, :, t0:t0 + n] = vs
         self.v_zero[:, :, t0:t0 + n] = vz
+        r0, r1 = t0 // V_RUN, (t0 + n + V_RUN - 1) // V_RUN
+        self.v_codes[:, :, r0:r1] = pack_values(
+            self.v_code_vals[:, :, r0 * V_RUN:r1 * V_RUN], self.bits)
 
     def prefill(self, K: np.ndarray, V: np.ndarray):
         """Quantize a prompt of T tokens at once (T quantized + r residual, reading R5).
@@ -349,9 +382,13 @@ class LayerCache:
         r = self.window_len(Tk)
         Tq = Tk - r
         if Tq:
-            self._store(K[:, :, :Tq], V[:, :, :Tq], 0)
+            self._store_k(K[:, :, :Tq], 0)
         self.k_resid[:, :, :r] = K[:, :, Tq:Tk]
-        self.v_resid[:, :, :r] = V[:, :, Tq:Tk]
+        # Values: with the Keys, or (R21) all but the most recent R
+        Tqv = Tq if self.v_window == "flush" else max(0, Tk - self.R)
+        if Tqv:
+            self._store_v(V[:, :, :Tqv], 0)
+        self.v_resid[:, :, :Tk - Tqv] = V[:, :, Tqv:Tk]
         self.T = T
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray):
@@ -364,40 +401,54 @@ class LayerCache:
             return
         Tk = self.Tk
         r = self.window_len(Tk)
+        token_v = self.v_window == "token"
         if r == self.R:
             # the window is full: its oldest n tokens go to the history (all R of them,
             # reading R5; one Key group, reading R16), the rest move to its front
             n = self.G if self.aging == "group" else self.R
-            self._store(self.k_resid[:, :, :n], self.v_resid[:, :, :n], Tk - self.R)
+            self._store_k(self.k_resid[:, :, :n], Tk - self.R)
             self.k_resid[:, :, :r - n] = self.k_resid[:, :, n:r].copy()
-            self.v_resid[:, :, :r - n] = self.v_resid[:, :, n:r].copy()
+            if not token_v:
+                self._store_v(self.v_resid[:, :, :n], Tk - self.R)
+                self.v_resid[:, :, :r - n] = self.v_resid[:, :, n:r].copy()
             r -= n
         self.k_resid[:, :, r] = k_new
-        self.v_resid[:, :, r] = v_new
+        if token_v:
+            # R21: a full Value window quantizes its oldest token, then slides
+            rv = min(Tk, self.R)
+            if rv == self.R:
+                self._store_v(self.v_resid[:, :, :1], Tk - self.R)
+                self.v_resid[:, :, :rv - 1] = self.v_resid[:, :, 1:rv].copy()
+                rv -= 1
+            self.v_resid[:, :, rv] = v_new
+        else:
+            self.v_resid[:, :, r] = v_new
         self.T += 1
 
     # -- reads ------------------------------------------------------------------------
     def quantized_codes(self):
-        """Unpacked codes of the quantized part: (k_codes, v_codes) uint8 [B,H,T_q,d]."""
-        Tq = self.Tq
+        """Unpacked codes of the quantized part: k_codes uint8 [B,H,T_q,d] and v_codes
+        uint8 [B,H,T_qv,d] (T_qv = T_q unless R21)."""
+        Tq, Tqv = self.Tq, self.Tqv
         kc = unpack_keys(self.k_codes[:, :, :Tq], self.bits)
-        vc = unpack_values(self.v_codes[:, :, :Tq // V_RUN], self.bits)
+        nrun = (Tqv + V_RUN - 1) // V_RUN
+        vc = unpack_values(self.v_codes[:, :, :nrun], self.bits)[:, :, :Tqv]
         return kc, vc
 
     def dequantized(self):
         """(K_hat, V_hat) float32 [B, H, T, d]: the sink rows, the dequantized history,
         then the residual window."""
         ns = min(self.T, self.S)
-        Tq = self.Tq
-        r = self.Tk - Tq
+        Tq, Tqv = self.Tq, self.Tqv
+        r, rv = self.Tk - Tq, self.Tk - Tqv
         kc, vc = self.quantized_codes()
         Kq = dequantize_keys(kc, self.k_scale[:, :, :Tq // self.G],
                              self.k_zero[:, :, :Tq // self.G], self.G)
-        Vq = dequantize_values(vc, self.v_scale[:, :, :Tq], self.v_zero[:, :, :Tq], self.Gv)
+        Vq = dequantize_values(vc, self.v_scale[:, :, :Tqv], self.v_zero[:, :, :Tqv], self.Gv)
         Kh = np.concatenate([self.k_sink[:, :, :ns].astype(F32), Kq,
                              self.k_resid[:, :, :r].astype(F32)], axis=2)
         Vh = np.concatenate([self.v_sink[:, :, :ns].astype(F32), Vq,
-                             self.v_resid[:, :, :r].astype(F32)], axis=2)
+                             self.v_resid[:, :, :rv].astype(F32)], axis=2)
         return Kh, Vh
 
     def attend(self, q: np.ndarray, sm_scale: float, pairs=None) -> np.ndarray:
@@ -423,17 +474,18 @@ class LayerCache:
     def dequantized_pair(self, b: int, h: int):
         """(K_hat, V_hat) float32 [T, d] for one (sequence, KV head) pair."""
         ns = min(self.T, self.S)
-        Tq = self.Tq
-        r = self.Tk - Tq
+        Tq, Tqv = self.Tq, self.Tqv
+        r, rv = self.Tk - Tq, self.Tk - Tqv
         kc = unpack_keys(self.k_codes[b, h, :Tq], self.bits)
-        vc = unpack_values(self.v_codes[b, h, :Tq // V_RUN], self.bits)
+        nrun = (Tqv + V_RUN - 1) // V_RUN
+        vc = unpack_values(self.v_codes[b, h, :nrun], self.bits)[:Tqv]
         Kq = dequantize_keys(kc, self.k_scale[b, h, :Tq // self.G],
                              self.k_zero[b, h, :Tq // self.G], self.G)
-        Vq = dequantize_values(vc, self.v_scale[b, h, :Tq], self.v_zero[b, h, :Tq], self.Gv)
+        Vq = dequantize_values(vc, self.v_scale[b, h, :Tqv], self.v_zero[b, h, :Tqv], self.Gv)
         Kh = np.concatenate([self.k_sink[b, h, :ns].astype(F32), Kq,
                              self.k_resid[b, h, :r].astype(F32)], axis=0)
         Vh = np.concatenate([self.v_sink[b, h, :ns].astype(F32), Vq,
-                             self.v_resid[b, h, :r].astype(F32)], axis=0)
+                             self.v_resid[b, h, :rv].astype(F32)], axis=0)
         return Kh, Vh
 
 
