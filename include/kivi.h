@@ -280,7 +280,9 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
                                       float* out, void* workspace, size_t workspace_bytes,
                                       void* stream);
 
-/* Workspace bytes kivi_decode_attn needs for T cached tokens (host-only). */
+/* Workspace bytes kivi_decode_attn needs for T cached tokens (host-only).  The size
+ * never falls as T grows, so a workspace sized for T serves every call at T or fewer
+ * tokens. */
 kivi_status kivi_decode_workspace_bytes(const kivi_dims* dims, int64_t T, size_t* bytes);
 
 /* Decode attention over the quantized cache of one layer, dequantizing inside the
