@@ -239,6 +239,38 @@ def test_decode_matches_oracle(bits, G, R, B, H, g, T, n_split):
     assert_close(out, ref, f"decode bits={bits} T={T} n_split={n_split}")
 
 
+@pytest.mark.parametrize("bits,G,R,g", [(2, 32, 64, 4), (4, 32, 32, 8), (2, 64, 128, 1)])
+def test_default_split_across_flushes_with_one_workspace(bits, G, R, g):
+    """The fused step at every T from 2 to 700 with one workspace sized for the last
+    T: the default split count changes along the way (it falls right after each
+    flush), and every output matches the oracle."""
+    k = kv()
+    d, B, H = 128, 1, 2
+    T_end = 700
+    w = W.Workload("steps", 94, 1, B, H, H * g, d, T_end, bits, G, d, R)
+    Tmax = w.max_tokens()
+    dims = dims_of(w, Tmax)
+    K, V = rand_kv(B, H, T_end, d, seed=R + g + bits, scale=3.0)
+    cache = gpu_prefill(w, dims, K, V, 1)
+    ws = k.new_workspace(dims, T_end)
+    Kh, Vh = K.cpu().numpy(), V.cpu().numpy()
+    oc = O.LayerCache(B, H, d, bits, G, d, R, Tmax)
+    oc.prefill(Kh[:, :, :1], Vh[:, :, :1])
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(bits + g)
+    out = torch.empty((B, H * g, d), dtype=torch.float32, device="cuda")
+    splits = set()
+    for t in range(1, T_end):
+        q = torch.randn((B, H * g, d), generator=gq, device="cuda").to(torch.float16)
+        k.kivi_append_decode(dims, cache, 0, t, K[:, :, t].contiguous(), V[:, :, t].contiguous(),
+                             q, 0.09, out, ws)
+        oc.append(Kh[:, :, t], Vh[:, :, t])
+        splits.add(k.kivi_decode_splits(dims, t + 1))
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), oc.attend(q.cpu().numpy(), 0.09), f"T={t + 1}")
+    assert len(splits) > 1, splits
+
+
 @pytest.mark.parametrize("bits,G,R,B,H,g", [(2, 32, 64, 2, 2, 4), (4, 64, 128, 1, 3, 2),
                                              (2, 32, 32, 2, 1, 8)])
 def test_append_decode_equals_append_then_decode(bits, G, R, B, H, g):
