@@ -117,3 +117,14 @@ def test_varlen_lens_pointer_is_checked():
         st, msg = call("kivi_decode_attn_varlen", ctypes.byref(d), ctypes.byref(fake_cache()), None,
                        0, lens, 16, FAKE, ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, None)
         assert st == status and "lens" in msg
+
+
+def test_codec_workspaces_never_shrink_as_T_grows():
+    """The FP8 and MXFP4 decodes check the workspace against the size for their own T;
+    the default split count (capped at one 32-token run per wave) only grows with T,
+    so a workspace sized for T serves every smaller T."""
+    for dims, size in ((fp8_dims(max_tokens=4096), kv.kivi_fp8_decode_workspace_bytes),
+                       (mx_dims(max_tokens=4096), kv.kivi_mxfp4_decode_workspace_bytes)):
+        sizes = [size(dims, T) for T in range(1, 3000, 7)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+        assert sizes[-1] > sizes[0]
