@@ -114,7 +114,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="llama8b_32k")
+    p.add_argument("--workload", default="llama8b_128k_2bit",
+                   help="workload name (default: the 131072-token shape at 2 bits, the bandwidth target point)")
     p.add_argument("--copies", type=int, default=0, help="layer caches to rotate over (0: auto)")
     p.add_argument("--n-split", type=int, default=0, help="token splits (0: library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -152,38 +153,69 @@ def calibrate_copy():
                       "launches": 5}), flush=True)
 
 
+# Launch shapes of the plain read (workgroups, threads, loads in flight per lane): one
+# persistent workgroup per CU with contiguous shares, and a few neighbours.
+READ_SHAPES = ((256, 1024, 8), (256, 512, 8), (256, 512, 16), (256, 1024, 4), (512, 512, 8),
+               (1024, 256, 8))
+READ_SIZES_MB = (88, 177, 705, 1024, 4096)
+
+
 def read_ceiling():
-    """Best-of-5 HIP-event time of kivi_stream_read (a plain 16-byte-load read) over
-    the decode working-set sizes, each repeat on a slice that is not in the 256 MB
-    last-level cache."""
+    """Best-of-5 HIP-event time of the plain streaming read (libkivi_readprobe.so, a
+    bench-only library) at the decode working-set sizes, for each launch shape in
+    READ_SHAPES; each timed read is of a slice that is not in the 256 MB last-level
+    cache.  The same launches under rocprofv3 give their kernel times."""
+    import ctypes
+
     import torch
-    from bit_quantization_amd import kivi as k
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_quantization_amd", "libkivi_readprobe.so"))
+    lib.kivi_probe_stream_read.restype = ctypes.c_int
+    lib.kivi_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
     torch.cuda.set_device(0)
-    total = 4 << 30
+    total = 8 << 30
     buf = torch.ones(total // 4, dtype=torch.int32, device="cuda")
-    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def read(off, n, shape):
+        wg, th, un = shape
+        st = lib.kivi_probe_stream_read(buf.data_ptr() + off, n, wg, th, un, sink.data_ptr(),
+                                        sink.numel() * 4, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"kivi_probe_stream_read failed ({st})")
+
     res = {}
-    for mb in (88, 177, 1024, 4096):
+    for mb in READ_SIZES_MB:
         n = mb << 20
         slices = total // n
-        best = float("inf")
-        for rep in range(5):
-            s0 = ((rep * 3 + 1) % slices) * n
-            # a 1 GB read of another slice first: it keeps the GPU busy while the timed
-            # interval is enqueued (so the interval holds no host time) and leaves the
-            # last-level cache without the timed slice
-            o = (((s0 >> 30) + 2) % (total >> 30)) << 30
-            k.kivi_stream_read(buf[o // 4:], 1 << 30, sink)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            k.kivi_stream_read(buf[s0 // 4:], n, sink)
-            b.record()
-            b.synchronize()
-            best = min(best, a.elapsed_time(b) / 1e3)
-        res[f"{mb}MB"] = {"us": round(best * 1e6, 2), "GB/s": round(n / best / 1e9, 1),
-                          "pct_of_peak": round(100 * n / best / 1e9 / HBM_PEAK_GBS, 1)}
-    print(json.dumps({"read_ceiling": res, "kernel": "kivi_stream_read (8192 x 256 threads, "
-                      "16-byte loads)", "timing": "HIP events, best of 5"}), flush=True)
+        per = {}
+        for shape in READ_SHAPES:
+            best = float("inf")
+            for rep in range(5):
+                s0 = ((rep * 3 + 1) % slices) * n
+                # a 1 GiB read of another part first: it keeps the GPU busy while the timed
+                # interval is enqueued and leaves the last-level cache without the slice
+                o = (((s0 >> 30) + 4) % (total >> 30)) << 30
+                read(o, 1 << 30, (256, 1024, 8))
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                read(s0, n, shape)
+                b.record(stream)
+                b.synchronize()
+                best = min(best, a.elapsed_time(b) / 1e3)
+            per["x".join(map(str, shape))] = round(best * 1e6, 2)
+        key = min(per, key=per.get)
+        t = per[key] / 1e6
+        res[f"{mb}MB"] = {"best_shape": key, "us": per[key], "GB/s": round(n / t / 1e9, 1),
+                          "pct_of_peak": round(100 * n / t / 1e9 / HBM_PEAK_GBS, 1),
+                          "us_by_shape": per}
+        print(f"[read] {mb} MB: {res[f'{mb}MB']}", file=sys.stderr, flush=True)
+    print(json.dumps({"read_ceiling": res,
+                      "kernel": "stream_read_kernel (persistent: workgroups x threads x loads "
+                                "in flight per lane, contiguous share per workgroup)",
+                      "timing": "HIP events, best of 5"}), flush=True)
 
 
 def prefill_bytes(w, T, S=0):

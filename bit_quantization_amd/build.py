@@ -1,6 +1,8 @@
-"""Build the HIP library ``libkivi.so`` in-tree for gfx950 with hipcc.
+"""Build the HIP libraries in-tree for gfx950 with hipcc.
 
-Every source under ``csrc/`` is compiled into one shared library next to this file.
+``libkivi.so``: the sources listed in SOURCES (the C ABI and its kernels).
+``libkivi_readprobe.so``: the plain streaming read the benchmark compares the decode
+with (``csrc/bench/``); not part of the method and not loaded by the package.
 Run as ``python bit_quantization_amd/build.py`` (by path: importing the package loads
 the library it builds).
 """
@@ -15,8 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libkivi.so")
+PROBE_LIB = os.path.join(HERE, "libkivi_readprobe.so")
 
-SOURCES = ["kivi_api.cpp", "quantize.hip", "decode.hip", "fp8.hip", "mxfp4.hip", "read_probe.hip"]
+SOURCES = ["kivi_api.cpp", "quantize.hip", "decode.hip", "fp8.hip", "mxfp4.hip"]
+PROBE_SOURCES = [os.path.join("bench", "read_probe.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -43,18 +47,24 @@ def hipcc() -> str:
     return exe
 
 
-def build_library(verbose: bool = True) -> str:
+def _build(sources, lib, verbose):
     srcs = []
-    for name in SOURCES:
+    for name in sources:
         # every source compiles as HIP (the API file includes the HIP runtime headers)
         srcs += ["-x", "hip", os.path.join(CSRC, name)]
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_library(verbose: bool = True) -> str:
+    """Build libkivi.so and the benchmark's read-probe library; returns libkivi.so's path."""
+    _build(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _build(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -993,7 +993,7 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   // The workspace holds partials for the count without that limit, which grows with T,
   // so a workspace sized for T serves every smaller T (the limited count does not: a
   // flush trades many window rows for a few blocks).
-  int64_t room = n_split_req > 0 ? n_split_req : kCUs / pairs;
+  int64_t room = n_split_req > 0 ? n_split_req : device_cus() / pairs;
   if (room > 1 + nblk) room = 1 + nblk;
   if (room < 1) room = 1;
   int64_t nw = room;

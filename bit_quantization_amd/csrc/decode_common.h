@@ -10,7 +10,6 @@ namespace {
 
 constexpr int D = kHeadDim;
 constexpr int PSTRIDE = D + 4;       // partial per head: acc[D], m, l, 2 unused (16-byte rows)
-constexpr int kCUs = 256;            // compute units of one MI355X
 // Each pair's arrival counter sits in a 256-byte slot of its own: atomics on one
 // cache line serialize.
 constexpr int kCounterStride = 64;

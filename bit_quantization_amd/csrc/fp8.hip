@@ -331,7 +331,7 @@ Fp8Plan plan_fp8_decode(int B, int H, int q_heads, int64_t T, int n_split_req) {
   const int gqa = q_heads / H;
   const int64_t nblk = (T + kFp8Run - 1) / kFp8Run;
   const int64_t pairs = (int64_t)B * H;
-  int64_t nw = n_split_req > 0 ? n_split_req : kCUs / pairs;
+  int64_t nw = n_split_req > 0 ? n_split_req : device_cus() / pairs;
   if (n_split_req <= 0) {
     // by default no more workgroups than keep every wave busy with a 32-token run:
     // beyond that they only add partials to merge (the count still grows with T, so a

@@ -6,8 +6,33 @@
 #include <cstring>
 #include <initializer_list>
 
+#include <atomic>
+
 #include "../../include/kivi.h"
 #include "kivi_internal.h"
+
+namespace kivi {
+
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace kivi
 
 namespace {
 
@@ -71,6 +96,13 @@ kivi_status check_dims(const kivi_dims* d) {
   if (d->max_tokens < 1 || d->max_tokens % d->group_k != 0 || d->max_tokens % kivi::kVRun != 0)
     return fail(KIVI_ERR_ARG, "max_tokens = %lld must be a positive multiple of group_k and 16",
                 (long long)d->max_tokens);
+  // The kernels address one pair's history with 32-bit buffer offsets; the codes are
+  // its largest buffer (d*b/8 bytes per token against at most 16 of scales).
+  if (d->max_tokens > kivi::kMaxPairBytes / (d->head_dim * d->bits / 8))
+    return fail(KIVI_ERR_UNSUPPORTED,
+                "max_tokens = %lld: a pair's %d-bit codes would exceed %lld bytes (at most %lld "
+                "tokens)", (long long)d->max_tokens, d->bits, (long long)kivi::kMaxPairBytes,
+                (long long)(kivi::kMaxPairBytes / (d->head_dim * d->bits / 8)));
   return KIVI_OK;
 }
 
@@ -291,7 +323,7 @@ kivi_status append_checks(const kivi_dims* dims, int64_t T_before, const void* k
 
 // ---- FP8 codec ---------------------------------------------------------------------
 
-kivi_status check_fp8_dims(const kivi_fp8_dims* d) {
+kivi_status check_fp8_shape(const kivi_fp8_dims* d) {
   if (!d) return fail(KIVI_ERR_ARG, "dims is NULL");
   if (d->layers < 1 || d->batch < 1 || d->kv_heads < 1 || d->q_heads < 1)
     return fail(KIVI_ERR_ARG, "layers, batch, kv_heads and q_heads must be >= 1");
@@ -313,6 +345,19 @@ kivi_status check_fp8_dims(const kivi_fp8_dims* d) {
   if (d->max_tokens < 1 || d->max_tokens % kivi::kFp8Run != 0)
     return fail(KIVI_ERR_ARG, "max_tokens = %lld must be a positive multiple of 32",
                 (long long)d->max_tokens);
+  return KIVI_OK;
+}
+
+// The shape rules, and one byte per channel and token: a pair's Key (or Value) codes
+// must stay within the kernels' 32-bit buffer offsets.
+kivi_status check_fp8_dims(const kivi_fp8_dims* d) {
+  kivi_status st = check_fp8_shape(d);
+  if (st != KIVI_OK) return st;
+  if (d->max_tokens > kivi::kMaxPairBytes / d->head_dim)
+    return fail(KIVI_ERR_UNSUPPORTED,
+                "max_tokens = %lld: a pair's FP8 codes would exceed %lld bytes (at most %lld "
+                "tokens)", (long long)d->max_tokens, (long long)kivi::kMaxPairBytes,
+                (long long)(kivi::kMaxPairBytes / d->head_dim));
   return KIVI_OK;
 }
 
@@ -362,7 +407,15 @@ kivi_status check_mx_dims(const kivi_mxfp4_dims* d) {
   if (d->reserved != 0) return fail(KIVI_ERR_ARG, "reserved = %d must be 0", d->reserved);
   const kivi_fp8_dims f{d->layers, d->batch, d->kv_heads, d->q_heads, d->head_dim, KIVI_FP8_E4M3,
                         d->max_tokens};
-  return check_fp8_dims(&f);                       // the same shape rules
+  kivi_status st = check_fp8_shape(&f);            // the same shape rules
+  if (st != KIVI_OK) return st;
+  // half a byte per channel and token: a pair's codes within 32-bit buffer offsets
+  if (d->max_tokens > kivi::kMaxPairBytes / (d->head_dim / 2))
+    return fail(KIVI_ERR_UNSUPPORTED,
+                "max_tokens = %lld: a pair's MXFP4 codes would exceed %lld bytes (at most %lld "
+                "tokens)", (long long)d->max_tokens, (long long)kivi::kMaxPairBytes,
+                (long long)(kivi::kMaxPairBytes / (d->head_dim / 2)));
+  return KIVI_OK;
 }
 
 void mx_sizes(const kivi_mxfp4_dims* d, size_t out[4]) {
@@ -821,21 +874,8 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
   return device_status(e, "kivi_append_decode_varlen launch");
 }
 
-kivi_status kivi_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
-                             void* stream) {
-  if (!buf || !sink) return fail(KIVI_ERR_ARG, "buf or sink is NULL");
-  if (!aligned16(buf) || !aligned16(sink)) return fail(KIVI_ERR_ALIGN, "buf or sink is not 16-byte aligned");
-  if (bytes % 16 != 0) return fail(KIVI_ERR_ARG, "bytes = %zu is not a multiple of 16", bytes);
-  const size_t need = (size_t)kivi::kStreamReadBlocks * 256 * sizeof(unsigned);
-  if (sink_bytes < need) return fail(KIVI_ERR_WORKSPACE, "sink has %zu bytes, needs %zu", sink_bytes, need);
-  if (bytes == 0) return ok();
-  hipError_t e = kivi::launch_stream_read(buf, bytes, static_cast<unsigned*>(sink),
-                                          static_cast<hipStream_t>(stream));
-  return device_status(e, "kivi_stream_read launch");
-}
-
 const char* kivi_last_error(void) { return g_err; }
 
-int32_t kivi_abi_version(void) { return 5; }
+int32_t kivi_abi_version(void) { return 6; }
 
 }  // extern "C"

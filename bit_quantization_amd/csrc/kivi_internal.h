@@ -9,6 +9,13 @@ namespace kivi {
 
 constexpr int kHeadDim = 128;   // head_dim this build's kernels are written for
 constexpr int kVRun = 16;       // tokens per packed Value run
+// Largest buffer of one (sequence, KV head) pair the kernels address: their buffer
+// offsets are 32-bit.
+constexpr int64_t kMaxPairBytes = 0x7FFFFF00;
+
+// Compute units of the current device (cached per device); 256, one MI355X's, when no
+// device can be queried (planning on a host without a GPU).
+int device_cus();
 
 // Device pointers of one layer, already offset to that layer, plus the dims.  The
 // history buffers hold one section per (b, h) pair of Tmax tokens, or, for a paged
@@ -211,10 +218,5 @@ hipError_t launch_mx_append(const MxView& L, const __half* k_new, const __half* 
 hipError_t launch_mx_decode(const MxView& L, int q_heads, int64_t T, const __half* q,
                             float sm_scale, float* out, void* ws, const Fp8Plan& plan,
                             const __half* k_new, const __half* v_new, hipStream_t s);
-
-// Measurement aid: a plain read of `bytes` (a multiple of 16) with kStreamReadBlocks
-// workgroups of 256 threads; sink holds one word per thread.
-constexpr int kStreamReadBlocks = 8192;
-hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 
 }  // namespace kivi

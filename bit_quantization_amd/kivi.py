@@ -27,7 +27,7 @@ EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_appen
            "kivi_append_decode", "kivi_paged_cache_sizes", "kivi_quantize_k_varlen",
            "kivi_quantize_v_varlen",
            "kivi_append_flush_varlen", "kivi_decode_attn_varlen", "kivi_append_decode_varlen",
-           "kivi_stream_read", "kivi_fp8_cache_sizes",
+           "kivi_fp8_cache_sizes",
            "kivi_fp8_quantize", "kivi_fp8_append", "kivi_fp8_decode_workspace_bytes",
            "kivi_fp8_decode_attn",
            "kivi_mxfp4_cache_sizes", "kivi_mxfp4_quantize", "kivi_mxfp4_append",
@@ -124,7 +124,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_append_flush_varlen": (I32, [D, C, PG, I32, P, I64, P, P, P]),
         "kivi_decode_attn_varlen": (I32, [D, C, PG, I32, P, I64, P, F32, P, P, SZ, P]),
         "kivi_append_decode_varlen": (I32, [D, C, PG, I32, P, I64, P, P, P, F32, P, P, SZ, P]),
-        "kivi_stream_read": (I32, [P, SZ, P, SZ, P]),
         "kivi_fp8_cache_sizes": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(SZ)]),
         "kivi_fp8_quantize": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(kivi_fp8_cache),
                                     I32, P, P, I64, I64, P]),
@@ -476,14 +475,6 @@ def prepare_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k
         if st != 0:
             _check(st)
     return call
-
-
-def kivi_stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=None):
-    """Measurement aid: read nbytes of buf once (see include/kivi.h)."""
-    if nbytes > buf.numel() * buf.element_size():
-        raise ValueError("nbytes exceeds the buffer")
-    _check(_lib.kivi_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(),
-                                 sink.numel() * sink.element_size(), _stream(stream)))
 
 
 # ---- FP8 KV cache ----------------------------------------------------------------------

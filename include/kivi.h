@@ -123,7 +123,10 @@ typedef struct kivi_dims {
                           sequence (0: none); see "Sink tokens" above */
   int32_t aging;       /* KIVI_AGING_WINDOW or KIVI_AGING_GROUP; see "Residual window" */
   int32_t reserved;    /* must be 0 */
-  int64_t max_tokens;  /* T_max: token capacity per sequence, a multiple of G and 16 */
+  int64_t max_tokens;  /* T_max: token capacity per sequence, a multiple of G and 16;
+                        * a pair's codes (T_max * d * b / 8 bytes) must stay below 2^31
+                        * bytes (the kernels' 32-bit buffer offsets), else every call
+                        * taking these dims returns KIVI_ERR_UNSUPPORTED */
 } kivi_dims;
 
 /* The nine device buffers of a cache; layout above.  scale_max is bookkeeping of
@@ -344,7 +347,8 @@ typedef struct {
   int32_t layers, batch, kv_heads, q_heads;
   int32_t head_dim;     /* 128 */
   int32_t format;       /* kivi_fp8_format */
-  int64_t max_tokens;   /* a positive multiple of 32 */
+  int64_t max_tokens;   /* a positive multiple of 32; T_max * d code bytes per pair below
+                         * 2^31, else KIVI_ERR_UNSUPPORTED */
 } kivi_fp8_dims;
 
 /* Device buffers, caller-owned, 16-byte aligned, sizes from kivi_fp8_cache_sizes:
@@ -401,7 +405,8 @@ typedef struct {
   int32_t layers, batch, kv_heads, q_heads;
   int32_t head_dim;     /* 128 */
   int32_t reserved;     /* must be 0 */
-  int64_t max_tokens;   /* a positive multiple of 32 */
+  int64_t max_tokens;   /* a positive multiple of 32; T_max * d / 2 code bytes per pair
+                         * below 2^31, else KIVI_ERR_UNSUPPORTED */
 } kivi_mxfp4_dims;
 
 /* Device buffers, caller-owned, 16-byte aligned, sizes from kivi_mxfp4_cache_sizes:
@@ -460,15 +465,6 @@ kivi_status kivi_mxfp4_append_decode(const kivi_mxfp4_dims* dims, const kivi_mxf
                                      const void* v_new, const void* q, float sm_scale,
                                      float* out, void* workspace, size_t workspace_bytes,
                                      void* stream);
-
-/* Measurement aid, not part of the method: read `bytes` (a multiple of 16) of device
- * memory at `buf` once with plain 16-byte loads (8192 workgroups of 256 threads,
- * grid-stride) and write one XOR word per thread to `sink` (device, at least
- * 8 MiB = 8192 * 256 * 4 bytes, else KIVI_ERR_WORKSPACE).  Timing it gives the rate at
- * which this GPU streams a working set of that size from HBM, the reference for the
- * decode kernels' bandwidth.  Enqueued on `stream`. */
-kivi_status kivi_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
-                             void* stream);
 
 /* ABI version of this library (bumped on any incompatible change). */
 int32_t kivi_abi_version(void);

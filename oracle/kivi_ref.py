@@ -451,42 +451,16 @@ class LayerCache:
                              self.v_resid[:, :, :rv].astype(F32)], axis=2)
         return Kh, Vh
 
-    def attend(self, q: np.ndarray, sm_scale: float, pairs=None) -> np.ndarray:
-        """Decode attention of q [B, H_q, d] float16 over the cache; float32 [B, H_q, d].
-
-        ``pairs`` optionally restricts the evaluation to a list of (b, kv_head) pairs
-        (others are left as NaN) so large layers can be sampled.
-        """
-        Kh, Vh = self.dequantized() if pairs is None else (None, None)
-        out = np.full(q.shape, np.nan, F32)
+    def attend(self, q: np.ndarray, sm_scale: float) -> np.ndarray:
+        """Decode attention of q [B, H_q, d] float16 over the cache; float32 [B, H_q, d]."""
+        Kh, Vh = self.dequantized()
+        out = np.empty(q.shape, F32)
         g = q.shape[1] // self.H
-        todo = pairs if pairs is not None else [(b, h) for b in range(self.B)
-                                                 for h in range(self.H)]
-        for b, h in todo:
-            if Kh is None:
-                Kbh, Vbh = self.dequantized_pair(b, h)
-            else:
-                Kbh, Vbh = Kh[b, h], Vh[b, h]
-            qs = q[b, h * g:(h + 1) * g]
-            out[b, h * g:(h + 1) * g] = attention_fp64(qs, Kbh, Vbh, sm_scale)
+        for b in range(self.B):
+            for h in range(self.H):
+                qs = q[b, h * g:(h + 1) * g]
+                out[b, h * g:(h + 1) * g] = attention_fp64(qs, Kh[b, h], Vh[b, h], sm_scale)
         return out
-
-    def dequantized_pair(self, b: int, h: int):
-        """(K_hat, V_hat) float32 [T, d] for one (sequence, KV head) pair."""
-        ns = min(self.T, self.S)
-        Tq, Tqv = self.Tq, self.Tqv
-        r, rv = self.Tk - Tq, self.Tk - Tqv
-        kc = unpack_keys(self.k_codes[b, h, :Tq], self.bits)
-        nrun = (Tqv + V_RUN - 1) // V_RUN
-        vc = unpack_values(self.v_codes[b, h, :nrun], self.bits)[:Tqv]
-        Kq = dequantize_keys(kc, self.k_scale[b, h, :Tq // self.G],
-                             self.k_zero[b, h, :Tq // self.G], self.G)
-        Vq = dequantize_values(vc, self.v_scale[b, h, :Tqv], self.v_zero[b, h, :Tqv], self.Gv)
-        Kh = np.concatenate([self.k_sink[b, h, :ns].astype(F32), Kq,
-                             self.k_resid[b, h, :r].astype(F32)], axis=0)
-        Vh = np.concatenate([self.v_sink[b, h, :ns].astype(F32), Vq,
-                             self.v_resid[b, h, :rv].astype(F32)], axis=0)
-        return Kh, Vh
 
 
 # --------------------------------------------------------------------------------------

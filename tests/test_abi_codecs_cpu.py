@@ -128,3 +128,33 @@ def test_codec_workspaces_never_shrink_as_T_grows():
         sizes = [size(dims, T) for T in range(1, 3000, 7)]
         assert all(a <= b for a, b in zip(sizes, sizes[1:]))
         assert sizes[-1] > sizes[0]
+
+
+# FP8 codes take one byte per channel and token, MXFP4 codes half a byte: a pair's
+# codes must stay below 2^31 bytes (the kernels' 32-bit buffer offsets).
+def test_fp8_capacity_beyond_32bit_offsets_is_unsupported():
+    sizes = (ctypes.c_size_t * 4)()
+    limit = (1 << 24) - 32
+    ok = fp8_dims(max_tokens=limit, layers=1, batch=1, kv_heads=1, q_heads=1).c()
+    st, msg = call("kivi_fp8_cache_sizes", ctypes.byref(ok), sizes)
+    assert st == 0, msg
+    bad = fp8_dims(max_tokens=limit + 32, layers=1, batch=1, kv_heads=1, q_heads=1).c()
+    st, msg = call("kivi_fp8_cache_sizes", ctypes.byref(bad), sizes)
+    assert st == 2 and "max_tokens" in msg
+    st, msg = call("kivi_fp8_quantize", ctypes.byref(bad), ctypes.byref(fake4(kv.kivi_fp8_cache)),
+                   0, FAKE, FAKE, 16, 16, None)
+    assert st == 2 and "max_tokens" in msg
+
+
+def test_mxfp4_capacity_beyond_32bit_offsets_is_unsupported():
+    sizes = (ctypes.c_size_t * 4)()
+    limit = (1 << 25) - 32
+    ok = mx_dims(max_tokens=limit, layers=1, batch=1, kv_heads=1, q_heads=1).c()
+    st, msg = call("kivi_mxfp4_cache_sizes", ctypes.byref(ok), sizes)
+    assert st == 0, msg
+    bad = mx_dims(max_tokens=limit + 32, layers=1, batch=1, kv_heads=1, q_heads=1).c()
+    st, msg = call("kivi_mxfp4_cache_sizes", ctypes.byref(bad), sizes)
+    assert st == 2 and "max_tokens" in msg
+    st, msg = call("kivi_mxfp4_quantize", ctypes.byref(bad), ctypes.byref(fake4(kv.kivi_mxfp4_cache)),
+                   0, FAKE, FAKE, 16, 16, None)
+    assert st == 2 and "max_tokens" in msg

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert kv.kivi_abi_version() == 5
+    assert kv.kivi_abi_version() == 6
 
 
 def good_dims(**kw):
@@ -284,3 +284,26 @@ def test_workspace_for_T_serves_every_smaller_T():
         assert all(a <= b for a, b in zip(sizes, sizes[1:]))
         splits = [kv.kivi_decode_splits(d, T) for T in range(1, 1400)]
         assert any(a > b for a, b in zip(splits, splits[1:]))   # the count itself does fall
+
+
+# The kernels address one (sequence, KV head) pair's history with 32-bit buffer offsets,
+# so a pair's codes (its largest buffer: d*b/8 bytes per token) must stay below 2^31
+# bytes: at 2 bits the largest capacity is the last multiple of 32 tokens under 2^26, at
+# 4 bits under 2^25.
+@pytest.mark.parametrize("bits,limit", [(2, (1 << 26) - 32), (4, (1 << 25) - 32)])
+def test_capacity_beyond_32bit_offsets_is_unsupported(bits, limit):
+    sizes = (ctypes.c_size_t * len(kv.BUFFERS))()
+    ok = good_dims(bits=bits, max_tokens=limit, layers=1, batch=1, kv_heads=1, q_heads=1)
+    st, msg = call("kivi_cache_sizes", ctypes.byref(ok.c()), sizes)
+    assert st == 0, msg
+    assert sizes[0] < (1 << 31)
+    bad = good_dims(bits=bits, max_tokens=limit + 32, layers=1, batch=1, kv_heads=1, q_heads=1)
+    st, msg = call("kivi_cache_sizes", ctypes.byref(bad.c()), sizes)
+    assert st == 2 and "max_tokens" in msg
+    # every entry point that takes the dims rejects it before launching
+    st, msg = call("kivi_quantize_k", ctypes.byref(bad.c()), ctypes.byref(fake_cache()), 0, FAKE,
+                   16, 16, None)
+    assert st == 2 and "max_tokens" in msg
+    need = ctypes.c_size_t(0)
+    st, msg = call("kivi_decode_workspace_bytes", ctypes.byref(bad.c()), 300, ctypes.byref(need))
+    assert st == 2
