@@ -130,6 +130,9 @@ def parse():
     p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2", "mxfp4"],
                    help="kivi: the workload's 2/4-bit KIVI cache (default); fp8_*: the same "
                         "workload stored as FP8 with per-head scales; mxfp4: stored as MXFP4")
+    p.add_argument("--no-settle", action="store_true",
+                   help="no untimed first step per cache (by default each cache takes one, "
+                        "which flushes the full window a prompt of a multiple of R leaves)")
     p.add_argument("--no-graph", action="store_true",
                    help="launch the timed steps one by one instead of as one HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -522,8 +525,6 @@ def main():
         w1 = w.replace(layers=1)
     else:
         w1 = w
-    # warmup, the eager loop timed per launch (roofline), then the K steps of the graph
-    total_steps = args.warmup + 2 * args.steps
     S = args.sink
     global AGING
     AGING = args.aging
@@ -541,6 +542,10 @@ def main():
     copies = args.copies or max(1, math.ceil(4 * MALL_BYTES / per_copy_bytes))
     if w.layers > 1:
         copies = args.copies or min(w.layers, max(copies, 2))
+    # one settling step per cache, the warmup, the eager loop timed per launch (roofline),
+    # then the K steps of the graph
+    settle = 0 if args.no_settle else copies
+    total_steps = settle + args.warmup + 2 * args.steps
     steps_per_copy = math.ceil(total_steps / copies) + 1
     extra_rows = max(steps_per_copy, 1024)          # rows appended on the GPU / by the oracle
     Tmax = w1.replace(stream_steps=steps_per_copy).max_tokens()
@@ -640,15 +645,30 @@ def main():
                                            w1.sm_scale, out, ws)
         return call, db, ab
 
-    for i in range(args.warmup):
+    # Settling: every cache takes its first decode step untimed.  A prompt whose length is
+    # a multiple of R leaves the float16 window full, so that step flushes it; the timed
+    # steps then see the steady state, where one step in R flushes (those first steps'
+    # launch times are reported as roofline.settle_steps).
+    settle_ms, settle_flush = [], 0
+    for i in range(settle):
+        call = prepare(i)[0]
+        settle_flush += flushes[i]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        settle_ms.append(e0.elapsed_time(e1))
+    for i in range(settle, settle + args.warmup):
         prepare(i)[0]()
     torch.cuda.synchronize()
 
     # Per-launch duration (roofline): K eager steps, each bracketed by HIP events on
     # the launch stream.
+    t_first = settle + args.warmup
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
-    steps = [prepare(args.warmup + i) for i in range(args.steps)]
+    steps = [prepare(t_first + i) for i in range(args.steps)]
     launch_bytes = sum(db + ab for _, db, ab in steps)   # each launch appends and attends
     torch.cuda.synchronize()
     for (call, _, _), (e0, e1) in zip(steps, events):
@@ -660,7 +680,7 @@ def main():
     # per-launch times of steps that flush a window (two launches) and of the others
     kinds = {}
     for name, want in (("flush", True), ("plain", False)):
-        ms = [t for i, t in enumerate(dec_ms) if flushes[args.warmup + i] == want]
+        ms = [t for i, t in enumerate(dec_ms) if flushes[t_first + i] == want]
         if ms:
             kinds[name] = {"steps": len(ms), "avg_us": round(sum(ms) / len(ms) * 1e3, 3)}
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
@@ -670,7 +690,7 @@ def main():
     # Whole-job throughput: the next K steps, launched as one HIP graph (captured with
     # each step's own arguments, so replaying it once runs exactly those K steps and
     # the host's per-call cost leaves the timed region), between two synchronizations.
-    first = args.warmup + args.steps
+    first = t_first + args.steps
     if args.no_graph:
         steps = [prepare(first + i) for i in range(args.steps)]
         torch.cuda.synchronize()
@@ -792,7 +812,10 @@ def main():
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
                      "traffic": measured_traffic(w.name)
                                 if S == 0 and AGING == "window" and not varlen else None,
-                     "step_kinds": kinds},
+                     "step_kinds": kinds,
+                     "settle_steps": ({"steps": settle, "flush_steps": settle_flush,
+                                       "avg_us": round(sum(settle_ms) / settle * 1e3, 3)}
+                                      if settle else None)},
         "cpu_baseline": cpu,
         "prefill_quantize": prefill,
         "quality": quality,

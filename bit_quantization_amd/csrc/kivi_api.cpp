@@ -259,10 +259,12 @@ kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int3
 }
 
 // Checks of a decode call over T tokens; fills *L and *plan.
+// check_ws false: every check but the workspace's (Lout, plan_out may then be NULL).
 kivi_status decode_checks(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
                           int64_t T, const void* q, float sm_scale, float* out, void* ws,
                           size_t ws_bytes, int32_t n_split, kivi::LayerView* Lout,
-                          kivi::DecodePlan* plan_out, const kivi_paging* pg = nullptr) {
+                          kivi::DecodePlan* plan_out, const kivi_paging* pg = nullptr,
+                          bool check_ws = true) {
   kivi_status st = check_common(dims, cache, layer);
   if (st != KIVI_OK) return st;
   st = check_paging(dims, pg);
@@ -282,6 +284,7 @@ kivi_status decode_checks(const kivi_dims* dims, const kivi_cache* cache, int32_
   if (!aligned16(q) || !aligned16(out)) return fail(KIVI_ERR_ALIGN, "q or out is not 16-byte aligned");
   if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
     return fail(KIVI_ERR_ARG, "sm_scale is not finite");
+  if (!check_ws) return KIVI_OK;
   const kivi::LayerView L = layer_view(dims, cache, layer, pg);
   const kivi::DecodePlan plan = kivi::plan_decode(L, dims->q_heads, T, n_split);
   if (!ws) return fail(KIVI_ERR_WORKSPACE, "workspace is NULL");
@@ -306,6 +309,37 @@ kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_
                                      out, ws, plan, nullptr, kivi::Lens{lens, T},
                                      static_cast<hipStream_t>(stream));
   return device_status(e, "kivi_decode_attn launch");
+}
+
+// The fused step after its dims, cache and append checks: decode checks (which size
+// the workspace), then the flush launch when the window is full and the decode launch.
+kivi_status append_decode_launch(const kivi_dims* dims, const kivi_cache* cache, int32_t layer,
+                                 int64_t T_before, const void* k_new, const void* v_new,
+                                 const void* q, float sm_scale, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const int64_t T = T_before + 1;
+  kivi::LayerView L;
+  kivi::DecodePlan plan;
+  kivi_status st = decode_checks(dims, cache, layer, T, q, sm_scale, out, workspace,
+                                 workspace_bytes, 0, &L, &plan);
+  if (st != KIVI_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const __half* kn = static_cast<const __half*>(k_new);
+  const __half* vn = static_cast<const __half*>(v_new);
+  const kivi::AppendPlan ap = kivi::plan_append(L, T_before);
+  const kivi::Lens none{nullptr, 0};
+  if (ap.flush) {
+    // the window is full: flush it (and store the new row) first, then attend
+    hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, none, false, s);
+    if (e != hipSuccess) return device_status(e, "kivi_append_decode flush launch");
+    e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale, out,
+                            workspace, plan, nullptr, none, s);
+    return device_status(e, "kivi_append_decode launch");
+  }
+  const kivi::NewRow nr{kn, vn, ap.slot};
+  hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
+                                     out, workspace, plan, &nr, none, s);
+  return device_status(e, "kivi_append_decode launch");
 }
 
 // Checks of an append at T_before.
@@ -778,29 +812,8 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
   if (st != KIVI_OK) return st;
   st = append_checks(dims, T_before, k_new, v_new);
   if (st != KIVI_OK) return st;
-  const int64_t T = T_before + 1;
-  kivi::LayerView L;
-  kivi::DecodePlan plan;
-  st = decode_checks(dims, cache, layer, T, q, sm_scale, out, workspace, workspace_bytes, 0, &L,
-                     &plan);
-  if (st != KIVI_OK) return st;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const __half* kn = static_cast<const __half*>(k_new);
-  const __half* vn = static_cast<const __half*>(v_new);
-  const kivi::AppendPlan ap = kivi::plan_append(L, T_before);
-  const kivi::Lens none{nullptr, 0};
-  if (ap.flush) {
-    // the window is full: flush it (and store the new row) first, then attend
-    hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, none, false, s);
-    if (e != hipSuccess) return device_status(e, "kivi_append_decode flush launch");
-    e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale, out,
-                            workspace, plan, nullptr, none, s);
-    return device_status(e, "kivi_append_decode launch");
-  }
-  const kivi::NewRow nr{kn, vn, ap.slot};
-  hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
-                                     out, workspace, plan, &nr, none, s);
-  return device_status(e, "kivi_append_decode launch");
+  return append_decode_launch(dims, cache, layer, T_before, k_new, v_new, q, sm_scale, out,
+                              workspace, workspace_bytes, stream);
 }
 
 // ---- ragged batches ------------------------------------------------------------------

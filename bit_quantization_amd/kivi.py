@@ -24,7 +24,8 @@ STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_E
 
 EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
            "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
-           "kivi_append_decode", "kivi_paged_cache_sizes", "kivi_quantize_k_varlen",
+           "kivi_append_decode", "kivi_paged_cache_sizes",
+           "kivi_quantize_k_varlen",
            "kivi_quantize_v_varlen",
            "kivi_append_flush_varlen", "kivi_decode_attn_varlen", "kivi_append_decode_varlen",
            "kivi_fp8_cache_sizes",
