@@ -7,6 +7,7 @@
 #include <initializer_list>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/kivi.h"
 #include "kivi_internal.h"
@@ -340,6 +341,53 @@ kivi_status append_decode_launch(const kivi_dims* dims, const kivi_cache* cache,
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
                                      out, workspace, plan, &nr, none, s);
   return device_status(e, "kivi_append_decode launch");
+}
+
+// ---- static decode scratch (kivi_append_decode_noalloc) ------------------------------
+
+// The decode workspace of callers that cannot allocate device memory: one copy per GPU
+// (each device that loads the library holds it until the process ends), shared by every
+// kivi_append_decode_noalloc call on that GPU.  Host code never uses the array's name
+// as an address: the address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Zeroes n16 16-byte words (a kernel, so that a caller capturing the stream into a
+// graph records a kernel node rather than a memset node).
+__global__ void zero_words_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxScratchDevices];
+
+// The current device's scratch address.  The first call on a device looks it up and
+// zeroes the array on `s` (the arrival counters must start at zero; every decode leaves
+// them at zero again, and each workgroup clears its own partial slot before use).
+kivi_status scratch_of_current_device(void** out, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(KIVI_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(KIVI_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s, static_cast<uint4*>(ptr),
+                       kScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return device_status(e, "static scratch clear launch");
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return KIVI_OK;
 }
 
 // Checks of an append at T_before.
@@ -814,6 +862,31 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
   if (st != KIVI_OK) return st;
   return append_decode_launch(dims, cache, layer, T_before, k_new, v_new, q, sm_scale, out,
                               workspace, workspace_bytes, stream);
+}
+
+kivi_status kivi_append_decode_noalloc(const kivi_dims* dims, const kivi_cache* cache,
+                                       int32_t layer, int64_t T_before, const void* k_new,
+                                       const void* v_new, const void* q, float sm_scale,
+                                       float* out, void* stream) {
+  kivi_status st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  st = append_checks(dims, T_before, k_new, v_new);
+  if (st != KIVI_OK) return st;
+  st = decode_checks(dims, cache, layer, T_before + 1, q, sm_scale, out, nullptr, 0, 0, nullptr,
+                     nullptr, nullptr, /*check_ws=*/false);
+  if (st != KIVI_OK) return st;
+  const kivi::DecodePlan plan =
+      kivi::plan_decode(shape_view(dims), dims->q_heads, T_before + 1, 0);
+  if (plan.ws_total > kScratchBytes)
+    return fail(KIVI_ERR_UNSUPPORTED,
+                "this step needs %zu bytes of decode scratch; the library's static scratch "
+                "holds %zu (use kivi_append_decode with a workspace)",
+                plan.ws_total, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws, static_cast<hipStream_t>(stream));
+  if (st != KIVI_OK) return st;
+  return append_decode_launch(dims, cache, layer, T_before, k_new, v_new, q, sm_scale, out, ws,
+                              kScratchBytes, stream);
 }
 
 // ---- ragged batches ------------------------------------------------------------------

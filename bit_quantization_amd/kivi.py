@@ -24,7 +24,7 @@ STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_E
 
 EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_append_flush",
            "kivi_decode_workspace_bytes", "kivi_decode_attn", "kivi_decode_attn_split",
-           "kivi_append_decode", "kivi_paged_cache_sizes",
+           "kivi_append_decode", "kivi_append_decode_noalloc", "kivi_paged_cache_sizes",
            "kivi_quantize_k_varlen",
            "kivi_quantize_v_varlen",
            "kivi_append_flush_varlen", "kivi_decode_attn_varlen", "kivi_append_decode_varlen",
@@ -119,6 +119,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_decode_attn": (I32, [D, C, I32, I64, P, F32, P, P, SZ, P]),
         "kivi_decode_attn_split": (I32, [D, C, I32, I64, P, F32, P, P, SZ, I32, P]),
         "kivi_append_decode": (I32, [D, C, I32, I64, P, P, P, F32, P, P, SZ, P]),
+        "kivi_append_decode_noalloc": (I32, [D, C, I32, I64, P, P, P, F32, P, P]),
         "kivi_paged_cache_sizes": (I32, [D, PG, ctypes.POINTER(SZ)]),
         "kivi_quantize_k_varlen": (I32, [D, C, PG, I32, P, P, I64, I64, P]),
         "kivi_quantize_v_varlen": (I32, [D, C, PG, I32, P, P, I64, I64, P]),
@@ -446,6 +447,20 @@ def prepare_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before:
     def call():
         _check(fn(*args))
     return call
+
+
+def kivi_append_decode_noalloc(dims: Dims, cache: Cache, layer: int, T_before: int, k_new,
+                               v_new, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                               stream=None):
+    """kivi_append_decode without a workspace (the library's static decode scratch)."""
+    need = dims.batch * dims.kv_heads * dims.head_dim
+    nq = dims.batch * dims.q_heads * dims.head_dim
+    _check(_lib.kivi_append_decode_noalloc(ctypes.byref(dims.c()), ctypes.byref(cache.c()), layer,
+                                           T_before, _ptr(k_new, torch.float16, "k_new", need),
+                                           _ptr(v_new, torch.float16, "v_new", need),
+                                           _ptr(q, torch.float16, "q", nq),
+                                           ctypes.c_float(sm_scale),
+                                           _ptr(out, torch.float32, "out", nq), _stream(stream)))
 
 
 def kivi_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,

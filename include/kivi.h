@@ -202,6 +202,26 @@ kivi_status kivi_append_decode(const kivi_dims* dims, const kivi_cache* cache, i
                                const void* q, float sm_scale, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* kivi_append_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, checks, kernels and results (outputs to float32 rounding, cache bytes
+ * equal) without the workspace: the decode's scratch (per-pair arrival counters and
+ * split partials) lives in a 4 MiB array of static device memory inside the library,
+ * one copy per GPU, held until the process ends.  The library calls no hipMalloc,
+ * hipFree or allocating routine here.
+ *   The first call on a device looks up that device's copy and enqueues a kernel on
+ *   `stream` that zeroes it; every later call leaves the counters at zero again.
+ *   A step whose scratch would exceed 4 MiB (kivi_decode_workspace_bytes(dims,
+ *   T_before + 1) > 4194304, e.g. beyond ~12,000 (sequence, KV head) pairs) returns
+ *   KIVI_ERR_UNSUPPORTED before anything is enqueued.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap in time
+ *   on one GPU (different streams without ordering between them) race and give wrong
+ *   results; calls in one stream, or ordered by events, are safe. */
+kivi_status kivi_append_decode_noalloc(const kivi_dims* dims, const kivi_cache* cache,
+                                       int32_t layer, int64_t T_before, const void* k_new,
+                                       const void* v_new, const void* q, float sm_scale,
+                                       float* out, void* stream);
+
 /* Paged caches ("KV Cache Quantization (KIVI & FP4)" §6: PagedAttention allocates the
  * cache in fixed pages, and under KIVI a page of the same bytes holds more tokens).
  * The quantized history of every sequence lives in pages of P tokens taken from a

@@ -307,3 +307,21 @@ def test_capacity_beyond_32bit_offsets_is_unsupported(bits, limit):
     need = ctypes.c_size_t(0)
     st, msg = call("kivi_decode_workspace_bytes", ctypes.byref(bad.c()), 300, ctypes.byref(need))
     assert st == 2
+
+
+def test_noalloc_step_rejects_scratch_beyond_its_maximum():
+    # 32768 (sequence, KV head) pairs need 8 MiB of arrival counters alone, more than the
+    # 4 MiB static scratch: rejected before anything is enqueued (fake pointers, no GPU)
+    d = good_dims(layers=1, batch=128, kv_heads=256, q_heads=1024, max_tokens=512)
+    st, msg = call("kivi_append_decode_noalloc", ctypes.byref(d.c()), ctypes.byref(fake_cache()),
+                   0, 300, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, None)
+    assert st == 2 and "scratch" in msg, msg
+    # argument checks come first, as for kivi_append_decode
+    st, msg = call("kivi_append_decode_noalloc", ctypes.byref(good_dims().c()),
+                   ctypes.byref(fake_cache()), 0, 512, FAKE, FAKE, FAKE, ctypes.c_float(0.1),
+                   FAKE, None)
+    assert st == 3, msg
+    st, msg = call("kivi_append_decode_noalloc", ctypes.byref(good_dims().c()),
+                   ctypes.byref(fake_cache()), 0, 300, None, FAKE, FAKE, ctypes.c_float(0.1),
+                   FAKE, None)
+    assert st == 1, msg
