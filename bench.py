@@ -130,6 +130,9 @@ def parse():
     p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2", "mxfp4"],
                    help="kivi: the workload's 2/4-bit KIVI cache (default); fp8_*: the same "
                         "workload stored as FP8 with per-head scales; mxfp4: stored as MXFP4")
+    p.add_argument("--deterministic", action="store_true",
+                   help="KIVI_FLAG_DETERMINISTIC: fixed block order, repeated calls give the "
+                        "same output bits")
     p.add_argument("--no-settle", action="store_true",
                    help="no untimed first step per cache (by default each cache takes one, "
                         "which flushes the full window a prompt of a multiple of R leaves)")
@@ -550,7 +553,8 @@ def main():
     extra_rows = max(steps_per_copy, 1024)          # rows appended on the GPU / by the oracle
     Tmax = w1.replace(stream_steps=steps_per_copy).max_tokens()
     dims = k.Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, w1.bits, w1.group_k,
-                  w1.group_v, w1.residual, Tmax, sink=S, aging=AGING)
+                  w1.group_v, w1.residual, Tmax, sink=S, aging=AGING,
+                  deterministic=args.deterministic)
     print(f"[bench] workload {w.name}: {copies} layer caches x {per_copy_bytes / 1e6:.1f} MB "
           f"decode reads, {args.warmup}+{args.steps} steps", file=sys.stderr, flush=True)
 
@@ -790,6 +794,7 @@ def main():
                    "q_heads": w1.q_heads, "head_dim": w1.head_dim, "tokens": w1.tokens,
                    "bits": w1.bits, "group_k": w1.group_k, "group_v": w1.group_v,
                    "residual": w1.residual, "sink": S, "aging": AGING,
+                   "deterministic": args.deterministic,
                    "lengths": ("tokens * (b + 1) / batch: " + ",".join(map(str, base))
                                if args.ragged else "uniform"),
                    "paged": (f"pages of {args.paged} tokens, shuffled pool" if args.paged

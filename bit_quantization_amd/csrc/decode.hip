@@ -46,6 +46,9 @@ namespace kivi {
 namespace {
 
 constexpr int BLK = 64;              // tokens per block step of a wave
+// Work of one 32-row float16 window chunk in blocks (it moves three blocks' bytes with
+// fewer loads in flight and takes about three blocks of wave time)
+constexpr int RES_COST = 3;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -193,6 +196,34 @@ template <int NMT>
 struct WaveLds {
   alignas(16) uint8_t qa[2][NMT][2][QA_KS];   // [group in block][M-tile][K-step][row*QA_ROW + jg*16 + pos]
   alignas(16) uint8_t pa[NMT][16][4][16];     // [M-tile][row][run][token in run]
+};
+
+// The items of one wave of a workgroup (window chunks first, then 64-token blocks).
+// By default waves take them from the workgroup's LDS counter, so that waves that run
+// ahead take more.  Deterministic decode (KIVI_FLAG_DETERMINISTIC): a fixed round-robin
+// instead, chunk c to wave c mod W and block turns in wave order, each wave skipping
+// RES_COST turns per chunk it holds, so that every wave's cost is within RES_COST of
+// the others' and the blocks a wave accumulates, and their order, do not depend on the
+// run.
+struct WaveItems {
+  int* counter;           // LDS counter (dynamic) or nullptr (round-robin)
+  int w, W, n_res, nb, C, A, cnext, r;
+  __device__ WaveItems(int* counter_, int w_, int W_, int n_res_, int nb_)
+      : counter(counter_), w(w_), W(W_), n_res(n_res_), nb(nb_), C(n_res_ / W_), A(n_res_ % W_),
+        cnext(w_), r(RES_COST * (n_res_ / W_ + (w_ < n_res_ % W_ ? 1 : 0))) {}
+  __device__ int next() {
+    if (counter) return grab_item(counter);
+    if (cnext < n_res) {
+      const int c = cnext;
+      cnext += W;
+      return c;
+    }
+    const int s0 = RES_COST * C;
+    const int k = A * max(0, r - s0 - RES_COST) + (W - A) * max(0, r - s0) +
+                  (r >= s0 + RES_COST ? min(w, A) : 0) + (r >= s0 ? max(0, w - A) : 0);
+    ++r;
+    return k < nb ? n_res + k : n_res + nb;
+  }
 };
 
 // ---- the quantized token range of one wave ----------------------------------------
@@ -525,7 +556,7 @@ __device__ __forceinline__ void process_block(BlockRegs<BITS>& R, int n_valid,
 // overlay lds: it is written after the last block.
 template <int BITS, int GQA, int G, bool PAGED>
 __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pair, int item, int n_res,
-                                int n_items, int64_t b_lo, int64_t b_hi, int* counter,
+                                int n_items, int64_t b_lo, int64_t b_hi, WaveItems* counter,
                                 WaveLds<(GQA + 3) / 4>& lds, float* comb) {
   constexpr int NMT = (GQA + 3) / 4;              // M-tiles of 4 heads x 4 limbs
   const LayerView& L = a.L;
@@ -630,10 +661,10 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
     const int nv = (int)(a.Tq - blk * BLK);
     load_block<BITS, G, false>(R, pb, hist(blk * BLK), nv, j);
     process_block<BITS, GQA, G, false, false>(R, nv, qk, lc, lds, st, lo, j, pb, 0);
-    item = grab_item(counter);
+    item = counter->next();
     if (item < n_items) load_block<BITS, G, true>(R, pb, hist(block_of(item) * BLK), BLK, j);
   }
-  int nxt = item < n_items ? grab_item(counter) : n_items;
+  int nxt = item < n_items ? counter->next() : n_items;
   int done = 0;
   // Paged: the refill target of the next iteration is looked up one block ahead, with
   // a vector load issued before this block's refill loads and read after the block,
@@ -645,7 +676,7 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
   if constexpr (PAGED)
     if (item < n_items) tgt_next = hist((nxt < n_items ? block_of(nxt) : block_of(item)) * BLK);
   while (item < n_items) {
-    const int after = nxt < n_items ? grab_item(counter) : n_items;
+    const int after = nxt < n_items ? counter->next() : n_items;
     const int64_t blk = block_of(item);
     const int64_t nb = nxt < n_items ? block_of(nxt) : blk;
     int64_t tgt = nb * BLK, na = 0;
@@ -850,7 +881,6 @@ __device__ __forceinline__ void residual_record(const ResidState<GQA>& rs, float
 // blocks evenly into contiguous shares.  Inside a workgroup, waves take window chunks,
 // then blocks, from an LDS counter.  The last workgroup of the pair to arrive merges
 // the partials.
-constexpr int RES_COST = 3;
 __device__ __forceinline__ void block_share(int64_t nblk, int n_res, int nw, int s,
                                             int64_t& b_lo, int64_t& b_hi) {
   const int64_t fair = (nblk + (int64_t)RES_COST * n_res) / nw;
@@ -926,7 +956,8 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   __syncthreads();
 
   // window chunks
-  int item = grab_item(&counter);
+  WaveItems witems(a.L.det ? nullptr : &counter, wave, WAVES, n_res, (int)(b_hi - b_lo));
+  int item = witems.next();
   {
     ResidState<GQA> rs;
 #pragma unroll
@@ -942,13 +973,13 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
       while (item < n_res) {
         const int c0 = 32 * item;
         residual_rows<GQA>(a, pair, c0, a.r - c0 < 32 ? a.r - c0 : 32, aq, pw[wave], rs);
-        item = grab_item(&counter);
+        item = witems.next();
       }
     }
     residual_record<GQA>(rs, comb[wave]);
   }
   // blocks (an empty share leaves an empty record: m = -inf, l = 0)
-  quantized_items<BITS, GQA, G, PAGED>(a, pair, item, n_res, n_items, b_lo, b_hi, &counter,
+  quantized_items<BITS, GQA, G, PAGED>(a, pair, item, n_res, n_items, b_lo, b_hi, &witems,
                                        wl[wave], reinterpret_cast<float*>(&wl[wave]));
   __syncthreads();
 

@@ -93,7 +93,10 @@ kivi_status check_dims(const kivi_dims* d) {
   if (d->aging != KIVI_AGING_WINDOW && d->aging != KIVI_AGING_GROUP)
     return fail(KIVI_ERR_ARG, "aging = %d; expected KIVI_AGING_WINDOW (0) or KIVI_AGING_GROUP (1)",
                 d->aging);
-  if (d->reserved != 0) return fail(KIVI_ERR_ARG, "reserved = %d must be 0", d->reserved);
+  if (d->flags & ~(KIVI_FLAG_VALUE_TOKEN_WINDOW | KIVI_FLAG_DETERMINISTIC))
+    return fail(KIVI_ERR_ARG, "flags = 0x%x: unknown bits", (unsigned)d->flags);
+  if (d->flags & KIVI_FLAG_VALUE_TOKEN_WINDOW)
+    return fail(KIVI_ERR_UNSUPPORTED, "KIVI_FLAG_VALUE_TOKEN_WINDOW is not built yet");
   if (d->max_tokens < 1 || d->max_tokens % d->group_k != 0 || d->max_tokens % kivi::kVRun != 0)
     return fail(KIVI_ERR_ARG, "max_tokens = %lld must be a positive multiple of group_k and 16",
                 (long long)d->max_tokens);
@@ -155,6 +158,8 @@ kivi::LayerView shape_view(const kivi_dims* d) {
   L.R = d->residual;
   L.S = d->sink;
   L.aging = d->aging;
+  L.vwin = (d->flags & KIVI_FLAG_VALUE_TOKEN_WINDOW) ? 1 : 0;
+  L.det = (d->flags & KIVI_FLAG_DETERMINISTIC) ? 1 : 0;
   L.Tmax = d->max_tokens;
   return L;
 }
@@ -962,6 +967,6 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
 
 const char* kivi_last_error(void) { return g_err; }
 
-int32_t kivi_abi_version(void) { return 6; }
+int32_t kivi_abi_version(void) { return 7; }
 
 }  // extern "C"

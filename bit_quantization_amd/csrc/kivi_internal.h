@@ -35,6 +35,8 @@ struct LayerView {
   int B, H, d, bits, G, Gv, R;
   int S;              // sink tokens kept in float16 (tokens [0, S) of each sequence)
   int aging;          // 0: a full window is flushed whole; 1: only its oldest Key group
+  int vwin;           // 1: the per-token Value window (Values leave it one at a time)
+  int det;            // 1: deterministic decode (fixed block order in every wave)
   int64_t Tmax;
   const int32_t* table;   // nullptr: contiguous history, one section per pair
   int page_log2;

@@ -51,11 +51,13 @@ class kivi_dims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group_k", ctypes.c_int32), ("group_v", ctypes.c_int32),
                 ("residual", ctypes.c_int32), ("sink", ctypes.c_int32),
-                ("aging", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("aging", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64)]
 
 
 AGING = {"window": 0, "group": 1}    # KIVI_AGING_WINDOW, KIVI_AGING_GROUP
+FLAG_VALUE_TOKEN_WINDOW = 1          # KIVI_FLAG_VALUE_TOKEN_WINDOW
+FLAG_DETERMINISTIC = 2               # KIVI_FLAG_DETERMINISTIC
 BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid",
            "scale_max")
 
@@ -196,11 +198,16 @@ class Dims:
     max_tokens: int
     sink: int = 0        # tokens kept in float16 at the start of every sequence
     aging: str = "window"  # "window": a full window flushes whole; "group": its oldest group
+    v_window: str = "flush"  # "flush": Values leave with the Keys; "token": one at a time
+    deterministic: bool = False  # decode output bits repeat exactly (fixed block order)
 
     def c(self) -> kivi_dims:
+        flags = ((FLAG_VALUE_TOKEN_WINDOW if self.v_window == "token" else 0)
+                 | (-1 if self.v_window not in ("flush", "token") else 0)
+                 | (FLAG_DETERMINISTIC if self.deterministic else 0))
         return kivi_dims(self.layers, self.batch, self.kv_heads, self.q_heads, self.head_dim,
                          self.bits, self.group_k, self.group_v, self.residual, self.sink,
-                         AGING.get(self.aging, -1), 0, self.max_tokens)
+                         AGING.get(self.aging, -1), flags, self.max_tokens)
 
 
 def kivi_cache_sizes(dims: Dims):

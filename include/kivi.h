@@ -99,6 +99,18 @@ typedef enum kivi_status {
 #define KIVI_AGING_WINDOW 0   /* a full window is flushed whole */
 #define KIVI_AGING_GROUP 1    /* a full window sends only its oldest Key group out */
 
+/* kivi_dims.flags.
+ * KIVI_FLAG_DETERMINISTIC: decode calls give the same output bits whenever they are
+ *   repeated with the same arguments.  Every wave of a workgroup then takes a fixed
+ *   round-robin share of the 64-token blocks instead of taking them from a queue as it
+ *   runs (measured 1-4% slower per step on the 8B-shaped workloads).  Without it,
+ *   repeated calls agree to float32 rounding.
+ * KIVI_FLAG_VALUE_TOKEN_WINDOW: the per-token Value window ("4.4 KV Cache quantization"
+ *   §3.2: each new Value pushes the oldest one out, quantized on its own); see "Value
+ *   window" below. */
+#define KIVI_FLAG_VALUE_TOKEN_WINDOW 1
+#define KIVI_FLAG_DETERMINISTIC 2
+
 /* Problem statement of one cache ("4.4 KV Cache quantization" §1 and §3: layers,
  * batch, KV heads, head_dim, bits, group size, residual length).
  *
@@ -122,7 +134,7 @@ typedef struct kivi_dims {
   int32_t sink;        /* S in [0, 1024]: tokens kept in float16 at the start of every
                           sequence (0: none); see "Sink tokens" above */
   int32_t aging;       /* KIVI_AGING_WINDOW or KIVI_AGING_GROUP; see "Residual window" */
-  int32_t reserved;    /* must be 0 */
+  int32_t flags;       /* KIVI_FLAG_* bits below; every other bit must be 0 */
   int64_t max_tokens;  /* T_max: token capacity per sequence, a multiple of G and 16;
                         * a pair's codes (T_max * d * b / 8 bytes) must stay below 2^31
                         * bytes (the kernels' 32-bit buffer offsets), else every call

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert kv.kivi_abi_version() == 6
+    assert kv.kivi_abi_version() == 7
 
 
 def good_dims(**kw):
@@ -206,8 +206,8 @@ def test_split_plan_is_clamped_and_workspace_grows_with_splits():
     assert kv.kivi_decode_workspace_bytes(d, 448, 7) > kv.kivi_decode_workspace_bytes(d, 448, 6)
 
 
-@pytest.mark.parametrize("field,value", [("aging", 2), ("aging", -1), ("reserved", 1)])
-def test_aging_and_reserved_fields_are_checked(field, value):
+@pytest.mark.parametrize("field,value", [("aging", 2), ("aging", -1), ("flags", 4), ("flags", -8)])
+def test_aging_and_flags_fields_are_checked(field, value):
     c = good_dims().c()
     setattr(c, field, value)
     st, msg = call("kivi_quantize_k", ctypes.byref(c), ctypes.byref(fake_cache()), 0, FAKE, 16, 16,
