@@ -63,6 +63,7 @@ def measured_traffic(workload):
 
 
 AGING = "window"     # "group" with --aging group
+V_WINDOW = "flush"   # "token" with --v-window token (the per-token Value window)
 
 
 def window_len(Tk, R, G):
@@ -82,14 +83,26 @@ def split(T, R, S=0, G=32):
     return ns + r, Tk - r
 
 
+def value_split(T, R, S=0, G=32):
+    """(float16 Value rows, quantized Values) at T tokens: as split(), or with the
+    per-token Value window the last min(Tk, R) Values in float16."""
+    if V_WINDOW != "token":
+        return split(T, R, S, G)
+    ns = min(T, S)
+    Tk = T - ns
+    Tqv = max(0, Tk - R)
+    return ns + Tk - Tqv, Tqv
+
+
 def decode_bytes(w, T, S=0):
     """Algorithmic bytes of one decode launch at T cached tokens (see module doc)."""
     rows, Tq = split(T, w.residual, S, w.group_k)
+    vrows, Tqv = value_split(T, w.residual, S, w.group_k)
     d = w.head_dim
-    per_pair = (2 * Tq * d * w.bits // 8            # K and V codes
+    per_pair = ((Tq + Tqv) * d * w.bits // 8        # K and V codes
                 + (Tq // w.group_k) * d * 4         # K scale + zero
-                + Tq * (d // w.group_v) * 4         # V scale + zero
-                + 2 * rows * d * 2)                 # float16 sink + window K and V
+                + Tqv * (d // w.group_v) * 4        # V scale + zero
+                + (rows + vrows) * d * 2)           # float16 sink + window K and V
     pairs = w.batch * w.kv_heads
     return pairs * per_pair + w.batch * w.q_heads * d * (2 + 4)
 
@@ -101,11 +114,15 @@ def append_bytes(w, T_before, S=0):
     rows = pairs * 2 * d * 2 * 2                    # k_new, v_new read; residual row written
     Tk = T_before - S
     r = 0 if Tk <= 0 else window_len(Tk, R, w.group_k)
+    token_v = V_WINDOW == "token"
     if r == R:                                      # flush the window (or its oldest group)
         n = w.group_k if AGING == "group" else R
-        codes = 2 * n * d * w.bits // 8
-        meta = (n // w.group_k) * d * 4 + n * (d // w.group_v) * 4
-        rows += pairs * (2 * n * d * 2 + codes + meta)
+        nv = 0 if token_v else n                    # Values leave with the Keys, or not
+        codes = (n + nv) * d * w.bits // 8
+        meta = (n // w.group_k) * d * 4 + nv * (d // w.group_v) * 4
+        rows += pairs * ((n + nv) * d * 2 + codes + meta)
+    if token_v and Tk >= R:                         # the oldest Value quantized on its own
+        rows += pairs * (d * 2 + d * w.bits // 8 + (d // w.group_v) * 4)
     return rows
 
 
@@ -130,6 +147,9 @@ def parse():
     p.add_argument("--codec", default="kivi", choices=["kivi", "fp8_e4m3", "fp8_e5m2", "mxfp4"],
                    help="kivi: the workload's 2/4-bit KIVI cache (default); fp8_*: the same "
                         "workload stored as FP8 with per-head scales; mxfp4: stored as MXFP4")
+    p.add_argument("--v-window", default="flush", choices=["flush", "token"],
+                   help="Values leave the float16 window with the Keys (flush) or one at a "
+                        "time (token: KIVI_FLAG_VALUE_TOKEN_WINDOW)")
     p.add_argument("--deterministic", action="store_true",
                    help="KIVI_FLAG_DETERMINISTIC: fixed block order, repeated calls give the "
                         "same output bits")
@@ -255,7 +275,7 @@ def cpu_baseline(w, host_pairs, budget_s, S=0):
         m = math.lcm(16, w.group_k, w.residual)
         cap = (T + len(k_rows) + 1 + m - 1) // m * m
         oc = O.LayerCache(1, 1, w.head_dim, w.bits, w.group_k, w.group_v, w.residual, cap,
-                          sink=S, aging=AGING)
+                          sink=S, aging=AGING, v_window=V_WINDOW)
         oc.prefill(Kh, Vh)
         caches.append((oc, k_rows, v_rows, qh))
     done_bytes, t_used, steps, T_last = 0, 0.0, 0, 0
@@ -529,8 +549,9 @@ def main():
     else:
         w1 = w
     S = args.sink
-    global AGING
+    global AGING, V_WINDOW
     AGING = args.aging
+    V_WINDOW = args.v_window
     one = w1.replace(batch=1)
     # prompt length of each sequence: all w1.tokens, or tokens * (b + 1) / batch
     base = [w1.tokens * (b + 1) // w1.batch if args.ragged else w1.tokens
@@ -554,7 +575,7 @@ def main():
     Tmax = w1.replace(stream_steps=steps_per_copy).max_tokens()
     dims = k.Dims(1, w1.batch, w1.kv_heads, w1.q_heads, w1.head_dim, w1.bits, w1.group_k,
                   w1.group_v, w1.residual, Tmax, sink=S, aging=AGING,
-                  deterministic=args.deterministic)
+                  v_window=V_WINDOW, deterministic=args.deterministic)
     print(f"[bench] workload {w.name}: {copies} layer caches x {per_copy_bytes / 1e6:.1f} MB "
           f"decode reads, {args.warmup}+{args.steps} steps", file=sys.stderr, flush=True)
 
@@ -628,8 +649,12 @@ def main():
         c = i % copies
         j = Ts[c]
         Ts[c] = j + 1
-        flushes[i] = any(t + j - S > 0 and window_len(t + j - S, w1.residual, w1.group_k)
-                         == w1.residual for t in base)
+        # steps with the append launch before the decode: a full window flushes, or
+        # (per-token Value window) a Value leaves a full Value window
+        flushes[i] = any(t + j - S > 0 and (window_len(t + j - S, w1.residual, w1.group_k)
+                                            == w1.residual
+                                            or (V_WINDOW == "token" and t + j - S >= w1.residual))
+                         for t in base)
         T_before = T_hi + j                         # the longest sequence's count
         T = T_before + 1
         kn, vn = news[c]
@@ -793,7 +818,7 @@ def main():
         "config": {"workload": w.name, "batch": w1.batch, "kv_heads": w1.kv_heads,
                    "q_heads": w1.q_heads, "head_dim": w1.head_dim, "tokens": w1.tokens,
                    "bits": w1.bits, "group_k": w1.group_k, "group_v": w1.group_v,
-                   "residual": w1.residual, "sink": S, "aging": AGING,
+                   "residual": w1.residual, "sink": S, "aging": AGING, "v_window": V_WINDOW,
                    "deterministic": args.deterministic,
                    "lengths": ("tokens * (b + 1) / batch: " + ",".join(map(str, base))
                                if args.ragged else "uniform"),
@@ -816,7 +841,8 @@ def main():
                      "p10_p90_launch_us": [round(sorted(dec_ms)[len(dec_ms) // 10] * 1e3, 3),
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
                      "traffic": measured_traffic(w.name)
-                                if S == 0 and AGING == "window" and not varlen else None,
+                                if S == 0 and AGING == "window" and V_WINDOW == "flush"
+                                and not varlen else None,
                      "step_kinds": kinds,
                      "settle_steps": ({"steps": settle, "flush_steps": settle_flush,
                                        "avg_us": round(sum(settle_ms) / settle * 1e3, 3)}

@@ -58,8 +58,13 @@ struct DecodeArgs {
   float* out;
   float* part;          // [P][n_parts][GQA][PSTRIDE]; slot s cleared by its owner first
   unsigned* counters;   // [P][kCounterStride]: arrival counter, zero between calls
-  int64_t Tq;           // quantized tokens
+  int64_t Tq;           // tokens of the 64-token blocks (with the per-token Value window,
+                        // the blocks end at 64 * floor(Tqv / 64))
   int64_t nblk;         // 64-token blocks per pair (the last may hold 32 tokens)
+  int64_t Tqk;          // quantized Key tokens (Tq unless the per-token Value window)
+  int64_t Tqv;          // quantized Value tokens (likewise)
+  int n_mix;            // 32-row chunks of [Tq, Tqk): quantized Keys, Values quantized
+                        // below Tqv and float16 from Tqv on
   int r;                // float16 tokens: sink rows, then the window
   int ring;             // window ring start: window token i is in row S + (ring + i) mod R
   int nw;               // workgroups per pair
@@ -122,7 +127,8 @@ __device__ __forceinline__ void ragged_split(DecodeArgs& a, int64_t b) {
     T = a.lens.get(b, 1);
   }
   const TokenSplit ts = split_tokens(a.L, T);
-  a.Tq = ts.Tq;
+  a.Tq = a.Tqk = a.Tqv = ts.Tq;
+  a.n_mix = 0;
   a.nblk = (ts.Tq + BLK - 1) / BLK;
   a.r = (int)ts.fp16_rows();
   a.ring = ts.ring;
@@ -871,6 +877,167 @@ __device__ __forceinline__ void residual_record(const ResidState<GQA>& rs, float
   }
 }
 
+// Rows [t0, t0 + 32) of the history with the per-token Value window, t0 >= a.Tq a
+// multiple of 32, all below a.Tqk: Keys from their codes, Values from their codes below
+// a.Tqv and from the float16 window (row S + (t mod R)) from a.Tqv on.  The dequantized
+// Keys (float32, code * scale + zero with one rounding) are split into two float16
+// terms hi + lo (after a 2^-4 prescale that keeps every value inside the float16
+// range), so Q.K^T runs on the float16 matrix cores as in residual_rows with products
+// exact in float32 and about 22 bits of each Key kept; P.V runs on the VALU.
+template <int BITS, int GQA, int G>
+__device__ __forceinline__ void mixed_rows(const DecodeArgs& a, int64_t pair, int64_t t0,
+                                           const f16x8 (&aq)[4], float* pw,
+                                           ResidState<GQA>& rs) {
+  const LayerView& L = a.L;
+  const int lane = threadIdx.x & 63, lo = lane & 15, j = lane >> 4;
+  constexpr int KB = D * BITS / 8;                 // Key code bytes per token
+  constexpr int VRB = kVRun * BITS / 8;            // Value code bytes per (run, channel)
+  const uint8_t* kc = L.k_codes + pair * L.kc_pair();
+  const __half* ksc = L.k_scale + pair * L.ks_pair() + (t0 / G) * D;
+  const __half* kze = L.k_zero + pair * L.ks_pair() + (t0 / G) * D;
+  const __half* vsc = L.v_scale + pair * L.vs_pair() + t0;   // G_v == d: one per token
+  const __half* vze = L.v_zero + pair * L.vs_pair() + t0;
+  const uint8_t* vc = L.v_codes + pair * L.vc_pair() + (t0 / kVRun) * (D * VRB);
+  const __half* vr = L.v_resid + pair * L.rs_pair();
+  float* palpha = pw + GQA * 32;
+  const int nq = a.Tqv - t0 <= 0 ? 0 : a.Tqv - t0 >= 32 ? 32 : (int)(a.Tqv - t0);
+  // Value inputs of the lane's channels 2*lane, 2*lane+1: the two 16-token runs' code
+  // words, the 32 tokens' scales and zeros, and the float16 rows
+  uint32_t vw[2][BITS == 2 ? 2 : 4];
+#pragma unroll
+  for (int run = 0; run < 2; ++run) {
+    const uint8_t* base = vc + (int64_t)run * D * VRB + 2 * lane * VRB;
+    if constexpr (BITS == 2) {
+      const uint2 u = *reinterpret_cast<const uint2*>(base);
+      vw[run][0] = u.x;
+      vw[run][1] = u.y;
+    } else {
+      const uint4 u = *reinterpret_cast<const uint4*>(base);
+      vw[run][0] = u.x;
+      vw[run][1] = u.y;
+      vw[run][2] = u.z;
+      vw[run][3] = u.w;
+    }
+  }
+  uint4 vs4[4], vz4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vs4[i] = reinterpret_cast<const uint4*>(vsc)[i];
+    vz4[i] = reinterpret_cast<const uint4*>(vze)[i];
+  }
+  __half2 vv[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int64_t row = L.S + (t0 + t) % L.R;
+    vv[t] = reinterpret_cast<const __half2*>(vr + row * D)[lane];
+  }
+  // Q.K^T: column lo of tile nt is token t0 + 16nt + lo; lane group j holds channels
+  // 32ks + 8j .. +7 of K-step ks
+  f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const f16x8 sc = *reinterpret_cast<const f16x8*>(ksc + 32 * ks + 8 * j);
+    const f16x8 ze = *reinterpret_cast<const f16x8*>(kze + 32 * ks + 8 * j);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint8_t* row = kc + (t0 + 16 * nt + lo) * KB;
+      f16x8 hi, lw;
+      if constexpr (BITS == 2) {
+        // channels 32ks + 8j + m: word 2ks + j/2, code 8(j%2) + m at byte m%4, bit
+        // 2((8(j%2) + m)/4)
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 4 * (2 * ks + (j >> 1)));
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t code = (w >> (8 * (m & 3) + 4 * (j & 1) + 2 * (m >> 2))) & 3u;
+          const float x = fmaf((float)code, (float)sc[m], (float)ze[m]) * 0.0625f;
+          const _Float16 h = (_Float16)x;
+          hi[m] = h;
+          lw[m] = (_Float16)(x - (float)h);
+        }
+      } else {
+        // channels 32ks + 8j + m: word 4ks + j, code m at byte m%4, bit 4(m/4)
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 4 * (4 * ks + j));
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t code = (w >> (8 * (m & 3) + 4 * (m >> 2))) & 15u;
+          const float x = fmaf((float)code, (float)sc[m], (float)ze[m]) * 0.0625f;
+          const _Float16 h = (_Float16)x;
+          hi[m] = h;
+          lw[m] = (_Float16)(x - (float)h);
+        }
+      }
+      d[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[ks], hi, d[nt], 0, 0, 0);
+      d[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[ks], lw, d[nt], 0, 0, 0);
+    }
+  }
+  // logits of head 4j + i, rows lo and 16 + lo, in base 2 (the 2^-4 prescale undone)
+  const float zs = a.qscale * 16.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hd = 4 * j + i;
+    const float z0 = d[0][i] * zs, z1 = d[1][i] * zs;
+    const float m_new = fmaxf(rs.m[i], row_max16(fmaxf(z0, z1)));
+    const float alpha = __builtin_amdgcn_exp2f(rs.m[i] - m_new);
+    const float p0 = __builtin_amdgcn_exp2f(z0 - m_new), p1 = __builtin_amdgcn_exp2f(z1 - m_new);
+    rs.l[i] = rs.l[i] * alpha + row_sum16(p0 + p1);
+    rs.m[i] = m_new;
+    if (hd < GQA) {
+      pw[hd * 32 + lo] = p0;
+      pw[hd * 32 + 16 + lo] = p1;
+      if (lo == 0) palpha[hd] = alpha;
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int hd = 0; hd < GQA; ++hd) {
+    const float al = palpha[hd];
+    rs.acc[hd][0] *= al;
+    rs.acc[hd][1] *= al;
+  }
+  // P.V, 4 rows at a time
+#pragma unroll
+  for (int t4 = 0; t4 < 8; ++t4) {
+    __builtin_amdgcn_sched_barrier(0);
+    float2 v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * t4 + e;
+      if (t < nq) {
+        const int run = t >> 4, q = t & 15;
+        uint32_t c0, c1;
+        if constexpr (BITS == 2) {
+          const int pos = 8 * (q & 3) + 2 * (q >> 2);
+          c0 = (vw[run][0] >> pos) & 3u;
+          c1 = (vw[run][1] >> pos) & 3u;
+        } else {
+          const int pos = 8 * (q & 3) + 4 * ((q & 7) >> 2);
+          c0 = (vw[run][q >> 3] >> pos) & 15u;
+          c1 = (vw[run][2 + (q >> 3)] >> pos) & 15u;
+        }
+        const uint32_t sw = reinterpret_cast<const uint32_t*>(&vs4[t >> 3])[(t & 7) >> 1];
+        const uint32_t zw = reinterpret_cast<const uint32_t*>(&vz4[t >> 3])[(t & 7) >> 1];
+        const float sv = h2f((unsigned short)(sw >> (16 * (t & 1))));
+        const float zv = h2f((unsigned short)(zw >> (16 * (t & 1))));
+        v[e] = make_float2(fmaf((float)c0, sv, zv), fmaf((float)c1, sv, zv));
+      } else {
+        v[e] = __half22float2(vv[t]);
+      }
+    }
+#pragma unroll
+    for (int hd = 0; hd < GQA; ++hd) {
+      const float4 p = reinterpret_cast<const float4*>(pw + hd * 32)[t4];
+      const float pv[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rs.acc[hd][0] = fmaf(pv[e], v[e].x, rs.acc[hd][0]);
+        rs.acc[hd][1] = fmaf(pv[e], v[e].y, rs.acc[hd][1]);
+      }
+      asm volatile("" : "+v"(rs.acc[hd][0]), "+v"(rs.acc[hd][1]));
+    }
+  }
+  wave_lds_sync();
+}
+
 // ---- the kernel ---------------------------------------------------------------------
 
 // One workgroup per CU holding every wave the register budget allows there: WAVES =
@@ -930,8 +1097,9 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   const int64_t b = pair / a.L.H, h = pair % a.L.H;
   if (a.lens.p) ragged_split(a, b);
 
-  // this workgroup's share: window chunks (workgroup 0 only), then blocks
-  const int n_res_all = (a.r + 31) / 32;
+  // this workgroup's share: window chunks (workgroup 0 only; first the mixed chunks of
+  // the per-token Value window, if any), then blocks
+  const int n_res_all = a.n_mix + (a.r + 31) / 32;
   int64_t b_lo, b_hi;
   block_share(a.nblk, n_res_all, a.nw, s, b_lo, b_hi);
   const int n_res = s == 0 ? n_res_all : 0;
@@ -971,8 +1139,12 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
       f16x8 aq[4];
       load_q_f16<GQA>(a.q + (b * a.L.H * GQA + h * GQA) * D, aq);
       while (item < n_res) {
-        const int c0 = 32 * item;
-        residual_rows<GQA>(a, pair, c0, a.r - c0 < 32 ? a.r - c0 : 32, aq, pw[wave], rs);
+        if (item < a.n_mix) {
+          mixed_rows<BITS, GQA, G>(a, pair, a.Tq + 32 * (int64_t)item, aq, pw[wave], rs);
+        } else {
+          const int c0 = 32 * (item - a.n_mix);
+          residual_rows<GQA>(a, pair, c0, a.r - c0 < 32 ? a.r - c0 : 32, aq, pw[wave], rs);
+        }
         item = witems.next();
       }
     }
@@ -1015,7 +1187,12 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   p.r = (int)ts.fp16_rows();          // sink rows and window tokens
   p.ring = ts.ring;
   p.n_groups = Tq / L.G;
-  const int64_t nblk = (Tq + BLK - 1) / BLK;
+  // with the per-token Value window the blocks stop at 64 * floor(Tqv / 64) and 32-row
+  // mixed chunks cover the rest of the Key history
+  const int64_t tblk = L.vwin ? ts.Tqv / BLK * BLK : Tq;
+  p.tq_blocks = tblk;
+  p.n_mix = (int)((Tq - tblk) / 32);
+  const int64_t nblk = (tblk + BLK - 1) / BLK;
   const int64_t pairs = (int64_t)L.B * L.H;
   // default: one round of CU-sized workgroups over the 256 CUs, but no more workgroups
   // per pair than keep every wave busy with a block or window chunk (a chunk counting
@@ -1030,7 +1207,7 @@ DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_r
   int64_t nw = room;
   if (n_split_req <= 0) {
     const int64_t waves = 4 * waves_per_simd(L.bits, gqa, L.G);
-    const int64_t items = nblk + (int64_t)RES_COST * ((p.r + 31) / 32);
+    const int64_t items = nblk + (int64_t)RES_COST * (p.n_mix + (p.r + 31) / 32);
     const int64_t busy = (items + waves - 1) / waves;
     if (nw > busy) nw = busy;
   }
@@ -1053,8 +1230,12 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.out = out;
   a.counters = reinterpret_cast<unsigned*>(ws);
   a.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + plan.ws_counters);
-  a.Tq = split_tokens(L, T).Tq;
+  const TokenSplit ts = split_tokens(L, T);
+  a.Tq = plan.tq_blocks;
   a.nblk = (a.Tq + BLK - 1) / BLK;
+  a.Tqk = ts.Tq;
+  a.Tqv = ts.Tqv;
+  a.n_mix = plan.n_mix;
   a.r = plan.r;
   a.ring = plan.ring;
   a.nw = plan.n_split;

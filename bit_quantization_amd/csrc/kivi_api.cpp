@@ -95,8 +95,6 @@ kivi_status check_dims(const kivi_dims* d) {
                 d->aging);
   if (d->flags & ~(KIVI_FLAG_VALUE_TOKEN_WINDOW | KIVI_FLAG_DETERMINISTIC))
     return fail(KIVI_ERR_ARG, "flags = 0x%x: unknown bits", (unsigned)d->flags);
-  if (d->flags & KIVI_FLAG_VALUE_TOKEN_WINDOW)
-    return fail(KIVI_ERR_UNSUPPORTED, "KIVI_FLAG_VALUE_TOKEN_WINDOW is not built yet");
   if (d->max_tokens < 1 || d->max_tokens % d->group_k != 0 || d->max_tokens % kivi::kVRun != 0)
     return fail(KIVI_ERR_ARG, "max_tokens = %lld must be a positive multiple of group_k and 16",
                 (long long)d->max_tokens);
@@ -215,6 +213,14 @@ kivi_status check_paging(const kivi_dims* d, const kivi_paging* pg) {
   return KIVI_OK;
 }
 
+// The per-token Value window is built for uniform batches in contiguous caches.
+kivi_status check_vwin(const kivi_dims* d, const int32_t* lens, const kivi_paging* pg) {
+  if ((d->flags & KIVI_FLAG_VALUE_TOKEN_WINDOW) && (lens || pg))
+    return fail(KIVI_ERR_UNSUPPORTED,
+                "KIVI_FLAG_VALUE_TOKEN_WINDOW with ragged batches or paged caches is not built");
+  return KIVI_OK;
+}
+
 kivi_status check_common(const kivi_dims* d, const kivi_cache* c, int32_t layer) {
   kivi_status st = check_dims(d);
   if (st != KIVI_OK) return st;
@@ -246,6 +252,8 @@ kivi_status quantize_common(const kivi_dims* dims, const kivi_cache* cache, int3
   kivi_status st = check_common(dims, cache, layer);
   if (st != KIVI_OK) return st;
   st = check_paging(dims, pg);
+  if (st != KIVI_OK) return st;
+  st = check_vwin(dims, lens, pg);
   if (st != KIVI_OK) return st;
   if (T < 0) return fail(KIVI_ERR_ARG, "T = %lld is negative", (long long)T);
   if (T > dims->max_tokens)
@@ -311,6 +319,8 @@ kivi_status decode_common(const kivi_dims* dims, const kivi_cache* cache, int32_
   kivi_status st = decode_checks(dims, cache, layer, T, q, sm_scale, out, ws, ws_bytes, n_split,
                                  &L, &plan, pg);
   if (st != KIVI_OK) return st;
+  st = check_vwin(dims, lens, pg);
+  if (st != KIVI_OK) return st;
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
                                      out, ws, plan, nullptr, kivi::Lens{lens, T},
                                      static_cast<hipStream_t>(stream));
@@ -334,8 +344,9 @@ kivi_status append_decode_launch(const kivi_dims* dims, const kivi_cache* cache,
   const __half* vn = static_cast<const __half*>(v_new);
   const kivi::AppendPlan ap = kivi::plan_append(L, T_before);
   const kivi::Lens none{nullptr, 0};
-  if (ap.flush) {
-    // the window is full: flush it (and store the new row) first, then attend
+  if (ap.flush || L.vwin) {
+    // the window is full (or, with the per-token Value window, a Value may leave it):
+    // the append launch first, then attend
     hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, none, false, s);
     if (e != hipSuccess) return device_status(e, "kivi_append_decode flush launch");
     e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale, out,
@@ -796,6 +807,8 @@ kivi_status append_common(const kivi_dims* dims, const kivi_cache* cache, int32_
   if (st != KIVI_OK) return st;
   st = check_paging(dims, pg);
   if (st != KIVI_OK) return st;
+  st = check_vwin(dims, lens, pg);
+  if (st != KIVI_OK) return st;
   st = append_checks(dims, T_before, k_new, v_new);
   if (st != KIVI_OK) return st;
   const kivi::LayerView L = layer_view(dims, cache, layer, pg);
@@ -943,6 +956,8 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
   kivi_status st = check_lens(T_before);
   if (st != KIVI_OK) return st;
   st = check_common(dims, cache, layer);
+  if (st != KIVI_OK) return st;
+  st = check_vwin(dims, T_before, paging);
   if (st != KIVI_OK) return st;
   st = append_checks(dims, T_hi, k_new, v_new);
   if (st != KIVI_OK) return st;

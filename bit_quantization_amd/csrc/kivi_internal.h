@@ -78,9 +78,17 @@ __host__ __device__ inline int64_t window_len(int64_t Tk, int R, int G, int agin
 // [S, S + R): token i after the sink sits in row S + (i mod R), so its r tokens
 // start at row S + ring and wrap after row S + R - 1 (ring = Tq mod R, a multiple
 // of G; 0 when the full window flushes).
+//
+// With the per-token Value window (L.vwin) Values follow their own rule: the Value
+// window holds the rv = min(Tk, R) most recent tokens after the sink, in the same ring
+// rows (token i in row S + (i mod R)), and the Tqv = Tk - rv tokens before them are the
+// quantized Value history.  Tqv <= Tq: tokens [Tqv, Tq) have quantized Keys and float16
+// Values.  Without it Tqv = Tq and rv = r.
 struct TokenSplit {
   int64_t ns, Tq, r;
   int ring;
+  int64_t Tqv, rv;
+  int ring_v;
   __host__ __device__ int64_t fp16_rows() const { return ns + r; }   // sink rows and window tokens
 };
 __host__ __device__ inline TokenSplit split_tokens(const LayerView& L, int64_t T) {
@@ -90,6 +98,9 @@ __host__ __device__ inline TokenSplit split_tokens(const LayerView& L, int64_t T
   t.r = window_len(Tk, L.R, L.G, L.aging);
   t.Tq = Tk - t.r;
   t.ring = (int)(t.Tq % L.R);
+  t.Tqv = L.vwin ? (Tk > L.R ? Tk - L.R : 0) : t.Tq;
+  t.rv = Tk - t.Tqv;
+  t.ring_v = (int)(t.Tqv % L.R);
   return t;
 }
 
@@ -97,21 +108,28 @@ __host__ __device__ inline TokenSplit split_tokens(const LayerView& L, int64_t T
 // ring row in the window, after flushing the oldest n window tokens (rows
 // [first, first + n), never wrapping) into the history at token t0 when the window
 // is full.  The new token then takes row `first`.
+// With the per-token Value window the flush moves Keys only; instead, once the Value
+// window is full (Tk >= R), its oldest token — in row `slot`, which the new token takes —
+// is quantized on its own into Value history token vt (vtok).
 struct AppendPlan {
   int flush;      // 1: quantize n window tokens into the history first
   int n;          // tokens flushed: R, or G with group aging
   int first;      // residual row of the oldest window token (flush only)
   int slot;       // residual row of the new token
   int64_t t0;     // history token of the oldest window token (flush only)
+  int vtok;       // 1: quantize the Value in row `slot` into history token vt first
+  int64_t vt;
 };
 __host__ __device__ inline AppendPlan plan_append(const LayerView& L, int64_t T_before) {
-  if (T_before < L.S) return AppendPlan{0, 0, 0, (int)T_before, 0};
+  if (T_before < L.S) return AppendPlan{0, 0, 0, (int)T_before, 0, 0, 0};
   const int64_t Tk = T_before - L.S;
   const int64_t r = window_len(Tk, L.R, L.G, L.aging);
   const int slot = L.S + (int)(Tk % L.R);
-  if (r < L.R) return AppendPlan{0, 0, 0, slot, 0};
+  const int vtok = L.vwin && Tk >= L.R;
+  const int64_t vt = vtok ? Tk - L.R : 0;
+  if (r < L.R) return AppendPlan{0, 0, 0, slot, 0, vtok, vt};
   const int64_t Tq = Tk - r;
-  return AppendPlan{1, L.aging ? L.G : L.R, L.S + (int)(Tq % L.R), slot, Tq};
+  return AppendPlan{1, L.aging ? L.G : L.R, L.S + (int)(Tq % L.R), slot, Tq, vtok, vt};
 }
 
 // Per-sequence token counts of a ragged batch: device int32 [B] holding T_b (or T_b
@@ -150,6 +168,8 @@ struct DecodePlan {
   int64_t n_groups;     // quantized Key groups per (b, kv head)
   int r;                // float16 tokens: sink rows and window
   int ring;             // window ring start (split_tokens)
+  int64_t tq_blocks;    // tokens the 64-token blocks cover
+  int n_mix;            // 32-row chunks of quantized Keys past them (per-token Value window)
   size_t ws_partials;   // bytes of partial results
   size_t ws_counters;   // bytes of per-pair arrival counters
   size_t ws_total;

@@ -175,13 +175,18 @@ __device__ __forceinline__ float quantize_k_group(const __half* __restrict__ src
 // packed codes ([D][16*BITS/8] bytes at `codes`) and 16*(D/GV) scales/zeros, and
 // returns the largest scale among the lane's groups.  `lds` holds V_LDS bytes private
 // to the wave.  -0 is handled as in quantize_k_group.
+// With n_valid < 16 (the last run of a Value history that ends inside a run, per-token
+// Value window only) tokens n_valid .. 15 get code 0 and no scale or zero: the bytes the
+// definition gives a run whose later tokens are not yet quantized.
 template <int BITS, int GV>
 __device__ __forceinline__ float quantize_v_run(const __half* __restrict__ src,
                                                 uint8_t* __restrict__ codes,
                                                 __half* __restrict__ scale,
-                                                __half* __restrict__ zero, uint8_t* lds) {
+                                                __half* __restrict__ zero, uint8_t* lds,
+                                                int n_valid = kVRun) {
   const int lane = threadIdx.x & 63;
   const int tau = lane >> 2, part = lane & 3;
+  const bool valid = tau < n_valid;
   const uint4* row = reinterpret_cast<const uint4*>(src + tau * D + part * 32);
   __half2 x2[16];                          // channels 2i, 2i+1 of the lane's 32
 #pragma unroll
@@ -218,10 +223,11 @@ __device__ __forceinline__ float quantize_v_run(const __half* __restrict__ src,
 #pragma unroll
   for (int k = 0; k < NSUB; ++k) {
     p[k] = group_params(mn[k] + 0.0f, mx[k] + 0.0f, BITS);   // -0 -> +0
-    smx = fmaxf(smx, p[k].s);
+    if (valid) smx = fmaxf(smx, p[k].s);
   }
   constexpr int NG = D / GV;               // groups per token
-  if constexpr (GV >= 32) {
+  if (!valid) {
+  } else if constexpr (GV >= 32) {
     if ((part % (GV / 32)) == 0) {
       const int j = part * 32 / GV;
       scale[tau * NG + j] = p[0].scale;
@@ -240,7 +246,8 @@ __device__ __forceinline__ float quantize_v_run(const __half* __restrict__ src,
   // banks)
   uint8_t* col = lds + part * (32 * 16 + 16) + tau;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) col[16 * i] = (uint8_t)quant_bits<BITS>(xh(i), p[i / SUB]);
+  for (int i = 0; i < 32; ++i)
+    col[16 * i] = valid ? (uint8_t)quant_bits<BITS>(xh(i), p[i / SUB]) : (uint8_t)0;
   wave_lds_sync();
   // Pack each channel's 16 tokens: dword k of the channel's 16 bytes holds tokens
   // 4k .. 4k+3, shifted by BITS*k into the word order of the Keys.
@@ -253,6 +260,50 @@ __device__ __forceinline__ float quantize_v_run(const __half* __restrict__ src,
     }
   }
   return smx;
+}
+
+// One wave quantizes one Value token (D float16 at `src`, groups of GV channels) into
+// position e of its 16-token run (`run`: [D][16*BITS/8] bytes), leaving the other
+// tokens' codes as they are: lane l owns channels 2l and 2l+1, and rewrites the bits of
+// its code in each channel's word(s) (code e of a run in byte e mod 4 at bit b*(e/4) of
+// its 32-bit word, the word order of quantize_v_run).  Writes the token's D/GV scales
+// and zeros and returns the lane's scale.  "4.4 KV Cache quantization" §3.2: the Value
+// that leaves the float16 window is quantized on its own.
+template <int BITS, int GV>
+__device__ __forceinline__ float quantize_v_token(const __half* __restrict__ src,
+                                                  uint8_t* __restrict__ run, int e,
+                                                  __half* __restrict__ scale,
+                                                  __half* __restrict__ zero) {
+  const int lane = threadIdx.x & 63;
+  const __half2 x = reinterpret_cast<const __half2*>(src)[lane];
+  // group min / max over the GV / 2 lanes of the group (float16 values, exact)
+  float mn = fminf(__low2float(x), __high2float(x));
+  float mx = fmaxf(__low2float(x), __high2float(x));
+#pragma unroll
+  for (int off = 1; off < GV / 2; off <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  const GroupParams p = group_params(mn + 0.0f, mx + 0.0f, BITS);   // -0 -> +0
+  if ((lane % (GV / 2)) == 0) {
+    scale[2 * lane / GV] = p.scale;
+    zero[2 * lane / GV] = p.zero;
+  }
+  const uint32_t c0 = quant_bits<BITS>(__low2half(x), p) & 0xFFu;
+  const uint32_t c1 = quant_bits<BITS>(__high2half(x), p) & 0xFFu;
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  if constexpr (BITS == 2) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(run) + 2 * lane;   // one word per channel
+    const int pos = 8 * (e & 3) + 2 * (e >> 2);
+    w[0] = (w[0] & ~(mask << pos)) | (c0 << pos);
+    w[1] = (w[1] & ~(mask << pos)) | (c1 << pos);
+  } else {
+    uint32_t* w = reinterpret_cast<uint32_t*>(run) + 4 * lane + (e >> 3);   // two per channel
+    const int pos = 8 * (e & 3) + 4 * ((e & 7) >> 2);
+    w[0] = (w[0] & ~(mask << pos)) | (c0 << pos);
+    w[2] = (w[2] & ~(mask << pos)) | (c1 << pos);
+  }
+  return p.s;
 }
 
 // Copy `rows` rows of D float16 from src to dst with one wave (16-byte moves).
@@ -339,10 +390,10 @@ __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const _
   const int64_t pair = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const TokenSplit ts = split_tokens(L, lens.p ? lens.get(pair / L.H, 0) : T);
-  const int64_t Tq = ts.Tq;
+  const int64_t Tqv = ts.Tqv;                     // Tq unless the per-token Value window
   const __half* s0 = src + pair * ld * D;
   const __half* s = s0 + (int64_t)L.S * D;        // the tokens after the sink
-  const int64_t nruns = Tq / kVRun;
+  const int64_t nruns = (Tqv + kVRun - 1) / kVRun;
   float smx = 0.f;
   for (int i = 0; i < npw; ++i) {
     const int64_t j = ((int64_t)blockIdx.x * npw + i) * QW + wave;
@@ -350,13 +401,15 @@ __global__ __launch_bounds__(64 * QW) void prefill_v_kernel(LayerView L, const _
       const Hist<PAGED> hs(L, pair);
       const int64_t ht = hs.token(L, pair / L.H, j * kVRun);
       const int64_t vc = hs.sec * hs.rows * (D * BITS / 8), vs = hs.sec * hs.rows * (D / GV);
+      const int n_valid = Tqv - j * kVRun < kVRun ? (int)(Tqv - j * kVRun) : kVRun;
       smx = fmaxf(smx, quantize_v_run<BITS, GV>(
                            s + j * kVRun * D,
                            L.v_codes + vc + (ht / kVRun) * (D * kVRun * BITS / 8),
                            L.v_scale + vs + ht * (D / GV), L.v_zero + vs + ht * (D / GV),
-                           lds[wave]));
+                           lds[wave], n_valid));
     } else if (j == nruns) {
-      store_fp16_rows(L, s0, s + Tq * D, L.v_resid + pair * L.rs_pair(), ts.ns, ts.r, ts.ring);
+      store_fp16_rows(L, s0, s + Tqv * D, L.v_resid + pair * L.rs_pair(), ts.ns, ts.rv,
+                      ts.ring_v);
     }
   }
   raise_scale_max<QW>(L.scale_max + 2 * pair + 1, smx, red);
@@ -378,11 +431,15 @@ int items_per_wave(int64_t items, int pairs) {
 // each sequence on the device: the grid has the blocks of the largest flush, blocks a
 // sequence does not need return at once, and with flush_only a sequence that does
 // not flush leaves its new row to the decode launch that follows.
+// With the per-token Value window (L.vwin; uniform batches only) Keys flush as above
+// over blocks [0, n/G) and block n/G (the only block when nothing flushes) quantizes
+// the Value leaving the window, if any (vtok: history token vt, read from row `slot`),
+// then stores the new Value row there (and the new Key row when no Key flush does).
 template <int BITS, int G, int GV>
 __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int slot, int n,
                                                     const __half* __restrict__ k_new,
                                                     const __half* __restrict__ v_new, Lens lens,
-                                                    int flush_only) {
+                                                    int flush_only, int vtok, int64_t vt) {
   constexpr int LBYTES = G * D > V_LDS ? G * D : V_LDS;
   __shared__ alignas(16) uint8_t lds[LBYTES];
   const int64_t pair = blockIdx.y;
@@ -397,14 +454,44 @@ __global__ __launch_bounds__(64) void append_kernel(LayerView L, int64_t t0, int
   const __half* vn = v_new + pair * D;
   __half* kr = L.k_resid + pair * L.rs_pair() + (int64_t)slot * D;
   __half* vr = L.v_resid + pair * L.rs_pair() + (int64_t)slot * D;
+  const int nk = n / G;
+  const int blk = blockIdx.x;
+  const int64_t sec = L.section(pair);
+  if (L.vwin) {
+    // per-token Value window: blocks [0, nk) flush Key groups (block 0 then stores the
+    // new Key row over the oldest), block nk the Value side
+    if (blk < nk) {
+      const int64_t ht = t0 + (int64_t)blk * G;
+      const float smx = quantize_k_group<BITS, G>(
+          kr + (int64_t)blk * G * D, L.k_codes + sec * L.kc_pair() + ht * (D * BITS / 8),
+          L.k_scale + sec * L.ks_pair() + (ht / G) * D, L.k_zero + sec * L.ks_pair() + (ht / G) * D,
+          lds);
+      raise_scale_max<1>(L.scale_max + 2 * pair, smx, nullptr);
+      if (blk == 0) {
+        __syncthreads();
+        copy_rows(kn, kr, 1);
+      }
+      return;
+    }
+    if (vtok) {
+      // the oldest Value leaves the full window: quantized on its own into history
+      // token vt (its row is the new token's slot), then the new Value takes the row
+      const float smx = quantize_v_token<BITS, GV>(
+          vr, L.v_codes + sec * L.vc_pair() + (vt / kVRun) * (D * kVRun * BITS / 8),
+          (int)(vt % kVRun), L.v_scale + sec * L.vs_pair() + vt * (D / GV),
+          L.v_zero + sec * L.vs_pair() + vt * (D / GV));
+      raise_scale_max<1>(L.scale_max + 2 * pair + 1, smx, nullptr);
+      __syncthreads();
+    }
+    copy_rows(vn, vr, 1);
+    if (nk == 0) copy_rows(kn, kr, 1);
+    return;
+  }
   if (n == 0) {
     copy_rows(kn, kr, 1);
     copy_rows(vn, vr, 1);
     return;
   }
-  const int nk = n / G;
-  const int blk = blockIdx.x;
-  const int64_t sec = L.section(pair);
   if (blk < nk) {
     const int64_t ht = L.hist_token(pair / L.H, t0 + (int64_t)blk * G);
     const float smx = quantize_k_group<BITS, G>(
@@ -486,11 +573,10 @@ hipError_t launch_quantize_k(const LayerView& L, const __half* src, int64_t ld, 
 hipError_t launch_quantize_v(const LayerView& L, const __half* src, int64_t ld, int64_t T,
                              Lens lens, hipStream_t s) {
   const TokenSplit ts = split_tokens(L, T);
-  const int64_t Tq = ts.Tq;
   const int pairs = L.B * L.H;
   hipLaunchKernelGGL(reset_scale_max_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s,
                      L.scale_max, 1, pairs);
-  const int64_t items = Tq / kVRun + 1;
+  const int64_t items = (ts.Tqv + kVRun - 1) / kVRun + 1;
   const int npw = items_per_wave(items, pairs);
   const dim3 grid((unsigned)((items + QW * npw - 1) / (QW * npw)), (unsigned)pairs);
   bool ok = dispatch_gv(L.Gv, [&](auto gv) {
@@ -522,12 +608,15 @@ hipError_t launch_append_flush(const LayerView& L, int64_t T_before, const __hal
   const int slot = ap.slot;
   const int64_t t0 = ap.t0;
   if (lens.p) n = L.aging ? L.G : L.R;           // room for any sequence's flush
-  const dim3 grid(n ? (unsigned)(n / L.G + n / kVRun) : 1u, (unsigned)(L.B * L.H));
+  const unsigned blocks = L.vwin ? (unsigned)(n / L.G + 1)
+                                 : n ? (unsigned)(n / L.G + n / kVRun) : 1u;
+  const dim3 grid(blocks, (unsigned)(L.B * L.H));
   bool ok = dispatch_bits_g(L.bits, L.G, [&](auto b, auto g) {
     return dispatch_gv(L.Gv, [&](auto gv) {
       hipLaunchKernelGGL(
           (append_kernel<decltype(b)::value, decltype(g)::value, decltype(gv)::value>), grid,
-          dim3(64), 0, s, L, t0, slot, n, k_new, v_new, lens, flush_only ? 1 : 0);
+          dim3(64), 0, s, L, t0, slot, n, k_new, v_new, lens, flush_only ? 1 : 0, ap.vtok,
+          ap.vt);
       return true;
     });
   });

@@ -325,3 +325,23 @@ def test_noalloc_step_rejects_scratch_beyond_its_maximum():
                    ctypes.byref(fake_cache()), 0, 300, None, FAKE, FAKE, ctypes.c_float(0.1),
                    FAKE, None)
     assert st == 1, msg
+
+
+def test_value_token_window_is_refused_for_ragged_and_paged_calls():
+    # KIVI_FLAG_VALUE_TOKEN_WINDOW is built for uniform batches in contiguous caches: the
+    # ragged and paged entry points refuse it before launching (fake pointers, no GPU)
+    d = good_dims(v_window="token")
+    pg = kv.kivi_paging(128, d.max_tokens // 128 + 1, 37, FAKE)
+    st, msg = call("kivi_quantize_k_varlen", ctypes.byref(d.c()), ctypes.byref(fake_cache()),
+                   ctypes.byref(pg), 0, FAKE, FAKE, 300, 300, None)
+    assert st == 2 and "VALUE_TOKEN_WINDOW" in msg, msg
+    st, msg = call("kivi_append_flush_varlen", ctypes.byref(d.c()), ctypes.byref(fake_cache()),
+                   None, 0, FAKE, 300, FAKE, FAKE, None)
+    assert st == 2 and "VALUE_TOKEN_WINDOW" in msg, msg
+    need = ctypes.c_size_t(1 << 20)
+    st, msg = call("kivi_append_decode_varlen", ctypes.byref(d.c()), ctypes.byref(fake_cache()),
+                   None, 0, FAKE, 300, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                   need, None)
+    assert st == 2 and "VALUE_TOKEN_WINDOW" in msg, msg
+    # the uniform calls accept it (sizes are the same as without it)
+    assert kv.kivi_cache_sizes(d) == kv.kivi_cache_sizes(good_dims())

@@ -69,3 +69,25 @@ def test_flush_steps_of_the_70b_stream(bench):
     for j in range(256):
         r = O.residual_len(w.tokens + j, w.residual)
         assert (j in flushing) == (r == w.residual)
+
+
+@pytest.mark.parametrize("aging", ["window", "group"])
+def test_decode_bytes_with_the_token_value_window(bench, aging):
+    """With the per-token Value window the decode reads the Key history and window as
+    before and the Values split at the oracle's T_qv: codes and scales of the quantized
+    Values, float16 rows of the rest."""
+    bench.AGING, bench.V_WINDOW = aging, "token"
+    try:
+        w = W.get("tiny").replace(residual=64)
+        d, b = w.head_dim, w.bits
+        for T in (1, 63, 64, 65, 100, 257, 1000):
+            oc = O.LayerCache(1, 1, d, b, w.group_k, w.group_v, w.residual, 1024, aging=aging,
+                              v_window="token")
+            oc.T = T                                    # only the split rule is used
+            Tq, Tqv = oc.Tq, oc.Tqv
+            r, rv = oc.Tk - Tq, oc.Tk - Tqv
+            ref = ((Tq + Tqv) * d * b // 8 + (Tq // w.group_k) * d * 4 + Tqv * 4
+                   + (r + rv) * d * 2 + w.q_heads * d * 6)
+            assert bench.decode_bytes(w, T) == ref, T
+    finally:
+        bench.AGING, bench.V_WINDOW = "window", "flush"
