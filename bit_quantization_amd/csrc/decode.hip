@@ -1063,8 +1063,10 @@ __device__ __forceinline__ void block_share(int64_t nblk, int n_res, int nw, int
   }
 }
 // PAGED: a paged cache (args.L.table set); its own instantiation, so that the block
-// loop of a contiguous cache carries no page-table lookup.
-template <int BITS, int GQA, int G, bool PAGED>
+// loop of a contiguous cache carries no page-table lookup.  VWIN: the per-token Value
+// window (contiguous caches only); its own instantiation too, so that the mixed chunks'
+// code and registers stay out of the other kernels.
+template <int BITS, int GQA, int G, bool PAGED, bool VWIN>
 __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_kernel(DecodeArgs args) {
   constexpr int NMT = (GQA + 3) / 4;
   constexpr int WAVES = 4 * waves_per_simd(BITS, GQA, G);
@@ -1139,8 +1141,9 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
       f16x8 aq[4];
       load_q_f16<GQA>(a.q + (b * a.L.H * GQA + h * GQA) * D, aq);
       while (item < n_res) {
-        if (item < a.n_mix) {
-          mixed_rows<BITS, GQA, G>(a, pair, a.Tq + 32 * (int64_t)item, aq, pw[wave], rs);
+        if (VWIN && item < a.n_mix) {
+          if constexpr (VWIN)
+            mixed_rows<BITS, GQA, G>(a, pair, a.Tq + 32 * (int64_t)item, aq, pw[wave], rs);
         } else {
           const int c0 = 32 * (item - a.n_mix);
           residual_rows<GQA>(a, pair, c0, a.r - c0 < 32 ? a.r - c0 : 32, aq, pw[wave], rs);
@@ -1249,10 +1252,13 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   bool ok = dispatch_decode(L.bits, gqa, L.G, [&](auto b, auto g, auto gg) {
     constexpr int B_ = decltype(b)::value, Q_ = decltype(g)::value, G_ = decltype(gg)::value;
     if (L.table)
-      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, true>), grid,
+      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, true, false>), grid,
+                         dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
+    else if (L.vwin)
+      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, false, true>), grid,
                          dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, false>), grid,
+      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, false, false>), grid,
                          dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
     return true;
   });
