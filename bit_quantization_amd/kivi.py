@@ -17,7 +17,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkivi.so")
+# KIVI_LIBRARY names another build of the same library (the host-sanitized build the CPU
+# tests run the ABI checks under); by default the in-tree libkivi.so
+LIB_PATH = os.environ.get("KIVI_LIBRARY") or os.path.join(_HERE, "libkivi.so")
 
 STATUS = {0: "KIVI_OK", 1: "KIVI_ERR_ARG", 2: "KIVI_ERR_UNSUPPORTED", 3: "KIVI_ERR_CAPACITY",
           4: "KIVI_ERR_ALIGN", 5: "KIVI_ERR_WORKSPACE", 6: "KIVI_ERR_DEVICE"}
