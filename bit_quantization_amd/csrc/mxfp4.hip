@@ -224,6 +224,44 @@ __device__ __forceinline__ f16x2 pow2_pair(uint32_t codes) {
   return __builtin_bit_cast(f16x2, (spread - 0x00700070u) << 10);
 }
 
+// Online softmax, one head per lane group.  The reference maximum m of a head moves
+// only when a run's maximum exceeds it by more than kLazyLog2 (base-2 units), so
+// probabilities stay below 2^kLazyLog2 and the rescale of l and the accumulators runs
+// on a few runs only (in a branch of its own: the empty asm keeps the compiler from
+// flattening it into selects on every run).
+// (m, l, acc) stay consistent for any reference, which is all the merge assumes.
+constexpr float kLazyLog2 = 8.f;
+__device__ __forceinline__ void lazy_rescale(float& m, float& l, f32x4 (&acc)[8], float mx) {
+  const bool up = mx > m + kLazyLog2;
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    asm volatile("" ::: "memory");
+    const float m_new = up ? mx : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = acc[mt] * alpha;
+  }
+}
+// p = 2^(z - m) for 8 logits as a float16 hi + lo pair per value (hi rounded toward
+// zero, lo the float16 of the exact float32 remainder: 22 significant bits in all);
+// returns the float32 sum of the p.
+__device__ __forceinline__ float split_probabilities(const float (&z)[8], float m, f16x8& ph,
+                                                     f16x8& pl) {
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(z[e] - m), p1 = __builtin_amdgcn_exp2f(z[e + 1] - m);
+    psum += p0 + p1;
+    const auto hi = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+    const auto lo = __builtin_amdgcn_cvt_pkrtz(p0 - (float)hi[0], p1 - (float)hi[1]);
+    ph[e] = hi[0];
+    ph[e + 1] = hi[1];
+    pl[e] = lo[0];
+    pl[e + 1] = lo[1];
+  }
+  return psum;
+}
 // Token of the run that k-slot e (0..7) of lane group j supplies to P.V.
 __device__ __forceinline__ int mx_slot_token(int j, int e) { return 4 * j + (e & 3) + 16 * (e >> 2); }
 
@@ -320,65 +358,69 @@ __global__ __launch_bounds__(256 * kMxWavesPerSimd, 1) void mx_decode_kernel(MxD
         d[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, bq[ks], d[nt], 0, 0, 0);
       }
     }
-    // logits of head lo, tokens mx_slot_token(j, e), base 2
-    const bool partial = t0 + kMxRun > a.T;
+    // logits of head lo, tokens mx_slot_token(j, e), base 2; positions past T (the
+    // pair's last run only) are masked in a branch of its own, so that full runs carry
+    // no selects (the empty asm keeps the compiler from flattening it)
     float z[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      z[e] = d[e >> 2][e & 3] * a.qscale;
-      if (partial && t0 + mx_slot_token(j, e) >= a.T) z[e] = -INFINITY;
+    for (int e = 0; e < 8; ++e) z[e] = d[e >> 2][e & 3] * a.qscale;
+    if (t0 + kMxRun > a.T) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t0 + mx_slot_token(j, e) >= a.T) z[e] = -INFINITY;
     }
     float mx = z[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
+    lazy_rescale(m, l, acc, mx);
     f16x8 ph, pl;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(z[e] - m_new);
-      psum += p;
-      const _Float16 hi = (_Float16)p;
-      ph[e] = hi;
-      pl[e] = (_Float16)(p - (float)hi);
-    }
-    l = l * alpha + psum;
+    const float psum = split_probabilities(z, m, ph, pl);
+    l += psum;
     // O^T += V^T P^T for the eight 16-channel tiles; a Value's scale is its token's
     // (positions past T hold code 0 and scale code 0: value 0).  Scale codes of 113 or
     // more (s >= -14, every block whose largest magnitude is 2^-12 or more) become
-    // float16 pairs multiplied in packed form; a run with a smaller one anywhere in the
-    // wave scales each value with v_ldexp_f16 instead (exact down to float16's
-    // subnormals).  The rescale by alpha is skipped when no head's maximum moved.
+    // float16 pairs, one set per MX block, multiplied in packed form; a run with a
+    // smaller one anywhere in the wave scales each value with v_ldexp_f16 instead
+    // (exact down to float16's subnormals), in a branch of its own.
     bool fast = true;
 #pragma unroll
     for (int q = 0; q < kNBlk; ++q)
       fast &= (((vsc[q][0] + 0x0F0F0F0Fu) & (vsc[q][1] + 0x0F0F0F0Fu) & 0x80808080u) == 0x80808080u);
     const bool all_fast = __builtin_amdgcn_ballot_w64(!fast) == 0;
-    const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      f16x8 vf = widen8_scaled(vw[mt], 1.f);
-      const u32x2 sw = vsc[mt / 2];
+    for (int q = 0; q < kNBlk; ++q) {
       if (all_fast) {
-        const f16x2 s0 = pow2_pair<0>(sw[0]), s1 = pow2_pair<2>(sw[0]);
-        const f16x2 s2 = pow2_pair<0>(sw[1]), s3 = pow2_pair<2>(sw[1]);
-        const f16x2 v0 = f16x2{vf[0], vf[1]} * s0, v1 = f16x2{vf[2], vf[3]} * s1;
-        const f16x2 v2 = f16x2{vf[4], vf[5]} * s2, v3 = f16x2{vf[6], vf[7]} * s3;
-        vf = f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-      } else {
+        const f16x2 s0 = pow2_pair<0>(vsc[q][0]), s1 = pow2_pair<2>(vsc[q][0]);
+        const f16x2 s2 = pow2_pair<0>(vsc[q][1]), s3 = pow2_pair<2>(vsc[q][1]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sc = (int)((sw[e / 4] >> (8 * (e % 4))) & 0xFF) - 127;
-          vf[e] = __builtin_amdgcn_ldexph(vf[e], sc);
+        for (int mt = 2 * q; mt < 2 * q + 2; ++mt) {
+          const f16x8 vf = widen8_scaled(vw[mt], 1.f);
+          const f16x2 v0 = f16x2{vf[0], vf[1]} * s0, v1 = f16x2{vf[2], vf[3]} * s1;
+          const f16x2 v2 = f16x2{vf[4], vf[5]} * s2, v3 = f16x2{vf[6], vf[7]} * s3;
+          const f16x8 vs = f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vs, ph, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vs, pl, acc[mt], 0, 0, 0);
+        }
+      } else {
+        // the scale words are made opaque here, so that their per-value extraction
+        // stays in this branch
+        u32x2 sw = vsc[q];
+        asm volatile("" : "+v"(sw[0]), "+v"(sw[1]));
+#pragma unroll
+        for (int mt = 2 * q; mt < 2 * q + 2; ++mt) {
+          f16x8 vf = widen8_scaled(vw[mt], 1.f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int sc = (int)((sw[e / 4] >> (8 * (e % 4))) & 0xFF) - 127;
+            vf[e] = __builtin_amdgcn_ldexph(vf[e], sc);
+          }
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, acc[mt], 0, 0, 0);
         }
       }
-      if (rescale) acc[mt] = acc[mt] * alpha;
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, acc[mt], 0, 0, 0);
     }
   }
 
