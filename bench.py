@@ -4,7 +4,9 @@
 One step = one decode step of the streaming hot path on one layer cache: append one
 float16 K/V token per sequence (flushing the residual window into the 2/4-bit store
 when it is full), then decode attention of the new query over all cached tokens,
-through kivi_append_decode (one kernel launch; flush steps add the flush launch).
+through kivi_append_decode (one kernel launch; flush steps add the flush launch, and
+so do, with the per-token Value window, steps whose leaving Value completes a 64-token
+block of the quantized history).
 With --n-split the step is kivi_append_flush + kivi_decode_attn_split.
 Steps rotate over ``copies`` independent layer caches (like the layers of a model)
 whose total size exceeds the 256 MB last-level cache, so that each step reads its
@@ -650,11 +652,15 @@ def main():
         j = Ts[c]
         Ts[c] = j + 1
         # steps with the append launch before the decode: a full window flushes, or
-        # (per-token Value window) a Value leaves a full Value window
-        flushes[i] = any(t + j - S > 0 and (window_len(t + j - S, w1.residual, w1.group_k)
-                                            == w1.residual
-                                            or (V_WINDOW == "token" and t + j - S >= w1.residual))
-                         for t in base)
+        # (per-token Value window) the Value leaving the window completes a 64-token
+        # block of the quantized history (the decode quantizes it itself otherwise)
+        def two_launch(Tk, R=w1.residual):
+            if Tk <= 0:
+                return False
+            if window_len(Tk, R, w1.group_k) == R:
+                return True
+            return V_WINDOW == "token" and Tk >= R and (Tk - R + 1) % 64 == 0
+        flushes[i] = any(two_launch(t + j - S) for t in base)
         T_before = T_hi + j                         # the longest sequence's count
         T = T_before + 1
         kn, vn = news[c]

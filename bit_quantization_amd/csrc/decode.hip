@@ -41,11 +41,12 @@
 #include <type_traits>
 
 #include "decode_common.h"
+#include "quantizer.h"
 
 namespace kivi {
 namespace {
 
-constexpr int BLK = 64;              // tokens per block step of a wave
+constexpr int BLK = kDecodeBlockTokens;   // tokens per block step of a wave
 // Work of one 32-row float16 window chunk in blocks (it moves three blocks' bytes with
 // fewer loads in flight and takes about three blocks of wave time)
 constexpr int RES_COST = 3;
@@ -72,6 +73,9 @@ struct DecodeArgs {
   const __half* k_new;  // [P][D]: window row new_slot comes from here (new_slot >= 0)
   const __half* v_new;
   int new_slot;         // -1: every window row is read from the cache
+  int64_t vt;           // per-token Value window, fused step: the history token whose
+                        // Value leaves the window in this step (its row is new_slot);
+                        // -1: none
   Lens lens;            // ragged batch: per-sequence counts (the fields above are for T)
 };
 
@@ -931,6 +935,63 @@ __device__ __forceinline__ void mixed_rows(const DecodeArgs& a, int64_t pair, in
     const int64_t row = L.S + (t0 + t) % L.R;
     vv[t] = reinterpret_cast<const __half2*>(vr + row * D)[lane];
   }
+  // A fused step (a.vt >= 0): the Value leaving the window, token a.vt, is quantized by
+  // the wave whose chunk holds it, from its float16 row (the appended token's row), with
+  // the append kernel's quantizer ("4.4 KV Cache quantization" §3.2: the oldest Value
+  // is quantized on its own).  Each lane rewrites its two channels' code bits in the
+  // token's 16-token run; lane 0 writes the scale and zero and raises the scale maximum.
+  // The wave attends with the new codes (vq) and then stores the appended token's rows
+  // over that row.  No other wave of the launch reads these bytes: the run is in this
+  // chunk, and the row holds no other token this launch reads.
+  const int64_t tv = a.vt - t0;
+  const bool leaving = a.vt >= 0 && tv >= 0 && tv < 32;
+  float2 vq = make_float2(0.f, 0.f);
+  if (leaving) {
+    const __half2 x = reinterpret_cast<const __half2*>(vr + (int64_t)a.new_slot * D)[lane];
+    float mn = fminf(__low2float(x), __high2float(x));
+    float mx = fmaxf(__low2float(x), __high2float(x));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {   // G_v == d: the group is the whole row
+      mn = fminf(mn, __shfl_xor(mn, off, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    }
+    const GroupParams gp = group_params(mn + 0.0f, mx + 0.0f, BITS);   // -0 -> +0
+    const uint32_t c0 = quant_bits<BITS>(__low2half(x), gp) & 0xFFu;
+    const uint32_t c1 = quant_bits<BITS>(__high2half(x), gp) & 0xFFu;
+    const int e = (int)(a.vt % kVRun);
+    uint32_t* w = reinterpret_cast<uint32_t*>(L.v_codes + pair * L.vc_pair() +
+                                              (a.vt / kVRun) * (D * VRB));
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    if constexpr (BITS == 2) {
+      w += 2 * lane;                                 // one word per channel
+      const int pos = 8 * (e & 3) + 2 * (e >> 2);
+      w[0] = (w[0] & ~(mask << pos)) | (c0 << pos);
+      w[1] = (w[1] & ~(mask << pos)) | (c1 << pos);
+    } else {
+      w += 4 * lane + (e >> 3);                      // two words per channel
+      const int pos = 8 * (e & 3) + 4 * ((e & 7) >> 2);
+      w[0] = (w[0] & ~(mask << pos)) | (c0 << pos);
+      w[2] = (w[2] & ~(mask << pos)) | (c1 << pos);
+    }
+    if (lane == 0) {
+      L.v_scale[pair * L.vs_pair() + a.vt] = gp.scale;
+      L.v_zero[pair * L.vs_pair() + a.vt] = gp.zero;
+      __hip_atomic_fetch_max(reinterpret_cast<unsigned*>(L.scale_max + 2 * pair + 1),
+                             __float_as_uint(gp.s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the dequantized pair, as the code path below forms it (float16 scale and zero,
+    // zero == mn exactly)
+    vq = make_float2(fmaf((float)c0, gp.s, gp.mn), fmaf((float)c1, gp.s, gp.mn));
+    // the row is read: it takes the appended token's Key and Value (the empty asm
+    // orders the stores after the codes, which depend on the row's loaded values)
+    asm volatile("" ::"v"(c0), "v"(c1) : "memory");
+    if (lane < 2 * (D / 8)) {
+      const int part = lane / (D / 8), k = lane % (D / 8);
+      const __half* src = (part ? a.v_new : a.k_new) + pair * D;
+      __half* dst = (part ? L.v_resid : L.k_resid) + pair * L.rs_pair() + (int64_t)a.new_slot * D;
+      reinterpret_cast<uint4*>(dst)[k] = reinterpret_cast<const uint4*>(src)[k];
+    }
+  }
   // Q.K^T: column lo of tile nt is token t0 + 16nt + lo; lane group j holds channels
   // 32ks + 8j .. +7 of K-step ks
   f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -1019,6 +1080,7 @@ __device__ __forceinline__ void mixed_rows(const DecodeArgs& a, int64_t pair, in
         const float sv = h2f((unsigned short)(sw >> (16 * (t & 1))));
         const float zv = h2f((unsigned short)(zw >> (16 * (t & 1))));
         v[e] = make_float2(fmaf((float)c0, sv, zv), fmaf((float)c1, sv, zv));
+        if (leaving && t == tv) v[e] = vq;
       } else {
         v[e] = __half22float2(vv[t]);
       }
@@ -1110,7 +1172,9 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   if (threadIdx.x == 0) counter = 0;
   // An appended token: workgroup 0 of the pair stores its rows into the window (read
   // by the next call; this one takes them from k_new / v_new).
-  if (a.new_slot >= 0 && s == 0 && threadIdx.x < 2 * (D / 8)) {
+  // (A fused step of the per-token Value window stores them in mixed_rows, after the
+  // leaving Value has been read from that row.)
+  if (a.new_slot >= 0 && !(VWIN && a.vt >= 0) && s == 0 && threadIdx.x < 2 * (D / 8)) {
     const int part = threadIdx.x / (D / 8), k = threadIdx.x % (D / 8);
     const __half* src = (part ? a.v_new : a.k_new) + pair * D;
     __half* dst = (part ? a.L.v_resid : a.L.k_resid) + pair * a.L.rs_pair() + (int64_t)a.new_slot * D;
@@ -1246,6 +1310,7 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.k_new = new_row ? new_row->k : nullptr;
   a.v_new = new_row ? new_row->v : nullptr;
   a.new_slot = new_row ? new_row->slot : -1;
+  a.vt = new_row ? new_row->vt : -1;
   a.lens = lens;
   const int64_t P = (int64_t)L.B * L.H;
   const dim3 grid((unsigned)(P * plan.n_split));

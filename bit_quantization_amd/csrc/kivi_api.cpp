@@ -344,16 +344,16 @@ kivi_status append_decode_launch(const kivi_dims* dims, const kivi_cache* cache,
   const __half* vn = static_cast<const __half*>(v_new);
   const kivi::AppendPlan ap = kivi::plan_append(L, T_before);
   const kivi::Lens none{nullptr, 0};
-  if (ap.flush || L.vwin) {
-    // the window is full (or, with the per-token Value window, a Value may leave it):
-    // the append launch first, then attend
+  if (ap.flush || (L.vwin && !kivi::vwin_fused_step(L, ap))) {
+    // the window is full (or, with the per-token Value window, the leaving Value
+    // completes a block): the append launch first, then attend
     hipError_t e = kivi::launch_append_flush(L, T_before, kn, vn, none, false, s);
     if (e != hipSuccess) return device_status(e, "kivi_append_decode flush launch");
     e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale, out,
                             workspace, plan, nullptr, none, s);
     return device_status(e, "kivi_append_decode launch");
   }
-  const kivi::NewRow nr{kn, vn, ap.slot};
+  const kivi::NewRow nr{kn, vn, ap.slot, L.vwin && ap.vtok ? ap.vt : -1};
   hipError_t e = kivi::launch_decode(L, dims->q_heads, T, static_cast<const __half*>(q), sm_scale,
                                      out, workspace, plan, &nr, none, s);
   return device_status(e, "kivi_append_decode launch");

@@ -132,6 +132,16 @@ __host__ __device__ inline AppendPlan plan_append(const LayerView& L, int64_t T_
   return AppendPlan{1, L.aging ? L.G : L.R, L.S + (int)(Tq % L.R), slot, Tq, vtok, vt};
 }
 
+// Tokens per block of the decode's quantized-history loop.
+constexpr int kDecodeBlockTokens = 64;
+// A step of the per-token Value window that flushes no Key group runs as one decode
+// launch (the decode quantizes the leaving Value), unless that Value completes a block
+// of the quantized-history loop: the block's codes are then read by other workgroups of
+// the same launch, so they are written by an append launch first.
+__host__ __device__ inline bool vwin_fused_step(const LayerView& L, const AppendPlan& ap) {
+  return L.vwin && !ap.flush && (!ap.vtok || (ap.vt + 1) % kDecodeBlockTokens != 0);
+}
+
 // Per-sequence token counts of a ragged batch: device int32 [B] holding T_b (or T_b
 // - 1 for a decode step that appends), clamped on the device into [lo, hi] so that
 // every access stays inside the cache whatever the array holds.
@@ -181,6 +191,8 @@ struct NewRow {
   const __half* k;
   const __half* v;
   int slot;
+  int64_t vt = -1;      // per-token Value window: history token whose Value leaves the
+                        // window in this step (its row is slot), quantized by the decode
 };
 // With lens.p set, sequence b attends over lens.get(b, 1) tokens (T = lens.hi), or,
 // with new_row set, appends at T_before = lens.get(b, 0) and attends over T_before + 1

@@ -180,20 +180,28 @@ def test_vwindow_decode_matches_oracle(bits, G, R, S, aging, B, H, g, T, n_split
                  f"vwindow decode T={T} n_split={n_split}")
 
 
-@pytest.mark.parametrize("bits,G,R,aging,g", [(2, 32, 64, "window", 4), (4, 64, 128, "group", 8)])
-def test_vwindow_fused_step_matches_oracle(bits, G, R, aging, g):
-    # kivi_append_decode (an append launch, then the decode) from inside the first window
-    # across slides and flushes; outputs at every step against the oracle, the cache
-    # bytes at the end
+@pytest.mark.parametrize("bits,G,R,aging,g,S", [
+    (2, 32, 64, "window", 4, 0),
+    (4, 64, 128, "group", 8, 0),
+    (2, 32, 32, "window", 2, 3),    # R < 64: ring rows recur inside one 64-token span
+    (4, 32, 64, "group", 4, 5),
+])
+def test_vwindow_fused_step_matches_oracle(bits, G, R, aging, g, S):
+    # kivi_append_decode from inside the first window across slides and flushes: most
+    # steps are one decode launch that quantizes the leaving Value itself; steps that
+    # flush Keys, or whose leaving Value completes a 64-token block, launch the append
+    # first.  Outputs and every cache byte against the oracle at every step.
     k = kv()
     B, H = 2, 2
-    Tp = R - 7
-    T1 = Tp + 2 * R + 40
-    dims = vdims(bits, G, D, R, 0, B, H, g, capacity(T1, R, G), aging)
-    K, V = rand_kv(B, H, T1, D, seed=R + g)
+    Tp = S + R - 7
+    T1 = Tp + 2 * R + 70
+    dims = vdims(bits, G, D, R, S, B, H, g, capacity(T1, R, G), aging)
+    print(f"[vwindow] fused bits={bits} G={G} R={R} aging={aging} g={g} S={S}", flush=True)
+    K, V = rand_kv(B, H, T1, D, seed=R + g + S)
     cache = prefill(dims, K, V, Tp)
     Kh, Vh = K.cpu().numpy(), V.cpu().numpy()
-    oc = O.LayerCache(B, H, D, bits, G, D, R, dims.max_tokens, aging=aging, v_window="token")
+    oc = O.LayerCache(B, H, D, bits, G, D, R, dims.max_tokens, sink=S, aging=aging,
+                      v_window="token")
     oc.prefill(Kh[:, :, :Tp], Vh[:, :, :Tp])
     ws = k.new_workspace(dims, T1)
     out = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
@@ -204,7 +212,40 @@ def test_vwindow_fused_step_matches_oracle(bits, G, R, aging, g):
         torch.cuda.synchronize()
         oc.append(Kh[:, :, t], Vh[:, :, t])
         assert_close(out.cpu().numpy(), oc.attend(q.cpu().numpy(), 0.09), f"fused step T={t + 1}")
-    compare(cache, oc, f"fused stream end T={T1}")
+        compare(cache, oc, f"fused step T={t + 1}")
+
+
+@pytest.mark.parametrize("bits,G,R,aging,S", [(2, 32, 64, "window", 0), (4, 32, 32, "group", 2)])
+def test_vwindow_fused_step_equals_two_launches(bits, G, R, aging, S):
+    # with KIVI_FLAG_DETERMINISTIC, kivi_append_decode (one launch on most steps) and
+    # kivi_append_flush + kivi_decode_attn give the same output bits and cache bytes at
+    # every step: the decode's own quantization of the leaving Value writes what the
+    # append kernel writes, and attends with the values the codes give
+    k = kv()
+    B, H, g = 2, 2, 4
+    Tp = S + R - 3
+    T1 = Tp + 2 * R + 70
+    dims = vdims(bits, G, D, R, S, B, H, g, capacity(T1, R, G), aging)
+    dims.deterministic = True
+    K, V = rand_kv(B, H, T1, D, seed=11 + R)
+    a = prefill(dims, K, V, Tp)
+    b_ = prefill(dims, K, V, Tp)
+    wa, wb = k.new_workspace(dims, T1), k.new_workspace(dims, T1)
+    oa = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    names = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid",
+             "v_resid", "scale_max")
+    for t in range(Tp, T1):
+        q = torch.randn((B, H * g, D), device="cuda").to(torch.float16)
+        kn, vn = K[:, :, t].contiguous(), V[:, :, t].contiguous()
+        k.kivi_append_flush(dims, a, 0, t, kn, vn)
+        k.kivi_decode_attn(dims, a, 0, t + 1, q, 0.09, oa, wa)
+        k.kivi_append_decode(dims, b_, 0, t, kn, vn, q, 0.09, ob, wb)
+        torch.cuda.synchronize()
+        assert np.array_equal(oa.cpu().numpy().view(np.uint32), ob.cpu().numpy().view(np.uint32)), \
+            f"output bits, step T={t + 1}"
+        for n in names:
+            assert torch.equal(a.view(n), b_.view(n)), f"{n}, step T={t + 1}"
 
 
 def test_vwindow_70b_stream_full_size():
