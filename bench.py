@@ -13,9 +13,11 @@ whose total size exceeds the 256 MB last-level cache, so that each step reads it
 cache from HBM.  Inputs are resident in HBM before timing starts.
 
 Printed (one JSON line): value = algorithmic bytes of the timed steps / wall time
-(GB/s), tokens/s, the step launch's roofline against the HBM peak (its algorithmic
-bytes per launch over its average duration from HIP events on the launch stream), the CPU oracle's throughput on a bounded sample,
-and the output quality against unquantized fp32 attention (reported, not gated).
+(GB/s), tokens/s, the decode kernel's roofline against the HBM peak (its algorithmic
+bytes per launch over its average duration, from HIP events that the launch itself
+records at the kernel's start and end on the launch stream), the CPU oracle's
+throughput on a bounded sample, and the output quality against unquantized fp32
+attention (reported, not gated).
 
 Algorithmic bytes of a decode launch, per (sequence, KV head): packed codes
 T_q*d*b/8 for K and for V, float16 scale+zero 4*d per Key group and 4*(d/G_v) per
@@ -94,6 +96,30 @@ def value_split(T, R, S=0, G=32):
     Tk = T - ns
     Tqv = max(0, Tk - R)
     return ns + Tk - Tqv, Tqv
+
+
+class KernelClock:
+    """Duration of each timed step's decode kernel itself: before each step the library
+    is armed (kivi_time_next_decode) to record a pair of HIP events at that kernel's own
+    start and end (hipExtLaunchKernel, on the launch stream), so the dispatch around it
+    stays out; the same quantity rocprofv3's kernel trace reports."""
+
+    def __init__(self, n, stream):
+        import torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        for a, b in self.ev:            # a first record creates the underlying events
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+
+    def arm(self, i):
+        from bit_quantization_amd import kivi as k
+        a, b = self.ev[i]
+        k.kivi_time_next_decode(a.cuda_event, b.cuda_event)
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev]
 
 
 def decode_bytes(w, T, S=0):
@@ -462,17 +488,18 @@ def fp8_main(args):
     for i in range(args.warmup):
         prepare(i)[0]()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    clock = KernelClock(args.steps, stream)
     steps = [prepare(args.warmup + i) for i in range(args.steps)]
-    launch_bytes = sum(db + ab for _, db, ab in steps)
+    # the decode kernel's bytes: the MXFP4 step's decode also codes the new token; the
+    # FP8 step's append is a launch of its own
+    one_launch = mx and not args.n_split
+    launch_bytes = sum(db + (ab if one_launch else 0) for _, db, ab in steps)
     torch.cuda.synchronize()
-    for (call, _, _), (e0, e1) in zip(steps, events):
-        e0.record(stream)
+    for i, (call, _, _) in enumerate(steps):
+        clock.arm(i)
         call()
-        e1.record(stream)
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in events]
+    ms = clock.ms()
     avg_s = sum(ms) / len(ms) / 1e3
     first = args.warmup + args.steps
     graph = torch.cuda.CUDAGraph()
@@ -508,13 +535,17 @@ def fp8_main(args):
                    "launch": "one HIP graph of the timed steps"},
         "tokens_per_s": round(w1.batch * args.steps / wall, 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": ("mx_decode_kernel (+ mx_append_kernel)" if mx
-                                                else "fp8_decode_kernel (+ fp8_append_kernel)"),
+        "roofline": {"bound": "hbm", "kernel": ("mx_decode_kernel (append fused)" if one_launch
+                                                else "mx_decode_kernel" if mx
+                                                else "fp8_decode_kernel"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(launch_bytes / args.steps),
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "median_launch_us": round(sorted(ms)[len(ms) // 2] * 1e3, 3),
+                     "p10_p90_launch_us": [round(sorted(ms)[len(ms) // 10] * 1e3, 3),
+                                           round(sorted(ms)[(9 * len(ms)) // 10] * 1e3, 3)],
+                     "timing": "decode kernel start/end events (kivi_time_next_decode)",
                      "traffic": None},
         "cpu_baseline": cpu,
     }
@@ -698,29 +729,33 @@ def main():
         prepare(i)[0]()
     torch.cuda.synchronize()
 
-    # Per-launch duration (roofline): K eager steps, each bracketed by HIP events on
-    # the launch stream.
+    # Duration of the dominant kernel (roofline): K eager steps; the decode kernel of
+    # each is timed by events at its own start and end (KernelClock).
     t_first = settle + args.warmup
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    clock = KernelClock(args.steps, stream)
     steps = [prepare(t_first + i) for i in range(args.steps)]
-    launch_bytes = sum(db + ab for _, db, ab in steps)   # each launch appends and attends
+    # the decode kernel's bytes: a one-launch step's decode also appends (and, with the
+    # per-token Value window, quantizes the leaving Value); a two-launch step's append
+    # kernel does that instead
+    kernel_bytes = [db + (0 if flushes[t_first + i] or args.n_split else ab)
+                    for i, (_, db, ab) in enumerate(steps)]
     torch.cuda.synchronize()
-    for (call, _, _), (e0, e1) in zip(steps, events):
-        e0.record(stream)
+    for i, (call, _, _) in enumerate(steps):
+        clock.arm(i)
         call()
-        e1.record(stream)
     torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in events]
-    # per-launch times of steps that flush a window (two launches) and of the others
+    dec_ms = clock.ms()
+    # decode-kernel times of steps with two launches (a window flush first) and of the
+    # others
     kinds = {}
     for name, want in (("flush", True), ("plain", False)):
-        ms = [t for i, t in enumerate(dec_ms) if flushes[t_first + i] == want]
-        if ms:
-            kinds[name] = {"steps": len(ms), "avg_us": round(sum(ms) / len(ms) * 1e3, 3)}
+        idx = [i for i in range(len(dec_ms)) if flushes[t_first + i] == want]
+        if idx:
+            kinds[name] = {"steps": len(idx),
+                           "avg_kernel_us": round(sum(dec_ms[i] for i in idx) / len(idx) * 1e3, 3)}
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     dec_med_s = sorted(dec_ms)[len(dec_ms) // 2] / 1e3
-    dec_per_launch = launch_bytes / args.steps
+    dec_per_launch = sum(kernel_bytes) / args.steps
 
     # Whole-job throughput: the next K steps, launched as one HIP graph (captured with
     # each step's own arguments, so replaying it once runs exactly those K steps and
@@ -846,6 +881,7 @@ def main():
                      "median_launch_us": round(dec_med_s * 1e6, 3),
                      "p10_p90_launch_us": [round(sorted(dec_ms)[len(dec_ms) // 10] * 1e3, 3),
                                            round(sorted(dec_ms)[(9 * len(dec_ms)) // 10] * 1e3, 3)],
+                     "timing": "decode kernel start/end events (kivi_time_next_decode)",
                      "traffic": measured_traffic(w.name)
                                 if S == 0 and AGING == "window" and V_WINDOW == "flush"
                                 and not varlen else None,

@@ -1317,14 +1317,14 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   bool ok = dispatch_decode(L.bits, gqa, L.G, [&](auto b, auto g, auto gg) {
     constexpr int B_ = decltype(b)::value, Q_ = decltype(g)::value, G_ = decltype(gg)::value;
     if (L.table)
-      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, true, false>), grid,
-                         dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
+      launch_decode_kernel(decode_kernel<B_, Q_, G_, true, false>, grid,
+                           dim3(256 * waves_per_simd(B_, Q_, G_)), s, a);
     else if (L.vwin)
-      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, false, true>), grid,
-                         dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
+      launch_decode_kernel(decode_kernel<B_, Q_, G_, false, true>, grid,
+                           dim3(256 * waves_per_simd(B_, Q_, G_)), s, a);
     else
-      hipLaunchKernelGGL((decode_kernel<B_, Q_, G_, false, false>), grid,
-                         dim3(256 * waves_per_simd(B_, Q_, G_)), 0, s, a);
+      launch_decode_kernel(decode_kernel<B_, Q_, G_, false, false>, grid,
+                           dim3(256 * waves_per_simd(B_, Q_, G_)), s, a);
     return true;
   });
   if (!ok) return hipErrorInvalidValue;

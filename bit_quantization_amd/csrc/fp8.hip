@@ -368,10 +368,10 @@ hipError_t launch_fp8_decode(const Fp8View& L, int q_heads, int64_t T, const __h
   bool ok = dispatch_fmt(L.fmt, [&](auto f) {
     constexpr int F = decltype(f)::value;
     switch (gqa) {
-      case 1: hipLaunchKernelGGL((fp8_decode_kernel<F, 1>), grid, block, 0, s, a); return true;
-      case 2: hipLaunchKernelGGL((fp8_decode_kernel<F, 2>), grid, block, 0, s, a); return true;
-      case 4: hipLaunchKernelGGL((fp8_decode_kernel<F, 4>), grid, block, 0, s, a); return true;
-      case 8: hipLaunchKernelGGL((fp8_decode_kernel<F, 8>), grid, block, 0, s, a); return true;
+      case 1: launch_decode_kernel(fp8_decode_kernel<F, 1>, grid, block, s, a); return true;
+      case 2: launch_decode_kernel(fp8_decode_kernel<F, 2>, grid, block, s, a); return true;
+      case 4: launch_decode_kernel(fp8_decode_kernel<F, 4>, grid, block, s, a); return true;
+      case 8: launch_decode_kernel(fp8_decode_kernel<F, 8>, grid, block, s, a); return true;
       default: return false;
     }
   });

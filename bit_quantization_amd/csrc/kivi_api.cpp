@@ -556,6 +556,16 @@ kivi::MxView mx_view(const kivi_mxfp4_dims* d, const kivi_mxfp4_cache* c, int la
 
 }  // namespace
 
+// The calling thread's armed kernel timer (kivi_time_next_decode).
+static thread_local kivi::KernelTimer g_timer;
+namespace kivi {
+KernelTimer take_kernel_timer() {
+  const KernelTimer t = g_timer;
+  g_timer = KernelTimer{};
+  return t;
+}
+}  // namespace kivi
+
 extern "C" {
 
 kivi_status kivi_mxfp4_cache_sizes(const kivi_mxfp4_dims* dims, size_t bytes[4]) {
@@ -982,6 +992,16 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
 
 const char* kivi_last_error(void) { return g_err; }
 
-int32_t kivi_abi_version(void) { return 7; }
+// ---- measurement aid ----------------------------------------------------------------
+
+kivi_status kivi_time_next_decode(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(KIVI_ERR_ARG, "start_event and stop_event must both be set or both be null");
+  g_timer.start = static_cast<hipEvent_t>(start_event);
+  g_timer.stop = static_cast<hipEvent_t>(stop_event);
+  return KIVI_OK;
+}
+
+int32_t kivi_abi_version(void) { return 8; }
 
 }  // extern "C"

@@ -1,6 +1,7 @@
 // Internal declarations shared by the C ABI layer and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -187,6 +188,24 @@ struct DecodePlan {
 DecodePlan plan_decode(const LayerView& L, int q_heads, int64_t T, int n_split_req);
 // A token appended by the decode launch itself: its rows are read from k/v (float16
 // [B][H_kv][d]) as window row `slot`, and the launch also stores them there.
+// Measurement aid (kivi_time_next_decode): a pair of events that the calling thread's
+// next decode-kernel launch records at the kernel's own start and end.
+struct KernelTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+KernelTimer take_kernel_timer();   // the armed pair (or none); disarms
+// Launches a decode kernel as hipLaunchKernelGGL does, or, with a timer armed, through
+// hipExtLaunchKernel with the timer's events.
+template <typename K, typename... Args>
+void launch_decode_kernel(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  const KernelTimer t = take_kernel_timer();
+  if (t.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
 struct NewRow {
   const __half* k;
   const __half* v;

@@ -480,10 +480,10 @@ hipError_t launch_mx_decode(const MxView& L, int q_heads, int64_t T, const __hal
   const dim3 grid((unsigned)((int64_t)L.B * L.H * plan.n_split));
   const dim3 block(256 * kMxWavesPerSimd);
   switch (gqa) {
-    case 1: hipLaunchKernelGGL((mx_decode_kernel<1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((mx_decode_kernel<2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((mx_decode_kernel<4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((mx_decode_kernel<8>), grid, block, 0, s, a); break;
+    case 1: launch_decode_kernel(mx_decode_kernel<1>, grid, block, s, a); break;
+    case 2: launch_decode_kernel(mx_decode_kernel<2>, grid, block, s, a); break;
+    case 4: launch_decode_kernel(mx_decode_kernel<4>, grid, block, s, a); break;
+    case 8: launch_decode_kernel(mx_decode_kernel<8>, grid, block, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

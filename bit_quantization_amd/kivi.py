@@ -37,7 +37,7 @@ EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_appen
            "kivi_mxfp4_decode_workspace_bytes", "kivi_mxfp4_decode_attn",
            "kivi_mxfp4_append_decode",
            "kivi_decode_workspace_bytes_split", "kivi_decode_splits", "kivi_last_error",
-           "kivi_abi_version")
+           "kivi_time_next_decode", "kivi_abi_version")
 
 
 class KiviError(RuntimeError):
@@ -147,6 +147,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_mxfp4_decode_attn": (I32, [MD, MC, I32, I64, P, F32, P, P, SZ, I32, P]),
         "kivi_mxfp4_append_decode": (I32, [MD, MC, I32, I64, P, P, P, F32, P, P, SZ, P]),
         "kivi_last_error": (ctypes.c_char_p, []),
+        "kivi_time_next_decode": (I32, [P, P]),
         "kivi_abi_version": (I32, []),
     }
     for name, (res, args) in sig.items():
@@ -702,6 +703,13 @@ def kivi_mxfp4_append_decode(dims: MxDims, cache: MxCache, layer: int, T_before:
                              workspace: torch.Tensor, stream=None):
     prepare_mxfp4_step(dims, cache, layer, T_before, k_new, v_new, q, sm_scale, out, workspace,
                        stream)()
+
+
+def kivi_time_next_decode(start=None, stop=None):
+    """Arm the calling thread's next decode-kernel launch to record two events (raw
+    hipEvent_t handles as ints, e.g. torch.cuda.Event(enable_timing=True).cuda_event
+    after a first record) at the kernel's own start and end; no arguments disarm."""
+    _check(_lib.kivi_time_next_decode(start, stop))
 
 
 def kivi_abi_version() -> int:

@@ -498,6 +498,18 @@ kivi_status kivi_mxfp4_append_decode(const kivi_mxfp4_dims* dims, const kivi_mxf
                                      float* out, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/* ==== Measurement aid ================================================================
+ * kivi_time_next_decode: arms the calling thread's next decode-kernel launch (by any
+ * kivi_*decode* call of any codec; an append launch that precedes it in the same call
+ * is not meant) to record start_event and stop_event, two hipEvent_t created by the
+ * caller on the launch's device, at the decode kernel's own start and end
+ * (hipExtLaunchKernel), so that hipEventElapsedTime(start, stop) is that kernel's
+ * duration without the dispatch around it.  The events belong to the caller; the
+ * library keeps the two handles until that launch only.  Both null disarms; exactly
+ * one null is KIVI_ERR_ARG.  Not for a stream that is being captured into a graph.
+ * Host-only; launches nothing. */
+kivi_status kivi_time_next_decode(void* start_event, void* stop_event);
+
 /* ABI version of this library (bumped on any incompatible change). */
 int32_t kivi_abi_version(void);
 

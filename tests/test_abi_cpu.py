@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert kv.kivi_abi_version() == 7
+    assert kv.kivi_abi_version() == 8
 
 
 def good_dims(**kw):
@@ -345,3 +345,12 @@ def test_value_token_window_is_refused_for_ragged_and_paged_calls():
     assert st == 2 and "VALUE_TOKEN_WINDOW" in msg, msg
     # the uniform calls accept it (sizes are the same as without it)
     assert kv.kivi_cache_sizes(d) == kv.kivi_cache_sizes(good_dims())
+
+
+def test_time_next_decode_arguments():
+    # host-only: the measurement aid takes both events or neither, and launches nothing
+    with pytest.raises(kv.KiviError, match="ARG"):
+        kv.kivi_time_next_decode(1, None)
+    with pytest.raises(kv.KiviError, match="ARG"):
+        kv.kivi_time_next_decode(None, 1)
+    kv.kivi_time_next_decode()
