@@ -211,14 +211,17 @@ def calibrate_copy():
 # persistent workgroup per CU with contiguous shares, and a few neighbours.
 READ_SHAPES = ((256, 1024, 8), (256, 512, 8), (256, 512, 16), (256, 1024, 4), (512, 512, 8),
                (1024, 256, 8))
-READ_SIZES_MB = (88, 177, 705, 1024, 4096)
+# MiB: the decode step's bytes per launch of each workload (84: 128k 2-bit, 149: 128k
+# 4-bit, 172: 32k, 340: 70B stream, 672: one 1M-token layer), then larger reads
+READ_SIZES_MB = (84, 149, 172, 340, 672, 1024, 4096)
 
 
 def read_ceiling():
-    """Best-of-5 HIP-event time of the plain streaming read (libkivi_readprobe.so, a
-    bench-only library) at the decode working-set sizes, for each launch shape in
-    READ_SHAPES; each timed read is of a slice that is not in the 256 MB last-level
-    cache.  The same launches under rocprofv3 give their kernel times."""
+    """Best-of-5 kernel time of the plain streaming read (libkivi_readprobe.so, a
+    bench-only library; HIP events that the launch records at the kernel's own start and
+    end, as for the decode's roofline) at the decode working-set sizes, for each launch
+    shape in READ_SHAPES; each timed read is of a slice that is not in the 256 MB
+    last-level cache."""
     import ctypes
 
     import torch
@@ -226,17 +229,18 @@ def read_ceiling():
     lib.kivi_probe_stream_read.restype = ctypes.c_int
     lib.kivi_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                           ctypes.c_size_t, ctypes.c_void_p]
+                                           ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]
     torch.cuda.set_device(0)
     total = 8 << 30
     buf = torch.ones(total // 4, dtype=torch.int32, device="cuda")
     sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def read(off, n, shape):
+    def read(off, n, shape, ev=(None, None)):
         wg, th, un = shape
         st = lib.kivi_probe_stream_read(buf.data_ptr() + off, n, wg, th, un, sink.data_ptr(),
-                                        sink.numel() * 4, stream.cuda_stream)
+                                        sink.numel() * 4, stream.cuda_stream, ev[0], ev[1])
         if st != 0:
             raise RuntimeError(f"kivi_probe_stream_read failed ({st})")
 
@@ -254,10 +258,10 @@ def read_ceiling():
                 o = (((s0 >> 30) + 4) % (total >> 30)) << 30
                 read(o, 1 << 30, (256, 1024, 8))
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                read(s0, n, shape)
+                a.record(stream)            # creates the events; the launch records them
                 b.record(stream)
-                b.synchronize()
+                read(s0, n, shape, (a.cuda_event, b.cuda_event))
+                torch.cuda.synchronize()
                 best = min(best, a.elapsed_time(b) / 1e3)
             per["x".join(map(str, shape))] = round(best * 1e6, 2)
         key = min(per, key=per.get)
@@ -269,7 +273,8 @@ def read_ceiling():
     print(json.dumps({"read_ceiling": res,
                       "kernel": "stream_read_kernel (persistent: workgroups x threads x loads "
                                 "in flight per lane, contiguous share per workgroup)",
-                      "timing": "HIP events, best of 5"}), flush=True)
+                      "timing": "kernel start/end events (hipExtLaunchKernel), best of 5"}),
+          flush=True)
 
 
 def prefill_bytes(w, T, S=0):

@@ -8,6 +8,7 @@
 // flight per iteration (the workgroup's U loads per lane cover U * threads * 16
 // contiguous bytes).  Each thread XORs what it read into one word of `sink`, so that
 // no load can be dropped.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,10 +43,13 @@ extern "C" {
 // Reads `bytes` (a multiple of 16) at `buf` (device, 16-byte aligned) with `workgroups`
 // workgroups of `threads` threads (a multiple of 64, at most 1024), `unroll` in {1, 2,
 // 4, 8, 16} loads per lane in flight; `sink` (device) must hold workgroups * threads
-// words.  Returns 0 when the launch was enqueued on `stream`, 1 for a bad argument, 2 for
-// a launch error.
+// words.  With start_event and stop_event (hipEvent_t, both or neither) the launch
+// records them at the kernel's own start and end (hipExtLaunchKernel).  Returns 0 when
+// the launch was enqueued on `stream`, 1 for a bad argument, 2 for a launch error.
 int kivi_probe_stream_read(const void* buf, size_t bytes, int workgroups, int threads, int unroll,
-                           void* sink, size_t sink_bytes, void* stream) {
+                           void* sink, size_t sink_bytes, void* stream, void* start_event,
+                           void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return 1;
   if (!buf || !sink || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
     return 1;
   if (workgroups < 1 || workgroups > 65536 || threads < 64 || threads > 1024 || threads % 64 != 0)
@@ -58,12 +62,20 @@ int kivi_probe_stream_read(const void* buf, size_t bytes, int workgroups, int th
   const uint4* p = static_cast<const uint4*>(buf);
   unsigned* k = static_cast<unsigned*>(sink);
   const dim3 g(workgroups), b(threads);
+  const hipEvent_t e0 = static_cast<hipEvent_t>(start_event);
+  const hipEvent_t e1 = static_cast<hipEvent_t>(stop_event);
+  auto launch = [&](auto kernel) {
+    if (e0)
+      hipExtLaunchKernelGGL(kernel, g, b, 0, s, e0, e1, 0, p, n16, share16, k);
+    else
+      hipLaunchKernelGGL(kernel, g, b, 0, s, p, n16, share16, k);
+  };
   switch (unroll) {
-    case 1: hipLaunchKernelGGL(stream_read_kernel<1>, g, b, 0, s, p, n16, share16, k); break;
-    case 2: hipLaunchKernelGGL(stream_read_kernel<2>, g, b, 0, s, p, n16, share16, k); break;
-    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, g, b, 0, s, p, n16, share16, k); break;
-    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, g, b, 0, s, p, n16, share16, k); break;
-    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, g, b, 0, s, p, n16, share16, k); break;
+    case 1: launch(stream_read_kernel<1>); break;
+    case 2: launch(stream_read_kernel<2>); break;
+    case 4: launch(stream_read_kernel<4>); break;
+    case 8: launch(stream_read_kernel<8>); break;
+    case 16: launch(stream_read_kernel<16>); break;
     default: return 1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 2;
