@@ -590,7 +590,18 @@ __device__ __forceinline__ void quantized_items(const DecodeArgs& a, int64_t pai
   pb.vc = make_rsrc(L.v_codes + sec * kc, kc);
   pb.vsc = make_rsrc(L.v_scale + sec * rows, rows * 2);
   pb.vze = make_rsrc(L.v_zero + sec * rows, rows * 2);
-  auto hist = [&](int64_t t) { return PAGED ? L.hist_token(b, t) : t; };
+  // (the page entry is read once per wave and made wave-uniform: b and t are, and a
+  // block base the compiler takes for a per-lane value turns every load of the loop,
+  // whose offsets carry it from block to block, into a loop over distinct lane values)
+  auto hist = [&](int64_t t) -> int64_t {
+    if constexpr (!PAGED) {
+      return t;
+    } else {
+      int64_t pg = __builtin_amdgcn_readfirstlane(L.table[b * L.pages_per_seq + (t >> L.page_log2)]);
+      pg = pg < 0 ? 0 : pg >= L.pages ? L.pages - 1 : pg;
+      return (pg << L.page_log2) + (t & ((int64_t(1) << L.page_log2) - 1));
+    }
+  };
   pb.off_k = 2 * lo * KB + j * (KB / 4);
   pb.off_v = j * D * VRB + 8 * lo * VRB;
   pb.off_ks = 16 * lo;
