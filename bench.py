@@ -192,6 +192,9 @@ def parse():
                         "and exit: the streaming-read rate this GPU reaches at each size")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
+    p.add_argument("--timeline", action="store_true",
+                   help="per-workgroup clock stamps of the decode kernel (libkivi_timeline.so) "
+                        "over back-to-back launches and launches with pauses, then exit")
     return p.parse_args()
 
 
@@ -275,6 +278,109 @@ def read_ceiling():
                                 "in flight per lane, contiguous share per workgroup)",
                       "timing": "kernel start/end events (hipExtLaunchKernel), best of 5"}),
           flush=True)
+
+
+def timeline(args):
+    """Where one decode launch's time goes and at what clock: the timeline build of the
+    library (libkivi_timeline.so, the same sources with KIVI_TIMELINE) has every workgroup
+    stamp the 100 MHz real-time counter and the shader clock counter when it starts, when
+    its blocks are done, when its arrival is counted and (last arriver) when the merge is
+    done.  On the workload's layer caches (rotated as in the benchmark) it runs 64 warmup
+    launches, then three series of 64: back to back, with 5 ms pauses, back to back.  Per
+    launch: the span from the first start to the last event, the start spread, blocks
+    done (first / median / last workgroup), arrival and merge times, all from the first
+    start, and the median over workgroups of the shader clock while streaming
+    (clock-counter ticks over real-time ticks between start and blocks done).  Prints one
+    JSON line of medians and per-launch series."""
+    import ctypes
+
+    import numpy as np
+    ROOT_LIB = os.path.join(ROOT, "bit_quantization_amd", "libkivi_timeline.so")
+    os.environ["KIVI_LIBRARY"] = ROOT_LIB         # read by the binding at import
+    import torch
+
+    import workloads as W
+    from bit_quantization_amd import kivi as k
+    if os.path.realpath(k.LIB_PATH) != os.path.realpath(ROOT_LIB):
+        raise RuntimeError("the timeline mode needs the binding to load libkivi_timeline.so")
+    lib = ctypes.CDLL(ROOT_LIB)
+    geo = (ctypes.c_int(), ctypes.c_int(), ctypes.c_int())
+    lib.kivi_timeline_geometry(*[ctypes.byref(x) for x in geo])
+    NS, NWG, NM = (x.value for x in geo)
+    torch.cuda.set_device(0)
+    w = W.get(args.workload).replace(layers=1)
+    dims = k.Dims(1, w.batch, w.kv_heads, w.q_heads, w.head_dim, w.bits, w.group_k,
+                  w.group_v, w.residual, w.max_tokens() + 64)
+    per_copy = decode_bytes(w, w.tokens + 1)
+    copies = args.copies or max(2, math.ceil(4 * MALL_BYTES / per_copy))
+    caches = []
+    for c in range(copies):
+        K, V = W.make_kv(w, c, device="cuda", total_tokens=w.tokens + 2)
+        cache = k.Cache(dims)
+        k.kivi_quantize_k(dims, cache, 0, K, w.tokens + 1, K.shape[2])
+        k.kivi_quantize_v(dims, cache, 0, V, w.tokens + 1, V.shape[2])
+        caches.append(cache)
+        del K, V
+    q = W.make_q(w, 0, 0, device="cuda")
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    T = w.tokens + 1
+    ws = k.new_workspace(dims, T)
+    n_split = k.kivi_decode_splits(dims, T)
+    nwg = w.batch * w.kv_heads * n_split
+    if nwg > NWG:
+        raise RuntimeError(f"{nwg} workgroups: the timeline build stamps at most {NWG}")
+    buf = np.zeros(NS * NWG * NM * 2, dtype=np.uint64)
+
+    def launch(i):
+        k.kivi_decode_attn(dims, caches[i % copies], 0, T, q, w.sm_scale, out, ws)
+
+    def series(pause):
+        for i in range(NS):
+            launch(i)
+            if pause:
+                torch.cuda.synchronize()
+                time.sleep(pause)
+        torch.cuda.synchronize()
+        if lib.kivi_timeline_read(buf.ctypes.data_as(ctypes.c_void_p), ctypes.c_size_t(buf.nbytes)):
+            raise RuntimeError("kivi_timeline_read failed")
+        A = buf.reshape(NS, NWG, NM, 2).astype(np.int64)[:, :nwg]
+        rows = []
+        for sl in range(NS):
+            a = A[sl]
+            rt = a[:, :, 0]
+            t0 = rt[:, 0].min()
+            us = lambda x: (x - t0) / 100.0
+            merged = rt[:, 3] > 0
+            arrived = rt[:, 2] > 0
+            end = max(rt[:, 1].max(), rt[arrived, 2].max() if arrived.any() else 0,
+                      rt[merged, 3].max() if merged.any() else 0)
+            clk = np.median((a[:, 1, 1] - a[:, 0, 1]) / np.maximum(rt[:, 1] - rt[:, 0], 1) * 100.0)
+            rows.append({"span_us": us(end), "start_spread_us": us(rt[:, 0].max()),
+                         "blocks_done_first_us": us(rt[:, 1].min()),
+                         "blocks_done_median_us": float(np.median(us(rt[:, 1]))),
+                         "blocks_done_last_us": us(rt[:, 1].max()),
+                         "arrival_median_us": (float(np.median(us(rt[arrived, 2])))
+                                               if arrived.any() else None),
+                         "arrival_last_us": us(rt[arrived, 2].max()) if arrived.any() else None,
+                         "merge_done_last_us": us(rt[merged, 3].max()) if merged.any() else None,
+                         "clock_mhz": float(clk)})
+        return rows
+
+    # clear the stamps of earlier launches, then warm up
+    for i in range(NS):
+        launch(i)
+    torch.cuda.synchronize()
+    res = {"timeline": args.workload, "workgroups": nwg, "n_split": n_split,
+           "layer_caches": copies, "series": {}}
+    for name, pause in (("back_to_back", 0), ("paused_5ms", 0.005), ("back_to_back_2", 0)):
+        rows = series(pause)
+        med = {key: round(float(np.median([r[key] for r in rows if r[key] is not None])), 2)
+               for key in rows[0]}
+        res["series"][name] = {"median": med,
+                               "span_us": [round(r["span_us"], 2) for r in rows],
+                               "clock_mhz": [round(r["clock_mhz"]) for r in rows]}
+        print(f"[timeline] {name}: {med}", file=sys.stderr, flush=True)
+    print(json.dumps(res), flush=True)
 
 
 def prefill_bytes(w, T, S=0):
@@ -568,6 +674,9 @@ def main():
         return
     if args.read_ceiling:
         read_ceiling()
+        return
+    if args.timeline:
+        timeline(args)
         return
     if args.codec != "kivi":
         fp8_main(args)

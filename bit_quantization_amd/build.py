@@ -3,6 +3,8 @@
 ``libkivi.so``: the sources listed in SOURCES (the C ABI and its kernels).
 ``libkivi_readprobe.so``: the plain streaming read the benchmark compares the decode
 with (``csrc/bench/``); not part of the method and not loaded by the package.
+``libkivi_timeline.so``: libkivi.so's sources built with KIVI_TIMELINE, whose decode
+kernel stamps per-workgroup clocks (``bench.py --timeline``); never the product.
 Run as ``python bit_quantization_amd/build.py`` (by path: importing the package loads
 the library it builds).
 """
@@ -18,6 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libkivi.so")
 PROBE_LIB = os.path.join(HERE, "libkivi_readprobe.so")
+TIMELINE_LIB = os.path.join(HERE, "libkivi_timeline.so")
 
 SOURCES = ["kivi_api.cpp", "quantize.hip", "decode.hip", "fp8.hip", "mxfp4.hip"]
 PROBE_SOURCES = [os.path.join("bench", "read_probe.hip")]
@@ -47,13 +50,14 @@ def hipcc() -> str:
     return exe
 
 
-def _build(sources, lib, verbose):
+def _build(sources, lib, verbose, defines=()):
     srcs = []
     for name in sources:
         # every source compiles as HIP (the API file includes the HIP runtime headers)
         srcs += ["-x", "hip", os.path.join(CSRC, name)]
     tmp = lib + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-I", INCLUDE, "-I", CSRC,
+           *srcs, "-o", tmp]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -62,8 +66,10 @@ def _build(sources, lib, verbose):
 
 
 def build_library(verbose: bool = True) -> str:
-    """Build libkivi.so and the benchmark's read-probe library; returns libkivi.so's path."""
+    """Build libkivi.so and the benchmark's read-probe and timeline libraries; returns
+    libkivi.so's path."""
     _build(PROBE_SOURCES, PROBE_LIB, verbose)
+    _build(SOURCES, TIMELINE_LIB, verbose, defines=("KIVI_TIMELINE=1",))
     return _build(SOURCES, LIB, verbose)
 
 

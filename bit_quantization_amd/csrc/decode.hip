@@ -73,6 +73,7 @@ struct DecodeArgs {
   const __half* k_new;  // [P][D]: window row new_slot comes from here (new_slot >= 0)
   const __half* v_new;
   int new_slot;         // -1: every window row is read from the cache
+  int tl_slot;          // timeline slot of this launch (measurement build), else -1
   int64_t vt;           // per-token Value window, fused step: the history token whose
                         // Value leaves the window in this step (its row is new_slot);
                         // -1: none
@@ -1155,6 +1156,7 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   // the hardware's round-robin placement of workgroups on the 8 XCDs spreads each pair
   // over several of them (measured ~2% faster than keeping a pair on one XCD: the XCDs
   // stream at different rates); a ragged batch: ragged_assign
+  tl_stamp(args.tl_slot, 0);
   int64_t pair = blockIdx.x / args.nw, slot0;
   int s = (int)(blockIdx.x % args.nw);
   DecodeArgs a = args;
@@ -1232,13 +1234,14 @@ __global__ __launch_bounds__(256 * waves_per_simd(BITS, GQA, G), 1) void decode_
   quantized_items<BITS, GQA, G, PAGED>(a, pair, item, n_res, n_items, b_lo, b_hi, &witems,
                                        wl[wave], reinterpret_cast<float*>(&wl[wave]));
   __syncthreads();
+  tl_stamp(a.tl_slot, 1);
 
   float* o = a.out + (b * a.L.H * GQA + h * GQA) * D;
   finish_pair<GQA, NTH, 2 * WAVES>(
       [&](int i) {
         return i < WAVES ? reinterpret_cast<const float*>(&wl[i]) : (const float*)comb[i - WAVES];
       },
-      parts, my, n_parts, a.counters + kCounterStride * pair, o, &comb[0][0]);
+      parts, my, n_parts, a.counters + kCounterStride * pair, o, &comb[0][0], a.tl_slot);
 }
 
 template <typename F>
@@ -1322,6 +1325,12 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
   a.v_new = new_row ? new_row->v : nullptr;
   a.new_slot = new_row ? new_row->slot : -1;
   a.vt = new_row ? new_row->vt : -1;
+#ifdef KIVI_TIMELINE
+  static int tl_launches = 0;                      // launch i stamps slot i mod kTlSlots
+  a.tl_slot = tl_launches++ % kTlSlots;
+#else
+  a.tl_slot = -1;
+#endif
   a.lens = lens;
   const int64_t P = (int64_t)L.B * L.H;
   const dim3 grid((unsigned)(P * plan.n_split));
@@ -1343,3 +1352,19 @@ hipError_t launch_decode(const LayerView& L, int q_heads, int64_t T, const __hal
 }
 
 }  // namespace kivi
+
+#ifdef KIVI_TIMELINE
+// Measurement build only: the stamps of the last kTlSlots launches, slot-major:
+// [slot][workgroup < kTlWgs][mark < kTlMarks][real-time counter, shader clock counter].
+extern "C" int kivi_timeline_read(void* host, size_t bytes) {
+  const size_t need = sizeof(kivi::g_timeline);
+  if (bytes < need) return 1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(kivi::g_timeline), need) == hipSuccess ? 0 : 2;
+}
+extern "C" int kivi_timeline_geometry(int* slots, int* wgs, int* marks) {
+  *slots = kivi::kTlSlots;
+  *wgs = kivi::kTlWgs;
+  *marks = kivi::kTlMarks;
+  return 0;
+}
+#endif

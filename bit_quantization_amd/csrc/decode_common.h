@@ -60,6 +60,29 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
                __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)));
 }
+// ---- timeline stamps (measurement build only) -----------------------------------------
+// With KIVI_TIMELINE defined (the benchmark's libkivi_timeline.so, never libkivi.so) the
+// decode kernel records, per launch slot and workgroup, the 100 MHz real-time counter
+// and the shader clock counter at: 0 start, 1 its blocks done (all waves), 2 its arrival
+// counted, 3 the merge done (last arriver only).  Otherwise the stamps compile to nothing.
+constexpr int kTlSlots = 64, kTlWgs = 1024, kTlMarks = 4;
+#ifdef KIVI_TIMELINE
+__device__ unsigned long long g_timeline[(size_t)kTlSlots * kTlWgs * kTlMarks * 2];
+__device__ __forceinline__ void tl_stamp(int slot, int mark) {
+  if (slot >= 0 && threadIdx.x == 0 && blockIdx.x < (unsigned)kTlWgs) {
+    const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long ck = __builtin_amdgcn_s_memtime();
+    const size_t o = (((size_t)slot * kTlWgs + blockIdx.x) * kTlMarks + mark) * 2;
+    if (mark == 0)                                 // the slot's older marks are cleared
+      for (int m = 1; m < kTlMarks; ++m) g_timeline[o + 2 * m] = g_timeline[o + 2 * m + 1] = 0;
+    g_timeline[o] = rt;
+    g_timeline[o + 1] = ck;
+  }
+}
+#else
+__device__ __forceinline__ void tl_stamp(int, int) {}
+#endif
+
 // LDS hand-off between lanes of one wave: LDS operations of a wave execute in order,
 // so only the compiler must be kept from moving LDS accesses across this point; the
 // wait covers LDS (lgkm) only and leaves prefetched global loads in flight.
@@ -267,7 +290,7 @@ __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_p
 template <int GQA, int NTH, int N, typename Src>
 __device__ __forceinline__ void finish_pair(Src rec, __amdgpu_buffer_rsrc_t parts, int my,
                                             int n_parts, unsigned* counter, float* out,
-                                            float* lds) {
+                                            float* lds, int tl_slot = -1) {
   __shared__ unsigned arrival;
   if (n_parts == 1) {
     combine<GQA, NTH, N>(
@@ -297,12 +320,14 @@ __device__ __forceinline__ void finish_pair(Src rec, __amdgpu_buffer_rsrc_t part
   if (threadIdx.x == 0)
     arrival = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+  tl_stamp(tl_slot, 2);
   if (arrival != (unsigned)(n_parts - 1)) return;
   // Last to arrive: other threads read this workgroup's own words back, so its stores
   // (issued an atomic round trip ago) must be complete first.
   wait_stores();
   __syncthreads();
   merge_pair<GQA, NTH>(parts, n_parts, out, lds);
+  tl_stamp(tl_slot, 3);
   if (threadIdx.x == 0)
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
