@@ -74,6 +74,19 @@
  * token T_q + i is in row i.  Prefill of T tokens gives the same bytes as T appends.
  * All sequences of a batch share T.
  *
+ * Value window (flags & KIVI_FLAG_VALUE_TOKEN_WINDOW; "4.4 KV Cache quantization" §3.2:
+ * each new Value enters the float16 window and pushes the oldest one out, which is
+ * quantized on its own): Keys keep the rule above, Values have a window of their own.
+ * After T tokens it holds the min(T, R) most recent Values, and the quantized Values
+ * are history tokens [0, T_qv(T)) with T_qv(T) = max(T - R, 0) <= T_q(T).  Value token
+ * i (T_qv <= i < T) sits in window row i mod R, the row of Key token i, so v_resid row
+ * i mod R holds Value i whether or not Key i is still in the window.  An append at
+ * T >= R first quantizes Value T - R (its G_v groups, the quantizer above) into
+ * history token T - R and then stores the new row.  A 16-token Value run fills token
+ * by token: codes of tokens not yet quantized are 0, their scale and zero rows untouched.
+ * Uniform batches in contiguous caches only (the ragged and paged calls return
+ * KIVI_ERR_UNSUPPORTED).
+ *
  * Grouped-query attention: query head j reads KV head j / (H_q / H_kv).
  */
 #ifndef KIVI_H
@@ -103,7 +116,7 @@ typedef enum kivi_status {
  * KIVI_FLAG_DETERMINISTIC: decode calls give the same output bits whenever they are
  *   repeated with the same arguments.  Every wave of a workgroup then takes a fixed
  *   round-robin share of the 64-token blocks instead of taking them from a queue as it
- *   runs (measured 1-4% slower per step on the 8B-shaped workloads).  Without it,
+ *   runs (measured 0-7% slower per step whole job, the 70B shape the most).  Without it,
  *   repeated calls agree to float32 rounding.
  * KIVI_FLAG_VALUE_TOKEN_WINDOW: the per-token Value window ("4.4 KV Cache quantization"
  *   §3.2: each new Value pushes the oldest one out, quantized on its own); see "Value
@@ -203,9 +216,13 @@ kivi_status kivi_append_flush(const kivi_dims* dims, const kivi_cache* cache, in
  * the query attends over history and window).  The result, and the cache it leaves,
  * equal kivi_append_flush(T_before, k_new, v_new) followed by
  * kivi_decode_attn(T = T_before + 1) (outputs to float32 rounding, as between any two
- * decode calls).  When r(T_before) < R this is one kernel launch: the attention
- * reads the new row from k_new / v_new and stores it into the window; when the
- * window is full it is the flush launch followed by the decode launch.
+ * decode calls; bit for bit with KIVI_FLAG_DETERMINISTIC).  When r(T_before) < R this
+ * is one kernel launch: the attention reads the new row from k_new / v_new and stores
+ * it into the window; when the window is full it is the flush launch followed by the
+ * decode launch.  With KIVI_FLAG_VALUE_TOKEN_WINDOW the decode launch also quantizes
+ * the Value that leaves the window (in the new row's window row, before the row takes
+ * the new token), except when that Value completes a 64-token block of the history:
+ * that step, like a flush step, is the append launch followed by the decode launch.
  *   Arguments as kivi_append_flush and kivi_decode_attn; the workspace must hold
  *   kivi_decode_workspace_bytes(dims, T_before + 1).
  * Every check of both calls runs before anything is enqueued. */
