@@ -41,14 +41,20 @@ if ROOT not in sys.path:
 METRIC = "quantized-KV decode attention: effective HBM GB/s & % of peak; tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20
-DECODE_SOURCE = os.path.join(ROOT, "bit_quantization_amd", "csrc", "decode.hip")
+# the decode kernel's sources: its file and the headers it includes
+DECODE_SOURCES = tuple(os.path.join(ROOT, "bit_quantization_amd", "csrc", n) for n in
+                       ("decode.hip", "decode_common.h", "quantizer.h", "kivi_internal.h"))
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic.json")
 
 
-def source_digest(path=DECODE_SOURCE):
+def source_digest(paths=DECODE_SOURCES):
+    """SHA-256 over the decode kernel's source files, in order."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
@@ -61,7 +67,7 @@ def measured_traffic(workload):
     except (OSError, ValueError):
         return None
     entry = rec.get("workloads", {}).get(workload)
-    if not entry or rec.get("decode_source_sha256") != source_digest():
+    if not entry or rec.get("decode_sources_sha256") != source_digest():
         return None
     return entry.get("traffic_bytes_per_launch")
 
@@ -284,14 +290,17 @@ def timeline(args):
     """Where one decode launch's time goes and at what clock: the timeline build of the
     library (libkivi_timeline.so, the same sources with KIVI_TIMELINE) has every workgroup
     stamp the 100 MHz real-time counter and the shader clock counter when it starts, when
-    its blocks are done, when its arrival is counted and (last arriver) when the merge is
-    done.  On the workload's layer caches (rotated as in the benchmark) it runs 64 warmup
-    launches, then three series of 64: back to back, with 5 ms pauses, back to back.  Per
-    launch: the span from the first start to the last event, the start spread, blocks
-    done (first / median / last workgroup), arrival and merge times, all from the first
-    start, and the median over workgroups of the shader clock while streaming
-    (clock-counter ticks over real-time ticks between start and blocks done).  Prints one
-    JSON line of medians and per-launch series."""
+    its blocks are done, when its arrival is counted and, in the last arriver, when its
+    own partial stores are complete, when the first round of partial loads is complete
+    and when the merge is done.  On the workload's layer caches (rotated as in the
+    benchmark) it runs 64 warmup launches, then three series of 64: back to back, with
+    5 ms pauses, back to back.  Per launch: the span from the first start to the last
+    event, the start spread, blocks done (first / median / last workgroup), arrival and
+    merge times, all from the first start; the last arrivers' median phases (arrival to
+    own stores complete, to partial loads complete, to merge done); and the median over
+    workgroups of the shader clock while streaming (clock-counter ticks over real-time
+    ticks between start and blocks done).  Prints one JSON line of medians and per-launch
+    series."""
     import ctypes
 
     import numpy as np
@@ -334,6 +343,12 @@ def timeline(args):
     def launch(i):
         k.kivi_decode_attn(dims, caches[i % copies], 0, T, q, w.sm_scale, out, ws)
 
+    def phase(rt, merged, m0, m1):
+        # median over a launch's last arrivers of the time from mark m0 to mark m1
+        if NM <= max(m0, m1) or not merged.any():
+            return None
+        return float(np.median(rt[merged, m1] - rt[merged, m0])) / 100.0
+
     def series(pause):
         for i in range(NS):
             launch(i)
@@ -363,6 +378,9 @@ def timeline(args):
                                                if arrived.any() else None),
                          "arrival_last_us": us(rt[arrived, 2].max()) if arrived.any() else None,
                          "merge_done_last_us": us(rt[merged, 3].max()) if merged.any() else None,
+                         "merger_stores_us": phase(rt, merged, 2, 4),
+                         "merger_loads_us": phase(rt, merged, 4, 5),
+                         "merger_fold_us": phase(rt, merged, 5, 3),
                          "clock_mhz": float(clk)})
         return rows
 

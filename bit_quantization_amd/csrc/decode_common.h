@@ -64,8 +64,10 @@ __device__ __forceinline__ float wave_max(float x) {
 // With KIVI_TIMELINE defined (the benchmark's libkivi_timeline.so, never libkivi.so) the
 // decode kernel records, per launch slot and workgroup, the 100 MHz real-time counter
 // and the shader clock counter at: 0 start, 1 its blocks done (all waves), 2 its arrival
-// counted, 3 the merge done (last arriver only).  Otherwise the stamps compile to nothing.
-constexpr int kTlSlots = 64, kTlWgs = 1024, kTlMarks = 4;
+// counted, and in the last arriver only 3 the merge done, 4 its own partial stores
+// complete (the merge begins) and 5 the first round of partial loads complete.
+// Otherwise the stamps compile to nothing.
+constexpr int kTlSlots = 64, kTlWgs = 1024, kTlMarks = 6;
 #ifdef KIVI_TIMELINE
 __device__ unsigned long long g_timeline[(size_t)kTlSlots * kTlWgs * kTlMarks * 2];
 __device__ __forceinline__ void tl_stamp(int slot, int mark) {
@@ -155,44 +157,42 @@ __device__ __forceinline__ void combine(Src src, Sink sink, SinkMl sink_ml) {
   }
 }
 
-// Final merge by the last workgroup of a pair to arrive, 32 (or 16) partials per
-// round.  A round's words count only when all carry the "written" mark; otherwise the
-// round is read again (a bounded wait: every other workgroup of the pair issued its
-// stores before it arrived, and this one waited for its own, so they become visible;
-// were the bound ever reached the output would be NaN).  Thread (head hd, channels
-// c, c+1) loads the accumulators of every partial of the round, all in flight
-// together; thread (partial u, head hd) loads that partial's (m, l) and, once the
-// round is complete, turns it into the partial's weight w = 2^(m - m*) and l w in LDS,
-// so the fold is multiply-adds only.  Indices past the last partial are clamped and
-// weighted 0, empty partials (l == 0) weigh 0, and rounds fold in split order with
-// an online rescale.
+// Final merge by the last workgroup of a pair to arrive, MC partials per round (the
+// round size is picked from the partial count, at most 32 / items per thread).  A
+// round's words count only when all carry the "written" mark; otherwise the round is
+// read again (a bounded wait: every other workgroup of the pair issued its stores
+// before it arrived, and this one waited for its own, so they become visible; were the
+// bound ever reached the output would be NaN).  A wave's items are the D / 2 channel
+// pairs of one head: lane (c / 2) loads the accumulators (c, c+1) of every partial of
+// the round, all in flight together, and lane u < MC also that partial's (m, l).  The
+// partial weights w_u = 2^(m_u - m*) are then found in registers (a wave maximum, one
+// exp2 per lane, a wave sum for l) and read lane by lane into the multiply-adds, with
+// no LDS tables.  Indices past the last partial are clamped and weighted 0, empty
+// partials (l == 0) weigh 0, and rounds fold in split order with an online rescale.
 constexpr int kMaxPolls = 1 << 20;
-template <int GQA, int NTH>
+template <int GQA, int NTH, int MC>
 __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_parts,
-                                           float* __restrict__ out, float* lds) {
+                                           float* __restrict__ out, int* vote, int tl_slot) {
   constexpr int ITEMS = GQA * (D / 2);
   constexpr int IPT = (ITEMS + NTH - 1) / NTH;     // (head, channel pair) items per thread
-  constexpr int MERGE_CH = 32 / IPT;               // partials per round
-  static_assert(MERGE_CH * GQA <= NTH, "one (m, l) load per thread and round");
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  float2* ml_lds = reinterpret_cast<float2*>(lds);                 // [GQA][MERGE_CH] (m, l)
-  float2* wl_lds = ml_lds + GQA * MERGE_CH;                        // [GQA][MERGE_CH] (w, l w)
-  float* alpha_lds = reinterpret_cast<float*>(wl_lds + GQA * MERGE_CH);   // [GQA]
-  int* vote = reinterpret_cast<int*>(alpha_lds + GQA);             // [3]
-  const bool loader = threadIdx.x < MERGE_CH * GQA;
-  const int lu = threadIdx.x / GQA, lh = threadIdx.x % GQA;        // loader's (partial, head)
-  float m_run = -INFINITY;                                         // loader's running max
-  float l[IPT], o0[IPT], o1[IPT];
+  static_assert(D / 2 == 64 && NTH % 64 == 0, "a wave's items are one head's channel pairs");
+  static_assert(MC <= 32 && MC * IPT <= 32, "loads in flight per thread");
+  const int lane = threadIdx.x & 63, c = 2 * lane;
+  float m_run[IPT], l[IPT], o0[IPT], o1[IPT];
 #pragma unroll
-  for (int it = 0; it < IPT; ++it) l[it] = o0[it] = o1[it] = 0.f;
+  for (int it = 0; it < IPT; ++it) {
+    m_run[it] = -INFINITY;
+    l[it] = o0[it] = o1[it] = 0.f;
+  }
   if (threadIdx.x < 3) vote[threadIdx.x] = 0;
   __syncthreads();
+  tl_stamp(tl_slot, 4);
   bool failed = false;
   int poll = 0;
-  for (int i0 = 0; i0 < n_parts; i0 += MERGE_CH) {
-    const int nc = n_parts - i0 < MERGE_CH ? n_parts - i0 : MERGE_CH;
-    float2 ov[IPT][MERGE_CH];
-    float2 ml = make_float2(-INFINITY, 0.f);
+  for (int i0 = 0; i0 < n_parts; i0 += MC) {
+    const int nc = n_parts - i0 < MC ? n_parts - i0 : MC;
+    float2 ov[IPT][MC];
+    float2 ml[IPT];
     for (;; ++poll) {
       // vote[poll % 3] collects this pass; vote[(poll + 1) % 3], last read two passes
       // ago, is cleared for the next one
@@ -201,25 +201,25 @@ __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_p
 #pragma unroll
       for (int it = 0; it < IPT; ++it) {
         const int idx = threadIdx.x + it * NTH;
-        const int hd = idx / (D / 2), c = 2 * (idx % (D / 2));
-        if (idx < ITEMS) {
+        const int hd = idx / (D / 2);
+        ml[it] = make_float2(-INFINITY, 0.f);
+        if (idx < ITEMS) {                           // the whole wave, or none of it
 #pragma unroll
-          for (int u = 0; u < MERGE_CH; ++u) {
+          for (int u = 0; u < MC; ++u) {
             const int i = min(i0 + u, n_parts - 1);
             const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
                 parts, ((i * GQA + hd) * PSTRIDE + c) * 4, 0, kCoherent);
             ov[it][u] = make_float2(unmarked(w.x), unmarked(w.y));
             stale |= (w.x & w.y & 1u) == 0u;
           }
+          if (lane < MC) {
+            const int i = min(i0 + lane, n_parts - 1);
+            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
+                parts, ((i * GQA + hd) * PSTRIDE + D) * 4, 0, kCoherent);
+            stale |= (w.x & w.y & 1u) == 0u;
+            if (lane < nc) ml[it] = make_float2(unmarked(w.x), unmarked(w.y));
+          }
         }
-      }
-      if (loader) {
-        const int i = min(i0 + lu, n_parts - 1);
-        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
-            parts, ((i * GQA + lh) * PSTRIDE + D) * 4, 0, kCoherent);
-        stale |= (w.x & w.y & 1u) == 0u;
-        ml = lu < nc ? make_float2(unmarked(w.x), unmarked(w.y)) : make_float2(-INFINITY, 0.f);
-        ml_lds[lh * MERGE_CH + lu] = ml;
       }
       if (stale) vote[poll % 3] = 1;
       __syncthreads();
@@ -232,51 +232,36 @@ __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_p
       __builtin_amdgcn_s_sleep(1);
     }
     ++poll;
-    // weights of the round's partials, one per loader thread
-    if (loader) {
-      const float4* mlp = reinterpret_cast<const float4*>(&ml_lds[lh * MERGE_CH]);
-      float mc = m_run;
-#pragma unroll
-      for (int u = 0; u < MERGE_CH; u += 2) {
-        const float4 q = mlp[u / 2];
-        mc = fmaxf(mc, q.y > 0.f ? q.x : -INFINITY);
-        mc = fmaxf(mc, q.w > 0.f ? q.z : -INFINITY);
-      }
-      const float mref = mc > -INFINITY ? mc : 0.f;
-      const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - mref) : 0.f;
-      wl_lds[lh * MERGE_CH + lu] = make_float2(w, ml.y * w);
-      if (lu == 0) alpha_lds[lh] = __builtin_amdgcn_exp2f(m_run - mref);
-      m_run = mc;
-    }
-    __syncthreads();
+    if (i0 == 0) tl_stamp(tl_slot, 5);
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
-      const int idx = threadIdx.x + it * NTH;
-      const int hd = min(idx / (D / 2), GQA - 1);
-      const float4* wlp = reinterpret_cast<const float4*>(&wl_lds[hd * MERGE_CH]);
-      const float al = alpha_lds[hd];
-      float lt = l[it] * al, a0 = o0[it] * al, a1 = o1[it] * al;
+      if (threadIdx.x + it * NTH >= ITEMS) continue;
+      const float mc = fmaxf(m_run[it], wave_max(ml[it].y > 0.f ? ml[it].x : -INFINITY));
+      const float mref = mc > -INFINITY ? mc : 0.f;
+      const float w = ml[it].y > 0.f ? __builtin_amdgcn_exp2f(ml[it].x - mref) : 0.f;
+      const int wb = __builtin_bit_cast(int, w);
+      // sum of l_u w_u over lanes 0 .. 31 (lanes from MC on hold 0)
+      const float lw = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, half_sum32(ml[it].y * w)), 0));
+      const float al = __builtin_amdgcn_exp2f(m_run[it] - mref);
+      m_run[it] = mc;
+      float a0 = o0[it] * al, a1 = o1[it] * al;
 #pragma unroll
-      for (int u = 0; u < MERGE_CH; u += 2) {
-        const float4 q = wlp[u / 2];
-        lt += q.y;
-        a0 = fmaf(ov[it][u].x, q.x, a0);
-        a1 = fmaf(ov[it][u].y, q.x, a1);
-        lt += q.w;
-        a0 = fmaf(ov[it][u + 1].x, q.z, a0);
-        a1 = fmaf(ov[it][u + 1].y, q.z, a1);
+      for (int u = 0; u < MC; ++u) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wb, u));
+        a0 = fmaf(ov[it][u].x, wu, a0);
+        a1 = fmaf(ov[it][u].y, wu, a1);
       }
-      l[it] = lt;
+      l[it] = fmaf(l[it], al, lw);
       o0[it] = a0;
       o1[it] = a1;
     }
-    __syncthreads();                                 // the LDS tables are rewritten next round
   }
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     const int idx = threadIdx.x + it * NTH;
     if (idx >= ITEMS) continue;
-    const int hd = idx / (D / 2), c = 2 * (idx % (D / 2));
+    const int hd = idx / (D / 2);
     const float inv = failed ? __builtin_nanf("") : 1.f / l[it];
     *reinterpret_cast<float2*>(out + (int64_t)hd * D + c) = make_float2(o0[it] * inv, o1[it] * inv);
   }
@@ -286,7 +271,7 @@ __device__ __forceinline__ void merge_pair(__amdgpu_buffer_rsrc_t parts, int n_p
 // output.  Otherwise the record goes to slot `my` of `parts` (marked, write-through,
 // nobody waits for it) and the workgroup counts its arrival on *counter; the last to
 // arrive waits for its own stores, merges every slot into `out` and resets the
-// counter.  `lds` holds the merge's tables (4 * 32 * GQA + GQA + 3 floats).
+// counter.  `lds` holds the merge's poll votes (3 words).
 template <int GQA, int NTH, int N, typename Src>
 __device__ __forceinline__ void finish_pair(Src rec, __amdgpu_buffer_rsrc_t parts, int my,
                                             int n_parts, unsigned* counter, float* out,
@@ -326,7 +311,14 @@ __device__ __forceinline__ void finish_pair(Src rec, __amdgpu_buffer_rsrc_t part
   // (issued an atomic round trip ago) must be complete first.
   wait_stores();
   __syncthreads();
-  merge_pair<GQA, NTH>(parts, n_parts, out, lds);
+  constexpr int MCMAX = 32 / ((GQA * (D / 2) + NTH - 1) / NTH);
+  int* vote = reinterpret_cast<int*>(lds);
+  if (n_parts <= 8)
+    merge_pair<GQA, NTH, (MCMAX < 8 ? MCMAX : 8)>(parts, n_parts, out, vote, tl_slot);
+  else if (n_parts <= 16)
+    merge_pair<GQA, NTH, (MCMAX < 16 ? MCMAX : 16)>(parts, n_parts, out, vote, tl_slot);
+  else
+    merge_pair<GQA, NTH, MCMAX>(parts, n_parts, out, vote, tl_slot);
   tl_stamp(tl_slot, 3);
   if (threadIdx.x == 0)
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
