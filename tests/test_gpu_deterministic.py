@@ -44,6 +44,8 @@ def bits_of(t):
     (2, 32, 32, 3, 1, 2, 999, 0, 5),       # a 32-token last block
     (2, 32, 128, 1, 2, 4, 3100, 1024, 0),  # 1024 sink rows: 36 window chunks over 8 waves
     (4, 32, 64, 1, 1, 1, 70, 6, 0),        # a few blocks, window-heavy
+    (2, 32, 64, 1, 2, 4, 5000, 0, 40),     # a merge of 40 partials in two rounds
+    (4, 64, 64, 1, 1, 8, 3000, 0, 37),     # 8 query heads: three rounds of up to 16
 ])
 def test_deterministic_decode_repeats_bits(bits, G, R, B, H, g, T, S, n_split):
     k = kv()

@@ -90,6 +90,7 @@ DECODE = [
     ("e4m3", 1, 1, 1, 1, 0), ("e4m3", 2, 3, 4, 1000, 0), ("e4m3", 2, 3, 4, 1000, 3),
     ("e4m3", 1, 2, 8, 777, 0), ("e4m3", 1, 1, 2, 33, 1), ("e5m2", 2, 2, 2, 1281, 0),
     ("e5m2", 1, 1, 8, 4096, 0), ("e5m2", 3, 1, 1, 96, 2), ("e4m3", 1, 8, 4, 20000, 0),
+    ("e4m3", 1, 2, 4, 4096, 40), ("e5m2", 1, 1, 8, 4096, 37),   # merges in several rounds
 ]
 
 

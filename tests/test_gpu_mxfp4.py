@@ -89,6 +89,7 @@ DECODE = [
     # B, H, g, T, n_split
     (1, 1, 1, 1, 0), (2, 3, 4, 1000, 0), (2, 3, 4, 1000, 3), (1, 2, 8, 777, 0), (1, 1, 2, 33, 1),
     (2, 2, 2, 1281, 0), (1, 1, 8, 4096, 0), (3, 1, 1, 96, 2), (1, 8, 4, 20000, 0),
+    (1, 2, 4, 4096, 40), (1, 1, 8, 4096, 37),   # merges in several rounds
 ]
 
 

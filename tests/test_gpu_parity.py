@@ -239,6 +239,51 @@ def test_decode_matches_oracle(bits, G, R, B, H, g, T, n_split):
     assert_close(out, ref, f"decode bits={bits} T={T} n_split={n_split}")
 
 
+# Explicit split counts around the merge's round sizes: rounds of 8, 16 or 32 partials
+# (16 at most with 8 query heads per KV head), so 9 and 17 partials take the larger
+# round with clamped, zero-weight slots, and 33 or more partials (17 or more at 8 query
+# heads) fold in several rounds with the online rescale between them.  Every count is
+# below the cap of one workgroup per 64-token block plus one.
+MERGE_ROUNDS = [
+    # bits, G, R, B, H, g, T, n_split
+    (2, 32, 64, 1, 2, 4, 5000, 9),
+    (2, 32, 64, 1, 2, 4, 5000, 17),
+    (2, 32, 64, 1, 2, 4, 5000, 33),
+    (2, 32, 64, 1, 2, 4, 5000, 64),
+    (4, 64, 64, 1, 1, 8, 3000, 17),
+    (4, 64, 64, 1, 1, 8, 3000, 40),
+    (2, 32, 128, 1, 1, 1, 4000, 50),
+    (2, 64, 128, 1, 2, 2, 4100, 37),
+]
+
+
+@pytest.mark.parametrize("bits,G,R,B,H,g,T,n_split", MERGE_ROUNDS)
+def test_decode_merge_rounds(bits, G, R, B, H, g, T, n_split):
+    d = 128
+    print(f"[parity] merge rounds bits={bits} G={G} R={R} B={B} H={H} g={g} T={T} "
+          f"n_split={n_split}", flush=True)
+    w = W.Workload("rounds", 94, 1, B, H, H * g, d, T, bits, G, d, R)
+    Tmax = w.max_tokens()
+    dims = dims_of(w, Tmax)
+    assert n_split <= (T - R) // 64 + 1
+    K, V = rand_kv(B, H, T, d, seed=T + n_split, scale=3.0)
+    K[:, :, :, 9] *= 20        # an outlier channel
+    # one strong key in the middle: the partials' maxima differ widely, so the weights
+    # and the rescale between rounds matter
+    K[:, :, T // 2 + 3] *= 6
+    cache = gpu_prefill(w, dims, K, V, T)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(T + n_split)
+    q = torch.randn((B, H * g, d), generator=gq, device="cuda").to(torch.float16)
+    sm = 1 / math.sqrt(d)
+    out, ws = gpu_decode(dims, cache, 0, T, q, sm, n_split)
+    assert int(torch.count_nonzero(ws[:B * H * 256])) == 0, "arrival counters not reset"
+    oc = O.LayerCache(B, H, d, bits, G, d, R, Tmax)
+    oc.prefill(K.cpu().numpy(), V.cpu().numpy())
+    ref = oc.attend(q.cpu().numpy(), sm)
+    assert_close(out, ref, f"merge rounds bits={bits} g={g} T={T} n_split={n_split}")
+
+
 @pytest.mark.parametrize("bits,G,R,g", [(2, 32, 64, 4), (4, 32, 32, 8), (2, 64, 128, 1)])
 def test_default_split_across_flushes_with_one_workspace(bits, G, R, g):
     """The fused step at every T from 2 to 700 with one workspace sized for the last
