@@ -194,8 +194,11 @@ def parse():
                    help="launch the timed steps one by one instead of as one HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--read-ceiling", action="store_true",
-                   help="time plain reads of the decode working-set sizes (torch reductions) "
-                        "and exit: the streaming-read rate this GPU reaches at each size")
+                   help="time plain reads of the decode working-set sizes (a persistent "
+                        "streaming-read kernel) and exit: the rate this GPU reaches at each size")
+    p.add_argument("--read-pattern", action="store_true",
+                   help="time the 2-bit decode's access pattern without its arithmetic, "
+                        "next to a plain read of the same bytes, and exit")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
     p.add_argument("--timeline", action="store_true",
@@ -225,21 +228,26 @@ READ_SHAPES = ((256, 1024, 8), (256, 512, 8), (256, 512, 16), (256, 1024, 4), (5
 READ_SIZES_MB = (84, 149, 172, 340, 672, 1024, 4096)
 
 
+def probe_library():
+    """libkivi_readprobe.so, the benchmark's reference reads (not part of libkivi.so)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_quantization_amd", "libkivi_readprobe.so"))
+    P, Z, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.kivi_probe_stream_read.restype = I
+    lib.kivi_probe_stream_read.argtypes = [P, Z, I, I, I, P, Z, P, P, P]
+    lib.kivi_probe_pattern_read.restype = I
+    lib.kivi_probe_pattern_read.argtypes = [P, Z, I, I, I, I, I, P, Z, P, P, P]
+    return lib
+
+
 def read_ceiling():
     """Best-of-5 kernel time of the plain streaming read (libkivi_readprobe.so, a
     bench-only library; HIP events that the launch records at the kernel's own start and
     end, as for the decode's roofline) at the decode working-set sizes, for each launch
     shape in READ_SHAPES; each timed read is of a slice that is not in the 256 MB
     last-level cache."""
-    import ctypes
-
     import torch
-    lib = ctypes.CDLL(os.path.join(ROOT, "bit_quantization_amd", "libkivi_readprobe.so"))
-    lib.kivi_probe_stream_read.restype = ctypes.c_int
-    lib.kivi_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                           ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
-                                           ctypes.c_void_p]
+    lib = probe_library()
     torch.cuda.set_device(0)
     total = 8 << 30
     buf = torch.ones(total // 4, dtype=torch.int32, device="cuda")
@@ -282,6 +290,77 @@ def read_ceiling():
     print(json.dumps({"read_ceiling": res,
                       "kernel": "stream_read_kernel (persistent: workgroups x threads x loads "
                                 "in flight per lane, contiguous share per workgroup)",
+                      "timing": "kernel start/end events (hipExtLaunchKernel), best of 5"}),
+          flush=True)
+
+
+# One decode step's quantized blocks at two workload shapes (the history's whole 64-token
+# blocks; the float16 window holds the rest): (workload, pairs, blocks per pair,
+# workgroups per pair as the decode plans them)
+PATTERN_SHAPES = (("llama8b_32k", 64, 510, 4), ("llama8b_128k_2bit", 8, 2046, 32))
+
+
+def read_pattern():
+    """The 2-bit decode's access pattern without its arithmetic (libkivi_readprobe.so,
+    kivi_probe_pattern_read): the bytes of one decode step of each PATTERN_SHAPES shape
+    (5376 B per 64-token block), read with the decode kernel's lane offsets from the six
+    arrays of the cache layout, or contiguously per block, with 1 to 3 blocks in flight per
+    wave; beside it the plain read of the same byte count (best launch shape of
+    READ_SHAPES).  Best-of-5 kernel-event times, each of a slice outside the last-level
+    cache after a 1 GiB read of another part."""
+    import torch
+    lib = probe_library()
+    torch.cuda.set_device(0)
+    total = 8 << 30
+    buf = torch.ones(total // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(n, launch):
+        slices = total // n
+        best = float("inf")
+        for rep in range(5):
+            s0 = ((rep * 3 + 1) % slices) * n
+            o = (((s0 >> 30) + 4) % (total >> 30)) << 30
+            if lib.kivi_probe_stream_read(buf.data_ptr() + o, 1 << 30, 256, 1024, 8,
+                                          sink.data_ptr(), sink.numel() * 4,
+                                          stream.cuda_stream, None, None):
+                raise RuntimeError("kivi_probe_stream_read failed")
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            st = launch(buf.data_ptr() + s0, a.cuda_event, b.cuda_event)
+            if st != 0:
+                raise RuntimeError(f"probe launch failed ({st})")
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) / 1e3)
+        return best * 1e6
+
+    res = {}
+    for name, pairs, blocks, nw in PATTERN_SHAPES:
+        n = pairs * blocks * 5376
+        plain = {}
+        for wg, th, un in READ_SHAPES:
+            plain["x".join(map(str, (wg, th, un)))] = round(timed(n, lambda p, e0, e1: (
+                lib.kivi_probe_stream_read(p, n, wg, th, un, sink.data_ptr(), sink.numel() * 4,
+                                           stream.cuda_stream, e0, e1))), 2)
+        best_plain = min(plain.values())
+        modes = {}
+        for fused in (0, 1):
+            for ahead in (1, 2, 3):
+                key = f"{'fused_blocks' if fused else 'six_arrays'}_ahead{ahead}"
+                modes[key] = round(timed(n, lambda p, e0, e1: (
+                    lib.kivi_probe_pattern_read(p, n, pairs, blocks, nw, ahead, fused,
+                                                sink.data_ptr(), sink.numel() * 4,
+                                                stream.cuda_stream, e0, e1))), 2)
+        res[name] = {"pairs": pairs, "blocks_per_pair": blocks, "workgroups_per_pair": nw,
+                     "bytes": n, "plain_read_us": best_plain, "plain_read_by_shape": plain,
+                     "pattern_us": modes,
+                     "pattern_over_plain": {k: round(v / best_plain, 3) for k, v in modes.items()}}
+        print(f"[pattern] {name}: plain {best_plain} us, {modes}", file=sys.stderr, flush=True)
+    print(json.dumps({"read_pattern": res,
+                      "kernel": "pattern_read_kernel (2-bit decode lane offsets, 8 waves per "
+                                "workgroup, a ring of register sets) and stream_read_kernel",
                       "timing": "kernel start/end events (hipExtLaunchKernel), best of 5"}),
           flush=True)
 
@@ -692,6 +771,9 @@ def main():
         return
     if args.read_ceiling:
         read_ceiling()
+        return
+    if args.read_pattern:
+        read_pattern()
         return
     if args.timeline:
         timeline(args)

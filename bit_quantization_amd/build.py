@@ -1,8 +1,9 @@
 """Build the HIP libraries in-tree for gfx950 with hipcc.
 
 ``libkivi.so``: the sources listed in SOURCES (the C ABI and its kernels).
-``libkivi_readprobe.so``: the plain streaming read the benchmark compares the decode
-with (``csrc/bench/``); not part of the method and not loaded by the package.
+``libkivi_readprobe.so``: the reference reads the benchmark compares the decode with, a
+plain streaming read and the decode's access pattern without its arithmetic
+(``csrc/bench/``); not part of the method and not loaded by the package.
 ``libkivi_timeline.so``: libkivi.so's sources built with KIVI_TIMELINE, whose decode
 kernel stamps per-workgroup clocks (``bench.py --timeline``); never the product.
 Run as ``python bit_quantization_amd/build.py`` (by path: importing the package loads
