@@ -105,6 +105,16 @@ def test_aging_decode_matches_oracle(bits, G, R, S, B, H, g, T, n_split):
                  f"aging decode T={T} n_split={n_split}")
 
 
+# split counts whose merge takes several rounds (32 partials a round, 16 with 8 query
+# heads per KV head)
+@pytest.mark.parametrize("bits,G,R,S,B,H,g,T,n_split", [
+    (2, 32, 128, 0, 1, 2, 4, 4000, 40),
+    (4, 32, 96, 7, 1, 1, 8, 3000, 36),
+])
+def test_aging_decode_merge_rounds(bits, G, R, S, B, H, g, T, n_split):
+    test_aging_decode_matches_oracle(bits, G, R, S, B, H, g, T, n_split)
+
+
 @pytest.mark.parametrize("bits,G,R,S,g", [(2, 32, 128, 0, 4), (4, 32, 64, 6, 2)])
 def test_aging_append_decode_matches_oracle(bits, G, R, S, g):
     # the fused step across group flushes and ring wraps, against the oracle at

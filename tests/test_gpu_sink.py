@@ -167,6 +167,16 @@ def test_sink_decode_matches_oracle(bits, G, R, S, B, H, g, T, n_split):
     assert_close(out.cpu().numpy(), ref, f"sink decode S={S} T={T} n_split={n_split}")
 
 
+# split counts whose merge takes several rounds (32 partials a round, 16 with 8 query
+# heads per KV head)
+@pytest.mark.parametrize("bits,G,R,S,B,H,g,T,n_split", [
+    (2, 32, 128, 1024, 1, 1, 4, 4000, 40),
+    (4, 32, 64, 7, 1, 2, 8, 3000, 35),
+])
+def test_sink_decode_merge_rounds(bits, G, R, S, B, H, g, T, n_split):
+    test_sink_decode_matches_oracle(bits, G, R, S, B, H, g, T, n_split)
+
+
 @pytest.mark.parametrize("bits,G,R,S,g", [(2, 32, 32, 5, 4), (4, 64, 64, 64, 2)])
 def test_sink_append_decode_matches_oracle(bits, G, R, S, g):
     # the fused step from inside the sink across the sink boundary and two flushes;

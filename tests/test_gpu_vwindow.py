@@ -180,6 +180,16 @@ def test_vwindow_decode_matches_oracle(bits, G, R, S, aging, B, H, g, T, n_split
                  f"vwindow decode T={T} n_split={n_split}")
 
 
+# split counts whose merge takes several rounds (32 partials a round, 16 with 8 query
+# heads per KV head)
+@pytest.mark.parametrize("bits,G,R,S,aging,B,H,g,T,n_split", [
+    (2, 32, 128, 0, "window", 2, 2, 4, 5000, 40),
+    (2, 32, 128, 0, "group", 1, 2, 8, 5003, 37),
+])
+def test_vwindow_decode_merge_rounds(bits, G, R, S, aging, B, H, g, T, n_split):
+    test_vwindow_decode_matches_oracle(bits, G, R, S, aging, B, H, g, T, n_split)
+
+
 @pytest.mark.parametrize("bits,G,R,aging,g,S", [
     (2, 32, 64, "window", 4, 0),
     (4, 64, 128, "group", 8, 0),
