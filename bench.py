@@ -375,11 +375,13 @@ def timeline(args):
     benchmark) it runs 64 warmup launches, then three series of 64: back to back, with
     5 ms pauses, back to back.  Per launch: the span from the first start to the last
     event, the start spread, blocks done (first / median / last workgroup), arrival and
-    merge times, all from the first start; the last arrivers' median phases (arrival to
-    own stores complete, to partial loads complete, to merge done); and the median over
-    workgroups of the shader clock while streaming (clock-counter ticks over real-time
-    ticks between start and blocks done).  Prints one JSON line of medians and per-launch
-    series."""
+    merge times, all from the first start; a workgroup's own stream time (start to blocks
+    done, median over workgroups); the last arrivers' median phases (arrival to own stores
+    complete, to partial loads complete, to merge done); and the median over workgroups
+    of the shader clock while streaming (clock-counter ticks over real-time ticks between
+    start and blocks done).  --n-split sets the workgroups per (sequence, KV head) pair
+    (at most one per 64-token block plus one).  Prints one JSON line of medians and
+    per-launch series."""
     import ctypes
 
     import numpy as np
@@ -412,15 +414,16 @@ def timeline(args):
     q = W.make_q(w, 0, 0, device="cuda")
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     T = w.tokens + 1
-    ws = k.new_workspace(dims, T)
-    n_split = k.kivi_decode_splits(dims, T)
+    ws = k.new_workspace(dims, T, args.n_split)
+    n_split = args.n_split or k.kivi_decode_splits(dims, T)
     nwg = w.batch * w.kv_heads * n_split
     if nwg > NWG:
         raise RuntimeError(f"{nwg} workgroups: the timeline build stamps at most {NWG}")
     buf = np.zeros(NS * NWG * NM * 2, dtype=np.uint64)
 
     def launch(i):
-        k.kivi_decode_attn(dims, caches[i % copies], 0, T, q, w.sm_scale, out, ws)
+        k.kivi_decode_attn(dims, caches[i % copies], 0, T, q, w.sm_scale, out, ws,
+                           n_split=args.n_split)
 
     def phase(rt, merged, m0, m1):
         # median over a launch's last arrivers of the time from mark m0 to mark m1
@@ -453,6 +456,7 @@ def timeline(args):
                          "blocks_done_first_us": us(rt[:, 1].min()),
                          "blocks_done_median_us": float(np.median(us(rt[:, 1]))),
                          "blocks_done_last_us": us(rt[:, 1].max()),
+                         "workgroup_stream_median_us": float(np.median(rt[:, 1] - rt[:, 0])) / 100.0,
                          "arrival_median_us": (float(np.median(us(rt[arrived, 2])))
                                                if arrived.any() else None),
                          "arrival_last_us": us(rt[arrived, 2].max()) if arrived.any() else None,

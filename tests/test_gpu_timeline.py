@@ -38,4 +38,5 @@ def test_timeline_stamps_are_ordered():
         phases = [m["merger_stores_us"], m["merger_loads_us"], m["merger_fold_us"]]
         assert all(p is not None and p >= 0 for p in phases)
         assert sum(phases) <= m["span_us"]
+        assert 0 < m["workgroup_stream_median_us"] <= m["blocks_done_last_us"]
         assert 500 < m["clock_mhz"] < 3000
