@@ -110,6 +110,8 @@ DECODE = [
     (4, 64, 128, 4, "window", 64, 2, [700, 3, 4, 131, 1301]),
     (2, 32, 128, 0, "group", 256, 8, [1000, 129, 97, 161]),
     (4, 32, 64, 7, "group", 128, 1, [7, 3000, 72]),
+    # one long sequence whose pairs merge in several rounds
+    (2, 32, 128, 0, "window", 128, 4, [20000, 100]),
 ]
 
 

@@ -99,6 +99,11 @@ DECODE = [
     (2, 32, 128, 0, "group", 8, [1000, 129, 97, 160, 161]),
     (4, 32, 64, 7, "group", 1, [7, 3000, 71, 72]),
     (2, 32, 128, 0, "window", 4, [4096, 1]),
+    # one long sequence: its pairs get 80 of the launch's workgroups (merged in rounds of
+    # 32), the short one 2
+    (2, 32, 128, 0, "window", 4, [20000, 100]),
+    # 8 query heads per KV head: the long sequence's pairs merge 60 partials in rounds of 16
+    (2, 32, 128, 0, "window", 8, [12000, 50, 3000]),
 ]
 
 
