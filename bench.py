@@ -172,6 +172,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sink", type=int, default=0,
                    help="attention-sink tokens kept in float16 at the start of each sequence")
+    p.add_argument("--device-lens", action="store_true",
+                   help="ragged or paged steps through kivi_append_decode_varlen (the flush "
+                        "launch on every step) instead of its host-length variant")
     p.add_argument("--ragged", action="store_true",
                    help="a ragged batch: sequence b holds tokens * (b + 1) / batch tokens")
     p.add_argument("--paged", type=int, default=0, metavar="P",
@@ -849,8 +852,10 @@ def main():
 
     def new_cache():
         return k.PagedCache(dims, paging) if paging else k.Cache(dims)
-    # per-sequence token counts before step j of a copy (ragged calls read them on the GPU)
+    # per-sequence token counts before step j of a copy (ragged calls read them on the GPU;
+    # the host copy lets a step without a flush skip the flush launch)
     lens_steps = torch.stack([base_t + j for j in range(steps_per_copy)]).contiguous()
+    lens_host = None if args.device_lens else lens_steps.cpu()
 
     def rows_from(X, j0, n):
         """X[b, :, base[b] + j0 + t] for t < n, as [n, B, H, d] (contiguous per step)."""
@@ -916,9 +921,9 @@ def main():
         q = qs[i % len(qs)]
         db, ab = step_bytes([t + j for t in base])
         if varlen:
-            call = k.prepare_append_decode_varlen(dims, caches[c], 0, lens_steps[j], T_before,
-                                                  kn[j], vn[j], q, w1.sm_scale, out, ws,
-                                                  paging=paging)
+            call = k.prepare_append_decode_varlen(
+                dims, caches[c], 0, lens_steps[j], T_before, kn[j], vn[j], q, w1.sm_scale, out,
+                ws, paging=paging, T_before_host=None if lens_host is None else lens_host[j])
         elif args.n_split:
             def call(c=c, T_before=T_before, T=T, kj=kn[j], vj=vn[j], q=q):
                 k.kivi_append_flush(dims, caches[c], 0, T_before, kj, vj)
@@ -954,8 +959,8 @@ def main():
     steps = [prepare(t_first + i) for i in range(args.steps)]
     # the decode kernel's bytes: a one-launch step's decode also appends (and, with the
     # per-token Value window, quantizes the leaving Value); a two-launch step's append
-    # kernel does that instead
-    kernel_bytes = [db + (0 if flushes[t_first + i] or args.n_split else ab)
+    # kernel does that instead, except in ragged steps, whose decode stores every new row
+    kernel_bytes = [db + (0 if (flushes[t_first + i] and not varlen) or args.n_split else ab)
                     for i, (_, db, ab) in enumerate(steps)]
     torch.cuda.synchronize()
     for i, (call, _, _) in enumerate(steps):
@@ -1085,7 +1090,11 @@ def main():
                              else "contiguous"),
                    "layer_caches": copies,
                    "n_split": n_split,
-                   "step": "append(+flush) + decode attention",
+                   "step": "append(+flush) + decode attention" + (
+                       "" if not varlen else
+                       "; lengths on the device only: flush launch every step"
+                       if args.device_lens else
+                       "; lengths also on the host: flush launch on flush steps only"),
                    "launch": "one HIP graph of the timed steps" if not args.no_graph
                              else "one call per step"},
         "tokens_per_s": round(w1.batch * args.steps / wall, 1),

@@ -957,12 +957,17 @@ kivi_status kivi_decode_attn_varlen(const kivi_dims* dims, const kivi_cache* cac
                        0, stream, lens, paging);
 }
 
-kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* cache,
-                                      const kivi_paging* paging, int32_t layer,
-                                      const int32_t* T_before, int64_t T_hi, const void* k_new,
-                                      const void* v_new, const void* q, float sm_scale,
-                                      float* out, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The ragged decode step.  host_lens, when given, is a host copy of T_before: a step in
+// which no sequence's window is full skips the flush launch, which would do nothing.
+kivi_status append_decode_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                 const kivi_paging* paging, int32_t layer, const int32_t* T_before,
+                                 const int32_t* host_lens, int64_t T_hi, const void* k_new,
+                                 const void* v_new, const void* q, float sm_scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   kivi_status st = check_lens(T_before);
   if (st != KIVI_OK) return st;
   st = check_common(dims, cache, layer);
@@ -976,18 +981,56 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
   st = decode_checks(dims, cache, layer, T_hi + 1, q, sm_scale, out, workspace, workspace_bytes,
                      0, &L, &plan, paging);
   if (st != KIVI_OK) return st;
+  bool flush_launch = true;
+  if (host_lens) {
+    flush_launch = false;
+    for (int b = 0; b < dims->batch; ++b) {
+      if (host_lens[b] < 0 || host_lens[b] > T_hi)
+        return fail(KIVI_ERR_ARG, "T_before_host entry outside [0, T_hi]");
+      if (kivi::plan_append(L, host_lens[b]).flush) flush_launch = true;
+    }
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const __half* kn = static_cast<const __half*>(k_new);
   const __half* vn = static_cast<const __half*>(v_new);
   const kivi::Lens ln{T_before, T_hi};
   // the sequences whose window is full flush first (the others' blocks return at once);
   // the decode launch then stores every new row and attends
-  hipError_t e = kivi::launch_append_flush(L, T_hi, kn, vn, ln, true, s);
-  if (e != hipSuccess) return device_status(e, "kivi_append_decode_varlen flush launch");
+  if (flush_launch) {
+    const hipError_t e = kivi::launch_append_flush(L, T_hi, kn, vn, ln, true, s);
+    if (e != hipSuccess) return device_status(e, "kivi_append_decode_varlen flush launch");
+  }
   const kivi::NewRow nr{kn, vn, kivi::plan_append(L, T_hi).slot};
-  e = kivi::launch_decode(L, dims->q_heads, T_hi + 1, static_cast<const __half*>(q), sm_scale,
-                          out, workspace, plan, &nr, ln, s);
+  const hipError_t e = kivi::launch_decode(L, dims->q_heads, T_hi + 1,
+                                           static_cast<const __half*>(q), sm_scale, out,
+                                           workspace, plan, &nr, ln, s);
   return device_status(e, "kivi_append_decode_varlen launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* cache,
+                                      const kivi_paging* paging, int32_t layer,
+                                      const int32_t* T_before, int64_t T_hi, const void* k_new,
+                                      const void* v_new, const void* q, float sm_scale,
+                                      float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return append_decode_varlen(dims, cache, paging, layer, T_before, nullptr, T_hi, k_new, v_new,
+                              q, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+kivi_status kivi_append_decode_varlen_host(const kivi_dims* dims, const kivi_cache* cache,
+                                           const kivi_paging* paging, int32_t layer,
+                                           const int32_t* T_before,
+                                           const int32_t* T_before_host, int64_t T_hi,
+                                           const void* k_new, const void* v_new, const void* q,
+                                           float sm_scale, float* out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (!T_before_host) return fail(KIVI_ERR_ARG, "T_before_host is NULL");
+  return append_decode_varlen(dims, cache, paging, layer, T_before, T_before_host, T_hi, k_new,
+                              v_new, q, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 const char* kivi_last_error(void) { return g_err; }
@@ -1002,6 +1045,6 @@ kivi_status kivi_time_next_decode(void* start_event, void* stop_event) {
   return KIVI_OK;
 }
 
-int32_t kivi_abi_version(void) { return 8; }
+int32_t kivi_abi_version(void) { return 9; }
 
 }  // extern "C"

@@ -30,6 +30,7 @@ EXPORTS = ("kivi_cache_sizes", "kivi_quantize_k", "kivi_quantize_v", "kivi_appen
            "kivi_quantize_k_varlen",
            "kivi_quantize_v_varlen",
            "kivi_append_flush_varlen", "kivi_decode_attn_varlen", "kivi_append_decode_varlen",
+           "kivi_append_decode_varlen_host",
            "kivi_fp8_cache_sizes",
            "kivi_fp8_quantize", "kivi_fp8_append", "kivi_fp8_decode_workspace_bytes",
            "kivi_fp8_decode_attn",
@@ -130,6 +131,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kivi_append_flush_varlen": (I32, [D, C, PG, I32, P, I64, P, P, P]),
         "kivi_decode_attn_varlen": (I32, [D, C, PG, I32, P, I64, P, F32, P, P, SZ, P]),
         "kivi_append_decode_varlen": (I32, [D, C, PG, I32, P, I64, P, P, P, F32, P, P, SZ, P]),
+        "kivi_append_decode_varlen_host": (I32, [D, C, PG, I32, P, P, I64, P, P, P, F32, P, P,
+                                                 SZ, P]),
         "kivi_fp8_cache_sizes": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(SZ)]),
         "kivi_fp8_quantize": (I32, [ctypes.POINTER(kivi_fp8_dims), ctypes.POINTER(kivi_fp8_cache),
                                     I32, P, P, I64, I64, P]),
@@ -387,6 +390,17 @@ def _lens(lens, dims):
     return _ptr(lens, torch.int32, "lens", dims.batch)
 
 
+def _host_lens(lens, dims):
+    """A host int32 [B] tensor's address (the library reads it during each call)."""
+    if not isinstance(lens, torch.Tensor):
+        raise TypeError("T_before_host must be a torch.Tensor")
+    if lens.is_cuda or lens.dtype != torch.int32 or not lens.is_contiguous():
+        raise ValueError("T_before_host must be a contiguous int32 CPU tensor")
+    if lens.numel() < dims.batch:
+        raise ValueError(f"T_before_host has {lens.numel()} elements, needs {dims.batch}")
+    return lens.data_ptr()
+
+
 def _paging(paging, dims):
     return None if paging is None else ctypes.byref(paging.c(dims))
 
@@ -440,19 +454,27 @@ def kivi_decode_attn_varlen(dims: Dims, cache: Cache, layer: int, lens: torch.Te
 def prepare_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
                                  T_hi: int, k_new, v_new, q: torch.Tensor, sm_scale: float,
                                  out: torch.Tensor, workspace: torch.Tensor, stream=None,
-                                 paging: Paging | None = None):
+                                 paging: Paging | None = None,
+                                 T_before_host: torch.Tensor | None = None):
     """kivi_append_decode_varlen with its arguments marshalled once (see
-    prepare_append_decode)."""
+    prepare_append_decode).  With T_before_host (a CPU int32 copy of T_before, read at
+    each call, so the caller may update it in place) the call is
+    kivi_append_decode_varlen_host, which skips the flush launch on steps without one."""
     need = dims.batch * dims.kv_heads * dims.head_dim
     nq = dims.batch * dims.q_heads * dims.head_dim
     pg = None if paging is None else paging.c(dims)    # kept alive by the closure
-    args = (ctypes.byref(dims.c()), ctypes.byref(cache.c()),
-            None if pg is None else ctypes.byref(pg), layer, _lens(T_before, dims), T_hi,
-            _ptr(k_new, torch.float16, "k_new", need), _ptr(v_new, torch.float16, "v_new", need),
-            _ptr(q, torch.float16, "q", nq), ctypes.c_float(sm_scale),
-            _ptr(out, torch.float32, "out", nq), _ptr(workspace, torch.uint8, "workspace"),
-            workspace.numel(), _stream(stream))
-    fn = _lib.kivi_append_decode_varlen
+    head = (ctypes.byref(dims.c()), ctypes.byref(cache.c()),
+            None if pg is None else ctypes.byref(pg), layer, _lens(T_before, dims))
+    tail = (T_hi, _ptr(k_new, torch.float16, "k_new", need),
+            _ptr(v_new, torch.float16, "v_new", need), _ptr(q, torch.float16, "q", nq),
+            ctypes.c_float(sm_scale), _ptr(out, torch.float32, "out", nq),
+            _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    if T_before_host is None:
+        args = head + tail
+        fn = _lib.kivi_append_decode_varlen
+    else:
+        args = head + (_host_lens(T_before_host, dims),) + tail
+        fn = _lib.kivi_append_decode_varlen_host
 
     def call():
         _check(fn(*args))
@@ -476,9 +498,10 @@ def kivi_append_decode_noalloc(dims: Dims, cache: Cache, layer: int, T_before: i
 def kivi_append_decode_varlen(dims: Dims, cache: Cache, layer: int, T_before: torch.Tensor,
                               T_hi: int, k_new, v_new, q: torch.Tensor, sm_scale: float,
                               out: torch.Tensor, workspace: torch.Tensor, stream=None,
-                              paging: Paging | None = None):
+                              paging: Paging | None = None,
+                              T_before_host: torch.Tensor | None = None):
     prepare_append_decode_varlen(dims, cache, layer, T_before, T_hi, k_new, v_new, q, sm_scale,
-                                 out, workspace, stream, paging)()
+                                 out, workspace, stream, paging, T_before_host)()
 
 
 def prepare_append_decode(dims: Dims, cache: Cache, layer: int, T_before: int, k_new, v_new,

@@ -331,6 +331,22 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
                                       const void* v_new, const void* q, float sm_scale,
                                       float* out, void* workspace, size_t workspace_bytes,
                                       void* stream);
+/* kivi_append_decode_varlen, also given T_before_host: a host copy of T_before
+ * (int32 [B], owned by the caller, read before the call returns).  A step in which no
+ * sequence's residual window is full (most steps: one in R, or one in G with group
+ * aging) runs as the decode launch alone; a step with a flush launches both, as
+ * kivi_append_decode_varlen does.  The host copy must equal the device one: when it
+ * does not, a flush that is due may be skipped and the cache no longer holds KIVI's
+ * state, but every access stays inside the cache, since the device lengths still drive
+ * the kernels.  Returns KIVI_ERR_ARG when T_before_host is NULL or an entry lies outside
+ * [0, T_hi], and otherwise the errors of kivi_append_decode_varlen. */
+kivi_status kivi_append_decode_varlen_host(const kivi_dims* dims, const kivi_cache* cache,
+                                           const kivi_paging* paging, int32_t layer,
+                                           const int32_t* T_before,
+                                           const int32_t* T_before_host, int64_t T_hi,
+                                           const void* k_new, const void* v_new, const void* q,
+                                           float sm_scale, float* out, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /* Workspace bytes kivi_decode_attn needs for T cached tokens (host-only).  The size
  * never falls as T grows, so a workspace sized for T serves every call at T or fewer

@@ -10,6 +10,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from tests.conftest import ROOT
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert kv.kivi_abi_version() == 8
+    assert kv.kivi_abi_version() == 9
 
 
 def good_dims(**kw):
@@ -354,3 +355,39 @@ def test_time_next_decode_arguments():
     with pytest.raises(kv.KiviError, match="ARG"):
         kv.kivi_time_next_decode(None, 1)
     kv.kivi_time_next_decode()
+
+
+def test_host_length_step_checks_its_host_copy():
+    # kivi_append_decode_varlen_host refuses a missing host copy and entries outside
+    # [0, T_hi] before it launches anything (fake device pointers, no GPU)
+    d = good_dims()
+    need = kv.kivi_decode_workspace_bytes(d, 301)
+    args = lambda host: (ctypes.byref(d.c()), ctypes.byref(fake_cache()), None, 0, FAKE, host,
+                         300, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, need, None)
+    st, msg = call("kivi_append_decode_varlen_host", *args(None))
+    assert st == 1 and "T_before_host" in msg, msg
+    for bad in ((0, 5, -1), (0, 301, 7)):
+        host = (ctypes.c_int32 * d.batch)(*bad)
+        st, msg = call("kivi_append_decode_varlen_host", *args(host))
+        assert st == 1 and "T_before_host" in msg, msg
+    # the checks shared with kivi_append_decode_varlen come first
+    host = (ctypes.c_int32 * d.batch)(0, 1, 2)
+    st, msg = call("kivi_append_decode_varlen_host", *args(host)[:4], None, host,
+                   *args(host)[6:])
+    assert st == 1 and "lens" in msg, msg
+    dw = good_dims(v_window="token")
+    st, msg = call("kivi_append_decode_varlen_host", ctypes.byref(dw.c()),
+                   *args(host)[1:])
+    assert st == 2 and "VALUE_TOKEN_WINDOW" in msg, msg
+
+
+def test_host_length_binding_takes_a_cpu_int32_tensor():
+    d = good_dims()
+    with pytest.raises(ValueError, match="CPU"):
+        kv._host_lens(torch.zeros(3, dtype=torch.int64), d)
+    with pytest.raises(ValueError, match="needs 3"):
+        kv._host_lens(torch.zeros(2, dtype=torch.int32), d)
+    with pytest.raises(TypeError):
+        kv._host_lens([0, 1, 2], d)
+    t = torch.zeros(3, dtype=torch.int32)
+    assert kv._host_lens(t, d) == t.data_ptr()

@@ -202,6 +202,51 @@ def test_varlen_append_decode_matches_oracle(aging, S):
     check_all(a, K, V, cur)
 
 
+@pytest.mark.parametrize("aging,S", [("window", 0), ("group", 5)])
+def test_host_length_step_matches_the_device_length_step(aging, S):
+    # kivi_append_decode_varlen_host (one launch on steps without a flush) against
+    # kivi_append_decode_varlen on a second cache, step by step through every sequence's
+    # flush: outputs to float32 rounding, caches bit-identical after each step.  The
+    # host copy is one CPU tensor updated in place between the calls of a prepared step.
+    k = kv()
+    bits, G, R, g = 2, 32, 64, 4
+    lens = [2, 70, 63, 64, 200, 31]
+    B, H = len(lens), 2
+    steps = R + G + 4
+    T_end = max(lens) + steps
+    dims = sink_dims(bits, G, 128, R, S, B, H, g, capacity(T_end, R), aging)
+    K, V = rand_kv(B, H, T_end, D, seed=17 + S)
+    a = varlen_prefill(dims, K, V, lens)
+    b_ = varlen_prefill(dims, K, V, lens)
+    wa = k.new_workspace(dims, T_end)
+    wb = k.new_workspace(dims, T_end)
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(12)
+    oa = torch.empty((B, H * g, D), dtype=torch.float32, device="cuda")
+    ob = torch.empty_like(oa)
+    host = torch.zeros(B, dtype=torch.int32)
+    cur = list(lens)
+    for step in range(steps):
+        q = torch.randn((B, H * g, D), generator=gq, device="cuda").to(torch.float16)
+        lt = lens_tensor(cur)
+        host.copy_(torch.tensor(cur, dtype=torch.int32))
+        kn = torch.stack([K[b, :, cur[b]] for b in range(B)]).contiguous()
+        vn = torch.stack([V[b, :, cur[b]] for b in range(B)]).contiguous()
+        k.prepare_append_decode_varlen(dims, a, 0, lt, max(cur), kn, vn, q, 0.09, oa, wa,
+                                       T_before_host=host)()
+        k.kivi_append_decode_varlen(dims, b_, 0, lt, max(cur), kn, vn, q, 0.09, ob, wb)
+        torch.cuda.synchronize()
+        assert np.allclose(oa.cpu().numpy(), ob.cpu().numpy(), rtol=1e-5, atol=1e-6), step
+        for name in k.BUFFERS:
+            assert torch.equal(a.view(name).cpu(), b_.view(name).cpu()), (step, name)
+        cur = [t + 1 for t in cur]
+    got = oa.cpu().numpy()
+    for b, T in enumerate(cur):
+        ref = seq_oracle(dims, K, V, b, T).attend(q[b:b + 1].cpu().numpy(), 0.09)
+        assert_close(got[b:b + 1], ref, f"host-length step, sequence {b}")
+    check_all(a, K, V, cur)
+
+
 def test_varlen_out_of_range_entries_stay_inside_the_cache():
     # entries beyond T_hi (or negative) are clamped on the device: the call completes
     # and the in-range sequences are unaffected
