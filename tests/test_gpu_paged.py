@@ -139,9 +139,12 @@ def test_paged_decode_matches_oracle(bits, G, R, S, aging, P, g, lens):
         assert_close(got[b:b + 1], ref, f"paged decode sequence {b} T={T}")
 
 
-def test_paged_append_decode_equals_contiguous():
+@pytest.mark.parametrize("host", [False, True])
+def test_paged_append_decode_equals_contiguous(host):
     # the fused ragged step on a paged cache against the same steps on a contiguous
-    # cache: outputs to float32 rounding, every sequence's history bytes identical
+    # cache: outputs to float32 rounding, every sequence's history bytes identical.
+    # host: the paged side steps through kivi_append_decode_varlen_host (a host copy of
+    # the counts; the flush launch only on the steps where some window is full)
     k = kv()
     bits, G, R, g, P = 2, 32, 64, 4, 64
     lens = [2, 70, 63, 64, 200]
@@ -168,7 +171,9 @@ def test_paged_append_decode_equals_contiguous():
         kn = torch.stack([K[b, :, cur[b]] for b in range(B)]).contiguous()
         vn = torch.stack([V[b, :, cur[b]] for b in range(B)]).contiguous()
         k.kivi_append_decode_varlen(dims, a, 0, lt, max(cur), kn, vn, q, 0.09, oa, wa,
-                                    paging=paging)
+                                    paging=paging,
+                                    T_before_host=torch.tensor(cur, dtype=torch.int32)
+                                    if host else None)
         k.kivi_append_decode_varlen(dims, b_, 0, lt, max(cur), kn, vn, q, 0.09, ob, wb)
         torch.cuda.synchronize()
         assert np.allclose(oa.cpu().numpy(), ob.cpu().numpy(), rtol=1e-5, atol=1e-6), step
