@@ -338,8 +338,10 @@ kivi_status kivi_append_decode_varlen(const kivi_dims* dims, const kivi_cache* c
  * kivi_append_decode_varlen does.  The host copy must equal the device one: when it
  * does not, a flush that is due may be skipped and the cache no longer holds KIVI's
  * state, but every access stays inside the cache, since the device lengths still drive
- * the kernels.  Returns KIVI_ERR_ARG when T_before_host is NULL or an entry lies outside
- * [0, T_hi], and otherwise the errors of kivi_append_decode_varlen. */
+ * the kernels.  The launches are chosen when the call is made: a call captured into a
+ * HIP graph replays the launches chosen at capture, so a graph serves only the step
+ * (counts) it was captured for.  Returns KIVI_ERR_ARG when T_before_host is NULL or an
+ * entry lies outside [0, T_hi], and otherwise the errors of kivi_append_decode_varlen. */
 kivi_status kivi_append_decode_varlen_host(const kivi_dims* dims, const kivi_cache* cache,
                                            const kivi_paging* paging, int32_t layer,
                                            const int32_t* T_before,
